@@ -1,0 +1,372 @@
+/*
+ * HHR decode-path ORACLE -- test infrastructure only.
+ *
+ * This file is a plain, slow, obviously-correct CPU statement of what the
+ * HHR decode path computes.  It exists to check the GPU library; nothing in
+ * the product may link, load or call it.  Only the test suite, the smoke
+ * entry point and the CPU-baseline leg of the benchmark use it.  It shares no
+ * source, header, table or helper with the GPU library.
+ *
+ * Sources (cited by page title and section; no formula survives on the
+ * pages, so every formula below is the plainest reading of the prose):
+ *   [ABS]  "HHR: Hierarchical Hash Retrieval for Efficient LLM Generation"
+ *          (arXiv 2610.01230), Abstract and the Chinese summary on the
+ *          modelscope paper card.
+ *   [FIG]  thelatestinai.com page on arXiv 2610.01230, "Figures & tables":
+ *          captions of Figure 2, Figure 3 and Figure 4; Appendix Table 4.
+ *   [BLOG] rit.work blog post on HHR (hhr-hash-retrieval-long-context),
+ *          sections "Почему расстояние Хэмминга пропускает важные ключи" and
+ *          "Два уровня маршрутизации решают разные ошибки".
+ *
+ * Precision rules (the pages fix none):
+ *   - Projections whose sign becomes a hash bit, and the rotated vectors that
+ *     feed the page metadata, use the "canonical chain": fp32 fused
+ *     multiply-add in ascending dimension order starting from +0.0f.  The
+ *     GPU takes the same integer decisions in the same precision.
+ *   - Page bounds are summed in fp64 in ascending dimension order; every
+ *     product of two fp32 numbers is exact in fp64.
+ *   - Attention is computed in fp64.
+ *
+ * Compile with -O2 -ffp-contract=off and without fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int32_t batch;      /* B                                   */
+    int32_t n_q_heads;  /* Hq                                  */
+    int32_t n_kv_heads; /* Hkv; Hq must be a multiple of Hkv    */
+    int32_t head_dim;   /* D                                   */
+    int32_t page_size;  /* P                                   */
+    int32_t hash_bits;  /* b, a multiple of 64                 */
+    int32_t max_ctx;    /* Tmax: row capacity of K, V, codes   */
+    int32_t kv_bf16;    /* 1: Q, K, V hold bf16 bit patterns (uint16); 0: fp32 */
+} oracle_dims;
+
+enum { ORACLE_OK = 0, ORACLE_BAD_DIMS = 1, ORACLE_NOMEM = 2 };
+
+static int dims_ok(const oracle_dims* d) {
+    if (d->batch < 1 || d->n_kv_heads < 1 || d->n_q_heads < d->n_kv_heads) return 0;
+    if (d->n_q_heads % d->n_kv_heads) return 0;
+    if (d->head_dim < 1 || d->page_size < 1 || d->max_ctx < 0) return 0;
+    if (d->hash_bits < 64 || d->hash_bits % 64) return 0;
+    return 1;
+}
+
+static int64_t n_pages_of(int64_t len, int64_t page) { return (len + page - 1) / page; }
+
+/* One element of a Q/K/V array, widened to fp32.  A bf16 value is the top
+ * half of an fp32 bit pattern, so widening it is exact. */
+static float elem(const void* base, int64_t i, int bf16) {
+    if (bf16) {
+        uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return f;
+    }
+    return ((const float*)base)[i];
+}
+
+/* Canonical chain: acc = +0; acc = fma(a[d], x[d], acc) for d ascending. */
+static float dot_canon(const float* a, const float* x, int n) {
+    float acc = 0.0f;
+    for (int d = 0; d < n; ++d) acc = fmaf(a[d], x[d], acc);
+    return acc;
+}
+
+/*
+ * Project one vector x (length D) of KV head h:
+ *   xrot[r] = (R_h x)_r            -- GKR's head-wise orthogonal transform [ABS]
+ *   bit j   = [ (W_h x)_j > 0 ]    -- LHP's head-wise projection, binarised [ABS]
+ * Bit j lives in word j/64 at bit position j%64 (least significant first).
+ * R is D x D row-major (xrot_r = sum_c R[r][c] x_c); W is b x D row-major.
+ */
+static void project(int D, int nbits, const float* R, const float* W, const float* x,
+                    float* xrot, uint64_t* code) {
+    if (xrot)
+        for (int r = 0; r < D; ++r) xrot[r] = dot_canon(R + (int64_t)r * D, x, D);
+    if (code) {
+        for (int w = 0; w < nbits / 64; ++w) code[w] = 0;
+        for (int j = 0; j < nbits; ++j) {
+            float y = dot_canon(W + (int64_t)j * D, x, D);
+            if (y > 0.0f) code[j / 64] |= (uint64_t)1 << (j % 64);
+        }
+    }
+}
+
+/* Public helper for the pins: project n vectors with one head's R and W. */
+int oracle_project(int32_t D, int32_t nbits, const float* R, const float* W, const float* X,
+                   int64_t n, float* Xrot, uint64_t* codes) {
+    if (D < 1 || nbits < 64 || nbits % 64) return ORACLE_BAD_DIMS;
+    for (int64_t i = 0; i < n; ++i)
+        project(D, nbits, R, W, X + i * D, Xrot ? Xrot + i * D : NULL,
+                codes ? codes + i * (nbits / 64) : NULL);
+    return ORACLE_OK;
+}
+
+/*
+ * Encode keys [start[b], start[b]+count[b]) of every sequence b.
+ *
+ * - codes[b][h][t][w] for t in that range: the LHP code of key t [ABS].
+ * - meta[b][h][p][r][0|1] = max|min over the keys t of page p (pages group P
+ *   adjacent keys [BLOG, "Два уровня..."]) of the rotated key (R_h k_t)_r,
+ *   for every page p the range touches, over that page's keys below
+ *   start+count.  These are the stored page bounds [BLOG, "Когда HHR...";
+ *   ABS].  A rotated value of -0 is taken as +0 so that max/min are unique.
+ * Layouts: K [B][Hkv][Tmax][D]; R [Hkv][D][D]; W [Hkv][b][D];
+ *          meta [B][Hkv][ceil(Tmax/P)][D][2] fp32; codes [B][Hkv][Tmax][b/64].
+ */
+int oracle_encode(const oracle_dims* dm, const void* K, const float* R, const float* W,
+                  const int32_t* start, const int32_t* count, float* meta, uint64_t* codes) {
+    if (!dims_ok(dm)) return ORACLE_BAD_DIMS;
+    const int B = dm->batch, Hkv = dm->n_kv_heads, D = dm->head_dim, P = dm->page_size;
+    const int nb = dm->hash_bits, NW = nb / 64;
+    const int64_t T = dm->max_ctx, NPmax = n_pages_of(T, P);
+    for (int b = 0; b < B; ++b)
+        if (start[b] < 0 || count[b] < 0 || (int64_t)start[b] + count[b] > T) return ORACLE_BAD_DIMS;
+    int status = ORACLE_OK;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            const int64_t s = start[b], e = (int64_t)start[b] + count[b];
+            if (e <= s) continue;
+            const float* Rh = R + (int64_t)h * D * D;
+            const float* Wh = W + (int64_t)h * nb * D;
+            float* x = malloc(sizeof(float) * D);
+            float* xr = malloc(sizeof(float) * D);
+            if (!x || !xr) {
+                free(x); free(xr);
+#pragma omp atomic write
+                status = ORACLE_NOMEM;
+                continue;
+            }
+            const int64_t kbase = ((int64_t)b * Hkv + h) * T;
+            for (int64_t p = s / P; p <= (e - 1) / P; ++p) {
+                float* m = meta + (((int64_t)b * Hkv + h) * NPmax + p) * D * 2;
+                const int64_t lo = p * P, hi = (p + 1) * P < e ? (p + 1) * P : e;
+                for (int64_t t = lo; t < hi; ++t) {
+                    for (int d = 0; d < D; ++d) x[d] = elem(K, (kbase + t) * D + d, dm->kv_bf16);
+                    project(D, nb, Rh, Wh, x, xr, t >= s ? codes + (kbase + t) * NW : NULL);
+                    for (int r = 0; r < D; ++r) {
+                        float v = xr[r] == 0.0f ? 0.0f : xr[r];
+                        if (t == lo || v > m[2 * r]) m[2 * r] = v;
+                        if (t == lo || v < m[2 * r + 1]) m[2 * r + 1] = v;
+                    }
+                }
+            }
+            free(x);
+            free(xr);
+        }
+    }
+    return status;
+}
+
+typedef struct { double s; int32_t p; } page_key;   /* order: s descending, then p ascending */
+typedef struct { int32_t h; int32_t t; } key_key;   /* order: h ascending, then t ascending  */
+
+static int cmp_page(const void* a, const void* b) {
+    const page_key* x = a; const page_key* y = b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->p > y->p) - (x->p < y->p);
+}
+static int cmp_key(const void* a, const void* b) {
+    const key_key* x = a; const key_key* y = b;
+    if (x->h != y->h) return (x->h > y->h) - (x->h < y->h);
+    return (x->t > y->t) - (x->t < y->t);
+}
+static int cmp_int(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * One decode step for one layer: every sequence b, every KV head h, with the
+ * G = Hq/Hkv query heads i = h*G .. h*G+G-1 that share KV head h.
+ *
+ * Steps, in the order the pages give them (coarse stage, then fine stage
+ * inside the surviving pages, then exact attention on the chosen keys)
+ * [ABS; BLOG, "Два уровня маршрутизации решают разные ошибки"]:
+ *  1. query prep: qrot_i = R_h q_i, code_q,i = LHP code of q_i.
+ *  2. page bound (GKR): U_i(p) = sum_r max(qrot_i,r * kmax[p][r],
+ *     qrot_i,r * kmin[p][r]) in fp64, r ascending.  It bounds qrot_i . krot_t
+ *     from above for every key t of page p; since R_h is orthogonal that is
+ *     q_i . k_t up to rounding [ABS; FIG, Figure 3].  The group shares one
+ *     selection, scored S(p) = max_i U_i(p).
+ *  3. page select: keep the `keep` pages with the largest S; equal S goes to
+ *     the lower page index.  keep = clamp(keep_pages[b], 1, min(NP, max_keep)).
+ *  4. candidates: keys t < L of the kept pages, ascending.
+ *  5. Hamming (LHP): H(t) = sum_i popcount(code_q,i XOR code_t), summed over
+ *     the group and over the code words [ABS; BLOG, "Почему расстояние..."].
+ *  6. key select (top-k): the k_eff = min(top_k, |C|) candidates with the
+ *     smallest (H, t); listed ascending, padded with -1 [FIG, Table 4 "Top-k"].
+ *  7. attention: out_i = softmax(scale * q_i . k_t) weighted sum of v_t over
+ *     the selected t, fp64; scale = 1/sqrt(D) when scale <= 0.
+ * An empty sequence (L = 0) yields out = 0, no pages, no keys.
+ *
+ * Outputs (any pointer may be NULL to skip it):
+ *   qrot  [B][Hq][D] fp32        code_q [B][Hq][b/64]
+ *   score [B][Hkv][NPmax] fp64   (+0.0 for p >= NP)
+ *   pages [B][Hkv][max_keep] int32 ascending, -1 padded; n_pages [B][Hkv]
+ *   ham   [B][Hkv][max_keep*P] uint16: H of candidate slot j*P + r = key
+ *         pages[j]*P + r; 0xFFFF where that key is >= L or the slot is unused
+ *   sel   [B][Hkv][top_k] int32 ascending, -1 padded; k_eff [B][Hkv]
+ *   out   [B][Hq][D] fp64
+ */
+int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const void* V,
+                  const float* R, const float* W, const float* meta, const uint64_t* codes,
+                  const int32_t* seq_len, const int32_t* keep_pages, int32_t max_keep,
+                  int32_t top_k, float scale_in,
+                  float* qrot_out, uint64_t* codeq_out, double* score_out,
+                  int32_t* pages_out, int32_t* npages_out, uint16_t* ham_out,
+                  int32_t* sel_out, int32_t* keff_out, double* out) {
+    if (!dims_ok(dm) || max_keep < 1 || top_k < 1) return ORACLE_BAD_DIMS;
+    const int B = dm->batch, Hq = dm->n_q_heads, Hkv = dm->n_kv_heads, G = Hq / Hkv;
+    const int D = dm->head_dim, P = dm->page_size, nb = dm->hash_bits, NW = nb / 64;
+    const int64_t T = dm->max_ctx, NPmax = n_pages_of(T, P);
+    const int bf = dm->kv_bf16;
+    const double scale = scale_in > 0.0f ? (double)scale_in : 1.0 / sqrt((double)D);
+    int status = ORACLE_OK;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_len[b];
+            if (L < 0) L = 0;
+            if (L > T) L = T;
+            const int64_t NP = n_pages_of(L, P);
+            const int64_t bh = (int64_t)b * Hkv + h;
+            const float* Rh = R + (int64_t)h * D * D;
+            const float* Wh = W + (int64_t)h * nb * D;
+
+            float* q = malloc(sizeof(float) * G * D);
+            float* qr = malloc(sizeof(float) * G * D);
+            uint64_t* cq = malloc(sizeof(uint64_t) * G * NW);
+            page_key* pk = malloc(sizeof(page_key) * (NP > 0 ? NP : 1));
+            int32_t* plist = malloc(sizeof(int32_t) * max_keep);
+            key_key* cand = malloc(sizeof(key_key) * (int64_t)max_keep * P);
+            int32_t* sel = malloc(sizeof(int32_t) * top_k);
+            double* sc = malloc(sizeof(double) * top_k);
+            if (!q || !qr || !cq || !pk || !plist || !cand || !sel || !sc) {
+                free(q); free(qr); free(cq); free(pk); free(plist); free(cand); free(sel); free(sc);
+#pragma omp atomic write
+                status = ORACLE_NOMEM;
+                continue;
+            }
+
+            /* 1. query prep */
+            for (int i = 0; i < G; ++i) {
+                const int64_t qi = (int64_t)b * Hq + h * G + i;
+                for (int d = 0; d < D; ++d) q[i * D + d] = elem(Q, qi * D + d, bf);
+                project(D, nb, Rh, Wh, q + i * D, qr + i * D, cq + i * NW);
+                if (qrot_out) memcpy(qrot_out + qi * D, qr + i * D, sizeof(float) * D);
+                if (codeq_out) memcpy(codeq_out + qi * NW, cq + i * NW, sizeof(uint64_t) * NW);
+            }
+
+            /* 2. page bounds */
+            for (int64_t p = 0; p < NP; ++p) {
+                const float* m = meta + (bh * NPmax + p) * D * 2;
+                double S = 0.0;
+                for (int i = 0; i < G; ++i) {
+                    double U = 0.0;
+                    for (int r = 0; r < D; ++r) {
+                        double a = (double)qr[i * D + r] * (double)m[2 * r];
+                        double c = (double)qr[i * D + r] * (double)m[2 * r + 1];
+                        U += a > c ? a : c;
+                    }
+                    if (i == 0 || U > S) S = U;
+                }
+                if (S == 0.0) S = 0.0; /* -0 and +0 are the same score */
+                pk[p].s = S;
+                pk[p].p = (int32_t)p;
+            }
+            if (score_out) {
+                for (int64_t p = 0; p < NPmax; ++p) score_out[bh * NPmax + p] = p < NP ? pk[p].s : 0.0;
+            }
+
+            /* 3. page select */
+            int64_t keep = keep_pages[b];
+            if (keep < 1) keep = 1;
+            if (keep > NP) keep = NP;
+            if (keep > max_keep) keep = max_keep;
+            qsort(pk, NP, sizeof(page_key), cmp_page);
+            for (int64_t j = 0; j < keep; ++j) plist[j] = pk[j].p;
+            qsort(plist, keep, sizeof(int32_t), cmp_int);
+            if (pages_out)
+                for (int64_t j = 0; j < max_keep; ++j) pages_out[bh * max_keep + j] = j < keep ? plist[j] : -1;
+            if (npages_out) npages_out[bh] = (int32_t)keep;
+
+            /* 4.-5. candidates and their Hamming distances */
+            int64_t nc = 0;
+            for (int64_t j = 0; j < (int64_t)max_keep * P && ham_out; ++j)
+                ham_out[bh * (int64_t)max_keep * P + j] = 0xFFFF;
+            for (int64_t j = 0; j < keep; ++j) {
+                for (int r = 0; r < P; ++r) {
+                    const int64_t t = (int64_t)plist[j] * P + r;
+                    if (t >= L) continue;
+                    int32_t H = 0;
+                    for (int i = 0; i < G; ++i)
+                        for (int w = 0; w < NW; ++w)
+                            H += __builtin_popcountll(cq[i * NW + w] ^ codes[(bh * T + t) * NW + w]);
+                    if (ham_out) ham_out[bh * (int64_t)max_keep * P + j * P + r] = (uint16_t)H;
+                    cand[nc].h = H;
+                    cand[nc].t = (int32_t)t;
+                    ++nc;
+                }
+            }
+
+            /* 6. key select */
+            const int64_t keff = nc < top_k ? nc : top_k;
+            qsort(cand, nc, sizeof(key_key), cmp_key);
+            for (int64_t j = 0; j < keff; ++j) sel[j] = cand[j].t;
+            qsort(sel, keff, sizeof(int32_t), cmp_int);
+            if (sel_out)
+                for (int64_t j = 0; j < top_k; ++j) sel_out[bh * top_k + j] = j < keff ? sel[j] : -1;
+            if (keff_out) keff_out[bh] = (int32_t)keff;
+
+            /* 7. attention over the selected keys */
+            if (out) {
+                for (int i = 0; i < G; ++i) {
+                    const int64_t qi = (int64_t)b * Hq + h * G + i;
+                    double* o = out + qi * D;
+                    for (int d = 0; d < D; ++d) o[d] = 0.0;
+                    if (keff == 0) continue;
+                    double mx = 0.0;
+                    for (int64_t j = 0; j < keff; ++j) {
+                        const int64_t row = (bh * T + sel[j]) * D;
+                        double s = 0.0;
+                        for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(K, row + d, bf);
+                        sc[j] = s * scale;
+                        if (j == 0 || sc[j] > mx) mx = sc[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < keff; ++j) {
+                        const double wgt = exp(sc[j] - mx);
+                        const int64_t row = (bh * T + sel[j]) * D;
+                        l += wgt;
+                        for (int d = 0; d < D; ++d) o[d] += wgt * (double)elem(V, row + d, bf);
+                    }
+                    for (int d = 0; d < D; ++d) o[d] /= l;
+                }
+            }
+            free(q); free(qr); free(cq); free(pk); free(plist); free(cand); free(sel); free(sc);
+        }
+    }
+    return status;
+}
+
+/* Threads an OpenMP region of this library will use. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

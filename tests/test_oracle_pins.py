@@ -1,0 +1,465 @@
+"""Pins of the CPU oracle against what the HHR pages and the mathematics fix.
+
+None of these checks retypes the oracle's code: each compares it with an
+independent statement -- a hand-worked example (tests/golden), a closed form,
+an invariant the pages state, a brute-force count, or a special case that
+reduces to a textbook routine (numpy lexsort, numpy softmax attention).
+Sources: "HHR: Hierarchical Hash Retrieval for Efficient LLM Generation",
+Abstract; rit.work HHR blog post, sections "Почему расстояние Хэмминга
+пропускает важные ключи" and "Два уровня маршрутизации решают разные
+ошибки"; thelatestinai.com page, Figure 3 caption and Appendix Table 4.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from synth import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_layer
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+U24 = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U24 / (1 - n * U24)
+
+
+def bits_of(codes):
+    """[..., W] uint64 -> [..., 64W] bool, bit j = bit j%64 of word j//64."""
+    c = np.asarray(codes, np.uint64)
+    j = np.arange(64, dtype=np.uint64)
+    b = ((c[..., None] >> j) & np.uint64(1)).astype(bool)
+    return b.reshape(*c.shape[:-1], c.shape[-1] * 64)
+
+
+def dims_for(o, wl: Workload):
+    return o.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits,
+                  wl.ctx, wl.dtype == "bf16")
+
+
+def f32(x, wl):
+    return bf16_bits_to_f32(x) if wl.dtype == "bf16" else np.asarray(x, np.float32)
+
+
+def run(o, wl, data, max_keep=None, top_k=None, keep=None, seq=None, scale=0.0):
+    dims = dims_for(o, wl)
+    seq = data["seq_len"] if seq is None else np.asarray(seq, np.int32)
+    meta, codes = o.encode(dims, data["K"], data["R"], data["W"], np.zeros(wl.batch, np.int32), seq)
+    mk = wl.max_keep if max_keep is None else max_keep
+    r = o.decode(dims, data["Q"], data["K"], data["V"], data["R"], data["W"], meta, codes, seq,
+                 data["keep"] if keep is None else keep, mk, wl.top_k if top_k is None else top_k, scale)
+    return dims, meta, codes, r
+
+
+SMALL = Workload("pin_small", 90, 2, 4, 2, 16, 96, 4, 64, 25, 16, "fp32")
+
+
+# ----------------------------------------------------------------------------- codes
+
+@pytest.mark.parametrize("D,nb", [(8, 64), (16, 128), (64, 64), (128, 128)])
+def test_codes_match_fp64_sign_within_rounding(oracle_mod, D, nb):
+    """sign(W x) with the canonical fp32 chain vs exact fp64: every disagreement is explained by
+    the fp32 rounding bound gamma_D * sum|W_jd x_d|."""
+    rng = np.random.default_rng(D * 1000 + nb)
+    R = np.eye(D, dtype=np.float32)
+    W = rng.standard_normal((nb, D)).astype(np.float32)
+    X = (rng.standard_normal((500, D)) * rng.lognormal(0, 1, D)).astype(np.float32)
+    _, codes = oracle_mod.project(R, W, X)
+    y64 = X.astype(np.float64) @ W.astype(np.float64).T
+    bound = gamma(D) * (np.abs(X.astype(np.float64)) @ np.abs(W.astype(np.float64)).T)
+    got = bits_of(codes)
+    want = y64 > 0
+    bad = (got != want) & (np.abs(y64) > bound)
+    assert not bad.any()
+    assert (got != want).mean() < 1e-3
+
+
+def test_code_bit_order_lsb_first(oracle_mod):
+    """W = diag(s), x = 1: bit j is set iff s_j > 0, in word j//64 at position j%64."""
+    D = 128
+    rng = np.random.default_rng(1)
+    s = np.where(rng.random(D) < 0.5, -1.0, 1.0).astype(np.float32)
+    W = np.diag(s).astype(np.float32)
+    _, codes = oracle_mod.project(np.eye(D, dtype=np.float32), W, np.ones((1, D), np.float32))
+    want0 = sum(1 << j for j in range(64) if s[j] > 0)
+    want1 = sum(1 << (j - 64) for j in range(64, 128) if s[j] > 0)
+    assert int(codes[0, 0]) == want0 and int(codes[0, 1]) == want1
+
+
+def test_code_identity_projection_is_sign_of_input(oracle_mod):
+    """W = I: bit j = [x_j > 0] exactly; zeros of either sign give 0."""
+    D = 64
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((50, D)).astype(np.float32)
+    X[0, :8] = 0.0
+    X[1, :8] = -0.0
+    _, codes = oracle_mod.project(np.eye(D, dtype=np.float32), np.eye(D, dtype=np.float32), X)
+    assert np.array_equal(bits_of(codes), X > 0)
+
+
+# ----------------------------------------------------------------------------- rotation
+
+def test_rotation_orientation_with_permutation(oracle_mod):
+    """R = permutation with R[r][perm[r]] = 1 gives xrot_r = x_perm[r] (catches a transposed R)."""
+    D = 16
+    perm = np.roll(np.arange(D), 3)  # not an involution
+    R = np.zeros((D, D), np.float32)
+    R[np.arange(D), perm] = 1.0
+    X = np.random.default_rng(3).standard_normal((10, D)).astype(np.float32)
+    xr, _ = oracle_mod.project(R, np.eye(64, D, dtype=np.float32), X)
+    assert np.array_equal(xr, X[:, perm])
+
+
+@pytest.mark.parametrize("D", [16, 64, 128])
+def test_rotation_preserves_logits(oracle_mod, D):
+    """Orthogonal R keeps q.k: |Rq.Rk - q.k| <= 1e-5 |q||k| (fp64 over the fp32 values)."""
+    rng = np.random.default_rng(D)
+    A = rng.standard_normal((D, D))
+    Qm, Rr = np.linalg.qr(A)
+    R = (Qm * np.sign(np.diag(Rr))).astype(np.float32)
+    X = (rng.standard_normal((200, D)) * rng.lognormal(0, 1, D)).astype(np.float32)
+    xr, _ = oracle_mod.project(R, np.eye(64, D, dtype=np.float32), X)
+    q, k = X[:100].astype(np.float64), X[100:].astype(np.float64)
+    qr, kr = xr[:100].astype(np.float64), xr[100:].astype(np.float64)
+    lhs = qr @ kr.T
+    rhs = q @ k.T
+    tol = 1e-5 * np.linalg.norm(q, axis=1)[:, None] * np.linalg.norm(k, axis=1)[None, :]
+    assert (np.abs(lhs - rhs) <= tol).all()
+
+
+def test_rotation_accuracy_against_fp64(oracle_mod):
+    """Each rotated coordinate is within gamma_D * sum|R x| of the exact fp64 product (no dropped term)."""
+    D = 128
+    rng = np.random.default_rng(5)
+    R = rng.standard_normal((D, D)).astype(np.float32)
+    X = rng.standard_normal((64, D)).astype(np.float32)
+    xr, _ = oracle_mod.project(R, np.eye(64, D, dtype=np.float32), X)
+    exact = X.astype(np.float64) @ R.astype(np.float64).T
+    bound = gamma(D) * (np.abs(X.astype(np.float64)) @ np.abs(R.astype(np.float64)).T)
+    assert (np.abs(xr - exact) <= bound).all()
+
+
+# ----------------------------------------------------------------------------- page metadata
+
+def test_meta_identity_rotation_is_raw_page_min_max(oracle_mod):
+    """R = I: meta is the textbook per-page per-channel max/min of the raw keys, partial page included."""
+    wl = SMALL.with_(batch=1, n_kv_heads=1, n_q_heads=2, ctx=90)
+    d = make_layer(wl)
+    d["R"] = np.broadcast_to(np.eye(wl.head_dim, dtype=np.float32), d["R"].shape).copy()
+    dims = dims_for(oracle_mod, wl)
+    L = 90
+    meta, _ = oracle_mod.encode(dims, d["K"], d["R"], d["W"], [0], [L])
+    K = f32(d["K"], wl)[0, 0]
+    for p in range(-(-L // wl.page_size)):
+        blk = K[p * wl.page_size:min((p + 1) * wl.page_size, L)]
+        assert np.array_equal(meta[0, 0, p, :, 0], blk.max(0))
+        assert np.array_equal(meta[0, 0, p, :, 1], blk.min(0))
+
+
+def test_meta_permutation_rotation(oracle_mod):
+    wl = SMALL.with_(batch=1, n_kv_heads=1, n_q_heads=1, ctx=32)
+    d = make_layer(wl)
+    D = wl.head_dim
+    perm = np.roll(np.arange(D), 5)
+    R = np.zeros((1, D, D), np.float32)
+    R[0, np.arange(D), perm] = 1.0
+    meta, _ = oracle_mod.encode(dims_for(oracle_mod, wl), d["K"], R, d["W"], [0], [32])
+    K = f32(d["K"], wl)[0, 0][:, perm]
+    for p in range(32 // wl.page_size):
+        blk = K[p * wl.page_size:(p + 1) * wl.page_size]
+        assert np.array_equal(meta[0, 0, p, :, 0], blk.max(0))
+        assert np.array_equal(meta[0, 0, p, :, 1], blk.min(0))
+
+
+@pytest.mark.parametrize("m", [1, 5, 37, 64])
+def test_encode_append_equals_single_shot(oracle_mod, m):
+    """Encoding [0,m) then [m,n) is bit-identical to encoding [0,n) (meta and codes)."""
+    wl = SMALL.with_(dtype="bf16")
+    d = make_layer(wl)
+    dims = dims_for(oracle_mod, wl)
+    n = 90
+    B = wl.batch
+    one_meta, one_codes = oracle_mod.encode(dims, d["K"], d["R"], d["W"], [0] * B, [n] * B)
+    meta, codes = oracle_mod.encode(dims, d["K"], d["R"], d["W"], [0] * B, [m] * B)
+    meta, codes = oracle_mod.encode(dims, d["K"], d["R"], d["W"], [m] * B, [n - m] * B, meta, codes)
+    npg = -(-n // wl.page_size)
+    assert np.array_equal(meta[:, :, :npg].view(np.uint32), one_meta[:, :, :npg].view(np.uint32))
+    assert np.array_equal(codes[:, :, :n], one_codes[:, :, :n])
+
+
+# ----------------------------------------------------------------------------- page bounds
+
+def _hand_case(o, case, keep=None):
+    D, P = case["head_dim"], case["page_size"]
+    Qv = np.array(case["queries"], np.float32)
+    Kv = np.array(case["keys"], np.float32)
+    G = Qv.shape[0]
+    T = Kv.shape[0]
+    L = case.get("length", T)
+    dims = o.Dims(1, G, 1, D, P, 64, T, False)
+    R = np.eye(D, dtype=np.float32)[None]
+    W = np.random.default_rng(0).standard_normal((1, 64, D)).astype(np.float32)
+    K = Kv[None, None]
+    V = np.ones_like(K)
+    meta, codes = o.encode(dims, K, R, W, [0], [L])
+    npg = -(-L // P)
+    kp = keep if keep is not None else case.get("keep", npg)
+    r = o.decode(dims, Qv[None], K, V, R, W, meta, codes, [L], [kp], npg, 4)
+    return meta, r
+
+
+def test_page_bound_hand_worked_examples(oracle_mod):
+    g = json.load(open(os.path.join(GOLDEN, "page_bound_hand.json")))
+    for case in g["cases"]:
+        meta, r = _hand_case(oracle_mod, case)
+        npg = len(case["scores"])
+        assert np.array_equal(meta[0, 0, :npg, :, 0], np.array(case["kmax"], np.float32)), case["name"]
+        assert np.array_equal(meta[0, 0, :npg, :, 1], np.array(case["kmin"], np.float32)), case["name"]
+        assert np.array_equal(r["score"][0, 0, :npg], np.array(case["scores"])), case["name"]
+        if "pages" in case:
+            assert list(r["pages"][0, 0, :len(case["pages"])]) == case["pages"], case["name"]
+
+
+@pytest.mark.parametrize("G,P", [(1, 1), (4, 4), (7, 16), (2, 3)])
+def test_page_bound_is_upper_bound_of_every_logit(oracle_mod, G, P):
+    """S(p) >= max over the page's keys and the group's heads of qrot.krot (exact up to fp64 rounding),
+    and >= the raw logit q.k minus the rotation tolerance; with P = 1 it is equal to the max logit."""
+    wl = Workload("pin_ub", 91, 2, 2 * G, 2, 32, 200, P, 64, 30, 32, "bf16", outliers=2, ragged=(150, 200))
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d, max_keep=-(-200 // P))
+    Qf, Kf = f32(d["Q"], wl), f32(d["K"], wl)
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        for h in range(wl.n_kv_heads):
+            kr, _ = oracle_mod.project(d["R"][h], d["W"][h], Kf[b, h, :L])
+            qr = r["q_rot"][b, h * G:(h + 1) * G].astype(np.float64)
+            lt = qr @ kr.astype(np.float64).T                          # [G][L] rotated logits
+            raw = Qf[b, h * G:(h + 1) * G].astype(np.float64) @ Kf[b, h, :L].astype(np.float64).T
+            qn = np.linalg.norm(Qf[b, h * G:(h + 1) * G].astype(np.float64), axis=1)[:, None]
+            kn = np.linalg.norm(Kf[b, h, :L].astype(np.float64), axis=1)[None, :]
+            for p in range(-(-L // P)):
+                sl = slice(p * P, min((p + 1) * P, L))
+                S = r["score"][b, h, p]
+                mag = np.abs(qr) @ np.abs(kr[sl].astype(np.float64)).T
+                assert S >= lt[:, sl].max() - 1e-12 * mag.max()
+                assert S >= (raw[:, sl] - 1e-5 * qn * kn[:, sl]).max()
+                if P == 1:
+                    assert abs(S - lt[:, sl].max()) <= 1e-12 * mag.max()
+
+
+def test_page_select_is_lexsort_of_scores(oracle_mod):
+    """Kept pages = textbook lexsort by (-S, p), first keep, ascending."""
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    for h in range(wl.n_kv_heads):
+        S = r["score"][0, h, :wl.max_pages]
+        order = np.lexsort((np.arange(len(S)), -S))
+        want = np.sort(order[:d["keep"][0]])
+        assert np.array_equal(r["pages"][0, h, :len(want)], want)
+        assert (r["pages"][0, h, len(want):] == -1).all()
+        assert r["n_pages"][0, h] == len(want)
+
+
+def test_page_select_ties_go_to_lower_index(oracle_mod):
+    """Duplicate pages have equal bounds; the lower index wins the last slot."""
+    wl = SMALL.with_(batch=1, n_kv_heads=1, n_q_heads=2, ctx=64, page_size=4, dtype="fp32")
+    d = make_layer(wl)
+    K = d["K"]
+    dup = [3, 9, 12]
+    for p in dup[1:]:
+        K[0, 0, p * 4:(p + 1) * 4] = K[0, 0, dup[0] * 4:(dup[0] + 1) * 4]
+    K[0, 0, dup[0] * 4:(dup[0] + 1) * 4] *= 50.0
+    for p in dup[1:]:
+        K[0, 0, p * 4:(p + 1) * 4] = K[0, 0, dup[0] * 4:(dup[0] + 1) * 4]
+    d["Q"][0] = K[0, 0, dup[0] * 4][None, :]  # make those pages the top three
+    dims, meta, codes, r = run(oracle_mod, wl, d, keep=[2], max_keep=4)
+    S = r["score"][0, 0]
+    assert S[3] == S[9] == S[12] and S[3] == S.max()
+    assert list(r["pages"][0, 0, :2]) == [3, 9]
+
+
+def test_keep_is_clamped(oracle_mod):
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    npg = wl.max_pages
+    for keep, mk, want in [(0, 8, 1), (-5, 8, 1), (10**6, npg + 5, npg), (500, 8, 8)]:
+        _, _, _, r = run(oracle_mod, wl, d, keep=[keep], max_keep=mk)
+        assert (r["n_pages"] == want).all()
+
+
+# ----------------------------------------------------------------------------- Hamming + top-k
+
+def _vec_from_code(code: int, D: int):
+    return np.array([1.0 if (code >> j) & 1 else -1.0 for j in range(D)], np.float32)
+
+
+def test_hamming_and_topk_hand_worked(oracle_mod):
+    g = json.load(open(os.path.join(GOLDEN, "hamming_hand.json")))
+    D, P = g["head_dim"], g["page_size"]
+    qs = np.stack([_vec_from_code(int(c, 16), D) for c in g["query_codes"]])
+    ks = np.stack([_vec_from_code(int(c, 16), D) for c in g["key_codes"]])
+    G, T = len(qs), len(ks)
+    dims = oracle_mod.Dims(1, G, 1, D, P, 64, T, False)
+    eye = np.eye(D, dtype=np.float32)[None]
+    meta, codes = oracle_mod.encode(dims, ks[None, None], eye, eye, [0], [T])
+    assert [hex(int(c)) for c in codes[0, 0, :, 0]] == [hex(int(c, 16)) for c in g["key_codes"]]
+    for k, want in g["top_k"].items():
+        r = oracle_mod.decode(dims, qs[None], ks[None, None], ks[None, None], eye, eye, meta, codes,
+                              [T], [T // P], T // P, int(k))
+        assert list(r["ham"][0, 0, :T]) == g["distances"]
+        assert list(r["sel"][0, 0, :len(want)]) == want
+        assert r["k_eff"][0, 0] == len(want)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_hamming_is_brute_force_popcount(oracle_mod, name):
+    """H of each candidate = sum over heads and words of Python int.bit_count(code_q ^ code_t)."""
+    wl = WORKLOADS["tiny"] if name == "tiny" else Workload("pin_rag", 92, 3, 6, 2, 32, 300, 8, 128, 20, 40,
+                                                          "bf16", ragged=(100, 300))
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    G, P, Wd = wl.group, wl.page_size, wl.hash_bits // 64
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        for h in range(wl.n_kv_heads):
+            cq = [[int(r["code_q"][b, h * G + i, w]) for w in range(Wd)] for i in range(G)]
+            for j in range(r["n_pages"][b, h]):
+                p = r["pages"][b, h, j]
+                for rr in range(P):
+                    t = p * P + rr
+                    slot = r["ham"][b, h, j * P + rr]
+                    if t >= L:
+                        assert slot == 0xFFFF
+                        continue
+                    want = sum((cq[i][w] ^ int(codes[b, h, t, w])).bit_count() for i in range(G) for w in range(Wd))
+                    assert slot == want
+
+
+def test_key_select_is_lexsort(oracle_mod):
+    """Selected keys = textbook lexsort of candidates by (H, t), first k_eff, ascending."""
+    wl = Workload("pin_ks", 93, 2, 8, 2, 32, 512, 8, 64, 25, 60, "fp32", ragged=(300, 512))
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    P = wl.page_size
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        for h in range(wl.n_kv_heads):
+            n = r["n_pages"][b, h]
+            t = (r["pages"][b, h, :n, None] * P + np.arange(P)[None, :]).ravel()
+            H = r["ham"][b, h, :n * P].astype(np.int64)
+            ok = t < L
+            t, H = t[ok], H[ok]
+            order = np.lexsort((t, H))
+            keff = min(wl.top_k, len(t))
+            want = np.sort(t[order[:keff]])
+            assert r["k_eff"][b, h] == keff
+            assert np.array_equal(r["sel"][b, h, :keff], want)
+            assert (r["sel"][b, h, keff:] == -1).all()
+
+
+def test_zero_hash_projection_selects_first_candidates(oracle_mod):
+    """W = 0: every code is 0, every H is 0, so the first k_eff candidates (ascending) win."""
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    d["W"] = np.zeros_like(d["W"])
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    assert not codes.any() and not r["code_q"].any()
+    P = wl.page_size
+    for h in range(wl.n_kv_heads):
+        t = (r["pages"][0, h, :r["n_pages"][0, h], None] * P + np.arange(P)[None, :]).ravel()
+        assert np.array_equal(r["sel"][0, h], t[:wl.top_k])
+
+
+def test_topk_larger_than_candidates_pads(oracle_mod):
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d, keep=[3], max_keep=3, top_k=100)
+    assert (r["k_eff"] == 48).all()
+    assert (r["sel"][..., 48:] == -1).all() and (r["sel"][..., :48] >= 0).all()
+
+
+# ----------------------------------------------------------------------------- attention
+
+def test_attention_hand_worked(oracle_mod):
+    g = json.load(open(os.path.join(GOLDEN, "attention_hand.json")))
+    q = np.array([g["query"]], np.float32)
+    K = np.array(g["keys"], np.float32)[None, None]
+    V = np.array(g["values"], np.float32)[None, None]
+    dims = oracle_mod.Dims(1, 1, 1, 2, 1, 64, 2, False)
+    R = np.eye(2, dtype=np.float32)[None]
+    W = np.ones((1, 64, 2), np.float32)
+    meta, codes = oracle_mod.encode(dims, K, R, W, [0], [2])
+    r = oracle_mod.decode(dims, q[None], K, V, R, W, meta, codes, [2], [2], 2, 2, g["scale"])
+    assert np.abs(r["out"][0, 0] - np.array(g["out"])).max() <= g["tol"]
+
+
+def _softmax_attention(q, K, V, scale):
+    s = (K @ q) * scale
+    w = np.exp(s - s.max())
+    return (w[:, None] * V).sum(0) / w.sum()
+
+
+@pytest.mark.parametrize("name", ["tiny", "bf16_ragged"])
+def test_full_selection_equals_full_attention(oracle_mod, name):
+    """keep every page and top_k >= L: the method is exact softmax attention over all keys."""
+    wl = WORKLOADS["tiny"].with_(ctx=1024) if name == "tiny" else \
+        Workload("pin_full", 94, 2, 6, 3, 32, 300, 16, 64, 100, 300, "bf16", outliers=2, ragged=(1, 300))
+    d = make_layer(wl)
+    npg = wl.max_pages
+    dims, meta, codes, r = run(oracle_mod, wl, d, keep=[npg] * wl.batch, max_keep=npg, top_k=wl.ctx)
+    Qf, Kf, Vf = (f32(d[k], wl).astype(np.float64) for k in ("Q", "K", "V"))
+    G = wl.group
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        for i in range(wl.n_q_heads):
+            h = i // G
+            ref = _softmax_attention(Qf[b, i], Kf[b, h, :L], Vf[b, h, :L], 1 / np.sqrt(wl.head_dim))
+            assert np.abs(r["out"][b, i] - ref).max() <= 1e-9 * max(1.0, np.abs(ref).max())
+        assert (r["k_eff"][b] == L).all()
+
+
+def test_sparse_attention_uses_selected_keys(oracle_mod):
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    Qf, Kf, Vf = (np.asarray(d[k], np.float64) for k in ("Q", "K", "V"))
+    for i in range(wl.n_q_heads):
+        h = i // wl.group
+        s = r["sel"][0, h, :r["k_eff"][0, h]]
+        ref = _softmax_attention(Qf[0, i], Kf[0, h, s], Vf[0, h, s], 1 / np.sqrt(wl.head_dim))
+        assert np.abs(r["out"][0, i] - ref).max() <= 1e-9 * max(1.0, np.abs(ref).max())
+
+
+def test_empty_sequence(oracle_mod):
+    wl = WORKLOADS["tiny"].with_(batch=2)
+    d = make_layer(wl, lengths=[0, 100])
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    assert (r["out"][0] == 0).all() and (r["k_eff"][0] == 0).all() and (r["sel"][0] == -1).all()
+    assert (r["n_pages"][0] == 0).all() and (r["pages"][0] == -1).all()
+    for h in range(wl.n_kv_heads):
+        pg = r["pages"][1, h, :r["n_pages"][1, h]]
+        assert r["k_eff"][1, h] == sum(min(wl.page_size, 100 - p * wl.page_size) for p in pg) > 0
+
+
+def test_rows_past_length_are_ignored(oracle_mod):
+    wl = Workload("pin_poison", 95, 2, 4, 2, 32, 256, 16, 64, 50, 40, "bf16", ragged=(100, 200))
+    d = make_layer(wl)
+    _, m0, c0, r0 = run(oracle_mod, wl, d)
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        d["K"][b, :, L:] = f32_to_bf16_bits(np.full((wl.n_kv_heads, wl.ctx - L, wl.head_dim), 1e4, np.float32))
+        d["V"][b, :, L:] = d["K"][b, :, L:]
+    _, m1, c1, r1 = run(oracle_mod, wl, d)
+    for k in ("score", "pages", "ham", "sel", "out"):
+        assert np.array_equal(r0[k], r1[k]), k
+
+
+def test_planted_keys_are_retrieved(oracle_mod):
+    """Sanity (not parity): on the tiny workload every planted high-logit key is selected."""
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    for h in range(wl.n_kv_heads):
+        assert set(d["planted"][0, h]) <= set(r["sel"][0, h])
