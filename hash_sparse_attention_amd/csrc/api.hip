@@ -1,0 +1,352 @@
+// Host side of libhhr: argument validation, workspace layout, and the
+// extern "C" entry points declared in include/hhr.h.  Every check runs
+// before anything is enqueued; kernels run on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hhr_internal.h"
+
+namespace hhr {
+namespace {
+
+thread_local std::string g_last_error;
+
+hhr_status fail(hhr_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+hhr_status ok() {
+    g_last_error.clear();
+    return HHR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hhr_status make_shape(const hhr_dims* d, Shape& s) {
+    if (!d) return fail(HHR_E_NULL, "dims is NULL");
+    if (d->batch < 1) return fail(HHR_E_SHAPE, "batch must be >= 1 (got %d)", d->batch);
+    if (d->n_kv_heads < 1) return fail(HHR_E_SHAPE, "n_kv_heads must be >= 1 (got %d)", d->n_kv_heads);
+    if (d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads)
+        return fail(HHR_E_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", d->n_q_heads,
+                    d->n_kv_heads);
+    const int G = d->n_q_heads / d->n_kv_heads;
+    if (G > 8) return fail(HHR_E_UNSUPPORTED, "query heads per KV head must be <= 8 (got %d)", G);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(HHR_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+    if (d->hash_bits != 64 && d->hash_bits != 128)
+        return fail(HHR_E_UNSUPPORTED, "hash_bits must be 64 or 128 (got %d)", d->hash_bits);
+    if (d->page_size < 1 || d->page_size > 64 || (d->page_size & (d->page_size - 1)))
+        return fail(HHR_E_UNSUPPORTED, "page_size must be a power of two in 1..64 (got %d)", d->page_size);
+    if (d->max_ctx < 1 || d->max_ctx > (1 << 26))
+        return fail(HHR_E_SHAPE, "max_ctx must be in 1..2^26 (got %d)", d->max_ctx);
+    if (d->kv_dtype != HHR_F32 && d->kv_dtype != HHR_BF16)
+        return fail(HHR_E_DTYPE, "kv_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->kv_dtype);
+    s.B = d->batch;
+    s.Hq = d->n_q_heads;
+    s.Hkv = d->n_kv_heads;
+    s.G = G;
+    s.D = d->head_dim;
+    s.P = d->page_size;
+    s.NB = d->hash_bits;
+    s.NW = d->hash_bits / 64;
+    s.T = d->max_ctx;
+    s.NPmax = ((int64_t)s.T + s.P - 1) / s.P;
+    s.NPB = (s.NPmax + 63) / 64;
+    s.bf16 = d->kv_dtype == HHR_BF16;
+    return HHR_OK;
+}
+
+hhr_status check_ptr(const void* p, const char* name, size_t align = 16) {
+    if (!p) return fail(HHR_E_NULL, "%s is NULL", name);
+    if (!aligned(p, align)) return fail(HHR_E_ALIGN, "%s is not %zu-byte aligned", name, align);
+    return HHR_OK;
+}
+
+hhr_status check_sel(const Shape& s, int max_keep, int top_k) {
+    if (max_keep < 1 || max_keep > s.NPmax)
+        return fail(HHR_E_RANGE, "max_keep_pages must be in 1..%lld (got %d)", (long long)s.NPmax, max_keep);
+    if ((int64_t)max_keep * s.P > (1 << 26)) return fail(HHR_E_RANGE, "max_keep_pages * page_size too large");
+    if (top_k < 1 || top_k > (1 << 24)) return fail(HHR_E_RANGE, "top_k must be in 1..2^24 (got %d)", top_k);
+    return HHR_OK;
+}
+
+#define HHR_TRY(expr)                       \
+    do {                                    \
+        const hhr_status st_ = (expr);      \
+        if (st_ != HHR_OK) return st_;      \
+    } while (0)
+
+hhr_status hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(HHR_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return HHR_OK;
+}
+
+// Common front half of the decode step and its stages.
+hhr_status prepare(const hhr_dims* dims, int max_keep, int top_k, void* workspace, size_t ws_bytes,
+                   DecodeArgs& a) {
+    HHR_TRY(make_shape(dims, a.s));
+    HHR_TRY(check_sel(a.s, max_keep, top_k));
+    HHR_TRY(check_ptr(workspace, "workspace", 256));
+    a.max_keep = max_keep;
+    a.top_k = top_k;
+    a.lay = ws_layout(a.s, max_keep, top_k);
+    if (ws_bytes < a.lay.total)
+        return fail(HHR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, a.lay.total);
+    a.ws = static_cast<char*>(workspace);
+    a.sel = reinterpret_cast<int32_t*>(a.ws + a.lay.sel);
+    a.scale = 0.f;
+    a.Q = a.K = a.V = nullptr;
+    a.R = a.W = a.meta = nullptr;
+    a.codes = nullptr;
+    a.seq_len = a.keep_pages = nullptr;
+    a.out = nullptr;
+    return HHR_OK;
+}
+
+float resolve_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)D); }
+
+}  // namespace
+
+WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
+    WsLayout l{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t BH = (size_t)s.B * s.Hkv, BQ = (size_t)s.B * s.Hq;
+    l.n_splits = (top_k + kAttnChunk - 1) / kAttnChunk;
+    l.q_rot = take(BQ * s.D * sizeof(float));
+    l.code_q = take(BQ * s.NW * sizeof(uint64_t));
+    l.q_split = take(BH * s.D * s.G * 2 * sizeof(double));
+    l.score = take(BH * (size_t)s.NPmax * sizeof(double));
+    l.pages = take(BH * (size_t)max_keep * sizeof(int32_t));
+    l.n_pages = take(BH * sizeof(int32_t));
+    l.ham = take(BH * (size_t)max_keep * s.P * sizeof(uint16_t));
+    l.sel = take(BH * (size_t)top_k * sizeof(int32_t));
+    l.k_eff = take(BH * sizeof(int32_t));
+    l.partial = take(BQ * (size_t)l.n_splits * (s.D + 2) * sizeof(float));
+    l.counters = take(BH * sizeof(uint32_t));
+    l.total = off;
+    return l;
+}
+
+}  // namespace hhr
+
+using namespace hhr;
+
+extern "C" {
+
+size_t hhr_meta_bytes(const hhr_dims* dims) {
+    Shape s;
+    if (make_shape(dims, s) != HHR_OK) return 0;
+    return (size_t)s.B * s.Hkv * (size_t)s.NPB * 64 * s.D * 2 * sizeof(float);
+}
+
+size_t hhr_codes_bytes(const hhr_dims* dims) {
+    Shape s;
+    if (make_shape(dims, s) != HHR_OK) return 0;
+    return (size_t)s.B * s.Hkv * (size_t)s.T * s.NW * sizeof(uint64_t);
+}
+
+hhr_status hhr_encode_cache(const hhr_dims* dims, const void* K, const float* R, const float* W,
+                            const int32_t* start, const int32_t* count, int32_t max_count, float* meta,
+                            uint64_t* codes, void* stream) {
+    Shape s;
+    HHR_TRY(make_shape(dims, s));
+    HHR_TRY(check_ptr(K, "K"));
+    HHR_TRY(check_ptr(R, "R"));
+    HHR_TRY(check_ptr(W, "W"));
+    HHR_TRY(check_ptr(start, "start", 4));
+    HHR_TRY(check_ptr(count, "count", 4));
+    HHR_TRY(check_ptr(meta, "meta"));
+    HHR_TRY(check_ptr(codes, "codes"));
+    if (max_count < 0 || max_count > s.T)
+        return fail(HHR_E_RANGE, "max_count must be in 0..max_ctx (got %d)", max_count);
+    if (max_count == 0) return ok();
+    HHR_TRY(hip_check(launch_encode(s, K, R, W, start, count, max_count, meta, codes,
+                                    static_cast<hipStream_t>(stream)),
+                      "encode launch"));
+    return ok();
+}
+
+size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, int32_t top_k) {
+    Shape s;
+    if (make_shape(dims, s) != HHR_OK || check_sel(s, max_keep_pages, top_k) != HHR_OK) return 0;
+    return ws_layout(s, max_keep_pages, top_k).total;
+}
+
+hhr_status hhr_decode_workspace_layout(const hhr_dims* dims, int32_t max_keep_pages, int32_t top_k,
+                                       hhr_workspace_layout* layout) {
+    Shape s;
+    HHR_TRY(make_shape(dims, s));
+    HHR_TRY(check_sel(s, max_keep_pages, top_k));
+    if (!layout) return fail(HHR_E_NULL, "layout is NULL");
+    const WsLayout l = ws_layout(s, max_keep_pages, top_k);
+    layout->q_rot = l.q_rot;
+    layout->code_q = l.code_q;
+    layout->q_split = l.q_split;
+    layout->score = l.score;
+    layout->pages = l.pages;
+    layout->n_pages = l.n_pages;
+    layout->ham = l.ham;
+    layout->sel = l.sel;
+    layout->k_eff = l.k_eff;
+    layout->partial = l.partial;
+    layout->counters = l.counters;
+    layout->total = l.total;
+    layout->n_splits = l.n_splits;
+    return ok();
+}
+
+hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, const void* V, const float* R,
+                           const float* W, const float* meta, const uint64_t* codes, const int32_t* seq_len,
+                           const int32_t* keep_pages, int32_t max_keep_pages, int32_t top_k, float softmax_scale,
+                           float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(Q, "Q"));
+    HHR_TRY(check_ptr(K, "K"));
+    HHR_TRY(check_ptr(V, "V"));
+    HHR_TRY(check_ptr(R, "R"));
+    HHR_TRY(check_ptr(W, "W"));
+    HHR_TRY(check_ptr(meta, "meta"));
+    HHR_TRY(check_ptr(codes, "codes"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    HHR_TRY(check_ptr(keep_pages, "keep_pages", 4));
+    HHR_TRY(check_ptr(out, "out"));
+    if (sel_idx) HHR_TRY(check_ptr(sel_idx, "sel_idx", 4));
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.R = R;
+    a.W = W;
+    a.meta = meta;
+    a.codes = codes;
+    a.seq_len = seq_len;
+    a.keep_pages = keep_pages;
+    a.out = out;
+    a.scale = resolve_scale(softmax_scale, a.s.D);
+    if (sel_idx) a.sel = sel_idx;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
+    HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
+    HHR_TRY(hip_check(launch_select_pages(a, st), "page-select launch"));
+    HHR_TRY(hip_check(launch_select_keys(a, st), "key-select launch"));
+    HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
+    return ok();
+}
+
+hhr_status hhr_stage_qprep(const hhr_dims* dims, const void* Q, const float* R, const float* W,
+                           int32_t max_keep_pages, int32_t top_k, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(Q, "Q"));
+    HHR_TRY(check_ptr(R, "R"));
+    HHR_TRY(check_ptr(W, "W"));
+    a.Q = Q;
+    a.R = R;
+    a.W = W;
+    HHR_TRY(hip_check(launch_qprep(a, static_cast<hipStream_t>(stream)), "qprep launch"));
+    return ok();
+}
+
+hhr_status hhr_stage_page_bounds(const hhr_dims* dims, const float* meta, const int32_t* seq_len,
+                                 int32_t max_keep_pages, int32_t top_k, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(meta, "meta"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    a.meta = meta;
+    a.seq_len = seq_len;
+    HHR_TRY(hip_check(launch_page_bounds(a, static_cast<hipStream_t>(stream)), "page-bound launch"));
+    return ok();
+}
+
+hhr_status hhr_stage_select_pages(const hhr_dims* dims, const int32_t* seq_len, const int32_t* keep_pages,
+                                  int32_t max_keep_pages, int32_t top_k, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    HHR_TRY(check_ptr(keep_pages, "keep_pages", 4));
+    a.seq_len = seq_len;
+    a.keep_pages = keep_pages;
+    HHR_TRY(hip_check(launch_select_pages(a, static_cast<hipStream_t>(stream)), "page-select launch"));
+    return ok();
+}
+
+hhr_status hhr_stage_select_keys(const hhr_dims* dims, const uint64_t* codes, const int32_t* seq_len,
+                                 int32_t max_keep_pages, int32_t top_k, int32_t* sel_idx, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(codes, "codes"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    if (sel_idx) HHR_TRY(check_ptr(sel_idx, "sel_idx", 4));
+    a.codes = codes;
+    a.seq_len = seq_len;
+    if (sel_idx) a.sel = sel_idx;
+    HHR_TRY(hip_check(launch_select_keys(a, static_cast<hipStream_t>(stream)), "key-select launch"));
+    return ok();
+}
+
+hhr_status hhr_stage_attend(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                            const int32_t* seq_len, int32_t max_keep_pages, int32_t top_k, float softmax_scale,
+                            const int32_t* sel_idx, float* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(Q, "Q"));
+    HHR_TRY(check_ptr(K, "K"));
+    HHR_TRY(check_ptr(V, "V"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    HHR_TRY(check_ptr(out, "out"));
+    if (sel_idx) HHR_TRY(check_ptr(sel_idx, "sel_idx", 4));
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.seq_len = seq_len;
+    a.out = out;
+    a.scale = resolve_scale(softmax_scale, a.s.D);
+    if (sel_idx) a.sel = const_cast<int32_t*>(sel_idx);
+    HHR_TRY(hip_check(launch_attend(a, true, static_cast<hipStream_t>(stream)), "attention launch"));
+    return ok();
+}
+
+const char* hhr_status_str(hhr_status st) {
+    switch (st) {
+        case HHR_OK: return "HHR_OK";
+        case HHR_E_NULL: return "HHR_E_NULL";
+        case HHR_E_SHAPE: return "HHR_E_SHAPE";
+        case HHR_E_DTYPE: return "HHR_E_DTYPE";
+        case HHR_E_ALIGN: return "HHR_E_ALIGN";
+        case HHR_E_WORKSPACE: return "HHR_E_WORKSPACE";
+        case HHR_E_RANGE: return "HHR_E_RANGE";
+        case HHR_E_UNSUPPORTED: return "HHR_E_UNSUPPORTED";
+        case HHR_E_HIP: return "HHR_E_HIP";
+    }
+    return "HHR_E_UNKNOWN";
+}
+
+const char* hhr_last_error(void) { return g_last_error.c_str(); }
+
+int32_t hhr_abi_version(void) { return HHR_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,247 @@
+/*
+ * hhr.h -- C ABI of the MI355X (gfx950) HHR decode-path library, libhhr.so.
+ *
+ * HHR (Hierarchical Hash Retrieval) selects, for each decode step, the keys a
+ * query attends to in two stages and then runs exact attention on them
+ * ("HHR: Hierarchical Hash Retrieval for Efficient LLM Generation", Abstract;
+ * rit.work HHR blog post, section "Два уровня маршрутизации решают разные
+ * ошибки"):
+ *   coarse  -- Geometry-Aware Key Routing (GKR): keys are rotated by a
+ *              per-KV-head orthogonal R_h, adjacent keys are grouped into
+ *              pages, each page stores per-dimension max/min of its rotated
+ *              keys, and a page whose logit upper bound is low is dropped;
+ *   fine    -- Learned Hash Projection (LHP): keys of the surviving pages are
+ *              ranked by the Hamming distance between sign(W_h q) and
+ *              sign(W_h k) bit codes and the top-k are kept;
+ *   attend  -- softmax attention of the query over the kept keys.
+ * R_h and W_h are inputs (learning them is outside this library).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer except `const hhr_dims*` and
+ *    the layout struct, which are host pointers.  The caller owns every
+ *    buffer; the library never allocates, frees or synchronizes, and it keeps
+ *    no state between calls except a thread-local error message.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.  Device faults surface at the
+ *    caller's next synchronization.
+ *  - All arguments are validated on the host before anything is enqueued.  On
+ *    failure nothing is enqueued, nothing is written, a nonzero hhr_status is
+ *    returned and hhr_last_error() describes it.  A failed launch returns
+ *    HHR_E_HIP with the HIP error text.
+ *  - Per-sequence values held in device arrays (start, count, seq_len,
+ *    keep_pages) are clamped inside the kernels so that no access leaves its
+ *    buffer: seq_len to [0, max_ctx]; start to [0, max_ctx]; count to
+ *    [0, min(max_count, max_ctx - start)].
+ *  - Inputs must not alias outputs.  Every array must be 16-byte aligned and
+ *    the workspace 256-byte aligned.  Non-finite inputs give undefined
+ *    (memory-safe) results.
+ *
+ * Dimensions (v1 limits)
+ * ----------------------
+ *   B  = batch >= 1                 Hkv = n_kv_heads >= 1
+ *   Hq = n_q_heads, G = Hq/Hkv in 1..8 (query head i uses KV head i/G)
+ *   D  = head_dim in {64, 128}      b   = hash_bits in {64, 128}, NW = b/64
+ *   P  = page_size, a power of two in 1..64;   T = max_ctx in 1..2^26 (row capacity)
+ *   NP(L) = ceil(L/P) pages of a sequence of length L; NPmax = NP(T);
+ *   NPB = ceil(NPmax/64) page blocks.
+ *
+ * Layouts (row-major, contiguous)
+ * -------------------------------
+ *   Q     [B][Hq][D]          kv_dtype (fp32, or bf16 bit patterns)
+ *   K, V  [B][Hkv][T][D]      kv_dtype
+ *   R     [Hkv][D][D]  fp32   rotated_r = sum_c R[h][r][c] * x_c
+ *   W     [Hkv][b][D]  fp32   bit j of a code = [ sum_c W[h][j][c] * x_c > 0 ]
+ *   codes [B][Hkv][T][NW] uint64; bit j of a code is bit j%64 of word j/64
+ *   meta  [B][Hkv][NPB][D/2][64][4] fp32, page-block interleaved: for page
+ *         p = 64*blk + lane and dimension pair (2e, 2e+1) the four floats are
+ *         (max_2e, min_2e, max_2e+1, min_2e+1) of the rotated keys of page p.
+ *         A wave of 64 lanes, one page each, reads one dimension pair of 64
+ *         pages as one contiguous 1 KiB span.
+ *   out   [B][Hq][D] fp32
+ *   sel_idx [B][Hkv][top_k] int32: the selected key positions, ascending,
+ *         padded with -1.
+ *
+ * Arithmetic (what makes codes and selections reproducible bit for bit)
+ * ---------------------------------------------------------------------
+ *   - A projection (rotation row or hash row) is the canonical chain
+ *     acc = +0.0f; for c = 0..D-1: acc = fmaf(M[r][c], x_c, acc)  (fp32, IEEE
+ *     round-to-nearest-even, denormals kept).  bf16 inputs widen exactly.
+ *   - A rotated key coordinate equal to -0 is stored as +0 before max/min.
+ *   - The page bound of query head i is
+ *       U_i(p) = sum over r ascending of max(qrot_i,r * kmax_r, qrot_i,r * kmin_r)
+ *     evaluated in fp64 (each product of two fp32 values is exact in fp64);
+ *     the score of the KV head's group is S(p) = max_i U_i(p), with -0 read
+ *     as +0.  The functional form is this library's reading of GKR's
+ *     page-level logit upper bound (the pages state none): it bounds
+ *     qrot_i . krot_t from above for every key t of the page, and an
+ *     orthogonal R_h keeps that equal to q_i . k_t up to rounding.
+ *   - The Hamming distance of key t is the sum over the group's query heads
+ *     and the code words of popcount(code_q XOR code_t).
+ *   - Attention accumulates in fp32 (online softmax over split chunks).
+ */
+#ifndef HHR_H
+#define HHR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HHR_ABI_VERSION 1
+
+typedef enum {
+    HHR_OK = 0,
+    HHR_E_NULL = 1,        /* a required pointer is NULL                    */
+    HHR_E_SHAPE = 2,       /* a dimension is out of range or inconsistent   */
+    HHR_E_DTYPE = 3,       /* unknown kv_dtype                              */
+    HHR_E_ALIGN = 4,       /* a pointer is not aligned as required          */
+    HHR_E_WORKSPACE = 5,   /* workspace smaller than required               */
+    HHR_E_RANGE = 6,       /* a scalar argument is out of range             */
+    HHR_E_UNSUPPORTED = 7, /* valid but not supported by this build         */
+    HHR_E_HIP = 8          /* a HIP launch failed                           */
+} hhr_status;
+
+typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
+
+typedef struct {
+    int32_t batch;      /* B                                              */
+    int32_t n_q_heads;  /* Hq                                             */
+    int32_t n_kv_heads; /* Hkv                                            */
+    int32_t head_dim;   /* D                                              */
+    int32_t page_size;  /* P                                              */
+    int32_t hash_bits;  /* b                                              */
+    int32_t max_ctx;    /* T: row capacity of K, V and codes              */
+    int32_t kv_dtype;   /* hhr_dtype of Q, K and V                        */
+} hhr_dims;
+
+/* Bytes of the meta and codes buffers for these dims (0 if the dims are invalid). */
+size_t hhr_meta_bytes(const hhr_dims* dims);
+size_t hhr_codes_bytes(const hhr_dims* dims);
+
+/*
+ * hhr_encode_cache -- GKR page metadata and LHP key codes
+ * ("HHR: Hierarchical Hash Retrieval for Efficient LLM Generation",
+ * Abstract; rit.work HHR blog post, sections "Два уровня маршрутизации
+ * решают разные ошибки" and "Когда HHR меняет планы запуска модели": the
+ * deployment stores page bounds).
+ *
+ * For every sequence b it encodes keys [s, e) with s = start[b] and
+ * e = s + count[b] (clamped as above; count[b] must not exceed max_count):
+ *   codes[b][h][t]  for t in [s, e): the LHP code of K[b][h][t];
+ *   meta of every page p with pP < e and (p+1)P > s: max/min over the keys
+ *   [pP, min((p+1)P, e)) of R_h K[b][h][t], recomputed from K, so a page
+ *   that straddles s includes the keys before s that K already holds.
+ * Encoding [0,m) and then [m,n) gives the same bits as encoding [0,n).
+ * Other parts of meta and codes are not touched.
+ *   K     device, read   R, W   device, read   start, count  device int32 [B]
+ *   max_count            host, >= 0 (0 enqueues nothing)
+ *   meta, codes          device, written (layouts above)
+ */
+hhr_status hhr_encode_cache(const hhr_dims* dims, const void* K, const float* R, const float* W,
+                            const int32_t* start, const int32_t* count, int32_t max_count,
+                            float* meta, uint64_t* codes, void* stream);
+
+/* Scratch the decode step needs for these arguments (0 if they are invalid). */
+size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, int32_t top_k);
+
+/*
+ * Byte offsets, inside the decode workspace, of the intermediate results the
+ * decode step leaves there (each region 256-byte aligned).  They stay valid
+ * until the next call that uses the same workspace, so a caller can inspect
+ * every stage of the last step:
+ *   q_rot   fp32   [B][Hq][D]      R_h q_i (canonical chain)
+ *   code_q  uint64 [B][Hq][NW]     LHP code of q_i
+ *   q_split fp64   [B][Hkv][D][G][2]  (max(q,0), min(q,0)) of q_rot, per dim and head
+ *   score   fp64   [B][Hkv][NPmax] page score S(p); entries p >= NP(L) unspecified
+ *   pages   int32  [B][Hkv][max_keep]  kept pages ascending, -1 padded
+ *   n_pages int32  [B][Hkv]
+ *   ham     uint16 [B][Hkv][max_keep*P] Hamming distance of candidate slot
+ *                  j*P + r, i.e. key pages[j]*P + r; 0xFFFF if that key is
+ *                  past the sequence or the slot is unused
+ *   sel     int32  [B][Hkv][top_k] selected keys (when sel_idx is NULL)
+ *   k_eff   int32  [B][Hkv] number of selected keys
+ *   partial, counters: internal
+ */
+typedef struct {
+    size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters;
+    size_t total;
+    int32_t n_splits; /* attention splits per KV head */
+} hhr_workspace_layout;
+
+hhr_status hhr_decode_workspace_layout(const hhr_dims* dims, int32_t max_keep_pages, int32_t top_k,
+                                       hhr_workspace_layout* layout);
+
+/*
+ * hhr_decode_step -- one HHR decode step of one layer
+ * ("HHR: Hierarchical Hash Retrieval for Efficient LLM Generation",
+ * Abstract; rit.work HHR blog post, section "Два уровня маршрутизации решают
+ * разные ошибки"; top-k selection as in Appendix Table 4 of the
+ * thelatestinai.com page on arXiv 2610.01230).
+ *
+ * For every sequence b (length L = seq_len[b]) and KV head h, with the G
+ * query heads of h sharing one selection:
+ *   1. qrot_i = R_h q_i and code_q,i (canonical chains);
+ *   2. S(p) for p < NP(L) (fp64, see above);
+ *   3. keep = clamp(keep_pages[b], 1, min(NP(L), max_keep_pages)) pages with
+ *      the largest S, equal S going to the lower page index;
+ *   4. candidates: keys t < L of the kept pages;
+ *   5. H(t) = group Hamming distance;
+ *   6. the k_eff = min(top_k, #candidates) candidates with the smallest
+ *      (H(t), t), written ascending to sel_idx (or the workspace), -1 padded;
+ *   7. out_i = sum_t softmax_t(scale * q_i . k_t) v_t over the selected t,
+ *      scale = softmax_scale if > 0, else 1/sqrt(D).
+ * L = 0 gives out = 0, no pages and no keys.
+ *   Q, K, V, R, W, meta, codes      device, read (meta/codes from hhr_encode_cache)
+ *   seq_len, keep_pages             device int32 [B], read
+ *   max_keep_pages >= 1, top_k >= 1 host; they size the workspace
+ *   out                             device fp32 [B][Hq][D], written
+ *   sel_idx                         device int32 [B][Hkv][top_k], written, or NULL
+ *   workspace, workspace_bytes      device scratch >= hhr_decode_workspace_bytes
+ */
+hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                           const float* R, const float* W, const float* meta, const uint64_t* codes,
+                           const int32_t* seq_len, const int32_t* keep_pages, int32_t max_keep_pages,
+                           int32_t top_k, float softmax_scale, float* out, int32_t* sel_idx,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage entry points: each runs one stage of hhr_decode_step on the same
+ * workspace (layout above), reading the previous stage's results from it and
+ * writing its own there, so a test can drive one stage from known inputs.
+ * Arguments mean what they mean for hhr_decode_step.
+ *   qprep         Q, R, W              -> q_rot, code_q, q_split
+ *   page_bounds   meta, seq_len        -> score            (reads q_split)
+ *   select_pages  seq_len, keep_pages  -> pages, n_pages   (reads score)
+ *   select_keys   codes, seq_len       -> ham, sel/sel_idx, k_eff (reads pages, n_pages, code_q)
+ *   attend        Q, K, V, seq_len     -> out              (reads sel/sel_idx, k_eff)
+ */
+hhr_status hhr_stage_qprep(const hhr_dims* dims, const void* Q, const float* R, const float* W,
+                           int32_t max_keep_pages, int32_t top_k, void* workspace,
+                           size_t workspace_bytes, void* stream);
+hhr_status hhr_stage_page_bounds(const hhr_dims* dims, const float* meta, const int32_t* seq_len,
+                                 int32_t max_keep_pages, int32_t top_k, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+hhr_status hhr_stage_select_pages(const hhr_dims* dims, const int32_t* seq_len, const int32_t* keep_pages,
+                                  int32_t max_keep_pages, int32_t top_k, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+hhr_status hhr_stage_select_keys(const hhr_dims* dims, const uint64_t* codes, const int32_t* seq_len,
+                                 int32_t max_keep_pages, int32_t top_k, int32_t* sel_idx,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+hhr_status hhr_stage_attend(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                            const int32_t* seq_len, int32_t max_keep_pages, int32_t top_k,
+                            float softmax_scale, const int32_t* sel_idx, float* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+const char* hhr_status_str(hhr_status status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* hhr_last_error(void);
+int32_t hhr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HHR_H */
