@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the HHR decode step on one MI355X.
+
+Workload: Llama-3.1-8B-shaped attention (32 query / 8 KV heads, head_dim 128),
+128K context, batch 1, 32 layers with independent seeded K/V, R_h, W_h; page
+16, 128-bit codes, keep 10% of pages, top-k 4096.  One step = for every layer
+in order: hhr_decode_step_append -- append the current token's key (its code
+and its page's GKR statistics), then query prep, page bounds, page select,
+Hamming top-k and gather attention.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is context keys covered per second (every key
+of every KV head of every layer, per decode step); the line also carries
+us_per_layer, algorithmic HBM GB/s, the roofline of the dominant kernel (the
+page-bound stream) and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-step latency (µs/layer) + keys scanned/s + HBM GB/s (% peak) at 128K ctx"
+HBM_PEAK_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "page_bound_llama8b_128k_pmc.json")
+BOUND_SRC = os.path.join(ROOT, "hash_sparse_attention_amd", "csrc", "decode.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total):
+    """Bytes the method must move for one layer of one step (append + decode)."""
+    B, Hkv, Hq, D, P, nb = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.page_size, wl.hash_bits
+    e = 2 if wl.dtype == "bf16" else 4
+    tot = 0
+    for b in range(B):
+        L = int(seq[b])
+        NP = -(-L // P)
+        cand = int(keep[b]) * P  # every kept page is full at these lengths
+        tot += Hkv * (NP * 2 * D * 4 + cand * nb // 8)
+    tot += k_eff_total * (2 * D * e + 4)                       # gathered K and V rows + indices
+    tot += Hkv * (D * D + nb * D) * 4                          # R_h, W_h
+    tot += B * Hq * D * (e + 4)                                # q in, out
+    tot += B * Hkv * (P * D * e + 2 * D * 4 + nb // 8)         # append: page keys in, page meta + code out
+    return tot
+
+
+def page_bound_bytes_per_launch(wl, seq):
+    """Per page: 2*D fp32 (max, min) read + one fp64 score written."""
+    pages = sum(-(-int(L) // wl.page_size) for L in seq) * wl.n_kv_heads
+    return pages * (2 * wl.head_dim * 4 + 8), pages
+
+
+def source_digest():
+    return hashlib.sha256(open(BOUND_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per page-bound launch from the committed rocprofv3 --pmc summary, if the kernel is unchanged."""
+    try:
+        rec = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, host_layer, steps_note):
+    """The oracle, as it stands, on layer 0 of the workload (all heads, full context)."""
+    import numpy as np
+
+    import oracle
+    od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
+                     wl.dtype == "bf16")
+    t0 = time.perf_counter()
+    meta, codes = oracle.encode(od, host_layer["K"], host_layer["R"], host_layer["W"], np.zeros(wl.batch, np.int32),
+                                host_layer["seq_len"])
+    t_enc = time.perf_counter() - t0
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        r = oracle.decode(od, host_layer["Q"], host_layer["K"], host_layer["V"], host_layer["R"], host_layer["W"],
+                          meta, codes, host_layer["seq_len"], host_layer["keep"], wl.max_keep, wl.top_k)
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[1]
+    keys = int(sum(host_layer["seq_len"])) * wl.n_kv_heads
+    threads = min(oracle.max_threads(), wl.batch * wl.n_kv_heads)
+    return dict(value=keys / t, unit="keys/s", cores=threads, kind="oracle",
+                us_per_layer=t * 1e6,
+                sample=(f"layer 0 of {wl.layers} (all {wl.n_kv_heads} KV heads, {wl.n_q_heads} query heads, "
+                        f"{int(host_layer['seq_len'][0])} keys): oracle decode step, median of 3 "
+                        f"({t:.3f} s each); oracle encode of that layer untimed ({t_enc:.1f} s); "
+                        f"OpenMP over the {wl.batch * wl.n_kv_heads} (sequence, KV head) units"),
+                cpu=_cpu_model()), r
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_128k")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bound-launches", type=int, default=96, help="page-bound launches timed for the roofline")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="also run N plain 1 GiB device copies (for rocprofv3 --pmc calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus N > 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    from synth import WORKLOADS, make_layer_torch
+
+    wl = WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_(layers=args.layers)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, ctx={wl.ctx}, device {torch.cuda.get_device_name(0)}")
+
+    dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
+                         wl.dtype == "bf16")
+    layers = []
+    t0 = time.perf_counter()
+    for l in range(wl.layers):
+        d = make_layer_torch(wl, l, dev)
+        meta, codes = hsa.alloc_cache(dims, dev)
+        zero = torch.zeros(wl.batch, dtype=torch.int32, device=dev)
+        hsa.encode_cache(dims, d["K"], d["R"], d["W"], zero, d["seq_len"], wl.ctx, meta, codes)
+        d.update(meta=meta, codes=codes)
+        d["out"] = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+        d["sel"] = torch.empty((wl.batch, wl.n_kv_heads, wl.top_k), dtype=torch.int32, device=dev)
+        d["app_start"] = (d["seq_len"] - 1).contiguous()
+        d["app_count"] = torch.ones(wl.batch, dtype=torch.int32, device=dev)
+        layers.append(d)
+    torch.cuda.synchronize()
+    log(f"inputs generated and encoded in {time.perf_counter() - t0:.1f} s")
+    ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
+
+    def step():
+        for d in layers:  # per layer: append the current token's key, then decode (one library call)
+            hsa.decode_step_append(dims, d["Q"], d["K"], d["V"], d["R"], d["W"], d["meta"], d["codes"],
+                                   d["app_start"], d["app_count"], 1, d["seq_len"], d["keep"], wl.max_keep,
+                                   wl.top_k, d["out"], ws, sel_idx=d["sel"])
+
+    # Eager reference of one step, then (optionally) a captured graph of the same step.
+    step()
+    torch.cuda.synchronize()
+    ref_out = torch.stack([d["out"].clone() for d in layers])
+    ref_sel = torch.stack([d["sel"].clone() for d in layers])
+    graph = None
+    if not args.no_graph:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step()
+        torch.cuda.current_stream().wait_stream(stream)
+        for rep in range(3):  # every replay must equal the eager step
+            for d in layers:
+                d["out"].fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(torch.stack([d["out"] for d in layers]), ref_out), f"graph replay {rep} differs"
+            assert torch.equal(torch.stack([d["sel"] for d in layers]), ref_sel), f"graph replay {rep} differs"
+        log("graph captured; 3 replays equal the eager step")
+    run = graph.replay if graph is not None else step
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"{args.steps} steps: {ms_per_step:.3f} ms/step (events), {t_wall / args.steps * 1e3:.3f} ms/step (wall)")
+
+    seq = layers[0]["seq_len_host"]
+    keep = layers[0]["keep_host"]
+    k_eff_total = int(sum(int(d["sel"].ge(0).sum()) for d in layers[:1]))
+    bytes_layer = algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total)
+    us_layer = ms_per_step * 1e3 / wl.layers
+    keys_step = int(sum(int(L) for L in seq)) * wl.n_kv_heads * wl.layers
+    cand_step = int(sum(int(k) for k in keep)) * wl.page_size * wl.n_kv_heads * wl.layers
+    gbps = bytes_layer / (us_layer * 1e-6) / 1e9
+
+    # Dominant kernel: page bounds (the metadata stream), timed alone on the step's stream; the
+    # workspace still holds the last layer's query, and any query streams the same bytes.
+    n_b = args.bound_launches
+    cur = torch.cuda.current_stream()
+    e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(len(layers)):  # warm the code path
+        hsa.stage_page_bounds(dims, layers[i]["meta"], layers[i]["seq_len"], wl.max_keep, wl.top_k, ws, stream=cur)
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
+    e_start.record(cur)
+    for i in range(n_b):
+        d = layers[i % len(layers)]  # cycle layers so the metadata is not cache-resident
+        pairs[i][0].record(cur)
+        hsa.stage_page_bounds(dims, d["meta"], d["seq_len"], wl.max_keep, wl.top_k, ws, stream=cur)
+        pairs[i][1].record(cur)
+    e_stop.record(cur)
+    torch.cuda.synchronize()
+    bound_us = sum(a.elapsed_time(b) for a, b in pairs) / n_b * 1e3
+    bound_bytes, n_pages = page_bound_bytes_per_launch(wl, seq)
+    achieved = bound_bytes / (bound_us * 1e-6) / 1e9
+    log(f"page-bound kernel: {bound_us:.2f} us/launch over {n_b} launches, {achieved:.0f} GB/s")
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.calibrate_copy):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    line = {
+        "metric": METRIC,
+        "value": keys_step / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; lognormal channel scales, 2 outlier key channels, planted keys)",
+        "config": {
+            "workload": (f"{wl.name}: Llama-3.1-8B-shaped decode step, {wl.layers} layers, batch {wl.batch}, "
+                         f"{wl.n_q_heads}q/{wl.n_kv_heads}kv heads, head_dim {wl.head_dim}, context {wl.ctx}, "
+                         f"page {wl.page_size}, {wl.hash_bits}-bit codes, keep {wl.keep_percent}% pages, "
+                         f"top-k {wl.top_k}; one step = per layer a 1-token append + decode"),
+            "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
+        },
+        "us_per_layer": us_layer,
+        "hamming_candidates_per_s": cand_step / (ms_per_step * 1e-3),
+        "hbm_algorithmic_bytes_per_layer": bytes_layer,
+        "hbm_GBps": gbps,
+        "hbm_frac_peak": gbps / HBM_PEAK_GBPS,
+        "roofline": {
+            "kernel": "page_bound_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic_from_profile(),
+            "algorithmic_bytes_per_launch": bound_bytes,
+            "pages_per_launch": n_pages,
+            "us_per_launch": bound_us,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        d0 = layers[0]
+        host = {
+            "Q": d0["Q"].view(torch.int16).cpu().numpy().view(np.uint16),
+            "K": d0["K"].view(torch.int16).cpu().numpy().view(np.uint16),
+            "V": d0["V"].view(torch.int16).cpu().numpy().view(np.uint16),
+            "R": d0["R"].cpu().numpy(), "W": d0["W"].cpu().numpy(),
+            "seq_len": d0["seq_len_host"], "keep": d0["keep_host"],
+        }
+        log("cpu baseline: oracle encode + decode of layer 0")
+        cb, r = cpu_baseline(wl, host, args.steps)
+        err = float(np.abs(ref_out[0].cpu().numpy().astype(np.float64) - r["out"]).max())
+        sel_ok = bool(np.array_equal(ref_sel[0].cpu().numpy(), r["sel"]))
+        cb["layer0_parity"] = {"selected_keys_equal": sel_ok, "attention_max_abs_diff": err}
+        line["cpu_baseline"] = cb
+        log(f"cpu baseline {cb['value']:.3g} keys/s on {cb['cores']} threads; layer-0 parity sel={sel_ok} err={err:.2e}")
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

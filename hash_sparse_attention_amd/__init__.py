@@ -60,6 +60,8 @@ def lib():
             "hhr_decode_workspace_bytes": (sz, [D, i32, i32]),
             "hhr_decode_workspace_layout": (ctypes.c_int, [D, i32, i32, ctypes.POINTER(WorkspaceLayout)]),
             "hhr_decode_step": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, i32, f32, p, p, p, sz, p]),
+            "hhr_decode_step_append": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, p, p, i32, i32, f32, p, p,
+                                                      p, sz, p]),
             "hhr_stage_qprep": (ctypes.c_int, [D, p, p, p, i32, i32, p, sz, p]),
             "hhr_stage_page_bounds": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
             "hhr_stage_select_pages": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
@@ -77,7 +79,7 @@ def lib():
 
 
 EXPORTED = ("hhr_meta_bytes", "hhr_codes_bytes", "hhr_encode_cache", "hhr_decode_workspace_bytes",
-            "hhr_decode_workspace_layout", "hhr_decode_step", "hhr_stage_qprep", "hhr_stage_page_bounds",
+            "hhr_decode_workspace_layout", "hhr_decode_step", "hhr_decode_step_append", "hhr_stage_qprep", "hhr_stage_page_bounds",
             "hhr_stage_select_pages", "hhr_stage_select_keys", "hhr_stage_attend", "hhr_status_str",
             "hhr_last_error", "hhr_abi_version")
 
@@ -154,6 +156,16 @@ def decode_step(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max
                                  _ptr(codes), _ptr(seq_len), _ptr(keep_pages), int(max_keep), int(top_k),
                                  float(scale), _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
+
+
+def decode_step_append(dims: Dims, Q, K, V, R, W, meta, codes, append_start, append_count, max_append: int,
+                       seq_len, keep_pages, max_keep: int, top_k: int, out, workspace, sel_idx=None,
+                       scale: float = 0.0, stream=None):
+    _check(lib().hhr_decode_step_append(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(R), _ptr(W), _ptr(meta),
+                                        _ptr(codes), _ptr(append_start), _ptr(append_count), int(max_append),
+                                        _ptr(seq_len), _ptr(keep_pages), int(max_keep), int(top_k), float(scale),
+                                        _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)))
 
 
 def stage_qprep(dims, Q, R, W, max_keep, top_k, workspace, stream=None):

@@ -178,9 +178,22 @@ hhr_status hhr_encode_cache(const hhr_dims* dims, const void* K, const float* R,
     if (max_count < 0 || max_count > s.T)
         return fail(HHR_E_RANGE, "max_count must be in 0..max_ctx (got %d)", max_count);
     if (max_count == 0) return ok();
-    HHR_TRY(hip_check(launch_encode(s, K, R, W, start, count, max_count, meta, codes,
-                                    static_cast<hipStream_t>(stream)),
-                      "encode launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (max_count <= kAppendMax) {
+        ProjectArgs p{};
+        p.keys = true;
+        p.K = K;
+        p.R = R;
+        p.W = W;
+        p.start = start;
+        p.count = count;
+        p.max_count = max_count;
+        p.meta = meta;
+        p.codes = codes;
+        HHR_TRY(hip_check(launch_project(s, p, st), "append launch"));
+    } else {
+        HHR_TRY(hip_check(launch_encode(s, K, R, W, start, count, max_count, meta, codes, st), "encode launch"));
+    }
     return ok();
 }
 
@@ -245,8 +258,75 @@ hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, c
     const hipStream_t st = static_cast<hipStream_t>(stream);
     HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
     HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
-    HHR_TRY(hip_check(launch_select_pages(a, st), "page-select launch"));
-    HHR_TRY(hip_check(launch_select_keys(a, st), "key-select launch"));
+    HHR_TRY(hip_check(launch_select(a, st), "select launch"));
+    HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
+    return ok();
+}
+
+hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                                  const float* R, const float* W, float* meta, uint64_t* codes,
+                                  const int32_t* append_start, const int32_t* append_count, int32_t max_append,
+                                  const int32_t* seq_len, const int32_t* keep_pages, int32_t max_keep_pages,
+                                  int32_t top_k, float softmax_scale, float* out, int32_t* sel_idx, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(Q, "Q"));
+    HHR_TRY(check_ptr(K, "K"));
+    HHR_TRY(check_ptr(V, "V"));
+    HHR_TRY(check_ptr(R, "R"));
+    HHR_TRY(check_ptr(W, "W"));
+    HHR_TRY(check_ptr(meta, "meta"));
+    HHR_TRY(check_ptr(codes, "codes"));
+    HHR_TRY(check_ptr(append_start, "append_start", 4));
+    HHR_TRY(check_ptr(append_count, "append_count", 4));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    HHR_TRY(check_ptr(keep_pages, "keep_pages", 4));
+    HHR_TRY(check_ptr(out, "out"));
+    if (sel_idx) HHR_TRY(check_ptr(sel_idx, "sel_idx", 4));
+    if (max_append < 0 || max_append > a.s.T)
+        return fail(HHR_E_RANGE, "max_append must be in 0..max_ctx (got %d)", max_append);
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.R = R;
+    a.W = W;
+    a.meta = meta;
+    a.codes = codes;
+    a.seq_len = seq_len;
+    a.keep_pages = keep_pages;
+    a.out = out;
+    a.scale = resolve_scale(softmax_scale, a.s.D);
+    if (sel_idx) a.sel = sel_idx;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (max_append > 0 && max_append <= kAppendMax) {
+        // One launch projects the appended keys and the queries.
+        ProjectArgs p{};
+        p.keys = true;
+        p.queries = true;
+        p.Q = Q;
+        p.K = K;
+        p.R = R;
+        p.W = W;
+        p.start = append_start;
+        p.count = append_count;
+        p.max_count = max_append;
+        p.meta = meta;
+        p.codes = codes;
+        p.q_rot = reinterpret_cast<float*>(a.ws + a.lay.q_rot);
+        p.code_q = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_q);
+        p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
+        p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
+        p.n_counters = a.s.B * a.s.Hkv;
+        HHR_TRY(hip_check(launch_project(a.s, p, st), "append + qprep launch"));
+    } else {
+        if (max_append > 0)
+            HHR_TRY(hip_check(launch_encode(a.s, K, R, W, append_start, append_count, max_append, meta, codes, st),
+                              "encode launch"));
+        HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
+    }
+    HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
+    HHR_TRY(hip_check(launch_select(a, st), "select launch"));
     HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
     return ok();
 }

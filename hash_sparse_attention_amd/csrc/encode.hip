@@ -8,16 +8,13 @@
 // c ascending from acc = +0, so any IEEE implementation of it -- on either
 // mapping below -- produces the same bits.
 //
-// Two mappings on gfx950 (wave64):
-//  - bulk (many keys): one lane per key.  The key row sits in VGPRs as fp32;
-//    the rows of [R_h; W_h] are wave-uniform, so they come in through scalar
-//    loads and feed v_fma as SGPR operands.  A page is P adjacent lanes: its
-//    max/min is a butterfly over P lanes.  Each lane packs its own code words
-//    and stores them contiguously.
-//  - append (few keys, e.g. the token just generated): one lane per row of
-//    [R_h; W_h] with the row in VGPRs and the page's keys staged in LDS (read
-//    as broadcasts); key groups split the page's keys across waves and meet
-//    in LDS for the max/min; each hash wave ballots 64 sign bits into a word.
+// This file holds the bulk mapping on gfx950 (wave64), used for many keys:
+// one lane per key.  The key row sits in VGPRs as fp32; the rows of
+// [R_h; W_h] are wave-uniform, so they come in through scalar loads and feed
+// v_fma as SGPR operands.  A page is P adjacent lanes: its max/min is a
+// butterfly over P lanes.  Each lane packs its own code words and stores
+// them contiguously.  Appends of a few keys (the token just generated) use
+// the row-per-lane projection kernel instead.
 #include "hhr_internal.h"
 
 namespace hhr {
@@ -124,112 +121,12 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
     }
 }
 
-// ------------------------------------------------------------------ append
-template <int D, int NB, bool BF16, int KG>
-__global__ __launch_bounds__((D + NB) * KG) void encode_append_kernel(
-    const void* __restrict__ K, const float* __restrict__ R, const float* __restrict__ W,
-    const int32_t* __restrict__ start, const int32_t* __restrict__ count, int max_count,
-    float* __restrict__ meta, uint64_t* __restrict__ codes, int Hkv, int T, int P, int64_t NPB) {
-    constexpr int NRW = (D + NB) / 64;  // waves per key group
-    constexpr int NW = NB / 64;
-    extern __shared__ float lds[];
-    float* kbuf = lds;                 // [P][D] keys of the page
-    float* red = lds + (size_t)P * D;  // [KG][D][2] max/min partials
-
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int kg = wv / NRW, row = (wv % NRW) * 64 + lane;
-    const int64_t bh = (int64_t)b * Hkv + h;
-    const EncRange rg = enc_range(start, count, b, max_count, T);
-    if (rg.e <= rg.s) return;
-    const int p = rg.s / P + blockIdx.x;  // one page per block
-    const int lo = p * P;
-    if (lo >= rg.e) return;
-    const int n = (lo + P < rg.e ? lo + P : rg.e) - lo;  // keys of this page below e
-
-    const float* src = row < D ? R + ((int64_t)h * D + row) * D : W + ((int64_t)h * NB + (row - D)) * D;
-    float m[D];
-#pragma unroll
-    for (int i = 0; i < D; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + i);
-        m[i] = v.x; m[i + 1] = v.y; m[i + 2] = v.z; m[i + 3] = v.w;
-    }
-
-    if (BF16) {
-        const uint16_t* kb = static_cast<const uint16_t*>(K) + (bh * T + lo) * D;
-        for (int i = tid * 8; i < n * D; i += blockDim.x * 8) {
-            const uint4 u = *reinterpret_cast<const uint4*>(kb + i);
-            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                kbuf[i + 2 * q] = __uint_as_float(w4[q] << 16);
-                kbuf[i + 2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
-            }
-        }
-    } else {
-        const float* kf = static_cast<const float*>(K) + (bh * T + lo) * D;
-        for (int i = tid * 4; i < n * D; i += blockDim.x * 4)
-            *reinterpret_cast<float4*>(kbuf + i) = *reinterpret_cast<const float4*>(kf + i);
-    }
-    __syncthreads();
-
-    float mx = -__builtin_inff(), mn = __builtin_inff();
-    // Rotation rows take every key of the page; hash rows only keys >= s.
-    const int jfirst = (row < D ? 0 : (rg.s - lo > 0 ? rg.s - lo : 0)) + kg;
-    for (int j = jfirst; j < n; j += KG) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < D; i += 4) {
-            const float4 kv = *reinterpret_cast<const float4*>(kbuf + j * D + i);
-            acc = __builtin_fmaf(m[i], kv.x, acc);
-            acc = __builtin_fmaf(m[i + 1], kv.y, acc);
-            acc = __builtin_fmaf(m[i + 2], kv.z, acc);
-            acc = __builtin_fmaf(m[i + 3], kv.w, acc);
-        }
-        if (row < D) {
-            const float v = acc == 0.f ? 0.f : acc;
-            mx = fmaxf(mx, v);
-            mn = fminf(mn, v);
-        } else {
-            const uint64_t word = __ballot(acc > 0.f);
-            if (lane == 0) codes[(bh * T + lo + j) * NW + (row - D) / 64] = word;
-        }
-    }
-
-    if (row < D) {
-        red[(kg * D + row) * 2] = mx;
-        red[(kg * D + row) * 2 + 1] = mn;
-    }
-    __syncthreads();
-    if (kg == 0 && row < D) {
-#pragma unroll
-        for (int g = 1; g < KG; ++g) {
-            mx = fmaxf(mx, red[(g * D + row) * 2]);
-            mn = fminf(mn, red[(g * D + row) * 2 + 1]);
-        }
-        float* mp = meta + (((bh * NPB + p / 64) * (D / 2) + row / 2) * 64 + (p & 63)) * 4 + (row & 1) * 2;
-        *reinterpret_cast<float2*>(mp) = make_float2(mx, mn);
-    }
-}
-
-// Appends of at most this many keys use the row-per-lane kernel.
-constexpr int kAppendMax = 64;
-
 template <int D, int NB, bool BF16>
 hipError_t launch_dnb(const Shape& s, const void* K, const float* R, const float* W, const int32_t* start,
                       const int32_t* count, int max_count, float* meta, uint64_t* codes, hipStream_t st) {
-    if (max_count <= kAppendMax) {
-        constexpr int NRW = (D + NB) / 64;
-        constexpr int KG = NRW >= 3 ? 2 : 4;          // <= 512 threads: each lane holds a D-float row
-        const int pages = (max_count - 1) / s.P + 2;  // pages that [s, s+count) can touch
-        const size_t lds = ((size_t)s.P * D + (size_t)KG * D * 2) * sizeof(float);
-        hipLaunchKernelGGL((encode_append_kernel<D, NB, BF16, KG>), dim3(pages, s.Hkv, s.B), dim3((D + NB) * KG),
-                           lds, st, K, R, W, start, count, max_count, meta, codes, s.Hkv, s.T, s.P, s.NPB);
-    } else {
-        const int tiles = (max_count + s.P - 1 + 255) / 256;  // keys [floor(s/P)P, e) in 256-key tiles
-        hipLaunchKernelGGL((encode_bulk_kernel<D, NB, BF16>), dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W,
-                           start, count, max_count, meta, codes, s.Hkv, s.T, s.P, s.NPB);
-    }
+    const int tiles = (max_count + s.P - 1 + 255) / 256;  // keys [floor(s/P)P, e) in 256-key tiles
+    hipLaunchKernelGGL((encode_bulk_kernel<D, NB, BF16>), dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W,
+                       start, count, max_count, meta, codes, s.Hkv, s.T, s.P, s.NPB);
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ struct Shape {
 };
 
 // Attention keys handled by one block (one split) of the attend kernel.
-constexpr int kAttnChunk = 64;
+constexpr int kAttnChunk = 256;
 
 // Region offsets of the decode workspace (bytes, 256-aligned).
 struct WsLayout {
@@ -48,8 +48,28 @@ struct DecodeArgs {
     WsLayout lay;
 };
 
+// Projection of a few vectors (appended keys and/or the queries) by [R_h; W_h].
+struct ProjectArgs {
+    bool keys, queries;
+    const void *Q, *K;
+    const float *R, *W;
+    const int32_t *start, *count;
+    int max_count;
+    float* meta;
+    uint64_t* codes;
+    float* q_rot;
+    uint64_t* code_q;
+    double* q_split;
+    uint32_t* counters;
+    int n_counters;
+};
+// Appends of at most this many keys per sequence go through the projection kernel.
+constexpr int kAppendMax = 64;
+
+hipError_t launch_project(const Shape& s, const ProjectArgs& a, hipStream_t stream);
 hipError_t launch_qprep(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_page_bounds(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_select(const DecodeArgs& a, hipStream_t stream);  // pages, then keys, one launch
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_attend(const DecodeArgs& a, bool zero_counters, hipStream_t stream);

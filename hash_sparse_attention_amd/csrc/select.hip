@@ -1,0 +1,399 @@
+// Selections of the HHR decode step, one 1024-thread block per (sequence,
+// KV head):
+//  - page select: the `keep` pages with the largest GKR bound, ties to the
+//    lower page index ("HHR: Hierarchical Hash Retrieval for Efficient LLM
+//    Generation", Abstract; rit.work HHR blog post, section "Два уровня
+//    маршрутизации решают разные ошибки": low-bound pages are dropped whole);
+//  - key select: LHP Hamming distances of the kept pages' keys and the top-k
+//    smallest (distance, index) (same blog post, section "Почему расстояние
+//    Хэмминга пропускает важные ключи"; Top-k of Appendix Table 4 on the
+//    thelatestinai.com page).
+// The decode step runs both in one launch, so the kept-page list goes from
+// the first half to the second through LDS; the stage entry points run each
+// half on its own.
+//
+// Latency matters more than bandwidth here (batch 1 gives 8 blocks), so each
+// thread owns a contiguous run of up to 16 items held in registers and every
+// global load is issued once, up front.  Page scores are fp64 turned into
+// order-preserving 64-bit keys; a block min/max finds the bits they share, so
+// the MSB-first radix select starts below them, 11 bits (2048 LDS bins) per
+// pass.  Hamming distances are small integers: one LDS histogram and one scan
+// find the threshold.  Ordered output positions come from a single block scan
+// of per-thread (before-threshold, at-threshold) counts, so every output list
+// is ascending without a sort.  Inputs larger than 16 items per thread loop
+// over chunks and re-read them.
+#include "hhr_internal.h"
+
+namespace hhr {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kRun = 16;                    // items per thread per chunk
+constexpr int kChunk = kSelThreads * kRun;  // items per chunk
+constexpr int kBits = 11;                   // radix digit width of the page select
+constexpr int kBins = 1 << kBits;
+constexpr int kListLds = 8192;              // kept-page ids staged in LDS
+
+__device__ __forceinline__ uint64_t order_key(double s) {
+    const uint64_t u = (uint64_t)__double_as_longlong(s);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+struct SelShared {
+    int hist[kBins];
+    int scan[32];
+    int found[3];
+    unsigned long long red[2][16];
+    int plist[kListLds];
+};
+
+// Block-wide min and max of a 64-bit value (every thread calls it).
+__device__ __forceinline__ void block_minmax(uint64_t vmin, uint64_t vmax, SelShared& sh, uint64_t& omin, uint64_t& omax) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t a = __shfl_xor((unsigned long long)vmin, off, 64);
+        const uint64_t b = __shfl_xor((unsigned long long)vmax, off, 64);
+        vmin = a < vmin ? a : vmin;
+        vmax = b > vmax ? b : vmax;
+    }
+    if (lane == 0) {
+        sh.red[0][wave] = vmin;
+        sh.red[1][wave] = vmax;
+    }
+    __syncthreads();
+    omin = sh.red[0][0];
+    omax = sh.red[1][0];
+    for (int w = 1; w < nw; ++w) {
+        omin = sh.red[0][w] < omin ? (uint64_t)sh.red[0][w] : omin;
+        omax = sh.red[1][w] > omax ? (uint64_t)sh.red[1][w] : omax;
+    }
+    __syncthreads();
+}
+
+// Kept pages of one (b, h) into `out` (ascending, -1 padded) and, if given,
+// into LDS.  Returns the number kept.
+__device__ __forceinline__ int select_pages_block(const double* __restrict__ sc, int NP, int keep, int max_keep,
+                                  int32_t* __restrict__ out, SelShared& sh, bool to_lds) {
+    const int tid = threadIdx.x;
+    const int nchunks = (NP + kChunk - 1) / kChunk;
+    const int run = nchunks <= 1 ? (NP + kSelThreads - 1) / kSelThreads : kRun;
+    uint64_t key[kRun];
+    auto load_chunk = [&](int c) {
+        const int p0 = c * kChunk + tid * run;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) key[k] = (k < run && p0 + k < NP) ? order_key(sc[p0 + k]) : 0;
+    };
+
+    uint64_t prefix = 0, mask = 0;
+    int need = keep;
+    bool all_in = keep == NP;  // every page is kept
+    int shift = 64;
+    if (!all_in) {
+        uint64_t lo = ~0ull, hi = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            load_chunk(c);
+            const int p0 = c * kChunk + tid * run;
+#pragma unroll
+            for (int k = 0; k < kRun; ++k)
+                if (k < run && p0 + k < NP) {
+                    lo = key[k] < lo ? key[k] : lo;
+                    hi = key[k] > hi ? key[k] : hi;
+                }
+        }
+        uint64_t kmin, kmax;
+        block_minmax(lo, hi, sh, kmin, kmax);
+        if (kmin == kmax) {
+            all_in = false;  // every score is equal: the first `keep` pages win
+            mask = ~0ull;
+            prefix = kmin;
+            shift = 0;
+        } else {
+            const int top = 63 - __clzll(kmin ^ kmax);  // highest bit where scores differ
+            mask = top == 63 ? 0ull : ~0ull << (top + 1);
+            prefix = kmin & mask;
+            shift = top + 1;
+        }
+    }
+    // Radix passes below the shared bits.
+    while (!all_in && shift > 0) {
+        const int width = shift < kBits ? shift : kBits;
+        shift -= width;
+        const int nb = 1 << width;
+        for (int i = tid; i < nb; i += blockDim.x) sh.hist[i] = 0;
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            if (nchunks > 1) load_chunk(c);
+            const int p0 = c * kChunk + tid * run;
+#pragma unroll
+            for (int k = 0; k < kRun; ++k)
+                if (k < run && p0 + k < NP && (key[k] & mask) == prefix)
+                    atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
+        }
+        __syncthreads();
+        // Descending digits: thread i owns digits nb-1-2i and nb-2-2i.
+        const int d0 = nb - 1 - 2 * tid, d1 = d0 - 1;
+        const int c0 = d0 >= 0 ? sh.hist[d0] : 0, c1 = d1 >= 0 ? sh.hist[d1] : 0;
+        int tot;
+        const int above = block_excl_scan(c0 + c1, sh.scan, tot);
+        if (above < need && above + c0 >= need) {
+            sh.found[0] = d0; sh.found[1] = above; sh.found[2] = c0;
+        } else if (above + c0 < need && above + c0 + c1 >= need) {
+            sh.found[0] = d1; sh.found[1] = above + c0; sh.found[2] = c1;
+        }
+        __syncthreads();
+        const int dig = sh.found[0];
+        need -= sh.found[1];
+        const int eq = sh.found[2];
+        prefix |= (uint64_t)dig << shift;
+        mask |= (uint64_t)(nb - 1) << shift;
+        if (eq == need) all_in = true;  // the whole boundary bucket is kept
+        __syncthreads();
+    }
+
+    // Page p is kept iff its masked key beats the boundary bucket, or it is in
+    // the bucket and (the bucket is kept whole, or it is among the first
+    // `need` of the bucket in page order).  One scan of packed (gt, eq) counts
+    // gives each thread its first output position.
+    int base = 0, eq_base = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        if (nchunks > 1 || keep == NP) load_chunk(c);
+        const int p0 = c * kChunk + tid * run;
+        int n_gt = 0, n_eq = 0;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run && p0 + k < NP) {
+                const uint64_t mk = key[k] & mask;
+                n_gt += mk > prefix;
+                n_eq += mk == prefix;
+            }
+        int tot;
+        const int packed = block_excl_scan((n_gt << 16) | n_eq, sh.scan, tot);
+        int gt_before = base + (packed >> 16), eq_rank = eq_base + (packed & 0xffff);
+        const int cap = all_in ? 0x7fffffff : need;
+        int pos = gt_before + (eq_rank < cap ? eq_rank : cap);
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run && p0 + k < NP) {
+                const uint64_t mk = key[k] & mask;
+                bool in = mk > prefix;
+                if (mk == prefix) {
+                    in = eq_rank < cap;
+                    ++eq_rank;
+                }
+                if (in) {
+                    if (pos < max_keep) {
+                        out[pos] = p0 + k;
+                        if (to_lds && pos < kListLds) sh.plist[pos] = p0 + k;
+                    }
+                    ++pos;
+                }
+            }
+        base += tot >> 16;
+        eq_base += tot & 0xffff;
+    }
+    for (int j = keep + tid; j < max_keep; j += blockDim.x) out[j] = -1;
+    return keep;
+}
+
+template <int NW, int G>
+__device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ ck, const uint64_t* __restrict__ cqg,
+                                  const int32_t* __restrict__ pl, int np, bool list_in_lds, int L, int P,
+                                  int max_keep, int top_k, uint16_t* __restrict__ hm, int32_t* __restrict__ so,
+                                  int32_t* __restrict__ keff_out, SelShared& sh) {
+    constexpr int NB = NW * 64;
+    constexpr int NBINS = G * NB + 1;
+    const int tid = threadIdx.x;
+    const int nslots = np * P;
+    const int lp = 31 - __clz(P);  // P is a power of two
+    uint64_t cq[G * NW];
+#pragma unroll
+    for (int i = 0; i < G * NW; ++i) cq[i] = cqg[i];
+    for (int i = tid; i < NBINS; i += blockDim.x) sh.hist[i] = 0;
+    __syncthreads();
+
+    const int nchunks = (nslots + kChunk - 1) / kChunk;
+    const int run = nchunks <= 1 ? (nslots + kSelThreads - 1) / kSelThreads : kRun;
+    int Hreg[kRun];
+    auto page_of = [&](int s) { return list_in_lds ? sh.plist[s >> lp] : pl[s >> lp]; };
+    auto distances = [&](int c) {
+        const int c0 = c * kChunk + tid * run;
+        uint64_t kc[kRun][NW];
+        bool ok[kRun];
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            const int s = c0 + k;
+            int t = -1;
+            if (k < run && s < nslots) {
+                t = page_of(s) * P + (s & (P - 1));
+                if (t < 0 || t >= L) t = -1;
+            }
+            ok[k] = t >= 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) kc[k][w] = ok[k] ? ck[(int64_t)t * NW + w] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            int hsum = 0;
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+#pragma unroll
+                for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
+            Hreg[k] = ok[k] ? hsum : -1;
+        }
+    };
+
+    for (int c = 0; c < nchunks; ++c) {
+        distances(c);
+        const int c0 = c * kChunk + tid * run;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run && c0 + k < nslots) {
+                hm[c0 + k] = Hreg[k] < 0 ? (uint16_t)0xFFFF : (uint16_t)Hreg[k];
+                if (Hreg[k] >= 0) atomicAdd(&sh.hist[Hreg[k]], 1);
+            }
+    }
+    for (int s = nslots + tid; s < max_keep * P; s += blockDim.x) hm[s] = 0xFFFF;
+    __syncthreads();
+
+    // Threshold h*: the ascending cumulative count reaches k_eff.
+    int hs, need, keff;
+    {
+        const int b0 = 2 * tid;
+        const int c0 = b0 < NBINS ? sh.hist[b0] : 0, c1 = b0 + 1 < NBINS ? sh.hist[b0 + 1] : 0;
+        int nvalid;
+        const int below0 = block_excl_scan(c0 + c1, sh.scan, nvalid);
+        keff = nvalid < top_k ? nvalid : top_k;
+        if (tid == 0) {
+            sh.found[0] = NBINS;
+            sh.found[1] = 0;
+        }
+        __syncthreads();
+        if (keff > 0) {
+            if (below0 < keff && below0 + c0 >= keff) {
+                sh.found[0] = b0; sh.found[1] = keff - below0;
+            } else if (below0 + c0 < keff && below0 + c0 + c1 >= keff) {
+                sh.found[0] = b0 + 1; sh.found[1] = keff - below0 - c0;
+            }
+        }
+        __syncthreads();
+        hs = sh.found[0];
+        need = sh.found[1];
+    }
+
+    // Keep H < h*, and the first `need` candidates with H == h* in slot order.
+    int base = 0, eq_base = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        if (nchunks > 1) distances(c);
+        const int c0 = c * kChunk + tid * run;
+        int n_lt = 0, n_eq = 0;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run && c0 + k < nslots && Hreg[k] >= 0) {
+                n_lt += Hreg[k] < hs;
+                n_eq += Hreg[k] == hs;
+            }
+        int tot;
+        const int packed = block_excl_scan((n_lt << 16) | n_eq, sh.scan, tot);
+        int eq_rank = eq_base + (packed & 0xffff);
+        int pos = base + (packed >> 16) + (eq_rank < need ? eq_rank : need);
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run && c0 + k < nslots && Hreg[k] >= 0) {
+                bool in = Hreg[k] < hs;
+                if (Hreg[k] == hs) {
+                    in = eq_rank < need;
+                    ++eq_rank;
+                }
+                if (in) {
+                    const int s = c0 + k;
+                    if (pos < top_k) so[pos] = page_of(s) * P + (s & (P - 1));
+                    ++pos;
+                }
+            }
+        base += tot >> 16;
+        eq_base += tot & 0xffff;
+    }
+    for (int j = keff + tid; j < top_k; j += blockDim.x) so[j] = -1;
+    if (tid == 0) *keff_out = keff;
+}
+
+template <int NW, int G, bool PAGES, bool KEYS>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
+    const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
+    int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
+    int32_t* __restrict__ k_eff_out, int Hq, int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
+    __shared__ SelShared sh;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int L = clamp_len(seq_len[b], T);
+    const int NP = (int)n_pages_of(L, P);
+    int32_t* pl = pages + bh * max_keep;
+    int np;
+    bool list_in_lds = false;
+    if (PAGES) {
+        int keep = keep_pages[b];
+        keep = keep < 1 ? 1 : keep;
+        keep = keep > NP ? NP : keep;
+        keep = keep > max_keep ? max_keep : keep;
+        np = select_pages_block(score + bh * NPmax, NP, keep, max_keep, pl, sh, KEYS);
+        if (threadIdx.x == 0) n_pages[bh] = np;
+        list_in_lds = KEYS && np <= kListLds;
+        __syncthreads();
+    } else {
+        np = n_pages[bh];
+        np = np < 0 ? 0 : (np > max_keep ? max_keep : np);  // memory safety for a hand-filled workspace
+        if (np <= kListLds) {
+            for (int i = threadIdx.x; i < np; i += blockDim.x) sh.plist[i] = pl[i];
+            list_in_lds = true;
+        }
+        __syncthreads();
+    }
+    if (KEYS)
+        select_keys_block<NW, G>(codes + bh * (int64_t)T * NW, code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW, pl,
+                                 np, list_in_lds, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
+                                 sel + bh * top_k, k_eff_out + bh, sh);
+}
+
+template <int NW, int G, bool PAGES, bool KEYS>
+hipError_t select_t(const DecodeArgs& a, hipStream_t st) {
+    const Shape& s = a.s;
+    hipLaunchKernelGGL((select_kernel<NW, G, PAGES, KEYS>), dim3(s.Hkv, s.B), dim3(kSelThreads), 0, st,
+                       reinterpret_cast<const double*>(a.ws + a.lay.score), a.keep_pages, a.codes,
+                       reinterpret_cast<const uint64_t*>(a.ws + a.lay.code_q), a.seq_len,
+                       reinterpret_cast<int32_t*>(a.ws + a.lay.pages), reinterpret_cast<int32_t*>(a.ws + a.lay.n_pages),
+                       reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
+                       reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep,
+                       a.top_k);
+    return hipGetLastError();
+}
+
+template <bool PAGES, bool KEYS, int NW>
+hipError_t select_nw(const DecodeArgs& a, hipStream_t st) {
+    switch (a.s.G) {
+        case 1: return select_t<NW, 1, PAGES, KEYS>(a, st);
+        case 2: return select_t<NW, 2, PAGES, KEYS>(a, st);
+        case 3: return select_t<NW, 3, PAGES, KEYS>(a, st);
+        case 4: return select_t<NW, 4, PAGES, KEYS>(a, st);
+        case 5: return select_t<NW, 5, PAGES, KEYS>(a, st);
+        case 6: return select_t<NW, 6, PAGES, KEYS>(a, st);
+        case 7: return select_t<NW, 7, PAGES, KEYS>(a, st);
+        default: return select_t<NW, 8, PAGES, KEYS>(a, st);
+    }
+}
+
+template <bool PAGES, bool KEYS>
+hipError_t select_mode(const DecodeArgs& a, hipStream_t st) {
+    return a.s.NW == 1 ? select_nw<PAGES, KEYS, 1>(a, st) : select_nw<PAGES, KEYS, 2>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_select(const DecodeArgs& a, hipStream_t st) { return select_mode<true, true>(a, st); }
+hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t st) {
+    return select_nw<true, false, 1>(a, st);  // the page half does not depend on the code width
+}
+hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) { return select_mode<false, true>(a, st); }
+
+}  // namespace hhr

@@ -208,6 +208,22 @@ hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, c
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hhr_decode_step_append -- append the token(s) just generated, then decode.
+ * Same result as hhr_encode_cache(dims, K, R, W, append_start, append_count,
+ * max_append, meta, codes, stream) followed by hhr_decode_step(...) with the
+ * same arguments, but with max_append <= 64 the key append and the query
+ * projection share one launch (the per-token path of a decode loop).  meta
+ * and codes are read and written; every other argument means what it means
+ * for those two calls.
+ */
+hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                                  const float* R, const float* W, float* meta, uint64_t* codes,
+                                  const int32_t* append_start, const int32_t* append_count, int32_t max_append,
+                                  const int32_t* seq_len, const int32_t* keep_pages, int32_t max_keep_pages,
+                                  int32_t top_k, float softmax_scale, float* out, int32_t* sel_idx, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Stage entry points: each runs one stage of hhr_decode_step on the same
  * workspace (layout above), reading the previous stage's results from it and
  * writing its own there, so a test can drive one stage from known inputs.

@@ -157,3 +157,165 @@ def test_mistral7b_b8_ragged_sampled(dev):
     d = make_layer(wl)
     g = run_gpu(wl, d, dev)
     _sampled(wl, d, g, [0, 5], "mistral7b_b8")
+
+
+def test_decode_step_append_matches_oracle(dev):
+    """hhr_decode_step_append (fused append + query projection) equals the oracle's single-shot encode +
+    decode, for a 1-token append, a ragged multi-token append, and an append larger than the fused limit."""
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    from gpu_common import gpu_dims, to_dev
+    wl = Workload("fused", 114, 3, 12, 3, 128, 700, 16, 128, 20, 48, "bf16", outliers=2)
+    d = make_layer(wl, lengths=[700, 650, 333])
+    o = run_oracle(wl, d)
+    for new in ([1, 1, 1], [5, 17, 1], [70, 3, 100]):
+        banner(f"decode_step_append new={new}")
+        new = np.array(new, np.int32)
+        seq = d["seq_len"]
+        pre = seq - new
+        dims = gpu_dims(wl)
+        t = {k: to_dev(d[k], dev) for k in ("Q", "K", "V", "R", "W")}
+        meta, codes = hsa.alloc_cache(dims, dev)
+        hsa.encode_cache(dims, t["K"], t["R"], t["W"], to_dev(np.zeros(3, np.int32), dev), to_dev(pre, dev),
+                         int(pre.max()), meta, codes)
+        ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
+        out = torch.empty((3, 12, 128), dtype=torch.float32, device=dev)
+        sel = torch.empty((3, 3, wl.top_k), dtype=torch.int32, device=dev)
+        hsa.decode_step_append(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], meta, codes, to_dev(pre, dev),
+                               to_dev(new, dev), int(new.max()), to_dev(seq, dev), to_dev(d["keep"], dev),
+                               wl.max_keep, wl.top_k, out, ws, sel_idx=sel)
+        torch.cuda.synchronize()
+        v = hsa.workspace_view(dims, wl.max_keep, wl.top_k, ws)
+        g = dict(meta=hsa.meta_to_pages(meta, dims).cpu().numpy(),
+                 codes=codes.cpu().numpy().view(np.uint64).reshape(3, 3, wl.ctx, 2),
+                 q_rot=v.q_rot.cpu().numpy(), code_q=v.code_q.cpu().numpy().view(np.uint64),
+                 score=v.score.cpu().numpy(), pages=v.pages.cpu().numpy(), n_pages=v.n_pages.cpu().numpy(),
+                 ham=v.ham.cpu().numpy().view(np.uint16), sel=sel.cpu().numpy(), k_eff=v.k_eff.cpu().numpy(),
+                 out=out.cpu().numpy())
+        compare(wl, seq, g, o, label=f"fused new={list(new)}")
+
+
+def test_repeated_steps_are_bitwise_deterministic(dev):
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    wl = WORKLOADS["llama8b_32k"].with_(batch=2, ragged=(20000, 32768))
+    banner("determinism: three decode steps, bitwise equal")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    x = g["_dev"]
+    outs = []
+    for _ in range(3):
+        x["out"].fill_(float("nan"))
+        hsa.decode_step(x["dims"], x["t"]["Q"], x["t"]["K"], x["t"]["V"], x["t"]["R"], x["t"]["W"], x["meta"],
+                        x["codes"], x["seq"], x["keep"], x["max_keep"], x["top_k"], x["out"], x["ws"],
+                        sel_idx=x["sel"])
+        torch.cuda.synchronize()
+        outs.append((x["out"].clone(), x["sel"].clone()))
+    for o_, s_ in outs[1:]:
+        assert torch.equal(o_, outs[0][0]) and torch.equal(s_, outs[0][1])
+    assert np.array_equal(outs[0][0].cpu().numpy(), g["out"])
+
+
+def test_graph_replay_matches_eager(dev):
+    """A captured HIP graph of append + decode replays to the eager result every time, with eager work and
+    synchronizations between replays."""
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    from gpu_common import gpu_dims, to_dev
+    wl = WORKLOADS["llama8b_32k"]
+    banner("graph capture and replay")
+    d = make_layer(wl)
+    dims = gpu_dims(wl)
+    t = {k: to_dev(d[k], dev) for k in ("Q", "K", "V", "R", "W")}
+    seq, keep = to_dev(d["seq_len"], dev), to_dev(d["keep"], dev)
+    meta, codes = hsa.alloc_cache(dims, dev)
+    hsa.encode_cache(dims, t["K"], t["R"], t["W"], to_dev(np.zeros(1, np.int32), dev), seq, wl.ctx, meta, codes)
+    ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev)
+    sel = torch.empty((1, 8, wl.top_k), dtype=torch.int32, device=dev)
+    a_start, a_count = (seq - 1).contiguous(), torch.ones(1, dtype=torch.int32, device=dev)
+
+    def step():
+        hsa.decode_step_append(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], meta, codes, a_start, a_count, 1,
+                               seq, keep, wl.max_keep, wl.top_k, out, ws, sel_idx=sel)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel = out.clone(), sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-9)
+        _ = (t["K"][0, 0, :8].float() * 2).sum().item()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(sel, ref_sel), f"replay {rep}"
+
+
+def test_stages_from_oracle_intermediates(dev):
+    """Each stage entry point, fed the oracle's result of the previous stage, reproduces the oracle's next
+    result (isolates a stage from the ones before it)."""
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    from gpu_common import gpu_dims, to_dev
+    wl = WORKLOADS["tiny"].with_(batch=2, ragged=(3000, 4096))
+    banner("stage isolation")
+    d = make_layer(wl)
+    o = run_oracle(wl, d)
+    dims = gpu_dims(wl)
+    mk, tk = wl.max_keep, wl.top_k
+    ws = hsa.alloc_workspace(dims, mk, tk, dev)
+    v = hsa.workspace_view(dims, mk, tk, ws)
+    seq, keep = to_dev(d["seq_len"], dev), to_dev(d["keep"], dev)
+    t = {k: to_dev(d[k], dev) for k in ("Q", "K", "V", "R", "W")}
+    # meta/codes from the oracle, converted to the library's layouts on the host
+    meta_gpu, codes_gpu = hsa.alloc_cache(dims, dev)
+    NPB = -(-wl.max_pages // 64)
+    om = np.zeros((2, wl.n_kv_heads, NPB * 64, wl.head_dim, 2), np.float32)
+    om[:, :, :wl.max_pages] = o["meta"]
+    om = om.reshape(2, wl.n_kv_heads, NPB, 64, wl.head_dim // 2, 2, 2).transpose(0, 1, 2, 4, 3, 5, 6)
+    meta_gpu.copy_(torch.from_numpy(np.ascontiguousarray(om).reshape(-1)).to(dev))
+    codes_gpu.copy_(torch.from_numpy(o["codes"].view(np.int64).reshape(-1)).to(dev))
+    # stage 1 (qprep) -> compare
+    hsa.stage_qprep(dims, t["Q"], t["R"], t["W"], mk, tk, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.q_rot.cpu().numpy().view(np.uint32), o["q_rot"].view(np.uint32))
+    assert np.array_equal(v.code_q.cpu().numpy().view(np.uint64), o["code_q"])
+    # stage 2 (bounds) on the oracle's meta
+    hsa.stage_page_bounds(dims, meta_gpu, seq, mk, tk, ws)
+    torch.cuda.synchronize()
+    sc = v.score.cpu().numpy()
+    for b in range(2):
+        NP = -(-int(d["seq_len"][b]) // wl.page_size)
+        assert np.array_equal(sc[b, :, :NP].view(np.uint64), o["score"][b, :, :NP].view(np.uint64))
+    # stage 3 (page select) from the oracle's scores
+    v.score.copy_(torch.from_numpy(o["score"]).to(dev))
+    hsa.stage_select_pages(dims, seq, keep, mk, tk, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.pages.cpu().numpy(), o["pages"]) and np.array_equal(v.n_pages.cpu().numpy(), o["n_pages"])
+    # stage 4 (key select) from the oracle's page lists and query codes
+    v.pages.copy_(torch.from_numpy(o["pages"]).to(dev))
+    v.n_pages.copy_(torch.from_numpy(o["n_pages"]).to(dev))
+    v.code_q.copy_(torch.from_numpy(o["code_q"].view(np.int64)).to(dev))
+    sel = torch.empty((2, wl.n_kv_heads, tk), dtype=torch.int32, device=dev)
+    hsa.stage_select_keys(dims, codes_gpu, seq, mk, tk, ws, sel_idx=sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.ham.cpu().numpy().view(np.uint16), o["ham"])
+    assert np.array_equal(sel.cpu().numpy(), o["sel"]) and np.array_equal(v.k_eff.cpu().numpy(), o["k_eff"])
+    # stage 5 (attention) from the oracle's selection
+    osel = torch.from_numpy(o["sel"]).to(dev)
+    v.k_eff.copy_(torch.from_numpy(o["k_eff"]).to(dev))
+    out = torch.empty((2, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    hsa.stage_attend(dims, t["Q"], t["K"], t["V"], seq, mk, tk, out, ws, sel_idx=osel)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy().astype(np.float64) - o["out"]).max() <= 2e-3
