@@ -106,15 +106,10 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const float si = lane < n ? s[i] * scale : -__builtin_inff();
-            float mx = si;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            const float mx = wave_max(si);
             p[i] = lane < n ? __expf(si - mx) : 0.f;
-            float l = p[i];
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, 64);
             m_i[i] = mx;
-            l_i[i] = l;
+            l_i[i] = wave_sum(p[i]);
         }
 
         // Phase B: o_i[lane slice] = sum_j p_i[j] * v_j, rows loaded VB at a time.

@@ -82,31 +82,74 @@ __device__ __forceinline__ int clamp_len(int L, int T) { return L < 0 ? 0 : (L >
 
 __device__ __forceinline__ int64_t n_pages_of(int64_t L, int P) { return (L + P - 1) / P; }
 
-// Exclusive prefix sum of v over the whole block (blockDim.x a multiple of 64,
-// at most 1024).  `scratch` holds >= 17 ints of LDS.  Returns the prefix and
-// the block total; every thread of the block must call it.
+// ---- wave64 primitives on DPP (row shifts within 16-lane rows, then row
+// broadcasts across rows).  A DPP step is a VALU op: far cheaper than a
+// cross-lane permute through LDS, which is what __shfl compiles to.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+    return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += dpp_i<kRowShr1, 0xf>(0, x);
+    x += dpp_i<kRowShr2, 0xf>(0, x);
+    x += dpp_i<kRowShr4, 0xf>(0, x);
+    x += dpp_i<kRowShr8, 0xf>(0, x);
+    x += dpp_i<kRowBcast15, 0xa>(0, x);
+    x += dpp_i<kRowBcast31, 0xc>(0, x);
+    return x;
+}
+
+// Wave-wide max / sum / OR, returned to every lane (a fixed combination
+// order, so float sums are reproducible bit for bit).
+__device__ __forceinline__ float wave_max(float x) {
+    const int id = __float_as_int(-__builtin_inff());
+    x = fmaxf(x, __int_as_float(dpp_i<kRowShr1, 0xf>(id, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowShr2, 0xf>(id, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowShr4, 0xf>(id, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowShr8, 0xf>(id, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowBcast15, 0xa>(id, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowBcast31, 0xc>(id, __float_as_int(x))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += __int_as_float(dpp_i<kRowShr1, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowShr2, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowShr4, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowShr8, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowBcast15, 0xa>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowBcast31, 0xc>(0, __float_as_int(x)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+    x |= (uint32_t)dpp_i<kRowShr1, 0xf>(0, (int)x);
+    x |= (uint32_t)dpp_i<kRowShr2, 0xf>(0, (int)x);
+    x |= (uint32_t)dpp_i<kRowShr4, 0xf>(0, (int)x);
+    x |= (uint32_t)dpp_i<kRowShr8, 0xf>(0, (int)x);
+    x |= (uint32_t)dpp_i<kRowBcast15, 0xa>(0, (int)x);
+    x |= (uint32_t)dpp_i<kRowBcast31, 0xc>(0, (int)x);
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Exclusive prefix sum of v over the whole block (blockDim.x a multiple of
+// 64, at most 1024).  `scratch` holds >= 16 ints of LDS.  Returns the prefix
+// and the block total; every thread of the block must call it.
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int n = __shfl_up(x, off, 64);
-        if (lane >= off) x += n;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) scratch[wave] = x;
     __syncthreads();
-    if (wave == 0) {
-        int w = lane < nw ? scratch[lane] : 0;
+    int base = 0, tot = 0;
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            int n = __shfl_up(w, off, 64);
-            if (lane >= off) w += n;
-        }
-        if (lane < nw) scratch[lane] = w;
+    for (int w = 0; w < 16; ++w) {
+        const int t = w < nw ? scratch[w] : 0;
+        base += w < wave ? t : 0;
+        tot += t;
     }
-    __syncthreads();
-    const int base = wave ? scratch[wave - 1] : 0;
-    total = scratch[nw - 1];
+    total = tot;
     __syncthreads();
     return base + x - v;
 }

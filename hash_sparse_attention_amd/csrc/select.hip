@@ -43,33 +43,9 @@ struct SelShared {
     int hist[kBins];
     int scan[32];
     int found[3];
-    unsigned long long red[2][16];
+    uint32_t red[2][16];
     int plist[kListLds];
 };
-
-// Block-wide min and max of a 64-bit value (every thread calls it).
-__device__ __forceinline__ void block_minmax(uint64_t vmin, uint64_t vmax, SelShared& sh, uint64_t& omin, uint64_t& omax) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t a = __shfl_xor((unsigned long long)vmin, off, 64);
-        const uint64_t b = __shfl_xor((unsigned long long)vmax, off, 64);
-        vmin = a < vmin ? a : vmin;
-        vmax = b > vmax ? b : vmax;
-    }
-    if (lane == 0) {
-        sh.red[0][wave] = vmin;
-        sh.red[1][wave] = vmax;
-    }
-    __syncthreads();
-    omin = sh.red[0][0];
-    omax = sh.red[1][0];
-    for (int w = 1; w < nw; ++w) {
-        omin = sh.red[0][w] < omin ? (uint64_t)sh.red[0][w] : omin;
-        omax = sh.red[1][w] > omax ? (uint64_t)sh.red[1][w] : omax;
-    }
-    __syncthreads();
-}
 
 // Kept pages of one (b, h) into `out` (ascending, -1 padded) and, if given,
 // into LDS.  Returns the number kept.
@@ -90,28 +66,33 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
     bool all_in = keep == NP;  // every page is kept
     int shift = 64;
     if (!all_in) {
-        uint64_t lo = ~0ull, hi = 0;
+        // Bits every key shares: OR over all keys of (key ^ key of page 0).
+        const uint64_t ref = order_key(sc[0]);
+        uint64_t diff = 0;
         for (int c = 0; c < nchunks; ++c) {
             load_chunk(c);
             const int p0 = c * kChunk + tid * run;
 #pragma unroll
             for (int k = 0; k < kRun; ++k)
-                if (k < run && p0 + k < NP) {
-                    lo = key[k] < lo ? key[k] : lo;
-                    hi = key[k] > hi ? key[k] : hi;
-                }
+                if (k < run && p0 + k < NP) diff |= key[k] ^ ref;
         }
-        uint64_t kmin, kmax;
-        block_minmax(lo, hi, sh, kmin, kmax);
-        if (kmin == kmax) {
-            all_in = false;  // every score is equal: the first `keep` pages win
-            mask = ~0ull;
-            prefix = kmin;
+        const uint32_t dh = wave_or((uint32_t)(diff >> 32)), dl = wave_or((uint32_t)diff);
+        if ((tid & 63) == 0) {
+            sh.red[0][tid >> 6] = dh;
+            sh.red[1][tid >> 6] = dl;
+        }
+        __syncthreads();
+        diff = 0;
+#pragma unroll
+        for (int w = 0; w < kSelThreads / 64; ++w) diff |= ((uint64_t)sh.red[0][w] << 32) | sh.red[1][w];
+        if (diff == 0) {
+            mask = ~0ull;  // every score is equal: the first `keep` pages win
+            prefix = ref;
             shift = 0;
         } else {
-            const int top = 63 - __clzll(kmin ^ kmax);  // highest bit where scores differ
+            const int top = 63 - __clzll(diff);  // highest bit where scores differ
             mask = top == 63 ? 0ull : ~0ull << (top + 1);
-            prefix = kmin & mask;
+            prefix = ref & mask;
             shift = top + 1;
         }
     }
