@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bound-launches", type=int, default=96, help="page-bound launches timed for the roofline")
     ap.add_argument("--calibrate-copy", type=int, default=0,
-                    help="also run N plain 1 GiB device copies (for rocprofv3 --pmc calibration)")
+                    help="also run N plain 1 GiB-in/1 GiB-out negations (for rocprofv3 --pmc calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -238,10 +238,11 @@ def main():
     log(f"page-bound kernel: {bound_us:.2f} us/launch over {n_b} launches, {achieved:.0f} GB/s")
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # A plain streaming kernel of known size (reads 1 GiB, writes 1 GiB) to scale the HBM counters.
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(args.calibrate_copy):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

@@ -262,8 +262,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
     if (tid == 0) counters[bh] = 0u;  // ready for the next call
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0u;
 }
 

@@ -134,18 +134,22 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
-// Exclusive prefix sum of v over the whole block (blockDim.x a multiple of
-// 64, at most 1024).  `scratch` holds >= 16 ints of LDS.  Returns the prefix
-// and the block total; every thread of the block must call it.
+// Exclusive prefix sum of v over a block of NT threads (a multiple of 64, at
+// most 1024; a constant, since blockDim.x is a load from the dispatch packet).
+// `scratch` holds >= 16 ints of LDS.  Returns the prefix and the block total;
+// every thread of the block must call it.
+template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    static_assert(NT % 64 == 0 && NT <= 1024, "block size");
+    constexpr int nw = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int x = wave_incl_scan(v);
     if (lane == 63) scratch[wave] = x;
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        const int t = w < nw ? scratch[w] : 0;
+    for (int w = 0; w < nw; ++w) {
+        const int t = scratch[w];
         base += w < wave ? t : 0;
         tot += t;
     }

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     const bool qblock = QUERIES && z == (KEYS ? key_blocks : 0);
 
     if (QUERIES && counters && qblock && blockIdx.x == 0 && blockIdx.y == 0)
-        for (int i = tid; i < n_counters; i += blockDim.x) counters[i] = 0u;
+        for (int i = tid; i < n_counters; i += kProjWaves * 64) counters[i] = 0u;
 
     // This block's vectors: n_rot for the rotation rows (first ones), of which
     // the last n_hash also go through the hash rows.
@@ -76,14 +76,14 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     const void* src = qblock ? Q : K;
     if (BF16) {
         const uint32_t* x2 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(src) + xrow0 * D);
-        for (int i = tid; i < n_rot * D / 2; i += blockDim.x) {
+        for (int i = tid; i < n_rot * D / 2; i += kProjWaves * 64) {
             const uint32_t u = x2[i];
             xs[2 * i] = __uint_as_float(u << 16);
             xs[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
         }
     } else {
         const float* xf = static_cast<const float*>(src) + xrow0 * D;
-        for (int i = tid; i < n_rot * D; i += blockDim.x) xs[i] = xf[i];
+        for (int i = tid; i < n_rot * D; i += kProjWaves * 64) xs[i] = xf[i];
     }
 
     // Roles: waves [0, RR*RVG) rotation rows, the next HR waves hash rows.

@@ -12,16 +12,19 @@
 // the first half to the second through LDS; the stage entry points run each
 // half on its own.
 //
-// Latency matters more than bandwidth here (batch 1 gives 8 blocks), so each
-// thread owns a contiguous run of up to 16 items held in registers and every
-// global load is issued once, up front.  Page scores are fp64 turned into
-// order-preserving 64-bit keys; a block min/max finds the bits they share, so
-// the MSB-first radix select starts below them, 11 bits (2048 LDS bins) per
-// pass.  Hamming distances are small integers: one LDS histogram and one scan
-// find the threshold.  Ordered output positions come from a single block scan
-// of per-thread (before-threshold, at-threshold) counts, so every output list
-// is ascending without a sort.  Inputs larger than 16 items per thread loop
-// over chunks and re-read them.
+// Latency matters more than bandwidth here (batch 1 gives 8 blocks).  Each
+// thread takes up to 16 items of a chunk of 16K, lane-strided (item
+// k * 1024 + tid) so every global load and store of a wave is contiguous, and
+// all of them are issued up front.  Page scores are fp64 turned into
+// order-preserving 64-bit keys; a block OR of (key ^ key of page 0) finds the
+// bits they all share, so the MSB-first radix select starts below them, 11
+// bits (2048 LDS bins) per pass.  Hamming distances are small integers: one
+// LDS histogram and one scan find the threshold.  The ordered compaction
+// reads per-item flags (pages) or distances (keys) back from LDS as a
+// contiguous run per thread, so a single block scan of packed (before,
+// at-threshold) counts gives every thread its first output position and the
+// output lists come out ascending without a sort.  Inputs of more than one
+// chunk loop over the chunks and re-read them.
 #include "hhr_internal.h"
 
 namespace hhr {
@@ -33,6 +36,7 @@ constexpr int kChunk = kSelThreads * kRun;  // items per chunk
 constexpr int kBits = 11;                   // radix digit width of the page select
 constexpr int kBins = 1 << kBits;
 constexpr int kListLds = 8192;              // kept-page ids staged in LDS
+constexpr uint16_t kNoKey = 0xFFFF;         // distance of a slot past the sequence
 
 __device__ __forceinline__ uint64_t order_key(double s) {
     const uint64_t u = (uint64_t)__double_as_longlong(s);
@@ -45,78 +49,89 @@ struct SelShared {
     int found[3];
     uint32_t red[2][16];
     int plist[kListLds];
+    union {
+        uint8_t pflag[kChunk];   // page select: bit 0 above the boundary bucket, bit 1 in it
+        uint16_t dist[kChunk];   // key select: Hamming distance per slot of the chunk
+    } u;
 };
 
-// Kept pages of one (b, h) into `out` (ascending, -1 padded) and, if given,
+// Kept pages of one (b, h) into `out` (ascending, -1 padded) and, if asked,
 // into LDS.  Returns the number kept.
 __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc, int NP, int keep, int max_keep,
-                                  int32_t* __restrict__ out, SelShared& sh, bool to_lds) {
+                                                  int32_t* __restrict__ out, SelShared& sh, bool to_lds) {
     const int tid = threadIdx.x;
+    for (int j = keep + tid; j < max_keep; j += kSelThreads) out[j] = -1;
+    if (keep == NP) {  // every page is kept
+        for (int j = tid; j < NP; j += kSelThreads) {
+            out[j] = j;
+            if (to_lds && j < kListLds) sh.plist[j] = j;
+        }
+        return keep;
+    }
     const int nchunks = (NP + kChunk - 1) / kChunk;
     const int run = nchunks <= 1 ? (NP + kSelThreads - 1) / kSelThreads : kRun;
     uint64_t key[kRun];
     auto load_chunk = [&](int c) {
-        const int p0 = c * kChunk + tid * run;
 #pragma unroll
-        for (int k = 0; k < kRun; ++k) key[k] = (k < run && p0 + k < NP) ? order_key(sc[p0 + k]) : 0;
+        for (int k = 0; k < kRun; ++k) {
+            const int i = c * kChunk + k * kSelThreads + tid;
+            key[k] = (k < run && i < NP) ? order_key(sc[i]) : 0;
+        }
     };
+    auto valid = [&](int c, int k) { return k < run && c * kChunk + k * kSelThreads + tid < NP; };
 
-    uint64_t prefix = 0, mask = 0;
-    int need = keep;
-    bool all_in = keep == NP;  // every page is kept
-    int shift = 64;
-    if (!all_in) {
-        // Bits every key shares: OR over all keys of (key ^ key of page 0).
-        const uint64_t ref = order_key(sc[0]);
-        uint64_t diff = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            load_chunk(c);
-            const int p0 = c * kChunk + tid * run;
+    // Bits every key shares: OR over all keys of (key ^ key of page 0).
+    const uint64_t ref = order_key(sc[0]);
+    uint64_t diff = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        load_chunk(c);
 #pragma unroll
-            for (int k = 0; k < kRun; ++k)
-                if (k < run && p0 + k < NP) diff |= key[k] ^ ref;
-        }
-        const uint32_t dh = wave_or((uint32_t)(diff >> 32)), dl = wave_or((uint32_t)diff);
-        if ((tid & 63) == 0) {
-            sh.red[0][tid >> 6] = dh;
-            sh.red[1][tid >> 6] = dl;
-        }
-        __syncthreads();
-        diff = 0;
-#pragma unroll
-        for (int w = 0; w < kSelThreads / 64; ++w) diff |= ((uint64_t)sh.red[0][w] << 32) | sh.red[1][w];
-        if (diff == 0) {
-            mask = ~0ull;  // every score is equal: the first `keep` pages win
-            prefix = ref;
-            shift = 0;
-        } else {
-            const int top = 63 - __clzll(diff);  // highest bit where scores differ
-            mask = top == 63 ? 0ull : ~0ull << (top + 1);
-            prefix = ref & mask;
-            shift = top + 1;
-        }
+        for (int k = 0; k < kRun; ++k)
+            if (valid(c, k)) diff |= key[k] ^ ref;
     }
+    const uint32_t dh = wave_or((uint32_t)(diff >> 32)), dl = wave_or((uint32_t)diff);
+    if ((tid & 63) == 0) {
+        sh.red[0][tid >> 6] = dh;
+        sh.red[1][tid >> 6] = dl;
+    }
+    __syncthreads();
+    diff = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) diff |= ((uint64_t)sh.red[0][w] << 32) | sh.red[1][w];
+    uint64_t prefix, mask;
+    int shift;
+    if (diff == 0) {
+        mask = ~0ull;  // every score is equal: the first `keep` pages win
+        prefix = ref;
+        shift = 0;
+    } else {
+        const int top = 63 - __clzll(diff);  // highest bit where scores differ
+        mask = top == 63 ? 0ull : ~0ull << (top + 1);
+        prefix = ref & mask;
+        shift = top + 1;
+    }
+    int need = keep;
+    bool all_in = false;  // the boundary bucket is kept whole
+
     // Radix passes below the shared bits.
     while (!all_in && shift > 0) {
         const int width = shift < kBits ? shift : kBits;
         shift -= width;
         const int nb = 1 << width;
-        for (int i = tid; i < nb; i += blockDim.x) sh.hist[i] = 0;
+        for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
             if (nchunks > 1) load_chunk(c);
-            const int p0 = c * kChunk + tid * run;
 #pragma unroll
             for (int k = 0; k < kRun; ++k)
-                if (k < run && p0 + k < NP && (key[k] & mask) == prefix)
-                    atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
+                if (valid(c, k) && (key[k] & mask) == prefix) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
         }
         __syncthreads();
         // Descending digits: thread i owns digits nb-1-2i and nb-2-2i.
         const int d0 = nb - 1 - 2 * tid, d1 = d0 - 1;
         const int c0 = d0 >= 0 ? sh.hist[d0] : 0, c1 = d1 >= 0 ? sh.hist[d1] : 0;
         int tot;
-        const int above = block_excl_scan(c0 + c1, sh.scan, tot);
+        const int above = block_excl_scan<kSelThreads>(c0 + c1, sh.scan, tot);
         if (above < need && above + c0 >= need) {
             sh.found[0] = d0; sh.found[1] = above; sh.found[2] = c0;
         } else if (above + c0 < need && above + c0 + c1 >= need) {
@@ -128,60 +143,78 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
         const int eq = sh.found[2];
         prefix |= (uint64_t)dig << shift;
         mask |= (uint64_t)(nb - 1) << shift;
-        if (eq == need) all_in = true;  // the whole boundary bucket is kept
+        if (eq == need) all_in = true;
         __syncthreads();
     }
 
     // Page p is kept iff its masked key beats the boundary bucket, or it is in
     // the bucket and (the bucket is kept whole, or it is among the first
-    // `need` of the bucket in page order).  One scan of packed (gt, eq) counts
-    // gives each thread its first output position.
+    // `need` of the bucket in page order).
+    const int cap = all_in ? 0x7fffffff : need;
     int base = 0, eq_base = 0;
     for (int c = 0; c < nchunks; ++c) {
-        if (nchunks > 1 || keep == NP) load_chunk(c);
-        const int p0 = c * kChunk + tid * run;
+        if (nchunks > 1) load_chunk(c);
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run) {
+                const uint64_t mk = key[k] & mask;
+                sh.u.pflag[k * kSelThreads + tid] =
+                    valid(c, k) ? (uint8_t)((mk > prefix) | ((mk == prefix) << 1)) : (uint8_t)0;
+            }
+        __syncthreads();
+        // Thread tid now owns the contiguous items [tid * run, tid * run + run).
+        uint8_t f[kRun];
         int n_gt = 0, n_eq = 0;
 #pragma unroll
-        for (int k = 0; k < kRun; ++k)
-            if (k < run && p0 + k < NP) {
-                const uint64_t mk = key[k] & mask;
-                n_gt += mk > prefix;
-                n_eq += mk == prefix;
-            }
+        for (int k = 0; k < kRun; ++k) {
+            f[k] = k < run ? sh.u.pflag[tid * run + k] : (uint8_t)0;
+            n_gt += f[k] & 1;
+            n_eq += f[k] >> 1;
+        }
         int tot;
-        const int packed = block_excl_scan((n_gt << 16) | n_eq, sh.scan, tot);
-        int gt_before = base + (packed >> 16), eq_rank = eq_base + (packed & 0xffff);
-        const int cap = all_in ? 0x7fffffff : need;
-        int pos = gt_before + (eq_rank < cap ? eq_rank : cap);
+        const int packed = block_excl_scan<kSelThreads>((n_gt << 16) | n_eq, sh.scan, tot);
+        int eq_rank = eq_base + (packed & 0xffff);
+        int pos = base + (packed >> 16) + (eq_rank < cap ? eq_rank : cap);
 #pragma unroll
-        for (int k = 0; k < kRun; ++k)
-            if (k < run && p0 + k < NP) {
-                const uint64_t mk = key[k] & mask;
-                bool in = mk > prefix;
-                if (mk == prefix) {
-                    in = eq_rank < cap;
-                    ++eq_rank;
-                }
-                if (in) {
-                    if (pos < max_keep) {
-                        out[pos] = p0 + k;
-                        if (to_lds && pos < kListLds) sh.plist[pos] = p0 + k;
-                    }
-                    ++pos;
-                }
+        for (int k = 0; k < kRun; ++k) {
+            bool in = f[k] & 1;
+            if (f[k] >> 1) {
+                in = eq_rank < cap;
+                ++eq_rank;
             }
+            if (in) {
+                const int p = c * kChunk + tid * run + k;
+                if (pos < max_keep) {
+                    out[pos] = p;
+                    if (to_lds && pos < kListLds) sh.plist[pos] = p;
+                }
+                ++pos;
+            }
+        }
         base += tot >> 16;
         eq_base += tot & 0xffff;
+        __syncthreads();  // pflag is rewritten by the next chunk
     }
-    for (int j = keep + tid; j < max_keep; j += blockDim.x) out[j] = -1;
     return keep;
+}
+
+template <int NW>
+__device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t, uint64_t (&kc)[NW]) {
+    if constexpr (NW == 2) {
+        const uint4 v = *reinterpret_cast<const uint4*>(ck + (int64_t)t * 2);
+        kc[0] = ((uint64_t)v.y << 32) | v.x;
+        kc[1] = ((uint64_t)v.w << 32) | v.z;
+    } else {
+        kc[0] = ck[t];
+    }
 }
 
 template <int NW, int G>
 __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ ck, const uint64_t* __restrict__ cqg,
-                                  const int32_t* __restrict__ pl, int np, bool list_in_lds, int L, int P,
-                                  int max_keep, int top_k, uint16_t* __restrict__ hm, int32_t* __restrict__ so,
-                                  int32_t* __restrict__ keff_out, SelShared& sh) {
+                                                  const int32_t* __restrict__ pl, int np, bool list_in_lds, int L,
+                                                  int P, int max_keep, int top_k, uint16_t* __restrict__ hm,
+                                                  int32_t* __restrict__ so, int32_t* __restrict__ keff_out,
+                                                  SelShared& sh) {
     constexpr int NB = NW * 64;
     constexpr int NBINS = G * NB + 1;
     const int tid = threadIdx.x;
@@ -190,28 +223,30 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
     uint64_t cq[G * NW];
 #pragma unroll
     for (int i = 0; i < G * NW; ++i) cq[i] = cqg[i];
-    for (int i = tid; i < NBINS; i += blockDim.x) sh.hist[i] = 0;
-    __syncthreads();
+    for (int i = tid; i < NBINS; i += kSelThreads) sh.hist[i] = 0;
 
     const int nchunks = (nslots + kChunk - 1) / kChunk;
     const int run = nchunks <= 1 ? (nslots + kSelThreads - 1) / kSelThreads : kRun;
     int Hreg[kRun];
     auto page_of = [&](int s) { return list_in_lds ? sh.plist[s >> lp] : pl[s >> lp]; };
+    // Distances of the chunk's slots c * kChunk + k * 1024 + tid (-1: no key).
     auto distances = [&](int c) {
-        const int c0 = c * kChunk + tid * run;
         uint64_t kc[kRun][NW];
-        bool ok[kRun];
 #pragma unroll
         for (int k = 0; k < kRun; ++k) {
-            const int s = c0 + k;
+            const int s = c * kChunk + k * kSelThreads + tid;
             int t = -1;
             if (k < run && s < nslots) {
                 t = page_of(s) * P + (s & (P - 1));
                 if (t < 0 || t >= L) t = -1;
             }
-            ok[k] = t >= 0;
+            Hreg[k] = t;
+            if (t >= 0) {
+                load_code<NW>(ck, t, kc[k]);
+            } else {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) kc[k][w] = ok[k] ? ck[(int64_t)t * NW + w] : 0;
+                for (int w = 0; w < NW; ++w) kc[k][w] = 0;
+            }
         }
 #pragma unroll
         for (int k = 0; k < kRun; ++k) {
@@ -220,21 +255,29 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
             for (int i = 0; i < G; ++i)
 #pragma unroll
                 for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
-            Hreg[k] = ok[k] ? hsum : -1;
+            Hreg[k] = Hreg[k] >= 0 ? hsum : -1;
         }
     };
+    auto stage = [&]() {  // the chunk's distances into LDS, lane-strided
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run) sh.u.dist[k * kSelThreads + tid] = Hreg[k] < 0 ? kNoKey : (uint16_t)Hreg[k];
+    };
+    __syncthreads();
 
     for (int c = 0; c < nchunks; ++c) {
         distances(c);
-        const int c0 = c * kChunk + tid * run;
 #pragma unroll
-        for (int k = 0; k < kRun; ++k)
-            if (k < run && c0 + k < nslots) {
-                hm[c0 + k] = Hreg[k] < 0 ? (uint16_t)0xFFFF : (uint16_t)Hreg[k];
+        for (int k = 0; k < kRun; ++k) {
+            const int s = c * kChunk + k * kSelThreads + tid;
+            if (k < run && s < nslots) {
+                hm[s] = Hreg[k] < 0 ? kNoKey : (uint16_t)Hreg[k];
                 if (Hreg[k] >= 0) atomicAdd(&sh.hist[Hreg[k]], 1);
             }
+        }
+        if (nchunks == 1) stage();
     }
-    for (int s = nslots + tid; s < max_keep * P; s += blockDim.x) hm[s] = 0xFFFF;
+    for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
     __syncthreads();
 
     // Threshold h*: the ascending cumulative count reaches k_eff.
@@ -243,7 +286,7 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
         const int b0 = 2 * tid;
         const int c0 = b0 < NBINS ? sh.hist[b0] : 0, c1 = b0 + 1 < NBINS ? sh.hist[b0 + 1] : 0;
         int nvalid;
-        const int below0 = block_excl_scan(c0 + c1, sh.scan, nvalid);
+        const int below0 = block_excl_scan<kSelThreads>(c0 + c1, sh.scan, nvalid);
         keff = nvalid < top_k ? nvalid : top_k;
         if (tid == 0) {
             sh.found[0] = NBINS;
@@ -265,37 +308,42 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
     // Keep H < h*, and the first `need` candidates with H == h* in slot order.
     int base = 0, eq_base = 0;
     for (int c = 0; c < nchunks; ++c) {
-        if (nchunks > 1) distances(c);
-        const int c0 = c * kChunk + tid * run;
+        if (nchunks > 1) {
+            distances(c);
+            stage();
+            __syncthreads();
+        }
+        // Thread tid owns the contiguous slots [tid * run, tid * run + run) of the chunk.
+        uint16_t hv[kRun];
         int n_lt = 0, n_eq = 0;
 #pragma unroll
-        for (int k = 0; k < kRun; ++k)
-            if (k < run && c0 + k < nslots && Hreg[k] >= 0) {
-                n_lt += Hreg[k] < hs;
-                n_eq += Hreg[k] == hs;
-            }
+        for (int k = 0; k < kRun; ++k) {
+            hv[k] = k < run ? sh.u.dist[tid * run + k] : kNoKey;
+            n_lt += hv[k] < hs;
+            n_eq += hv[k] == hs;
+        }
         int tot;
-        const int packed = block_excl_scan((n_lt << 16) | n_eq, sh.scan, tot);
+        const int packed = block_excl_scan<kSelThreads>((n_lt << 16) | n_eq, sh.scan, tot);
         int eq_rank = eq_base + (packed & 0xffff);
         int pos = base + (packed >> 16) + (eq_rank < need ? eq_rank : need);
 #pragma unroll
-        for (int k = 0; k < kRun; ++k)
-            if (k < run && c0 + k < nslots && Hreg[k] >= 0) {
-                bool in = Hreg[k] < hs;
-                if (Hreg[k] == hs) {
-                    in = eq_rank < need;
-                    ++eq_rank;
-                }
-                if (in) {
-                    const int s = c0 + k;
-                    if (pos < top_k) so[pos] = page_of(s) * P + (s & (P - 1));
-                    ++pos;
-                }
+        for (int k = 0; k < kRun; ++k) {
+            bool in = hv[k] < hs;
+            if (hv[k] == hs) {
+                in = eq_rank < need;
+                ++eq_rank;
             }
+            if (in) {
+                const int s = c * kChunk + tid * run + k;
+                if (pos < top_k) so[pos] = page_of(s) * P + (s & (P - 1));
+                ++pos;
+            }
+        }
         base += tot >> 16;
         eq_base += tot & 0xffff;
+        __syncthreads();  // dist is rewritten by the next chunk
     }
-    for (int j = keff + tid; j < top_k; j += blockDim.x) so[j] = -1;
+    for (int j = keff + tid; j < top_k; j += kSelThreads) so[j] = -1;
     if (tid == 0) *keff_out = keff;
 }
 
@@ -326,7 +374,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         np = n_pages[bh];
         np = np < 0 ? 0 : (np > max_keep ? max_keep : np);  // memory safety for a hand-filled workspace
         if (np <= kListLds) {
-            for (int i = threadIdx.x; i < np; i += blockDim.x) sh.plist[i] = pl[i];
+            for (int i = threadIdx.x; i < np; i += kSelThreads) sh.plist[i] = pl[i];
             list_in_lds = true;
         }
         __syncthreads();
