@@ -5,21 +5,75 @@
 // attention on the retrieved keys).
 //
 // gfx950 mapping, built for latency at batch 1: grid (splits, Hkv, B); a
-// block owns 256 consecutive entries of the KV head's selected list and each
-// of its 4 waves owns 64 of them.
-//  phase A (lane = key): the lane loads its whole K row in one batch and
-//    runs G independent fp32 FMA chains q_i . k; the queries are
-//    wave-uniform, so they arrive through scalar loads as SGPR operands;
-//  wave softmax per head over its 64 keys (butterfly max and sum);
-//  phase B (lane = dimension slice): all 64 V rows of the wave are loaded
-//    up front; the weights move from the key lanes with v_readlane;
-//  the 4 waves merge in LDS into the block's (o, m, l) per query head, and
-//    the last block of the KV head (device-scope counter) merges all splits
-//    with a log-sum-exp, writes out and resets the counter.
+// block owns 128 consecutive entries of the KV head's selected list, each of
+// its 4 waves 32 of them, and each 16-lane row of a wave 8 entries (entries
+// e, e + 4, ..., e + 28).  A row reads a whole K or V row with one 16-byte
+// load per lane (a wave instruction fetches 4 rows, fully coalesced), and
+// every K and V load of the block is issued before any arithmetic.
+//  scores: each lane dots its D/16 dimensions with the G queries, and four
+//    DPP rotations within the row leave the full dot product in every lane;
+//  softmax per row over its 8 keys, then the row accumulates p * v for its
+//    D/16 dimensions;
+//  the 16 row partials (o, m, l) of the block merge in LDS with a log-sum-exp
+//    into the split's partial, and the last block of the KV head
+//    (device-scope counter) merges all splits -- every partial load of a
+//    round in flight at once, online rescaling across rounds -- writes out
+//    and resets the counter.
 #include "hhr_internal.h"
 
 namespace hhr {
 namespace {
+
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Sum over the 16 lanes of a DPP row, returned to every lane of the row.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __int_as_float(dpp_i<kRowRor8, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowRor4, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowRor2, 0xf>(0, __float_as_int(x)));
+    x += __int_as_float(dpp_i<kRowRor1, 0xf>(0, __float_as_int(x)));
+    return x;
+}
+
+// Load this lane's D/16 elements of a K/V/Q row as raw 32-bit words.
+template <int D, bool BF16>
+__device__ __forceinline__ void load_slice(const void* base, int64_t row, int sub, uint32_t (&w)[BF16 ? D / 32 : D / 16]) {
+    constexpr int NWD = BF16 ? D / 32 : D / 16;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(base) + row * (BF16 ? D / 2 : D) + sub * NWD;
+    if constexpr (NWD == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int x = 0; x < NWD; x += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p + x);
+            w[x] = v.x; w[x + 1] = v.y; w[x + 2] = v.z; w[x + 3] = v.w;
+        }
+    }
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ float slice_elem(const uint32_t* w, int d) {
+    if (BF16) return __uint_as_float((d & 1) ? (w[d >> 1] & 0xffff0000u) : (w[d >> 1] << 16));
+    return __uint_as_float(w[d]);
+}
+
+// Split partials cross XCDs, whose L2s are not coherent with each other.  They
+// are written and read with relaxed agent-scope atomics (coherent per access)
+// and each block waits for its own stores before it bumps the split counter,
+// so no agent-scope fence -- a full L2 write-back per block -- is needed.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_agent2(const float* p) {
+    const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ float4 ld_agent4(const float* p) {
+    const float2 a = ld_agent2(p), b = ld_agent2(p + 2);
+    return make_float4(a.x, a.y, b.x, b.y);
+}
 
 template <int D, bool BF16, int G>
 __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q, const void* __restrict__ K,
@@ -28,238 +82,201 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
                                                      float* __restrict__ part_ml, uint32_t* __restrict__ counters,
                                                      float* __restrict__ out, int Hq, int Hkv, int T, int top_k,
                                                      int n_splits, float scale) {
-    constexpr int CH = kAttnChunk;            // keys per block (4 waves x 64)
-    constexpr int DPL = D / 64;               // dims per lane in phase B
-    constexpr int VB = BF16 ? 64 : 32;        // V rows in flight per batch
-    constexpr int MAXS = 64;                  // splits merged per round by the last block
-    __shared__ float wo[4][G][D];
-    __shared__ float wml[4][G][2];
+    constexpr int NI = 8;                     // entries per row
+    constexpr int CH = 16 * NI;               // entries per block (4 waves x 4 rows)
+    static_assert(CH == kAttnChunk, "split size");
+    constexpr int DPL = D / 16;               // dimensions per lane
+    constexpr int NWD = BF16 ? DPL / 2 : DPL; // 32-bit words per lane per row
+    constexpr int NP = 16;                    // row partials per block
+    constexpr int MAXS = 32;                  // splits merged per round by the last block
+    __shared__ float wo[NP][G][D];
+    __shared__ float wml[NP][G][2];
     __shared__ float cml[G][MAXS][2];
+    __shared__ float lred[256];
     __shared__ int last_flag;
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, sub = lane & 15;
+    const int rw = tid >> 4;                  // row of the block, 0..15
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t q0 = (int64_t)b * Hq + (int64_t)h * G;
     int keff = k_eff[bh];
     keff = keff < 0 ? 0 : (keff > top_k ? top_k : keff);
-    const int c0 = split * CH + wv * 64;                     // this wave's first list entry
-    const int n = keff - c0 < 0 ? 0 : (keff - c0 > 64 ? 64 : keff - c0);  // its keys (wave-uniform)
+    const int e0 = split * CH + (rw >> 2) * (4 * NI) + (rw & 3);  // entries e0 + 4j
 
+    // Indices, then every K and V load of the row.
+    int t[NI];
+    bool ok[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int e = e0 + 4 * j;
+        ok[j] = e < keff;
+        int tj = ok[j] ? sel[bh * top_k + e] : 0;
+        tj = (tj < 0 || tj >= T) ? 0 : tj;
+        t[j] = tj;
+    }
+    const int64_t kvb = bh * T;
+    uint32_t kw[NI][NWD], vw[NI][NWD];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) load_slice<D, BF16>(K, kvb + t[j], sub, kw[j]);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) load_slice<D, BF16>(V, kvb + t[j], sub, vw[j]);
+    float qv[G][DPL];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        uint32_t qw[NWD];
+        load_slice<D, BF16>(Q, q0 + i, sub, qw);
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) qv[i][d] = slice_elem<D, BF16>(qw, d);
+    }
+
+    // Scores of the row's entries for the G heads.
+    float sc[NI][G];
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) a = __builtin_fmaf(qv[i][d], slice_elem<D, BF16>(kw[j], d), a);
+            sc[j][i] = a;
+        }
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+        for (int i = 0; i < G; ++i) sc[j][i] = row_sum16(sc[j][i]);
+
+    // Row softmax and p * v over the row's entries.
     float m_i[G], l_i[G], o[G][DPL];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-        m_i[i] = -__builtin_inff();
-        l_i[i] = 0.f;
+        float mx = -__builtin_inff();
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[i][k] = 0.f;
+        for (int j = 0; j < NI; ++j)
+            if (ok[j]) mx = fmaxf(mx, sc[j][i] * scale);
+        float l = 0.f;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) o[i][d] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const float p = ok[j] ? __expf(sc[j][i] * scale - mx) : 0.f;
+            l += p;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) o[i][d] = __builtin_fmaf(p, slice_elem<D, BF16>(vw[j], d), o[i][d]);
+        }
+        m_i[i] = mx;
+        l_i[i] = l;
     }
-
-    if (n > 0) {
-        int t = lane < n ? sel[bh * top_k + c0 + lane] : 0;
-        t = (t < 0 || t >= T) ? 0 : t;
-        const int64_t kvb = bh * T;
-
-        // Phase A: logits of key `lane` for the G heads.
-        float s[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) s[i] = 0.f;
-        if (BF16) {
-            const uint4* kr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(K) + (kvb + t) * D);
-            uint4 u[D / 8];
-#pragma unroll
-            for (int x = 0; x < D / 8; ++x) u[x] = kr[x];
-            const uint32_t* qw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(Q) + q0 * D);
-#pragma unroll
-            for (int x = 0; x < D / 8; ++x) {
-                const uint32_t w4[4] = {u[x].x, u[x].y, u[x].z, u[x].w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float k0 = __uint_as_float(w4[q] << 16), k1 = __uint_as_float(w4[q] & 0xffff0000u);
-#pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        const uint32_t qq = qw[(i * D + 8 * x + 2 * q) / 2];
-                        s[i] = __builtin_fmaf(__uint_as_float(qq << 16), k0, s[i]);
-                        s[i] = __builtin_fmaf(__uint_as_float(qq & 0xffff0000u), k1, s[i]);
-                    }
-                }
-            }
-        } else {
-            const float4* kr = reinterpret_cast<const float4*>(static_cast<const float*>(K) + (kvb + t) * D);
-            float4 f[D / 4];
-#pragma unroll
-            for (int x = 0; x < D / 4; ++x) f[x] = kr[x];
-            const float* qf = static_cast<const float*>(Q) + q0 * D;
-#pragma unroll
-            for (int x = 0; x < D / 4; ++x) {
-                const float kv[4] = {f[x].x, f[x].y, f[x].z, f[x].w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int i = 0; i < G; ++i) s[i] = __builtin_fmaf(qf[i * D + 4 * x + q], kv[q], s[i]);
-            }
-        }
-
-        // Wave softmax over the wave's keys.
-        float p[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const float si = lane < n ? s[i] * scale : -__builtin_inff();
-            const float mx = wave_max(si);
-            p[i] = lane < n ? __expf(si - mx) : 0.f;
-            m_i[i] = mx;
-            l_i[i] = wave_sum(p[i]);
-        }
-
-        // Phase B: o_i[lane slice] = sum_j p_i[j] * v_j, rows loaded VB at a time.
-        for (int j0 = 0; j0 < n; j0 += VB) {
-            uint32_t vraw[VB][BF16 ? 1 : DPL];
-#pragma unroll
-            for (int j = 0; j < VB; ++j) {
-                const int tj = __builtin_amdgcn_readlane(t, (j0 + j) & 63);  // rows >= n are harmless, weight 0
-                if (BF16) {
-                    const uint16_t* vp = static_cast<const uint16_t*>(V) + (kvb + tj) * D + lane * DPL;
-                    vraw[j][0] = DPL == 2 ? *reinterpret_cast<const uint32_t*>(vp) : (uint32_t)vp[0] << 16;
-                } else {
-                    const float* vp = static_cast<const float*>(V) + (kvb + tj) * D + lane * DPL;
-#pragma unroll
-                    for (int k = 0; k < DPL; ++k) vraw[j][BF16 ? 0 : k] = __float_as_uint(vp[k]);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < VB; ++j) {
-                float vv[DPL];
-                if (BF16) {
-                    vv[0] = __uint_as_float(DPL == 2 ? vraw[j][0] << 16 : vraw[j][0]);
-                    if (DPL == 2) vv[DPL - 1] = __uint_as_float(vraw[j][0] & 0xffff0000u);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < DPL; ++k) vv[k] = __uint_as_float(vraw[j][BF16 ? 0 : k]);
-                }
-#pragma unroll
-                for (int i = 0; i < G; ++i) {
-                    const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                                    __builtin_bit_cast(int, p[i]), (j0 + j) & 63));
-#pragma unroll
-                    for (int k = 0; k < DPL; ++k) o[i][k] = __builtin_fmaf(pj, vv[k], o[i][k]);
-                }
-            }
-        }
-    }
-
-    // Merge the 4 waves of the block.
 #pragma unroll
     for (int i = 0; i < G; ++i) {
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) wo[wv][i][lane * DPL + k] = o[i][k];
-        if (lane == 0) {
-            wml[wv][i][0] = m_i[i];
-            wml[wv][i][1] = l_i[i];
+        for (int d = 0; d < DPL; ++d) wo[rw][i][sub * DPL + d] = o[i][d];
+        if (sub == 0) {
+            wml[rw][i][0] = m_i[i];
+            wml[rw][i][1] = l_i[i];
         }
     }
     __syncthreads();
+
+    // Merge the block's rows into this split's partial.
     const int blk_keys = keff - split * CH;
     if (blk_keys > 0) {
         for (int x = tid; x < G * D; x += 256) {
             const int i = x / D, d = x % D;
-            float M = wml[0][i][0];
+            float M = -__builtin_inff();
 #pragma unroll
-            for (int w = 1; w < 4; ++w) M = fmaxf(M, wml[w][i][0]);
+            for (int r = 0; r < NP; ++r) M = fmaxf(M, wml[r][i][0]);
             float acc = 0.f, L = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float sc = wml[w][i][1] > 0.f ? __expf(wml[w][i][0] - M) : 0.f;
-                acc = __builtin_fmaf(wo[w][i][d], sc, acc);
-                L = __builtin_fmaf(wml[w][i][1], sc, L);
+            for (int r = 0; r < NP; ++r) {
+                const float f = wml[r][i][1] > 0.f ? __expf(wml[r][i][0] - M) : 0.f;
+                acc = __builtin_fmaf(wo[r][i][d], f, acc);
+                L = __builtin_fmaf(wml[r][i][1], f, L);
             }
-            part_o[((q0 + i) * n_splits + split) * D + d] = acc;
+            st_agent(part_o + ((q0 + i) * n_splits + split) * D + d, acc);
             if (d == 0) {
-                part_ml[((q0 + i) * n_splits + split) * 2] = M;
-                part_ml[((q0 + i) * n_splits + split) * 2 + 1] = L;
+                st_agent(part_ml + ((q0 + i) * n_splits + split) * 2, M);
+                st_agent(part_ml + ((q0 + i) * n_splits + split) * 2 + 1, L);
             }
         }
     }
 
     // The last block of this KV head merges the splits.
-    __threadfence();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    if (tid == 0) last_flag = atomicAdd(&counters[bh], 1u) == (uint32_t)(n_splits - 1);
+    if (tid == 0)
+        last_flag = __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (uint32_t)(n_splits - 1);
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();
 
+    // Columns of 4 output floats; NGR groups of threads split the splits.
     const int used = (keff + CH - 1) / CH;
-    constexpr int R = (G * D + 255) / 256;
-    float acc[R], Mx[R], Ls[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        acc[r] = 0.f;
-        Ls[r] = 0.f;
-        Mx[r] = -__builtin_inff();
-    }
-    // Split maxima first (all splits), then weighted sums in rounds of MAXS.
+    constexpr int NC = G * D / 4, NGR = 256 / NC, NB = 16;  // NB: loads in flight per batch
+    const int c = tid % NC, g = tid / NC, qi = c / (D / 4);
+    const bool act = g < NGR;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lacc = 0.f, Mrun = -__builtin_inff();
     for (int s0 = 0; s0 < used; s0 += MAXS) {
         const int ns = used - s0 < MAXS ? used - s0 : MAXS;
         for (int x = tid; x < G * ns; x += 256) {
             const int i = x / ns, sI = x % ns;
-            const float* ml = part_ml + ((q0 + i) * n_splits + s0 + sI) * 2;
-            cml[i][sI][0] = ml[0];
-            cml[i][sI][1] = ml[1];
+            const float2 ml = ld_agent2(part_ml + ((q0 + i) * n_splits + s0 + sI) * 2);
+            cml[i][sI][0] = ml.x;
+            cml[i][sI][1] = ml.y;
         }
         __syncthreads();
+        if (act) {
+            float Mr = Mrun;
+            for (int sI = 0; sI < ns; ++sI) Mr = fmaxf(Mr, cml[qi][sI][0]);
+            const float f = Mrun == -__builtin_inff() ? 0.f : __expf(Mrun - Mr);
+            acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+            Lacc *= f;
+            Mrun = Mr;
+            const float* po = part_o + ((q0 + qi) * n_splits + s0) * D + (c % (D / 4)) * 4;
+            for (int b0 = g; b0 < ns; b0 += NB * NGR) {
+                float4 v[NB];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int x = tid + r * 256;
-            if (x < G * D) {
-                const int i = x / D;
-                for (int sI = 0; sI < ns; ++sI) Mx[r] = fmaxf(Mx[r], cml[i][sI][0]);
-            }
-        }
-        __syncthreads();
-    }
-    for (int s0 = 0; s0 < used; s0 += MAXS) {
-        const int ns = used - s0 < MAXS ? used - s0 : MAXS;
-        for (int x = tid; x < G * ns; x += 256) {
-            const int i = x / ns, sI = x % ns;
-            const float* ml = part_ml + ((q0 + i) * n_splits + s0 + sI) * 2;
-            cml[i][sI][0] = ml[0];
-            cml[i][sI][1] = ml[1];
-        }
-        __syncthreads();
+                for (int u = 0; u < NB; ++u) {
+                    const int sI = b0 + u * NGR;
+                    v[u] = sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int x = tid + r * 256;
-            if (x < G * D) {
-                const int i = x / D, d = x % D;
-                const float* po = part_o + ((q0 + i) * n_splits + s0) * D + d;
-                int sI = 0;
-                for (; sI + 8 <= ns; sI += 8) {
-                    float v8[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) v8[u] = po[(int64_t)(sI + u) * D];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const float w = __expf(cml[i][sI + u][0] - Mx[r]);
-                        acc[r] = __builtin_fmaf(v8[u], w, acc[r]);
-                        Ls[r] = __builtin_fmaf(cml[i][sI + u][1], w, Ls[r]);
+                for (int u = 0; u < NB; ++u) {
+                    const int sI = b0 + u * NGR;
+                    if (sI < ns && cml[qi][sI][1] > 0.f) {
+                        const float w = __expf(cml[qi][sI][0] - Mr);
+                        acc.x = __builtin_fmaf(v[u].x, w, acc.x);
+                        acc.y = __builtin_fmaf(v[u].y, w, acc.y);
+                        acc.z = __builtin_fmaf(v[u].z, w, acc.z);
+                        acc.w = __builtin_fmaf(v[u].w, w, acc.w);
+                        Lacc = __builtin_fmaf(cml[qi][sI][1], w, Lacc);
                     }
                 }
-                for (; sI < ns; ++sI) {
-                    const float w = __expf(cml[i][sI][0] - Mx[r]);
-                    acc[r] = __builtin_fmaf(po[(int64_t)sI * D], w, acc[r]);
-                    Ls[r] = __builtin_fmaf(cml[i][sI][1], w, Ls[r]);
-                }
             }
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int x = tid + r * 256;
-        if (x < G * D) out[(q0 + x / D) * D + x % D] = used > 0 ? acc[r] / Ls[r] : 0.f;
+    // Sum the groups and normalise.
+    float4* red = reinterpret_cast<float4*>(&wo[0][0][0]);  // NGR * NC <= 16 * G * D / 4 float4
+    if (act) {
+        red[g * NC + c] = acc;
+        lred[g * NC + c] = Lacc;
     }
-    if (tid == 0) counters[bh] = 0u;  // ready for the next call
+    __syncthreads();
+    if (act && g == 0) {
+        for (int r = 1; r < NGR; ++r) {
+            const float4 a = red[r * NC + c];
+            acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+            Lacc += lred[r * NC + c];
+        }
+        const float inv = Lacc > 0.f ? 1.f / Lacc : 0.f;
+        *reinterpret_cast<float4*>(out + (q0 + qi) * D + (c % (D / 4)) * 4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n) {

@@ -19,7 +19,7 @@ struct Shape {
 };
 
 // Attention keys handled by one block (one split) of the attend kernel.
-constexpr int kAttnChunk = 256;
+constexpr int kAttnChunk = 128;
 
 // Region offsets of the decode workspace (bytes, 256-aligned).
 struct WsLayout {
