@@ -17,42 +17,76 @@ namespace {
 // of the two products is zero, the other is the larger of q*kmax and q*kmin,
 // and every such product is exact in fp64.  q_split is uniform across the
 // block (scalar loads).
-template <int D, int G, int UNROLL>
+//
+// The order of the sum ties each page to one lane, so a launch has one wave
+// per SIMD at 64K pages; the stream stays busy because every lane keeps the
+// next batch of U float4 loads in flight while it sums the current one.  The
+// query terms are staged once per block in LDS and read as broadcasts.
+template <int G, int U>
+__device__ __forceinline__ void bound_batch(const float4 (&v)[U], const double2* __restrict__ qs, int j0,
+                                            double (&acc)[G]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int d = 2 * (j0 + u);
+        const double a0 = v[u].x, c0 = v[u].y, a1 = v[u].z, c1 = v[u].w;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const double2 q0 = qs[d * G + i], q1 = qs[(d + 1) * G + i];
+            acc[i] = __builtin_fma(q0.x, a0, acc[i]);
+            acc[i] = __builtin_fma(q0.y, c0, acc[i]);
+            acc[i] = __builtin_fma(q1.x, a1, acc[i]);
+            acc[i] = __builtin_fma(q1.y, c1, acc[i]);
+        }
+    }
+}
+
+template <int D, int G, int U>
 __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
                                                          int64_t NPB, int64_t NPmax) {
+    constexpr int NJ = D / 2;  // float4 per page
+    static_assert(NJ % U == 0, "batches");
+    __shared__ double2 qs[D * G];  // (max(q,0), min(q,0)) per dimension and query head
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
     const int64_t NP = n_pages_of(L, P);
     const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if ((int64_t)blockIdx.x * 256 >= NP) return;
+    if ((int64_t)blockIdx.x * 256 >= NP) return;  // block-uniform
+
+    const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
+    for (int x = threadIdx.x; x < D * G; x += 256) qs[x] = qg[x];
+    __syncthreads();
     if (p >= NP) return;
 
     const float4* mp = reinterpret_cast<const float4*>(meta) + (bh * NPB + p / 64) * (D / 2) * 64 + (p & 63);
-    const double* qs = q_split + bh * D * G * 2;
     double acc[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.0;
 
-    for (int j0 = 0; j0 < D / 2; j0 += UNROLL) {
-        float4 v[UNROLL];
+    // Double buffering, fully unrolled: batch k + 1 is in flight while batch k
+    // is summed.  The empty asm statements are compiler barriers for memory
+    // operations, so the loads stay where they are written.
+    constexpr int NBT = NJ / U;
+    float4 A[U], B[U];
+    auto load = [&](float4 (&v)[U], int k) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = mp[(int64_t)(j0 + u) * 64];
+        for (int u = 0; u < U; ++u) v[u] = mp[(int64_t)(k * U + u) * 64];
+    };
+    load(A, 0);
+    asm volatile("" ::: "memory");
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int d = 2 * (j0 + u);
-            const double a0 = v[u].x, c0 = v[u].y, a1 = v[u].z, c1 = v[u].w;
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                acc[i] = __builtin_fma(qs[(d * G + i) * 2], a0, acc[i]);
-                acc[i] = __builtin_fma(qs[(d * G + i) * 2 + 1], c0, acc[i]);
-                acc[i] = __builtin_fma(qs[((d + 1) * G + i) * 2], a1, acc[i]);
-                acc[i] = __builtin_fma(qs[((d + 1) * G + i) * 2 + 1], c1, acc[i]);
-            }
-        }
+    for (int k = 0; k < NBT; k += 2) {
+        if (k + 1 < NBT) load(B, k + 1);
+        asm volatile("" ::: "memory");
+        bound_batch<G, U>(A, qs, k * U, acc);
+        asm volatile("" ::: "memory");
+        if (k + 2 < NBT) load(A, k + 2);
+        asm volatile("" ::: "memory");
+        if (k + 1 < NBT) bound_batch<G, U>(B, qs, (k + 1) * U, acc);
+        asm volatile("" ::: "memory");
     }
     double S = acc[0];
 #pragma unroll
