@@ -140,7 +140,11 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     l.sel = take(BH * (size_t)top_k * sizeof(int32_t));
     l.k_eff = take(BH * sizeof(int32_t));
     l.partial = take(BQ * (size_t)l.n_splits * (s.D + 2) * sizeof(float));
-    l.counters = take(BH * sizeof(uint32_t));
+    l.counters = take(2 * BH * sizeof(uint32_t));
+    const size_t slots = (size_t)max_keep * s.P;
+    l.sel_splits = (slots >= 4096 && slots <= (size_t)kSelChunk && max_keep <= kSelListLds) ? kSelSplit : 1;
+    l.kscratch_per_bh = l.sel_splits > 1 ? (size_t)l.sel_splits * (s.G * s.NB + 1) + slots : 0;
+    l.kscratch = take(BH * l.kscratch_per_bh * sizeof(uint32_t));
     l.total = off;
     return l;
 }
@@ -317,7 +321,7 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         p.code_q = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_q);
         p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
         p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
-        p.n_counters = a.s.B * a.s.Hkv;
+        p.n_counters = 2 * a.s.B * a.s.Hkv;
         HHR_TRY(hip_check(launch_project(a.s, p, st), "append + qprep launch"));
     } else {
         if (max_append > 0)

@@ -313,12 +313,14 @@ hipError_t attend_dt(const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t st) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_attend(const DecodeArgs& a, bool zero_counters, hipStream_t st) {
     if (zero_counters) {
-        const int n = a.s.B * a.s.Hkv;
-        hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
-                           reinterpret_cast<uint32_t*>(a.ws + a.lay.counters), n);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t*>(a.ws + a.lay.counters), a.s.B * a.s.Hkv, st);
         if (e != hipSuccess) return e;
     }
     const Shape& s = a.s;

@@ -21,10 +21,20 @@ struct Shape {
 // Attention keys handled by one block (one split) of the attend kernel.
 constexpr int kAttnChunk = 128;
 
-// Region offsets of the decode workspace (bytes, 256-aligned).
+// Key select: candidate slots per block-local chunk, and blocks per (b, h)
+// sharing the Hamming scan when every candidate fits one chunk.
+constexpr int kSelChunk = 16384;
+constexpr int kSelSplit = 4;
+constexpr int kSelListLds = 8192;  // kept-page ids the select kernel holds in LDS
+
+// Region offsets of the decode workspace (bytes, 256-aligned).  counters:
+// [0, B*Hkv) attention splits, [B*Hkv, 2*B*Hkv) key-select blocks.  kscratch
+// (private): per (b, h), sel_splits Hamming histograms then one distance per
+// candidate slot, used when sel_splits > 1.
 struct WsLayout {
-    size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters, total;
-    int n_splits;
+    size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters, kscratch, total;
+    int n_splits, sel_splits;
+    size_t kscratch_per_bh;  // u32 entries per (b, h)
 };
 
 WsLayout ws_layout(const Shape& s, int max_keep, int top_k);
@@ -73,6 +83,7 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t stream);  // pages, th
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_attend(const DecodeArgs& a, bool zero_counters, hipStream_t stream);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -35,7 +35,8 @@ constexpr int kRun = 16;                    // items per thread per chunk
 constexpr int kChunk = kSelThreads * kRun;  // items per chunk
 constexpr int kBits = 11;                   // radix digit width of the page select
 constexpr int kBins = 1 << kBits;
-constexpr int kListLds = 8192;              // kept-page ids staged in LDS
+constexpr int kListLds = kSelListLds;       // kept-page ids staged in LDS
+static_assert(kChunk == kSelChunk, "chunk size");
 constexpr uint16_t kNoKey = 0xFFFF;         // distance of a slot past the sequence
 
 __device__ __forceinline__ uint64_t order_key(double s) {
@@ -43,27 +44,45 @@ __device__ __forceinline__ uint64_t order_key(double s) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+constexpr int kRefine = 64;                 // boundary-bucket size ranked exactly by one wave
+
 struct SelShared {
     int hist[kBins];
     int scan[32];
     int found[3];
     uint32_t red[2][16];
+    int n_bucket;                           // boundary-bucket items gathered for the exact rank
+    int bidx[kRefine];
+    uint64_t bkey[kRefine];
+    uint64_t thr_key;                       // the keep-th (key, page) in (key desc, page asc)
+    int thr_idx;
+    int last;                               // this block finishes the key select
     int plist[kListLds];
     union {
-        uint8_t pflag[kChunk];   // page select: bit 0 above the boundary bucket, bit 1 in it
+        uint8_t pflag[kChunk];   // page select: bit 0 kept outright, bit 1 in the boundary bucket
         uint16_t dist[kChunk];   // key select: Hamming distance per slot of the chunk
     } u;
 };
 
 // Kept pages of one (b, h) into `out` (ascending, -1 padded) and, if asked,
-// into LDS.  Returns the number kept.
+// into LDS.  Returns the number kept.  `pre` holds the keys of the first
+// chunk when the caller loaded them (lane-strided, any value past NP).
+//
+// One 11-bit radix pass below the bits all keys share usually leaves a
+// boundary bucket of a few pages.  If it has at most 64, one wave ranks them
+// exactly by (key desc, page asc) and the keep-th of that order, (kt, it),
+// decides every page: kept iff key > kt or (key == kt and page <= it).
+// Otherwise further passes narrow the bucket and the compaction keeps the
+// first `need` pages of the final bucket in page order.
 __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc, int NP, int keep, int max_keep,
-                                                  int32_t* __restrict__ out, SelShared& sh, bool to_lds) {
+                                                  int32_t* __restrict__ out, bool write_out, SelShared& sh,
+                                                  bool to_lds, const uint64_t (&pre)[kRun], bool preloaded) {
     const int tid = threadIdx.x;
-    for (int j = keep + tid; j < max_keep; j += kSelThreads) out[j] = -1;
+    if (write_out)
+        for (int j = keep + tid; j < max_keep; j += kSelThreads) out[j] = -1;
     if (keep == NP) {  // every page is kept
         for (int j = tid; j < NP; j += kSelThreads) {
-            out[j] = j;
+            if (write_out) out[j] = j;
             if (to_lds && j < kListLds) sh.plist[j] = j;
         }
         return keep;
@@ -75,25 +94,34 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
 #pragma unroll
         for (int k = 0; k < kRun; ++k) {
             const int i = c * kChunk + k * kSelThreads + tid;
-            key[k] = (k < run && i < NP) ? order_key(sc[i]) : 0;
+            key[k] = order_key(sc[i < NP ? i : 0]);  // entries past NP are masked by valid()
         }
     };
     auto valid = [&](int c, int k) { return k < run && c * kChunk + k * kSelThreads + tid < NP; };
 
     // Bits every key shares: OR over all keys of (key ^ key of page 0).
-    const uint64_t ref = order_key(sc[0]);
     uint64_t diff = 0;
-    for (int c = 0; c < nchunks; ++c) {
-        load_chunk(c);
+    const uint64_t ref = order_key(sc[0]);
+    if (nchunks == 1 && preloaded) {
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) key[k] = pre[k];
 #pragma unroll
         for (int k = 0; k < kRun; ++k)
-            if (valid(c, k)) diff |= key[k] ^ ref;
+            if (valid(0, k)) diff |= key[k] ^ ref;
+    } else {
+        for (int c = 0; c < nchunks; ++c) {
+            load_chunk(c);
+#pragma unroll
+            for (int k = 0; k < kRun; ++k)
+                if (valid(c, k)) diff |= key[k] ^ ref;
+        }
     }
     const uint32_t dh = wave_or((uint32_t)(diff >> 32)), dl = wave_or((uint32_t)diff);
     if ((tid & 63) == 0) {
         sh.red[0][tid >> 6] = dh;
         sh.red[1][tid >> 6] = dl;
     }
+    if (tid == 0) sh.n_bucket = 0;
     __syncthreads();
     diff = 0;
 #pragma unroll
@@ -111,10 +139,13 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
         shift = top + 1;
     }
     int need = keep;
-    bool all_in = false;  // the boundary bucket is kept whole
+    bool all_in = false;   // the boundary bucket is kept whole
+    bool by_pair = false;  // the exact (kt, it) rule decides
+    uint64_t kt = 0;
+    int it = 0;
 
     // Radix passes below the shared bits.
-    while (!all_in && shift > 0) {
+    while (!all_in && !by_pair && shift > 0) {
         const int width = shift < kBits ? shift : kBits;
         shift -= width;
         const int nb = 1 << width;
@@ -143,13 +174,44 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
         const int eq = sh.found[2];
         prefix |= (uint64_t)dig << shift;
         mask |= (uint64_t)(nb - 1) << shift;
-        if (eq == need) all_in = true;
+        if (eq == need) {
+            all_in = true;
+        } else if (nchunks == 1 && eq <= kRefine) {
+            // Rank the bucket's pages exactly with one wave.
+#pragma unroll
+            for (int k = 0; k < kRun; ++k)
+                if (valid(0, k) && (key[k] & mask) == prefix) {
+                    const int slot = atomicAdd(&sh.n_bucket, 1);
+                    sh.bkey[slot] = key[k];
+                    sh.bidx[slot] = k * kSelThreads + tid;
+                }
+            __syncthreads();
+            if (tid < 64) {
+                const int n = sh.n_bucket;
+                const uint64_t mk = tid < n ? sh.bkey[tid] : 0;
+                const int mi = tid < n ? sh.bidx[tid] : 0;
+                int rank = 0;
+                for (int j = 0; j < n; ++j) {
+                    const uint64_t kj = sh.bkey[j];
+                    rank += kj > mk || (kj == mk && sh.bidx[j] < mi);
+                }
+                if (tid < n && rank == need - 1) {
+                    sh.thr_key = mk;
+                    sh.thr_idx = mi;
+                }
+            }
+            __syncthreads();
+            kt = sh.thr_key;
+            it = sh.thr_idx;
+            by_pair = true;
+        }
         __syncthreads();
     }
 
-    // Page p is kept iff its masked key beats the boundary bucket, or it is in
-    // the bucket and (the bucket is kept whole, or it is among the first
-    // `need` of the bucket in page order).
+    // Page p is kept iff (by_pair) its (key, p) is at or before (kt, it) in
+    // (key desc, page asc) order; else iff its masked key beats the boundary
+    // bucket, or it is in the bucket and (the bucket is kept whole, or it is
+    // among the first `need` of the bucket in page order).
     const int cap = all_in ? 0x7fffffff : need;
     int base = 0, eq_base = 0;
     for (int c = 0; c < nchunks; ++c) {
@@ -157,17 +219,26 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
 #pragma unroll
         for (int k = 0; k < kRun; ++k)
             if (k < run) {
-                const uint64_t mk = key[k] & mask;
-                sh.u.pflag[k * kSelThreads + tid] =
-                    valid(c, k) ? (uint8_t)((mk > prefix) | ((mk == prefix) << 1)) : (uint8_t)0;
+                const int i = c * kChunk + k * kSelThreads + tid;
+                uint8_t f = 0;
+                if (valid(c, k)) {
+                    if (by_pair) {
+                        f = key[k] > kt || (key[k] == kt && i <= it);
+                    } else {
+                        const uint64_t mk = key[k] & mask;
+                        f = (uint8_t)((mk > prefix) | ((mk == prefix) << 1));
+                    }
+                }
+                sh.u.pflag[k * kSelThreads + tid] = f;
             }
         __syncthreads();
         // Thread tid now owns the contiguous items [tid * run, tid * run + run).
         uint8_t f[kRun];
         int n_gt = 0, n_eq = 0;
 #pragma unroll
+        for (int k = 0; k < kRun; ++k) f[k] = k < run ? sh.u.pflag[tid * run + k] : (uint8_t)0;
+#pragma unroll
         for (int k = 0; k < kRun; ++k) {
-            f[k] = k < run ? sh.u.pflag[tid * run + k] : (uint8_t)0;
             n_gt += f[k] & 1;
             n_eq += f[k] >> 1;
         }
@@ -185,7 +256,7 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
             if (in) {
                 const int p = c * kChunk + tid * run + k;
                 if (pos < max_keep) {
-                    out[pos] = p;
+                    if (write_out) out[pos] = p;
                     if (to_lds && pos < kListLds) sh.plist[pos] = p;
                 }
                 ++pos;
@@ -209,12 +280,28 @@ __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t
     }
 }
 
-template <int NW, int G>
+// LDSLIST: the kept-page list is read from LDS (else from the workspace); a
+// compile-time choice, so every read is a plain LDS or global load rather
+// than a generic one that waits on both queues.
+__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// S > 1 (every candidate in one chunk, the page list in LDS): the S blocks of
+// a (b, h) each scan 1/S of the candidate slots and publish their distances
+// and histogram with agent-scope stores (coherent across XCDs, no L2
+// write-back); the last block to bump the counter merges the histograms,
+// gathers the distances into LDS and runs the threshold and the compaction.
+template <int NW, int G, bool LDSLIST>
 __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ ck, const uint64_t* __restrict__ cqg,
-                                                  const int32_t* __restrict__ pl, int np, bool list_in_lds, int L,
+                                                  const int32_t* __restrict__ pl, int np, int L,
                                                   int P, int max_keep, int top_k, uint16_t* __restrict__ hm,
                                                   int32_t* __restrict__ so, int32_t* __restrict__ keff_out,
-                                                  SelShared& sh) {
+                                                  SelShared& sh, int split, int S, uint32_t* __restrict__ kh,
+                                                  uint32_t* __restrict__ kd, uint32_t* __restrict__ kcnt) {
     constexpr int NB = NW * 64;
     constexpr int NBINS = G * NB + 1;
     const int tid = threadIdx.x;
@@ -228,26 +315,25 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
     const int nchunks = (nslots + kChunk - 1) / kChunk;
     const int run = nchunks <= 1 ? (nslots + kSelThreads - 1) / kSelThreads : kRun;
     int Hreg[kRun];
-    auto page_of = [&](int s) { return list_in_lds ? sh.plist[s >> lp] : pl[s >> lp]; };
+    auto page_of = [&](int s) { return LDSLIST ? sh.plist[s >> lp] : pl[s >> lp]; };
     // Distances of the chunk's slots c * kChunk + k * 1024 + tid (-1: no key).
     auto distances = [&](int c) {
         uint64_t kc[kRun][NW];
+        // Every page lookup, then every code load, before any use; the item
+        // guard is uniform (a scalar branch), the lane guard only clamps.
 #pragma unroll
         for (int k = 0; k < kRun; ++k) {
-            const int s = c * kChunk + k * kSelThreads + tid;
-            int t = -1;
-            if (k < run && s < nslots) {
-                t = page_of(s) * P + (s & (P - 1));
-                if (t < 0 || t >= L) t = -1;
-            }
-            Hreg[k] = t;
-            if (t >= 0) {
-                load_code<NW>(ck, t, kc[k]);
-            } else {
-#pragma unroll
-                for (int w = 0; w < NW; ++w) kc[k][w] = 0;
+            Hreg[k] = -1;
+            if (k < run) {
+                const int s = c * kChunk + k * kSelThreads + tid;
+                const int ss = s < nslots ? s : 0;
+                const int t = page_of(ss) * P + (ss & (P - 1));
+                Hreg[k] = (s < nslots && t >= 0 && t < L) ? t : -1;
             }
         }
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < run) load_code<NW>(ck, Hreg[k] >= 0 ? Hreg[k] : 0, kc[k]);
 #pragma unroll
         for (int k = 0; k < kRun; ++k) {
             int hsum = 0;
@@ -265,20 +351,96 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
     };
     __syncthreads();
 
-    for (int c = 0; c < nchunks; ++c) {
-        distances(c);
+    if (LDSLIST && S > 1) {
+        const int per = (nslots + S - 1) / S;
+        const int lo = split * per, hi = lo + per < nslots ? lo + per : nslots;
+        const int kr = hi > lo ? (hi - lo + kSelThreads - 1) / kSelThreads : 0;
+        uint64_t kc[kRun][NW];
 #pragma unroll
-        for (int k = 0; k < kRun; ++k) {
-            const int s = c * kChunk + k * kSelThreads + tid;
-            if (k < run && s < nslots) {
-                hm[s] = Hreg[k] < 0 ? kNoKey : (uint16_t)Hreg[k];
-                if (Hreg[k] >= 0) atomicAdd(&sh.hist[Hreg[k]], 1);
+        for (int k = 0; k < kRun; ++k) {  // lookups, then every code load, before any use
+            Hreg[k] = -1;
+            if (k < kr) {
+                const int s = lo + k * kSelThreads + tid;
+                const int ss = s < hi ? s : 0;
+                const int t = sh.plist[ss >> lp] * P + (ss & (P - 1));
+                Hreg[k] = (s < hi && t >= 0 && t < L) ? t : -1;
             }
         }
-        if (nchunks == 1) stage();
+#pragma unroll
+        for (int k = 0; k < kRun; ++k)
+            if (k < kr) load_code<NW>(ck, Hreg[k] >= 0 ? Hreg[k] : 0, kc[k]);
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            const int s = lo + k * kSelThreads + tid;
+            if (k >= kr) continue;
+            int hsum = 0;
+#pragma unroll
+            for (int i = 0; i < G; ++i)
+#pragma unroll
+                for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
+            if (Hreg[k] >= 0) atomicAdd(&sh.hist[hsum], 1);
+            if (s < hi) {
+                const uint16_t hv = Hreg[k] < 0 ? kNoKey : (uint16_t)hsum;
+                hm[s] = hv;
+                st_agent_u32(kd + s, hv);
+            }
+        }
+        if (split == 0)
+            for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
+        __syncthreads();
+        for (int i = tid; i < NBINS; i += kSelThreads) st_agent_u32(kh + split * NBINS + i, (uint32_t)sh.hist[i]);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's distance and histogram stores are complete
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (tid == 0)
+            sh.last = __hip_atomic_fetch_add(kcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1);
+        __syncthreads();
+        if (!sh.last) return;
+        // Every load of the gather is issued before any of them is used.
+        constexpr int HPT = (NBINS + kSelThreads - 1) / kSelThreads;  // histogram bins per thread
+        uint32_t hv[HPT][kSelSplit], dv[kRun];
+#pragma unroll
+        for (int r = 0; r < HPT; ++r)
+#pragma unroll
+            for (int j = 0; j < kSelSplit; ++j) {
+                const int i = tid + r * kSelThreads;
+                hv[r][j] = ld_agent_u32(kh + j * NBINS + (i < NBINS ? i : 0));
+            }
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            const int s = k * kSelThreads + tid;
+            if (k < run) dv[k] = ld_agent_u32(kd + (s < nslots ? s : 0));
+        }
+#pragma unroll
+        for (int r = 0; r < HPT; ++r) {
+            const int i = tid + r * kSelThreads;
+            uint32_t sum = 0;
+#pragma unroll
+            for (int j = 0; j < kSelSplit; ++j) sum += hv[r][j];
+            if (i < NBINS) sh.hist[i] = (int)sum;
+        }
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            const int s = k * kSelThreads + tid;
+            if (k < run) sh.u.dist[s] = s < nslots ? (uint16_t)dv[k] : kNoKey;
+        }
+        if (tid == 0) st_agent_u32(kcnt, 0u);  // ready for the next call
+        __syncthreads();
+    } else {
+        for (int c = 0; c < nchunks; ++c) {
+            distances(c);
+#pragma unroll
+            for (int k = 0; k < kRun; ++k) {
+                const int s = c * kChunk + k * kSelThreads + tid;
+                if (k < run && s < nslots) hm[s] = Hreg[k] < 0 ? kNoKey : (uint16_t)Hreg[k];
+                if (Hreg[k] >= 0) atomicAdd(&sh.hist[Hreg[k]], 1);
+            }
+            if (nchunks == 1) stage();
+        }
+        for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
+        __syncthreads();
     }
-    for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
-    __syncthreads();
 
     // Threshold h*: the ascending cumulative count reaches k_eff.
     int hs, need, keff;
@@ -315,10 +477,21 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
         }
         // Thread tid owns the contiguous slots [tid * run, tid * run + run) of the chunk.
         uint16_t hv[kRun];
+        int pg[kRun];
         int n_lt = 0, n_eq = 0;
 #pragma unroll
         for (int k = 0; k < kRun; ++k) {
-            hv[k] = k < run ? sh.u.dist[tid * run + k] : kNoKey;
+            hv[k] = kNoKey;
+            pg[k] = 0;
+            if (k < run) {
+                hv[k] = sh.u.dist[tid * run + k];
+                const int s = c * kChunk + tid * run + k;
+                pg[k] = page_of(s < nslots ? s : 0);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+            if (k >= run) hv[k] = kNoKey;
             n_lt += hv[k] < hs;
             n_eq += hv[k] == hs;
         }
@@ -335,7 +508,7 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
             }
             if (in) {
                 const int s = c * kChunk + tid * run + k;
-                if (pos < top_k) so[pos] = page_of(s) * P + (s & (P - 1));
+                if (pos < top_k) so[pos] = pg[k] * P + (s & (P - 1));
                 ++pos;
             }
         }
@@ -352,10 +525,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
-    int32_t* __restrict__ k_eff_out, int Hq, int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ kcount, uint32_t* __restrict__ kscratch,
+    int64_t kscr_per_bh, int S, int Hq, int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
     __shared__ SelShared sh;
-    const int h = blockIdx.x, b = blockIdx.y;
+    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
+    // The first chunk of scores is loaded before the length is known (every
+    // load is inside the (b, h) row of NPmax scores), so the two overlap.
+    uint64_t pre[kRun];
+    const bool preloaded = PAGES && NPmax <= kChunk;
+    if (preloaded) {
+        const double* scp = score + bh * NPmax;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {  // every load issued before any use
+            const int64_t i = (int64_t)k * kSelThreads + threadIdx.x;
+            pre[k] = 0;
+            if ((int64_t)k * kSelThreads < NPmax) pre[k] = order_key(scp[i < NPmax ? i : 0]);
+        }
+    }
     const int L = clamp_len(seq_len[b], T);
     const int NP = (int)n_pages_of(L, P);
     int32_t* pl = pages + bh * max_keep;
@@ -366,8 +553,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         keep = keep < 1 ? 1 : keep;
         keep = keep > NP ? NP : keep;
         keep = keep > max_keep ? max_keep : keep;
-        np = select_pages_block(score + bh * NPmax, NP, keep, max_keep, pl, sh, KEYS);
-        if (threadIdx.x == 0) n_pages[bh] = np;
+        np = select_pages_block(score + bh * NPmax, NP, keep, max_keep, pl, split == 0, sh, KEYS, pre, preloaded);
+        if (threadIdx.x == 0 && split == 0) n_pages[bh] = np;
         list_in_lds = KEYS && np <= kListLds;
         __syncthreads();
     } else {
@@ -379,22 +566,34 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         __syncthreads();
     }
-    if (KEYS)
-        select_keys_block<NW, G>(codes + bh * (int64_t)T * NW, code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW, pl,
-                                 np, list_in_lds, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
-                                 sel + bh * top_k, k_eff_out + bh, sh);
+    if (KEYS) {
+        const uint64_t* ck = codes + bh * (int64_t)T * NW;
+        const uint64_t* cq = code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW;
+        uint16_t* hm = ham + bh * (int64_t)max_keep * P;
+        uint32_t* kh = kscratch + bh * kscr_per_bh;
+        uint32_t* kd = kh + S * (G * NW * 64 + 1);
+        if (list_in_lds)
+            select_keys_block<NW, G, true>(ck, cq, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
+                                           k_eff_out + bh, sh, split, S, kh, kd, kcount + bh);
+        else if (split == 0)  // the page list is not in LDS: one block does the whole key select
+            select_keys_block<NW, G, false>(ck, cq, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
+                                            k_eff_out + bh, sh, 0, 1, kh, kd, kcount + bh);
+    }
 }
 
 template <int NW, int G, bool PAGES, bool KEYS>
 hipError_t select_t(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
-    hipLaunchKernelGGL((select_kernel<NW, G, PAGES, KEYS>), dim3(s.Hkv, s.B), dim3(kSelThreads), 0, st,
+    const int S = KEYS ? a.lay.sel_splits : 1;
+    uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
+    hipLaunchKernelGGL((select_kernel<NW, G, PAGES, KEYS>), dim3(s.Hkv, s.B, S), dim3(kSelThreads), 0, st,
                        reinterpret_cast<const double*>(a.ws + a.lay.score), a.keep_pages, a.codes,
                        reinterpret_cast<const uint64_t*>(a.ws + a.lay.code_q), a.seq_len,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.pages), reinterpret_cast<int32_t*>(a.ws + a.lay.n_pages),
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
-                       reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep,
-                       a.top_k);
+                       reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), counters + (size_t)s.B * s.Hkv,
+                       reinterpret_cast<uint32_t*>(a.ws + a.lay.kscratch), (int64_t)a.lay.kscratch_per_bh, S, s.Hq,
+                       s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k);
     return hipGetLastError();
 }
 
@@ -423,6 +622,13 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st) { return select_mo
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t st) {
     return select_nw<true, false, 1>(a, st);  // the page half does not depend on the code width
 }
-hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) { return select_mode<false, true>(a, st); }
+hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) {
+    if (a.lay.sel_splits > 1) {  // the stage runs without the query prep, which clears the counters
+        const hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)a.s.B * a.s.Hkv,
+                                             a.s.B * a.s.Hkv, st);
+        if (e != hipSuccess) return e;
+    }
+    return select_mode<false, true>(a, st);
+}
 
 }  // namespace hhr

@@ -163,7 +163,7 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, 
  *                  past the sequence or the slot is unused
  *   sel     int32  [B][Hkv][top_k] selected keys (when sel_idx is NULL)
  *   k_eff   int32  [B][Hkv] number of selected keys
- *   partial, counters: internal
+ *   partial, counters: internal (private scratch may follow; total covers it)
  */
 typedef struct {
     size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters;
