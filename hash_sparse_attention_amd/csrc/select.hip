@@ -17,8 +17,8 @@
 // k * 1024 + tid) so every global load and store of a wave is contiguous, and
 // all of them are issued up front.  Page scores are fp64 turned into
 // order-preserving 64-bit keys; a block OR of (key ^ key of page 0) finds the
-// bits they all share, so the MSB-first radix select starts below them, 11
-// bits (2048 LDS bins) per pass.  Hamming distances are small integers: one
+// bits they all share, so the MSB-first radix select starts below them, 12
+// bits (4096 LDS bins) per pass.  Hamming distances are small integers: one
 // LDS histogram and one scan find the threshold.  The ordered compaction
 // reads per-item flags (pages) or distances (keys) back from LDS as a
 // contiguous run per thread, so a single block scan of packed (before,
@@ -33,7 +33,7 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kRun = 16;                    // items per thread per chunk
 constexpr int kChunk = kSelThreads * kRun;  // items per chunk
-constexpr int kBits = 11;                   // radix digit width of the page select
+constexpr int kBits = 12;                   // radix digit width of the page select
 constexpr int kBins = 1 << kBits;
 constexpr int kListLds = kSelListLds;       // kept-page ids staged in LDS
 static_assert(kChunk == kSelChunk, "chunk size");
@@ -52,8 +52,8 @@ struct SelShared {
     int found[3];
     uint32_t red[2][16];
     int n_bucket;                           // boundary-bucket items gathered for the exact rank
-    int bidx[kRefine];
-    uint64_t bkey[kRefine];
+    int bidx[kRefine + 8];                  // padded: the rank loop reads 8 entries per step
+    uint64_t bkey[kRefine + 8];
     uint64_t thr_key;                       // the keep-th (key, page) in (key desc, page asc)
     int thr_idx;
     int last;                               // this block finishes the key select
@@ -68,7 +68,7 @@ struct SelShared {
 // into LDS.  Returns the number kept.  `pre` holds the keys of the first
 // chunk when the caller loaded them (lane-strided, any value past NP).
 //
-// One 11-bit radix pass below the bits all keys share usually leaves a
+// One 12-bit radix pass below the bits all keys share usually leaves a
 // boundary bucket of a few pages.  If it has at most 64, one wave ranks them
 // exactly by (key desc, page asc) and the keep-th of that order, (kt, it),
 // decides every page: kept iff key > kt or (key == kt and page <= it).
@@ -158,15 +158,23 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
                 if (valid(c, k) && (key[k] & mask) == prefix) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
         }
         __syncthreads();
-        // Descending digits: thread i owns digits nb-1-2i and nb-2-2i.
-        const int d0 = nb - 1 - 2 * tid, d1 = d0 - 1;
-        const int c0 = d0 >= 0 ? sh.hist[d0] : 0, c1 = d1 >= 0 ? sh.hist[d1] : 0;
+        // Descending digits: thread i owns digits nb-1-DPT*i-j, j < DPT.
+        constexpr int DPT = kBins / kSelThreads;
+        int cnt[DPT], sum = 0;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            const int d = nb - 1 - DPT * tid - j;
+            cnt[j] = d >= 0 ? sh.hist[d] : 0;
+            sum += cnt[j];
+        }
         int tot;
-        const int above = block_excl_scan<kSelThreads>(c0 + c1, sh.scan, tot);
-        if (above < need && above + c0 >= need) {
-            sh.found[0] = d0; sh.found[1] = above; sh.found[2] = c0;
-        } else if (above + c0 < need && above + c0 + c1 >= need) {
-            sh.found[0] = d1; sh.found[1] = above + c0; sh.found[2] = c1;
+        int above = block_excl_scan<kSelThreads>(sum, sh.scan, tot);
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            if (above < need && above + cnt[j] >= need) {
+                sh.found[0] = nb - 1 - DPT * tid - j; sh.found[1] = above; sh.found[2] = cnt[j];
+            }
+            above += cnt[j];
         }
         __syncthreads();
         const int dig = sh.found[0];
@@ -191,9 +199,17 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
                 const uint64_t mk = tid < n ? sh.bkey[tid] : 0;
                 const int mi = tid < n ? sh.bidx[tid] : 0;
                 int rank = 0;
-                for (int j = 0; j < n; ++j) {
-                    const uint64_t kj = sh.bkey[j];
-                    rank += kj > mk || (kj == mk && sh.bidx[j] < mi);
+                for (int j0 = 0; j0 < n; j0 += 8) {  // 8 broadcast reads in flight per step
+                    uint64_t kj[8];
+                    int ij[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        kj[u] = sh.bkey[j0 + u];  // entries past n are unused slots of the array
+                        ij[u] = sh.bidx[j0 + u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        rank += j0 + u < n && (kj[u] > mk || (kj[u] == mk && ij[u] < mi));
                 }
                 if (tid < n && rank == need - 1) {
                     sh.thr_key = mk;
