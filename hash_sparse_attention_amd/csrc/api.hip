@@ -139,12 +139,26 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     l.ham = take(BH * (size_t)max_keep * s.P * sizeof(uint16_t));
     l.sel = take(BH * (size_t)top_k * sizeof(int32_t));
     l.k_eff = take(BH * sizeof(int32_t));
-    l.partial = take(BQ * (size_t)l.n_splits * (s.D + 2) * sizeof(float));
-    l.counters = take(2 * BH * sizeof(uint32_t));
+    // Split key select: about 512 candidate slots per block, at most
+    // kCompactSlots, and no more blocks than the GPU holds at once (each one
+    // repeats the page select).
     const size_t slots = (size_t)max_keep * s.P;
-    l.sel_splits = (slots >= 4096 && slots <= (size_t)kSelChunk && max_keep <= kSelListLds) ? kSelSplit : 1;
-    l.kscratch_per_bh = l.sel_splits > 1 ? (size_t)l.sel_splits * (s.G * s.NB + 1) + slots : 0;
-    l.kscratch = take(BH * l.kscratch_per_bh * sizeof(uint32_t));
+    const size_t BHs = BH > 0 ? BH : 1;
+    int S = 1;
+    if (slots <= (size_t)kSelChunk && max_keep <= kSelListLds) {
+        size_t want = (slots + 511) / 512, cap = 256 / BHs;
+        want = want < cap ? want : cap;
+        want = want > 64 ? 64 : want;
+        if (want >= 2 && (slots + want - 1) / want <= (size_t)kCompactSlots) S = (int)want;
+    }
+    l.sel_splits = S;
+    l.nbins = s.G * s.NB + 1;
+    l.part_splits = l.n_splits > S ? l.n_splits : S;
+    l.partial = take(BQ * (size_t)l.part_splits * (s.D + 2) * sizeof(float));
+    l.ghist_off = BH;
+    l.n_clear = (int)(BH + (S > 1 ? BH * l.nbins : 0));
+    l.counters = take((size_t)l.n_clear * sizeof(uint32_t));
+    l.kcum = take(S > 1 ? BH * S * (size_t)l.nbins * sizeof(uint32_t) : 0);
     l.total = off;
     return l;
 }
@@ -263,7 +277,10 @@ hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, c
     HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
     HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
     HHR_TRY(hip_check(launch_select(a, st), "select launch"));
-    HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
+    if (a.lay.sel_splits > 1)
+        HHR_TRY(hip_check(launch_compact_attend(a, st), "compaction and attention launch"));
+    else
+        HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
     return ok();
 }
 
@@ -321,7 +338,7 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         p.code_q = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_q);
         p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
         p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
-        p.n_counters = 2 * a.s.B * a.s.Hkv;
+        p.n_counters = a.lay.n_clear;
         HHR_TRY(hip_check(launch_project(a.s, p, st), "append + qprep launch"));
     } else {
         if (max_append > 0)
@@ -331,7 +348,10 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
     }
     HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
     HHR_TRY(hip_check(launch_select(a, st), "select launch"));
-    HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
+    if (a.lay.sel_splits > 1)
+        HHR_TRY(hip_check(launch_compact_attend(a, st), "compaction and attention launch"));
+    else
+        HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
     return ok();
 }
 

@@ -75,25 +75,141 @@ __device__ __forceinline__ float4 ld_agent4(const float* p) {
     return make_float4(a.x, a.y, b.x, b.y);
 }
 
+constexpr int kMergeRound = 32;  // split partials merged per round by the last block
+
+template <int D, int G>
+struct AttnShared {
+    float wo[16][G][D];     // row partials (o), reused by the final reduction
+    float wml[16][G][2];    // row partials (m, l)
+    float cml[G][kMergeRound][2];
+    float lred[256];
+    int last_flag;
+};
+
+// The 16 row partials of a block (m, l, o per query head, in LDS) merge
+// with a log-sum-exp into the block's split partial, published with
+// agent-scope stores; the last block of the (b, h) to finish merges the
+// `used` splits and writes out.  `stride`: splits per query head in the
+// partial arrays; `nblocks`: blocks that report to the counter.  Every thread
+// of the block calls it, after a barrier that follows the row writes.
+template <int D, int G>
+__device__ __forceinline__ void merge_splits(AttnShared<D, G>& sh, bool has_keys, int split, int stride,
+                                             int nblocks, int used, int64_t q0, float* __restrict__ part_o,
+                                             float* __restrict__ part_ml, uint32_t* __restrict__ counter,
+                                             float* __restrict__ out) {
+    constexpr int NP = 16;
+    const int tid = threadIdx.x;
+    if (has_keys) {
+        for (int x = tid; x < G * D; x += 256) {
+            const int i = x / D, d = x % D;
+            float M = -__builtin_inff();
+#pragma unroll
+            for (int r = 0; r < NP; ++r) M = fmaxf(M, sh.wml[r][i][0]);
+            float acc = 0.f, L = 0.f;
+#pragma unroll
+            for (int r = 0; r < NP; ++r) {
+                const float f = sh.wml[r][i][1] > 0.f ? __expf(sh.wml[r][i][0] - M) : 0.f;
+                acc = __builtin_fmaf(sh.wo[r][i][d], f, acc);
+                L = __builtin_fmaf(sh.wml[r][i][1], f, L);
+            }
+            st_agent(part_o + ((q0 + i) * stride + split) * D + d, acc);
+            if (d == 0) {
+                st_agent(part_ml + ((q0 + i) * stride + split) * 2, M);
+                st_agent(part_ml + ((q0 + i) * stride + split) * 2 + 1, L);
+            }
+        }
+    }
+
+    // The last block of this KV head merges the splits.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0)
+        sh.last_flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)(nblocks - 1);
+    __syncthreads();
+    if (!sh.last_flag) return;
+
+    // Columns of 4 output floats; NGR groups of threads split the splits.
+    constexpr int NC = G * D / 4, NGR = 256 / NC, NB = 16;  // NB: loads in flight per batch
+    const int c = tid % NC, g = tid / NC, qi = c / (D / 4);
+    const bool act = g < NGR;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lacc = 0.f, Mrun = -__builtin_inff();
+    for (int s0 = 0; s0 < used; s0 += kMergeRound) {
+        const int ns = used - s0 < kMergeRound ? used - s0 : kMergeRound;
+        for (int x = tid; x < G * ns; x += 256) {
+            const int i = x / ns, sI = x % ns;
+            const float2 ml = ld_agent2(part_ml + ((q0 + i) * stride + s0 + sI) * 2);
+            sh.cml[i][sI][0] = ml.x;
+            sh.cml[i][sI][1] = ml.y;
+        }
+        __syncthreads();
+        if (act) {
+            float Mr = Mrun;
+            for (int sI = 0; sI < ns; ++sI) Mr = fmaxf(Mr, sh.cml[qi][sI][0]);
+            const float f = Mrun == -__builtin_inff() ? 0.f : __expf(Mrun - Mr);
+            acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+            Lacc *= f;
+            Mrun = Mr;
+            const float* po = part_o + ((q0 + qi) * stride + s0) * D + (c % (D / 4)) * 4;
+            for (int b0 = g; b0 < ns; b0 += NB * NGR) {
+                float4 v[NB];
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    const int sI = b0 + u * NGR;
+                    v[u] = sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    const int sI = b0 + u * NGR;
+                    if (sI < ns && sh.cml[qi][sI][1] > 0.f) {
+                        const float w = __expf(sh.cml[qi][sI][0] - Mr);
+                        acc.x = __builtin_fmaf(v[u].x, w, acc.x);
+                        acc.y = __builtin_fmaf(v[u].y, w, acc.y);
+                        acc.z = __builtin_fmaf(v[u].z, w, acc.z);
+                        acc.w = __builtin_fmaf(v[u].w, w, acc.w);
+                        Lacc = __builtin_fmaf(sh.cml[qi][sI][1], w, Lacc);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // Sum the groups and normalise.
+    float4* red = reinterpret_cast<float4*>(&sh.wo[0][0][0]);  // NGR * NC <= 16 * G * D / 4 float4
+    if (act) {
+        red[g * NC + c] = acc;
+        sh.lred[g * NC + c] = Lacc;
+    }
+    __syncthreads();
+    if (act && g == 0) {
+        for (int r = 1; r < NGR; ++r) {
+            const float4 a = red[r * NC + c];
+            acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+            Lacc += sh.lred[r * NC + c];
+        }
+        const float inv = Lacc > 0.f ? 1.f / Lacc : 0.f;
+        *reinterpret_cast<float4*>(out + (q0 + qi) * D + (c % (D / 4)) * 4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
+}
+
 template <int D, bool BF16, int G>
 __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q, const void* __restrict__ K,
                                                      const void* __restrict__ V, const int32_t* __restrict__ sel,
                                                      const int32_t* __restrict__ k_eff, float* __restrict__ part_o,
                                                      float* __restrict__ part_ml, uint32_t* __restrict__ counters,
                                                      float* __restrict__ out, int Hq, int Hkv, int T, int top_k,
-                                                     int n_splits, float scale) {
+                                                     int n_splits, int stride, float scale) {
     constexpr int NI = 8;                     // entries per row
     constexpr int CH = 16 * NI;               // entries per block (4 waves x 4 rows)
     static_assert(CH == kAttnChunk, "split size");
     constexpr int DPL = D / 16;               // dimensions per lane
     constexpr int NWD = BF16 ? DPL / 2 : DPL; // 32-bit words per lane per row
-    constexpr int NP = 16;                    // row partials per block
-    constexpr int MAXS = 32;                  // splits merged per round by the last block
-    __shared__ float wo[NP][G][D];
-    __shared__ float wml[NP][G][2];
-    __shared__ float cml[G][MAXS][2];
-    __shared__ float lred[256];
-    __shared__ int last_flag;
+    __shared__ AttnShared<D, G> sh;
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 15;
@@ -170,113 +286,260 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
 #pragma unroll
     for (int i = 0; i < G; ++i) {
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) wo[rw][i][sub * DPL + d] = o[i][d];
+        for (int d = 0; d < DPL; ++d) sh.wo[rw][i][sub * DPL + d] = o[i][d];
         if (sub == 0) {
-            wml[rw][i][0] = m_i[i];
-            wml[rw][i][1] = l_i[i];
+            sh.wml[rw][i][0] = m_i[i];
+            sh.wml[rw][i][1] = l_i[i];
         }
     }
     __syncthreads();
 
-    // Merge the block's rows into this split's partial.
-    const int blk_keys = keff - split * CH;
-    if (blk_keys > 0) {
-        for (int x = tid; x < G * D; x += 256) {
-            const int i = x / D, d = x % D;
-            float M = -__builtin_inff();
-#pragma unroll
-            for (int r = 0; r < NP; ++r) M = fmaxf(M, wml[r][i][0]);
-            float acc = 0.f, L = 0.f;
-#pragma unroll
-            for (int r = 0; r < NP; ++r) {
-                const float f = wml[r][i][1] > 0.f ? __expf(wml[r][i][0] - M) : 0.f;
-                acc = __builtin_fmaf(wo[r][i][d], f, acc);
-                L = __builtin_fmaf(wml[r][i][1], f, L);
-            }
-            st_agent(part_o + ((q0 + i) * n_splits + split) * D + d, acc);
-            if (d == 0) {
-                st_agent(part_ml + ((q0 + i) * n_splits + split) * 2, M);
-                st_agent(part_ml + ((q0 + i) * n_splits + split) * 2 + 1, L);
-            }
-        }
-    }
+    merge_splits<D, G>(sh, keff - split * CH > 0, split, stride, n_splits, (keff + CH - 1) / CH, q0, part_o,
+                       part_ml, counters + bh, out);
+}
 
-    // The last block of this KV head merges the splits.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (tid == 0)
-        last_flag = __hip_atomic_fetch_add(&counters[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    (uint32_t)(n_splits - 1);
-    __syncthreads();
-    if (!last_flag) return;
+// ------------------------------------------------------------------ compact + attend
+// The decode step's tail when the Hamming scan ran as S blocks per (b, h):
+// block j owns candidate slots [j*per, (j+1)*per) and
+//  - finds the head's threshold h* (the k_eff-th smallest distance) from the
+//    head histogram, and how many of the keys at h* earlier blocks take (the
+//    first `need` in slot order win ties) from their cumulative histograms;
+//  - compacts its own selected keys, in slot order (ascending key index),
+//    into sel at its offset and into an LDS list;
+//  - runs gather attention over that list (16-lane rows, online softmax over
+//    batches of 16 * NI keys) and merges with the other blocks as above.
+template <int D, bool BF16, int G>
+__global__ __launch_bounds__(256) void compact_attend_kernel(
+    const void* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
+    const int32_t* __restrict__ pages, const int32_t* __restrict__ n_pages, const uint16_t* __restrict__ ham,
+    const uint32_t* __restrict__ cum, const uint32_t* __restrict__ ghist, const int32_t* __restrict__ seq_len,
+    int32_t* __restrict__ sel, int32_t* __restrict__ k_eff_out, float* __restrict__ part_o,
+    float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out, int Hq, int Hkv, int T,
+    int P, int max_keep, int top_k, int S, int stride, int nbins, float scale) {
+    constexpr int SPT = kCompactSlots / 256;  // slots per thread
+    constexpr int BPT = 5;                    // histogram bins per thread (nbins <= 1025)
+    constexpr int NI = G <= 4 ? 8 : 4;        // entries per row per batch
+    constexpr int DPL = D / 16;
+    constexpr int NWD = BF16 ? DPL / 2 : DPL;
+    constexpr uint16_t kNoKey = 0xFFFF;
+    __shared__ AttnShared<D, G> sh;
+    __shared__ uint16_t hs[kCompactSlots];
+    __shared__ int ts[kCompactSlots];
+    __shared__ int list[kCompactSlots];
+    __shared__ int scan[16];
+    __shared__ int thr[2];
+    __shared__ int offs[3];
 
-    // Columns of 4 output floats; NGR groups of threads split the splits.
-    const int used = (keff + CH - 1) / CH;
-    constexpr int NC = G * D / 4, NGR = 256 / NC, NB = 16;  // NB: loads in flight per batch
-    const int c = tid % NC, g = tid / NC, qi = c / (D / 4);
-    const bool act = g < NGR;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float Lacc = 0.f, Mrun = -__builtin_inff();
-    for (int s0 = 0; s0 < used; s0 += MAXS) {
-        const int ns = used - s0 < MAXS ? used - s0 : MAXS;
-        for (int x = tid; x < G * ns; x += 256) {
-            const int i = x / ns, sI = x % ns;
-            const float2 ml = ld_agent2(part_ml + ((q0 + i) * n_splits + s0 + sI) * 2);
-            cml[i][sI][0] = ml.x;
-            cml[i][sI][1] = ml.y;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, sub = lane & 15, rw = tid >> 4;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t q0 = (int64_t)b * Hq + (int64_t)h * G;
+    int np = n_pages[bh];
+    np = np < 0 ? 0 : (np > max_keep ? max_keep : np);
+    const int nslots = np * P, lp = 31 - __clz(P);
+    const int per = (nslots + S - 1) / S;
+    const int lo = split * per < nslots ? split * per : nslots;
+    const int hi = lo + per < nslots ? lo + per : nslots;
+    const int nmine = hi - lo;  // <= kCompactSlots (the split count is chosen so)
+    const uint16_t* hm = ham + bh * (int64_t)max_keep * P;
+    const int32_t* pl = pages + bh * (int64_t)max_keep;
+
+    // Every load of the head histogram and of this block's slots, then use.
+    uint32_t gh[BPT];
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+        const int bn = tid * BPT + r;
+        gh[r] = ghist[bh * nbins + (bn < nbins ? bn : 0)];
+    }
+    uint16_t hk[SPT];
+    int pk[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int s = lo + k * 256 + tid;
+        const int ss = s < hi ? s : 0;
+        hk[k] = hm[ss];
+        pk[k] = pl[ss >> lp];
+    }
+    if (tid == 0) {
+        thr[0] = nbins;
+        thr[1] = 0;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int r = 0; r < BPT; ++r)
+        if (tid * BPT + r < nbins) sum += (int)gh[r];
+    int nvalid;
+    int run = block_excl_scan<256>(sum, scan, nvalid);
+    const int keff = nvalid < top_k ? nvalid : top_k;
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+        const int bn = tid * BPT + r;
+        const int c = bn < nbins ? (int)gh[r] : 0;
+        if (keff > 0 && run < keff && run + c >= keff) {
+            thr[0] = bn;
+            thr[1] = keff - run;
         }
-        __syncthreads();
-        if (act) {
-            float Mr = Mrun;
-            for (int sI = 0; sI < ns; ++sI) Mr = fmaxf(Mr, cml[qi][sI][0]);
-            const float f = Mrun == -__builtin_inff() ? 0.f : __expf(Mrun - Mr);
-            acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
-            Lacc *= f;
-            Mrun = Mr;
-            const float* po = part_o + ((q0 + qi) * n_splits + s0) * D + (c % (D / 4)) * 4;
-            for (int b0 = g; b0 < ns; b0 += NB * NGR) {
-                float4 v[NB];
+        run += c;
+    }
+    // Stage this block's slots (distance, key) in slot order.
 #pragma unroll
-                for (int u = 0; u < NB; ++u) {
-                    const int sI = b0 + u * NGR;
-                    v[u] = sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int u = 0; u < NB; ++u) {
-                    const int sI = b0 + u * NGR;
-                    if (sI < ns && cml[qi][sI][1] > 0.f) {
-                        const float w = __expf(cml[qi][sI][0] - Mr);
-                        acc.x = __builtin_fmaf(v[u].x, w, acc.x);
-                        acc.y = __builtin_fmaf(v[u].y, w, acc.y);
-                        acc.z = __builtin_fmaf(v[u].z, w, acc.z);
-                        acc.w = __builtin_fmaf(v[u].w, w, acc.w);
-                        Lacc = __builtin_fmaf(cml[qi][sI][1], w, Lacc);
-                    }
-                }
+    for (int k = 0; k < SPT; ++k) {
+        const int s = lo + k * 256 + tid;
+        if (s < hi) {
+            hs[s - lo] = hk[k];
+            ts[s - lo] = pk[k] * P + (s & (P - 1));
+        }
+    }
+    __syncthreads();
+    const int hstar = thr[0], need = thr[1];
+
+    // Earlier blocks' counts below and at h* (one thread per block).
+    if (tid < 64) {
+        int lt = 0, eq = 0, own_eq = 0;
+        for (int i = tid; i <= split; i += 64) {
+            const uint32_t* ci = cum + (bh * S + i) * (int64_t)nbins;
+            const int below = hstar > 0 ? (int)ci[(hstar < nbins ? hstar : nbins) - 1] : 0;
+            const int at = hstar < nbins ? (int)ci[hstar] - below : 0;
+            if (i < split) {
+                lt += below;
+                eq += at;
+            } else {
+                own_eq = at;
             }
         }
-        __syncthreads();
-    }
-    // Sum the groups and normalise.
-    float4* red = reinterpret_cast<float4*>(&wo[0][0][0]);  // NGR * NC <= 16 * G * D / 4 float4
-    if (act) {
-        red[g * NC + c] = acc;
-        lred[g * NC + c] = Lacc;
+        lt = wave_incl_scan(lt);
+        eq = wave_incl_scan(eq);
+        own_eq = wave_incl_scan(own_eq);
+        if (tid == 63) {
+            offs[0] = lt;
+            offs[1] = eq;
+            offs[2] = own_eq;
+        }
     }
     __syncthreads();
-    if (act && g == 0) {
-        for (int r = 1; r < NGR; ++r) {
-            const float4 a = red[r * NC + c];
-            acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-            Lacc += lred[r * NC + c];
-        }
-        const float inv = Lacc > 0.f ? 1.f / Lacc : 0.f;
-        *reinterpret_cast<float4*>(out + (q0 + qi) * D + (c % (D / 4)) * 4) =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    const int E = offs[1], own_eq = offs[2];
+    const int offset = offs[0] + (need < E ? need : E);
+    int incl = need - E;
+    incl = incl < 0 ? 0 : (incl > own_eq ? own_eq : incl);
+
+    // Ordered compaction of this block's slots (thread tid: slots [tid*SPT, tid*SPT + SPT)).
+    uint16_t hv[SPT];
+    int tv[SPT];
+    int n_lt = 0, n_eq = 0;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int i = tid * SPT + k;
+        hv[k] = i < nmine ? hs[i] : kNoKey;
+        tv[k] = i < nmine ? ts[i] : 0;
+        n_lt += hv[k] < hstar;
+        n_eq += hv[k] == hstar;
     }
-    if (tid == 0) __hip_atomic_store(&counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
+    int tot;
+    const int packed = block_excl_scan<256>((n_lt << 16) | n_eq, scan, tot);
+    int eq_rank = packed & 0xffff;
+    int pos = (packed >> 16) + (eq_rank < incl ? eq_rank : incl);
+    int32_t* so = sel + bh * (int64_t)top_k;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        bool in = hv[k] < hstar;
+        if (hv[k] == hstar) {
+            in = eq_rank < incl;
+            ++eq_rank;
+        }
+        if (in) {
+            if (offset + pos < top_k) so[offset + pos] = tv[k];
+            list[pos] = tv[k];
+            ++pos;
+        }
+    }
+    const int cnt = (tot >> 16) + ((tot & 0xffff) < incl ? (tot & 0xffff) : incl);
+    if (split == 0) {
+        for (int j = keff + tid; j < top_k; j += 256) so[j] = -1;
+        if (tid == 0) k_eff_out[bh] = keff;
+    }
+    __syncthreads();
+
+    // Attention over list[0, cnt): row rw takes entries e0 + rw + 16 j.
+    const int L = clamp_len(seq_len[b], T);
+    const int64_t kvb = bh * T;
+    float qv[G][DPL];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        uint32_t qw[NWD];
+        load_slice<D, BF16>(Q, q0 + i, sub, qw);
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) qv[i][d] = slice_elem<D, BF16>(qw, d);
+    }
+    float m_i[G], l_i[G], o[G][DPL];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        m_i[i] = -__builtin_inff();
+        l_i[i] = 0.f;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) o[i][d] = 0.f;
+    }
+    for (int e0 = 0; e0 < cnt; e0 += 16 * NI) {
+        int t[NI];
+        bool ok[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int e = e0 + rw + 16 * j;
+            ok[j] = e < cnt;
+            int tj = list[ok[j] ? e : 0];
+            tj = (tj < 0 || tj >= L) ? 0 : tj;
+            t[j] = tj;
+        }
+        uint32_t kw[NI][NWD], vw[NI][NWD];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) load_slice<D, BF16>(K, kvb + t[j], sub, kw[j]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) load_slice<D, BF16>(V, kvb + t[j], sub, vw[j]);
+        float sc[NI][G];
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                float a = 0.f;
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) a = __builtin_fmaf(qv[i][d], slice_elem<D, BF16>(kw[j], d), a);
+                sc[j][i] = a;
+            }
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int i = 0; i < G; ++i) sc[j][i] = row_sum16(sc[j][i]) * scale;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            float mb = m_i[i];
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                if (ok[j]) mb = fmaxf(mb, sc[j][i]);
+            const float f = m_i[i] == -__builtin_inff() ? 0.f : __expf(m_i[i] - mb);
+            float l = l_i[i] * f;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) o[i][d] *= f;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const float p = ok[j] ? __expf(sc[j][i] - mb) : 0.f;
+                l += p;
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) o[i][d] = __builtin_fmaf(p, slice_elem<D, BF16>(vw[j], d), o[i][d]);
+            }
+            m_i[i] = mb;
+            l_i[i] = l;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) sh.wo[rw][i][sub * DPL + d] = o[i][d];
+        if (sub == 0) {
+            sh.wml[rw][i][0] = m_i[i];
+            sh.wml[rw][i][1] = l_i[i];
+        }
+    }
+    __syncthreads();
+    merge_splits<D, G>(sh, true, split, stride, S, S, q0, part_o, part_ml, counters + bh, out);
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n) {
@@ -289,11 +552,11 @@ hipError_t attend_g(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
     const dim3 grid(a.lay.n_splits, s.Hkv, s.B);
     float* po = reinterpret_cast<float*>(a.ws + a.lay.partial);
-    float* pml = po + (size_t)s.B * s.Hq * a.lay.n_splits * s.D;
+    float* pml = po + (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     hipLaunchKernelGGL((attend_kernel<D, BF16, G>), grid, dim3(256), 0, st, a.Q, a.K, a.V, a.sel,
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.k_eff), po, pml,
                        reinterpret_cast<uint32_t*>(a.ws + a.lay.counters), a.out, s.Hq, s.Hkv, s.T, a.top_k,
-                       a.lay.n_splits, a.scale);
+                       a.lay.n_splits, a.lay.part_splits, a.scale);
     return hipGetLastError();
 }
 
@@ -311,7 +574,44 @@ hipError_t attend_dt(const DecodeArgs& a, hipStream_t st) {
     }
 }
 
+template <int D, bool BF16, int G>
+hipError_t compact_g(const DecodeArgs& a, hipStream_t st) {
+    const Shape& s = a.s;
+    const int S = a.lay.sel_splits;
+    float* po = reinterpret_cast<float*>(a.ws + a.lay.partial);
+    float* pml = po + (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
+    uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
+    hipLaunchKernelGGL((compact_attend_kernel<D, BF16, G>), dim3(S, s.Hkv, s.B), dim3(256), 0, st, a.Q, a.K, a.V,
+                       reinterpret_cast<const int32_t*>(a.ws + a.lay.pages),
+                       reinterpret_cast<const int32_t*>(a.ws + a.lay.n_pages),
+                       reinterpret_cast<const uint16_t*>(a.ws + a.lay.ham),
+                       reinterpret_cast<const uint32_t*>(a.ws + a.lay.kcum), counters + a.lay.ghist_off, a.seq_len,
+                       a.sel, reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), po, pml, counters, a.out, s.Hq, s.Hkv,
+                       s.T, s.P, a.max_keep, a.top_k, S, a.lay.part_splits, a.lay.nbins, a.scale);
+    return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t compact_dt(const DecodeArgs& a, hipStream_t st) {
+    switch (a.s.G) {
+        case 1: return compact_g<D, BF16, 1>(a, st);
+        case 2: return compact_g<D, BF16, 2>(a, st);
+        case 3: return compact_g<D, BF16, 3>(a, st);
+        case 4: return compact_g<D, BF16, 4>(a, st);
+        case 5: return compact_g<D, BF16, 5>(a, st);
+        case 6: return compact_g<D, BF16, 6>(a, st);
+        case 7: return compact_g<D, BF16, 7>(a, st);
+        default: return compact_g<D, BF16, 8>(a, st);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_compact_attend(const DecodeArgs& a, hipStream_t st) {
+    const Shape& s = a.s;
+    if (s.D == 64) return s.bf16 ? compact_dt<64, true>(a, st) : compact_dt<64, false>(a, st);
+    return s.bf16 ? compact_dt<128, true>(a, st) : compact_dt<128, false>(a, st);
+}
 
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t st) {
     hipLaunchKernelGGL(zero_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n);

@@ -132,7 +132,7 @@ hipError_t launch_qprep(const DecodeArgs& a, hipStream_t st) {
     p.code_q = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_q);
     p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
     p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
-    p.n_counters = 2 * a.s.B * a.s.Hkv;
+    p.n_counters = a.lay.n_clear;
     return launch_project(a.s, p, st);
 }
 

@@ -21,20 +21,24 @@ struct Shape {
 // Attention keys handled by one block (one split) of the attend kernel.
 constexpr int kAttnChunk = 128;
 
-// Key select: candidate slots per block-local chunk, and blocks per (b, h)
-// sharing the Hamming scan when every candidate fits one chunk.
+// Key select: candidate slots per block-local chunk, the kept pages the
+// select kernel holds in LDS, and the candidate slots one compact+attend
+// block owns (8 per thread).
 constexpr int kSelChunk = 16384;
-constexpr int kSelSplit = 4;
-constexpr int kSelListLds = 8192;  // kept-page ids the select kernel holds in LDS
+constexpr int kSelListLds = 8192;
+constexpr int kCompactSlots = 2048;
 
 // Region offsets of the decode workspace (bytes, 256-aligned).  counters:
-// [0, B*Hkv) attention splits, [B*Hkv, 2*B*Hkv) key-select blocks.  kscratch
-// (private): per (b, h), sel_splits Hamming histograms then one distance per
-// candidate slot, used when sel_splits > 1.
+// [0, B*Hkv) attention-split counters, then (sel_splits > 1) the per-(b, h)
+// Hamming histograms of the head, ghist_off u32 entries in; both are cleared
+// by the query prep of every step.  kcum (private, sel_splits > 1): per
+// (b, h) and select block, the block's cumulative Hamming histogram.
+// part_splits: split stride of the attention partials.
 struct WsLayout {
-    size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters, kscratch, total;
-    int n_splits, sel_splits;
-    size_t kscratch_per_bh;  // u32 entries per (b, h)
+    size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters, kcum, total;
+    int n_splits, sel_splits, part_splits, nbins;
+    size_t ghist_off;  // u32 entries from counters to the head histograms
+    int n_clear;       // u32 entries the query prep clears from counters
 };
 
 WsLayout ws_layout(const Shape& s, int max_keep, int top_k);
@@ -83,6 +87,8 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t stream);  // pages, th
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_attend(const DecodeArgs& a, bool zero_counters, hipStream_t stream);
+// Threshold, ordered compaction and attention of the split key select (the decode step when sel_splits > 1).
+hipError_t launch_compact_attend(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers

@@ -56,7 +56,6 @@ struct SelShared {
     uint64_t bkey[kRefine + 8];
     uint64_t thr_key;                       // the keep-th (key, page) in (key desc, page asc)
     int thr_idx;
-    int last;                               // this block finishes the key select
     int plist[kListLds];
     union {
         uint8_t pflag[kChunk];   // page select: bit 0 kept outright, bit 1 in the boundary bucket
@@ -299,25 +298,18 @@ __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t
 // LDSLIST: the kept-page list is read from LDS (else from the workspace); a
 // compile-time choice, so every read is a plain LDS or global load rather
 // than a generic one that waits on both queues.
-__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
-    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// S > 1 (every candidate in one chunk, the page list in LDS): the S blocks of
-// a (b, h) each scan 1/S of the candidate slots and publish their distances
-// and histogram with agent-scope stores (coherent across XCDs, no L2
-// write-back); the last block to bump the counter merges the histograms,
-// gathers the distances into LDS and runs the threshold and the compaction.
+// S > 1 (the decode step; every candidate in one chunk, the page list in
+// LDS): the S blocks of a (b, h) each scan 1/S of the candidate slots, write
+// their distances, their cumulative histogram (cum) and add their histogram
+// into the head's (ghist).  The threshold, the ordered compaction and the
+// attention then run in the compact+attend kernel.
 template <int NW, int G, bool LDSLIST>
 __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ ck, const uint64_t* __restrict__ cqg,
                                                   const int32_t* __restrict__ pl, int np, int L,
                                                   int P, int max_keep, int top_k, uint16_t* __restrict__ hm,
                                                   int32_t* __restrict__ so, int32_t* __restrict__ keff_out,
-                                                  SelShared& sh, int split, int S, uint32_t* __restrict__ kh,
-                                                  uint32_t* __restrict__ kd, uint32_t* __restrict__ kcnt) {
+                                                  SelShared& sh, int split, int S, uint32_t* __restrict__ cum,
+                                                  uint32_t* __restrict__ ghist) {
     constexpr int NB = NW * 64;
     constexpr int NBINS = G * NB + 1;
     const int tid = threadIdx.x;
@@ -395,54 +387,26 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
 #pragma unroll
                 for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
             if (Hreg[k] >= 0) atomicAdd(&sh.hist[hsum], 1);
-            if (s < hi) {
-                const uint16_t hv = Hreg[k] < 0 ? kNoKey : (uint16_t)hsum;
-                hm[s] = hv;
-                st_agent_u32(kd + s, hv);
-            }
+            if (s < hi) hm[s] = Hreg[k] < 0 ? kNoKey : (uint16_t)hsum;
         }
         if (split == 0)
             for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
         __syncthreads();
-        for (int i = tid; i < NBINS; i += kSelThreads) st_agent_u32(kh + split * NBINS + i, (uint32_t)sh.hist[i]);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's distance and histogram stores are complete
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
-        if (tid == 0)
-            sh.last = __hip_atomic_fetch_add(kcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1);
-        __syncthreads();
-        if (!sh.last) return;
-        // Every load of the gather is issued before any of them is used.
-        constexpr int HPT = (NBINS + kSelThreads - 1) / kSelThreads;  // histogram bins per thread
-        uint32_t hv[HPT][kSelSplit], dv[kRun];
-#pragma unroll
-        for (int r = 0; r < HPT; ++r)
-#pragma unroll
-            for (int j = 0; j < kSelSplit; ++j) {
-                const int i = tid + r * kSelThreads;
-                hv[r][j] = ld_agent_u32(kh + j * NBINS + (i < NBINS ? i : 0));
-            }
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) {
-            const int s = k * kSelThreads + tid;
-            if (k < run) dv[k] = ld_agent_u32(kd + (s < nslots ? s : 0));
+        // Thread i owns bins 2i and 2i+1: inclusive cumulative counts, and the
+        // head's histogram (device atomics on the bins this block hit).
+        const int b0 = 2 * tid;
+        const int c0 = b0 < NBINS ? sh.hist[b0] : 0, c1 = b0 + 1 < NBINS ? sh.hist[b0 + 1] : 0;
+        int tot;
+        const int before = block_excl_scan<kSelThreads>(c0 + c1, sh.scan, tot);
+        if (b0 < NBINS) {
+            cum[split * NBINS + b0] = (uint32_t)(before + c0);
+            if (c0) atomicAdd(&ghist[b0], (uint32_t)c0);
         }
-#pragma unroll
-        for (int r = 0; r < HPT; ++r) {
-            const int i = tid + r * kSelThreads;
-            uint32_t sum = 0;
-#pragma unroll
-            for (int j = 0; j < kSelSplit; ++j) sum += hv[r][j];
-            if (i < NBINS) sh.hist[i] = (int)sum;
+        if (b0 + 1 < NBINS) {
+            cum[split * NBINS + b0 + 1] = (uint32_t)(before + c0 + c1);
+            if (c1) atomicAdd(&ghist[b0 + 1], (uint32_t)c1);
         }
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) {
-            const int s = k * kSelThreads + tid;
-            if (k < run) sh.u.dist[s] = s < nslots ? (uint16_t)dv[k] : kNoKey;
-        }
-        if (tid == 0) st_agent_u32(kcnt, 0u);  // ready for the next call
-        __syncthreads();
+        return;
     } else {
         for (int c = 0; c < nchunks; ++c) {
             distances(c);
@@ -541,8 +505,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
-    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ kcount, uint32_t* __restrict__ kscratch,
-    int64_t kscr_per_bh, int S, int Hq, int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, int S, int Hq,
+    int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -586,65 +550,59 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const uint64_t* ck = codes + bh * (int64_t)T * NW;
         const uint64_t* cq = code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW;
         uint16_t* hm = ham + bh * (int64_t)max_keep * P;
-        uint32_t* kh = kscratch + bh * kscr_per_bh;
-        uint32_t* kd = kh + S * (G * NW * 64 + 1);
+        constexpr int NBINS = G * NW * 64 + 1;
+        uint32_t* cb = cum + bh * (int64_t)S * NBINS;
+        uint32_t* gb = ghist + bh * (int64_t)NBINS;
         if (list_in_lds)
             select_keys_block<NW, G, true>(ck, cq, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
-                                           k_eff_out + bh, sh, split, S, kh, kd, kcount + bh);
+                                           k_eff_out + bh, sh, split, S, cb, gb);
         else if (split == 0)  // the page list is not in LDS: one block does the whole key select
             select_keys_block<NW, G, false>(ck, cq, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
-                                            k_eff_out + bh, sh, 0, 1, kh, kd, kcount + bh);
+                                            k_eff_out + bh, sh, 0, 1, cb, gb);
     }
 }
 
 template <int NW, int G, bool PAGES, bool KEYS>
-hipError_t select_t(const DecodeArgs& a, hipStream_t st) {
+hipError_t select_t(const DecodeArgs& a, int S, hipStream_t st) {
     const Shape& s = a.s;
-    const int S = KEYS ? a.lay.sel_splits : 1;
-    uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
     hipLaunchKernelGGL((select_kernel<NW, G, PAGES, KEYS>), dim3(s.Hkv, s.B, S), dim3(kSelThreads), 0, st,
                        reinterpret_cast<const double*>(a.ws + a.lay.score), a.keep_pages, a.codes,
                        reinterpret_cast<const uint64_t*>(a.ws + a.lay.code_q), a.seq_len,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.pages), reinterpret_cast<int32_t*>(a.ws + a.lay.n_pages),
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
-                       reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), counters + (size_t)s.B * s.Hkv,
-                       reinterpret_cast<uint32_t*>(a.ws + a.lay.kscratch), (int64_t)a.lay.kscratch_per_bh, S, s.Hq,
-                       s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k);
+                       reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), reinterpret_cast<uint32_t*>(a.ws + a.lay.kcum),
+                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, S, s.Hq, s.Hkv, s.T, s.P,
+                       s.NPmax, a.max_keep, a.top_k);
     return hipGetLastError();
 }
 
 template <bool PAGES, bool KEYS, int NW>
-hipError_t select_nw(const DecodeArgs& a, hipStream_t st) {
+hipError_t select_nw(const DecodeArgs& a, int S, hipStream_t st) {
     switch (a.s.G) {
-        case 1: return select_t<NW, 1, PAGES, KEYS>(a, st);
-        case 2: return select_t<NW, 2, PAGES, KEYS>(a, st);
-        case 3: return select_t<NW, 3, PAGES, KEYS>(a, st);
-        case 4: return select_t<NW, 4, PAGES, KEYS>(a, st);
-        case 5: return select_t<NW, 5, PAGES, KEYS>(a, st);
-        case 6: return select_t<NW, 6, PAGES, KEYS>(a, st);
-        case 7: return select_t<NW, 7, PAGES, KEYS>(a, st);
-        default: return select_t<NW, 8, PAGES, KEYS>(a, st);
+        case 1: return select_t<NW, 1, PAGES, KEYS>(a, S, st);
+        case 2: return select_t<NW, 2, PAGES, KEYS>(a, S, st);
+        case 3: return select_t<NW, 3, PAGES, KEYS>(a, S, st);
+        case 4: return select_t<NW, 4, PAGES, KEYS>(a, S, st);
+        case 5: return select_t<NW, 5, PAGES, KEYS>(a, S, st);
+        case 6: return select_t<NW, 6, PAGES, KEYS>(a, S, st);
+        case 7: return select_t<NW, 7, PAGES, KEYS>(a, S, st);
+        default: return select_t<NW, 8, PAGES, KEYS>(a, S, st);
     }
 }
 
 template <bool PAGES, bool KEYS>
-hipError_t select_mode(const DecodeArgs& a, hipStream_t st) {
-    return a.s.NW == 1 ? select_nw<PAGES, KEYS, 1>(a, st) : select_nw<PAGES, KEYS, 2>(a, st);
+hipError_t select_mode(const DecodeArgs& a, int S, hipStream_t st) {
+    return a.s.NW == 1 ? select_nw<PAGES, KEYS, 1>(a, S, st) : select_nw<PAGES, KEYS, 2>(a, S, st);
 }
 
 }  // namespace
 
-hipError_t launch_select(const DecodeArgs& a, hipStream_t st) { return select_mode<true, true>(a, st); }
+hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
+    return select_mode<true, true>(a, a.lay.sel_splits, st);
+}
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t st) {
-    return select_nw<true, false, 1>(a, st);  // the page half does not depend on the code width
+    return select_nw<true, false, 1>(a, 1, st);  // the page half does not depend on the code width
 }
-hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) {
-    if (a.lay.sel_splits > 1) {  // the stage runs without the query prep, which clears the counters
-        const hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + (size_t)a.s.B * a.s.Hkv,
-                                             a.s.B * a.s.Hkv, st);
-        if (e != hipSuccess) return e;
-    }
-    return select_mode<false, true>(a, st);
-}
+hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) { return select_mode<false, true>(a, 1, st); }
 
 }  // namespace hhr

@@ -147,7 +147,7 @@ def test_workspace_layout_regions(hsa):
     sizes = {"q_rot": B * Hq * D * 4, "code_q": B * Hq * 8, "q_split": B * Hkv * D * G * 16,
              "score": B * Hkv * 157 * 8, "pages": B * Hkv * 17 * 4, "n_pages": B * Hkv * 4,
              "ham": B * Hkv * 17 * P * 2, "sel": B * Hkv * 300 * 4, "k_eff": B * Hkv * 4,
-             "partial": B * Hq * lay.n_splits * (D + 2) * 4, "counters": 2 * B * Hkv * 4}
+             "partial": B * Hq * lay.n_splits * (D + 2) * 4, "counters": B * Hkv * 4}
     spans = sorted((getattr(lay, k), getattr(lay, k) + v) for k, v in sizes.items())
     for (a0, a1), (b0, _) in zip(spans, spans[1:]):
         assert a1 <= b0
