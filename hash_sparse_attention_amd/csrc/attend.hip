@@ -77,30 +77,30 @@ __device__ __forceinline__ float4 ld_agent4(const float* p) {
 
 constexpr int kMergeRound = 32;  // split partials merged per round by the last block
 
-template <int D, int G>
+template <int D, int G, int NR = 16>
 struct AttnShared {
-    float wo[16][G][D];     // row partials (o), reused by the final reduction
-    float wml[16][G][2];    // row partials (m, l)
+    float wo[NR][G][D];     // row partials (o), reused by the final reduction
+    float wml[NR][G][2];    // row partials (m, l)
     float cml[G][kMergeRound][2];
-    float lred[256];
+    float lred[NR * 16];
     int last_flag;
 };
 
-// The 16 row partials of a block (m, l, o per query head, in LDS) merge
+// The NT / 16 row partials of a block (m, l, o per query head, in LDS) merge
 // with a log-sum-exp into the block's split partial, published with
 // agent-scope stores; the last block of the (b, h) to finish merges the
 // `used` splits and writes out.  `stride`: splits per query head in the
 // partial arrays; `nblocks`: blocks that report to the counter.  Every thread
 // of the block calls it, after a barrier that follows the row writes.
-template <int D, int G>
-__device__ __forceinline__ void merge_splits(AttnShared<D, G>& sh, bool has_keys, int split, int stride,
+template <int D, int G, int NT = 256>
+__device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool has_keys, int split, int stride,
                                              int nblocks, int used, int64_t q0, float* __restrict__ part_o,
                                              float* __restrict__ part_ml, uint32_t* __restrict__ counter,
                                              float* __restrict__ out) {
-    constexpr int NP = 16;
+    constexpr int NP = NT / 16;
     const int tid = threadIdx.x;
     if (has_keys) {
-        for (int x = tid; x < G * D; x += 256) {
+        for (int x = tid; x < G * D; x += NT) {
             const int i = x / D, d = x % D;
             float M = -__builtin_inff();
 #pragma unroll
@@ -132,14 +132,14 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G>& sh, bool has_keys
     if (!sh.last_flag) return;
 
     // Columns of 4 output floats; NGR groups of threads split the splits.
-    constexpr int NC = G * D / 4, NGR = 256 / NC, NB = 16;  // NB: loads in flight per batch
+    constexpr int NC = G * D / 4, NGR = NT / NC, NB = 16;  // NB: loads in flight per batch
     const int c = tid % NC, g = tid / NC, qi = c / (D / 4);
     const bool act = g < NGR;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float Lacc = 0.f, Mrun = -__builtin_inff();
     for (int s0 = 0; s0 < used; s0 += kMergeRound) {
         const int ns = used - s0 < kMergeRound ? used - s0 : kMergeRound;
-        for (int x = tid; x < G * ns; x += 256) {
+        for (int x = tid; x < G * ns; x += NT) {
             const int i = x / ns, sI = x % ns;
             const float2 ml = ld_agent2(part_ml + ((q0 + i) * stride + s0 + sI) * 2);
             sh.cml[i][sI][0] = ml.x;
@@ -178,7 +178,7 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G>& sh, bool has_keys
         __syncthreads();
     }
     // Sum the groups and normalise.
-    float4* red = reinterpret_cast<float4*>(&sh.wo[0][0][0]);  // NGR * NC <= 16 * G * D / 4 float4
+    float4* red = reinterpret_cast<float4*>(&sh.wo[0][0][0]);  // NGR * NC <= NP * G * D / 4 float4
     if (act) {
         red[g * NC + c] = acc;
         sh.lred[g * NC + c] = Lacc;
@@ -308,21 +308,25 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
 //    into sel at its offset and into an LDS list;
 //  - runs gather attention over that list (16-lane rows, online softmax over
 //    batches of 16 * NI keys) and merges with the other blocks as above.
+constexpr int kCompactThreads = 512;
+
 template <int D, bool BF16, int G>
-__global__ __launch_bounds__(256) void compact_attend_kernel(
+__global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     const void* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
     const int32_t* __restrict__ pages, const int32_t* __restrict__ n_pages, const uint16_t* __restrict__ ham,
     const uint32_t* __restrict__ cum, const uint32_t* __restrict__ ghist, const int32_t* __restrict__ seq_len,
     int32_t* __restrict__ sel, int32_t* __restrict__ k_eff_out, float* __restrict__ part_o,
     float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out, int Hq, int Hkv, int T,
     int P, int max_keep, int top_k, int S, int stride, int nbins, float scale) {
-    constexpr int SPT = kCompactSlots / 256;  // slots per thread
-    constexpr int BPT = 5;                    // histogram bins per thread (nbins <= 1025)
+    constexpr int NT = kCompactThreads;
+    constexpr int NR = NT / 16;               // 16-lane rows
+    constexpr int SPT = kCompactSlots / NT;   // slots per thread
+    constexpr int BPT = (1025 + NT - 1) / NT; // histogram bins per thread (nbins <= 1025)
     constexpr int NI = G <= 4 ? 8 : 4;        // entries per row per batch
     constexpr int DPL = D / 16;
     constexpr int NWD = BF16 ? DPL / 2 : DPL;
     constexpr uint16_t kNoKey = 0xFFFF;
-    __shared__ AttnShared<D, G> sh;
+    __shared__ AttnShared<D, G, NR> sh;
     __shared__ uint16_t hs[kCompactSlots];
     __shared__ int ts[kCompactSlots];
     __shared__ int list[kCompactSlots];
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
     int pk[SPT];
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
-        const int s = lo + k * 256 + tid;
+        const int s = lo + k * NT + tid;
         const int ss = s < hi ? s : 0;
         hk[k] = hm[ss];
         pk[k] = pl[ss >> lp];
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
     for (int r = 0; r < BPT; ++r)
         if (tid * BPT + r < nbins) sum += (int)gh[r];
     int nvalid;
-    int run = block_excl_scan<256>(sum, scan, nvalid);
+    int run = block_excl_scan<NT>(sum, scan, nvalid);
     const int keff = nvalid < top_k ? nvalid : top_k;
 #pragma unroll
     for (int r = 0; r < BPT; ++r) {
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
     // Stage this block's slots (distance, key) in slot order.
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
-        const int s = lo + k * 256 + tid;
+        const int s = lo + k * NT + tid;
         if (s < hi) {
             hs[s - lo] = hk[k];
             ts[s - lo] = pk[k] * P + (s & (P - 1));
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
         n_eq += hv[k] == hstar;
     }
     int tot;
-    const int packed = block_excl_scan<256>((n_lt << 16) | n_eq, scan, tot);
+    const int packed = block_excl_scan<NT>((n_lt << 16) | n_eq, scan, tot);
     int eq_rank = packed & 0xffff;
     int pos = (packed >> 16) + (eq_rank < incl ? eq_rank : incl);
     int32_t* so = sel + bh * (int64_t)top_k;
@@ -454,12 +458,12 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
     }
     const int cnt = (tot >> 16) + ((tot & 0xffff) < incl ? (tot & 0xffff) : incl);
     if (split == 0) {
-        for (int j = keff + tid; j < top_k; j += 256) so[j] = -1;
+        for (int j = keff + tid; j < top_k; j += NT) so[j] = -1;
         if (tid == 0) k_eff_out[bh] = keff;
     }
     __syncthreads();
 
-    // Attention over list[0, cnt): row rw takes entries e0 + rw + 16 j.
+    // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
     const int L = clamp_len(seq_len[b], T);
     const int64_t kvb = bh * T;
     float qv[G][DPL];
@@ -478,12 +482,12 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
 #pragma unroll
         for (int d = 0; d < DPL; ++d) o[i][d] = 0.f;
     }
-    for (int e0 = 0; e0 < cnt; e0 += 16 * NI) {
+    for (int e0 = 0; e0 < cnt; e0 += NR * NI) {
         int t[NI];
         bool ok[NI];
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int e = e0 + rw + 16 * j;
+            const int e = e0 + rw + NR * j;
             ok[j] = e < cnt;
             int tj = list[ok[j] ? e : 0];
             tj = (tj < 0 || tj >= L) ? 0 : tj;
@@ -539,7 +543,7 @@ __global__ __launch_bounds__(256) void compact_attend_kernel(
         }
     }
     __syncthreads();
-    merge_splits<D, G>(sh, true, split, stride, S, S, q0, part_o, part_ml, counters + bh, out);
+    merge_splits<D, G, NT>(sh, true, split, stride, S, S, q0, part_o, part_ml, counters + bh, out);
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n) {
@@ -581,7 +585,8 @@ hipError_t compact_g(const DecodeArgs& a, hipStream_t st) {
     float* po = reinterpret_cast<float*>(a.ws + a.lay.partial);
     float* pml = po + (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
-    hipLaunchKernelGGL((compact_attend_kernel<D, BF16, G>), dim3(S, s.Hkv, s.B), dim3(256), 0, st, a.Q, a.K, a.V,
+    hipLaunchKernelGGL((compact_attend_kernel<D, BF16, G>), dim3(S, s.Hkv, s.B), dim3(kCompactThreads), 0, st, a.Q,
+                       a.K, a.V,
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.pages),
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.n_pages),
                        reinterpret_cast<const uint16_t*>(a.ws + a.lay.ham),
