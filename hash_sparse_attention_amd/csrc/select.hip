@@ -516,12 +516,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const bool preloaded = PAGES && NPmax <= kChunk;
     if (preloaded) {
         const double* scp = score + bh * NPmax;
+        double raw[kRun];
 #pragma unroll
-        for (int k = 0; k < kRun; ++k) {  // every load issued before any use
+        for (int k = 0; k < kRun; ++k) {  // every load issued, unconditionally (clamped), before any use
             const int64_t i = (int64_t)k * kSelThreads + threadIdx.x;
-            pre[k] = 0;
-            if ((int64_t)k * kSelThreads < NPmax) pre[k] = order_key(scp[i < NPmax ? i : 0]);
+            raw[k] = scp[i < NPmax ? i : NPmax - 1];
         }
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) pre[k] = order_key(raw[k]);
     }
     const int L = clamp_len(seq_len[b], T);
     const int NP = (int)n_pages_of(L, P);
