@@ -45,6 +45,7 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 }
 
 constexpr int kRefine = 64;                 // boundary-bucket size ranked exactly by one wave
+constexpr int kMaxGroup = 8;                // query heads per KV head
 
 struct SelShared {
     int hist[kBins];
@@ -284,6 +285,181 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
     return keep;
 }
 
+// select_pages_block for at most RUN * 1024 pages, RUN known at compile time
+// and the keys already loaded (lane-strided, any value past NP): the same
+// selection with static loops and no chunking.
+template <int RUN>
+__device__ __forceinline__ int select_pages_fast(const double* __restrict__ sc, int NP, int keep, int max_keep,
+                                                 int32_t* __restrict__ out, bool write_out, SelShared& sh,
+                                                 bool to_lds, const uint64_t (&key)[RUN]) {
+    const int tid = threadIdx.x;
+    if (write_out)
+        for (int j = keep + tid; j < max_keep; j += kSelThreads) out[j] = -1;
+    if (keep == NP) {  // every page is kept
+        for (int j = tid; j < NP; j += kSelThreads) {
+            if (write_out) out[j] = j;
+            if (to_lds && j < kListLds) sh.plist[j] = j;
+        }
+        return keep;
+    }
+    bool valid[RUN];
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) valid[k] = k * kSelThreads + tid < NP;
+
+    // Bits every key shares: OR over all keys of (key ^ key of page 0).
+    const uint64_t ref = order_key(sc[0]);
+    uint64_t diff = 0;
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) diff |= valid[k] ? key[k] ^ ref : 0;
+    const uint32_t dh = wave_or((uint32_t)(diff >> 32)), dl = wave_or((uint32_t)diff);
+    if ((tid & 63) == 0) {
+        sh.red[0][tid >> 6] = dh;
+        sh.red[1][tid >> 6] = dl;
+    }
+    if (tid == 0) sh.n_bucket = 0;
+    __syncthreads();
+    diff = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) diff |= ((uint64_t)sh.red[0][w] << 32) | sh.red[1][w];
+    uint64_t prefix, mask;
+    int shift;
+    if (diff == 0) {
+        mask = ~0ull;  // every score is equal: the first `keep` pages win
+        prefix = ref;
+        shift = 0;
+    } else {
+        const int top = 63 - __clzll(diff);
+        mask = top == 63 ? 0ull : ~0ull << (top + 1);
+        prefix = ref & mask;
+        shift = top + 1;
+    }
+    int need = keep;
+    bool all_in = false, by_pair = false;
+    uint64_t kt = 0;
+    int it = 0;
+    while (!all_in && !by_pair && shift > 0) {
+        const int width = shift < kBits ? shift : kBits;
+        shift -= width;
+        const int nb = 1 << width;
+        for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < RUN; ++k)
+            if (valid[k] && (key[k] & mask) == prefix) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
+        __syncthreads();
+        constexpr int DPT = kBins / kSelThreads;
+        int cnt[DPT], sum = 0;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            const int d = nb - 1 - DPT * tid - j;
+            cnt[j] = d >= 0 ? sh.hist[d] : 0;
+            sum += cnt[j];
+        }
+        int tot;
+        int above = block_excl_scan<kSelThreads>(sum, sh.scan, tot);
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            if (above < need && above + cnt[j] >= need) {
+                sh.found[0] = nb - 1 - DPT * tid - j; sh.found[1] = above; sh.found[2] = cnt[j];
+            }
+            above += cnt[j];
+        }
+        __syncthreads();
+        const int dig = sh.found[0];
+        need -= sh.found[1];
+        const int eq = sh.found[2];
+        prefix |= (uint64_t)dig << shift;
+        mask |= (uint64_t)(nb - 1) << shift;
+        if (eq == need) {
+            all_in = true;
+        } else if (eq <= kRefine) {
+#pragma unroll
+            for (int k = 0; k < RUN; ++k)
+                if (valid[k] && (key[k] & mask) == prefix) {
+                    const int slot = atomicAdd(&sh.n_bucket, 1);
+                    sh.bkey[slot] = key[k];
+                    sh.bidx[slot] = k * kSelThreads + tid;
+                }
+            __syncthreads();
+            if (tid < 64) {
+                const int n = sh.n_bucket;
+                const uint64_t mk = tid < n ? sh.bkey[tid] : 0;
+                const int mi = tid < n ? sh.bidx[tid] : 0;
+                int rank = 0;
+                for (int j0 = 0; j0 < n; j0 += 8) {
+                    uint64_t kj[8];
+                    int ij[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        kj[u] = sh.bkey[j0 + u];
+                        ij[u] = sh.bidx[j0 + u];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        rank += j0 + u < n && (kj[u] > mk || (kj[u] == mk && ij[u] < mi));
+                }
+                if (tid < n && rank == need - 1) {
+                    sh.thr_key = mk;
+                    sh.thr_idx = mi;
+                }
+            }
+            __syncthreads();
+            kt = sh.thr_key;
+            it = sh.thr_idx;
+            by_pair = true;
+        }
+        __syncthreads();
+    }
+
+    const int cap = all_in ? 0x7fffffff : need;
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) {
+        const int i = k * kSelThreads + tid;
+        uint8_t f = 0;
+        if (valid[k]) {
+            if (by_pair) {
+                f = key[k] > kt || (key[k] == kt && i <= it);
+            } else {
+                const uint64_t mk = key[k] & mask;
+                f = (uint8_t)((mk > prefix) | ((mk == prefix) << 1));
+            }
+        }
+        sh.u.pflag[k * kSelThreads + tid] = f;
+    }
+    __syncthreads();
+    // Thread tid now owns the contiguous items [tid * RUN, tid * RUN + RUN).
+    uint8_t f[RUN];
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) {
+        f[k] = sh.u.pflag[tid * RUN + k];
+        n_gt += f[k] & 1;
+        n_eq += f[k] >> 1;
+    }
+    int tot;
+    const int packed = block_excl_scan<kSelThreads>((n_gt << 16) | n_eq, sh.scan, tot);
+    int eq_rank = packed & 0xffff;
+    int pos = (packed >> 16) + (eq_rank < cap ? eq_rank : cap);
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) {
+        bool in = f[k] & 1;
+        if (f[k] >> 1) {
+            in = eq_rank < cap;
+            ++eq_rank;
+        }
+        if (in) {
+            const int pg = tid * RUN + k;
+            if (pos < max_keep) {
+                if (write_out) out[pos] = pg;
+                if (to_lds && pos < kListLds) sh.plist[pos] = pg;
+            }
+            ++pos;
+        }
+    }
+    __syncthreads();
+    return keep;
+}
+
 template <int NW>
 __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t, uint64_t (&kc)[NW]) {
     if constexpr (NW == 2) {
@@ -303,21 +479,21 @@ __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t
 // their distances, their cumulative histogram (cum) and add their histogram
 // into the head's (ghist).  The threshold, the ordered compaction and the
 // attention then run in the compact+attend kernel.
-template <int NW, int G, bool LDSLIST>
+template <int NW, bool LDSLIST>
 __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ ck, const uint64_t* __restrict__ cqg,
-                                                  const int32_t* __restrict__ pl, int np, int L,
+                                                  int G, const int32_t* __restrict__ pl, int np, int L,
                                                   int P, int max_keep, int top_k, uint16_t* __restrict__ hm,
                                                   int32_t* __restrict__ so, int32_t* __restrict__ keff_out,
                                                   SelShared& sh, int split, int S, uint32_t* __restrict__ cum,
                                                   uint32_t* __restrict__ ghist) {
     constexpr int NB = NW * 64;
-    constexpr int NBINS = G * NB + 1;
+    const int NBINS = G * NB + 1;
     const int tid = threadIdx.x;
     const int nslots = np * P;
     const int lp = 31 - __clz(P);  // P is a power of two
-    uint64_t cq[G * NW];
+    uint64_t cq[kMaxGroup * NW];
 #pragma unroll
-    for (int i = 0; i < G * NW; ++i) cq[i] = cqg[i];
+    for (int i = 0; i < kMaxGroup * NW; ++i) cq[i] = cqg[i < G * NW ? i : 0];
     for (int i = tid; i < NBINS; i += kSelThreads) sh.hist[i] = 0;
 
     const int nchunks = (nslots + kChunk - 1) / kChunk;
@@ -346,9 +522,11 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
         for (int k = 0; k < kRun; ++k) {
             int hsum = 0;
 #pragma unroll
-            for (int i = 0; i < G; ++i)
+            for (int i = 0; i < kMaxGroup; ++i) {
+                if (i >= G) break;  // uniform
 #pragma unroll
                 for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
+            }
             Hreg[k] = Hreg[k] >= 0 ? hsum : -1;
         }
     };
@@ -383,9 +561,11 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
             if (k >= kr) continue;
             int hsum = 0;
 #pragma unroll
-            for (int i = 0; i < G; ++i)
+            for (int i = 0; i < kMaxGroup; ++i) {
+                if (i >= G) break;  // uniform
 #pragma unroll
                 for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
+            }
             if (Hreg[k] >= 0) atomicAdd(&sh.hist[hsum], 1);
             if (s < hi) hm[s] = Hreg[k] < 0 ? kNoKey : (uint16_t)hsum;
         }
@@ -500,31 +680,41 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
     if (tid == 0) *keff_out = keff;
 }
 
-template <int NW, int G, bool PAGES, bool KEYS>
+// Key half of the select kernels, after the page list (LDS or workspace).
+template <int NW, bool KEYS>
+__device__ __forceinline__ void keys_half(SelShared& sh, const uint64_t* __restrict__ codes,
+                                          const uint64_t* __restrict__ code_q, int32_t* __restrict__ pl, int np,
+                                          bool list_in_lds, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
+                                          int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum,
+                                          uint32_t* __restrict__ ghist, int split, int S, int b, int h, int64_t bh,
+                                          int G, int Hq, int T, int P, int L, int max_keep, int top_k) {
+    if (!KEYS) return;
+    const uint64_t* ck = codes + bh * (int64_t)T * NW;
+    const uint64_t* cq = code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW;
+    uint16_t* hm = ham + bh * (int64_t)max_keep * P;
+    const int NBINS = G * NW * 64 + 1;
+    uint32_t* cb = cum + bh * (int64_t)S * NBINS;
+    uint32_t* gb = ghist + bh * (int64_t)NBINS;
+    if (list_in_lds)
+        select_keys_block<NW, true>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k, k_eff_out + bh,
+                                    sh, split, S, cb, gb);
+    else if (split == 0)  // the page list is not in LDS: one block does the whole key select
+        select_keys_block<NW, false>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
+                                     k_eff_out + bh, sh, 0, 1, cb, gb);
+}
+
+// General select kernel: any number of pages (chunks of 16K) and slots.
+template <int NW, bool PAGES, bool KEYS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
-    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, int S, int Hq,
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, int S, int G, int Hq,
     int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
-    // The first chunk of scores is loaded before the length is known (every
-    // load is inside the (b, h) row of NPmax scores), so the two overlap.
-    uint64_t pre[kRun];
-    const bool preloaded = PAGES && NPmax <= kChunk;
-    if (preloaded) {
-        const double* scp = score + bh * NPmax;
-        double raw[kRun];
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) {  // every load issued, unconditionally (clamped), before any use
-            const int64_t i = (int64_t)k * kSelThreads + threadIdx.x;
-            raw[k] = scp[i < NPmax ? i : NPmax - 1];
-        }
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) pre[k] = order_key(raw[k]);
-    }
+    uint64_t pre[kRun];  // unused here: the general page select loads its chunks itself
     const int L = clamp_len(seq_len[b], T);
     const int NP = (int)n_pages_of(L, P);
     int32_t* pl = pages + bh * max_keep;
@@ -535,7 +725,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         keep = keep < 1 ? 1 : keep;
         keep = keep > NP ? NP : keep;
         keep = keep > max_keep ? max_keep : keep;
-        np = select_pages_block(score + bh * NPmax, NP, keep, max_keep, pl, split == 0, sh, KEYS, pre, preloaded);
+        np = select_pages_block(score + bh * NPmax, NP, keep, max_keep, pl, split == 0, sh, KEYS, pre, false);
         if (threadIdx.x == 0 && split == 0) n_pages[bh] = np;
         list_in_lds = KEYS && np <= kListLds;
         __syncthreads();
@@ -548,63 +738,82 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         __syncthreads();
     }
-    if (KEYS) {
-        const uint64_t* ck = codes + bh * (int64_t)T * NW;
-        const uint64_t* cq = code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW;
-        uint16_t* hm = ham + bh * (int64_t)max_keep * P;
-        constexpr int NBINS = G * NW * 64 + 1;
-        uint32_t* cb = cum + bh * (int64_t)S * NBINS;
-        uint32_t* gb = ghist + bh * (int64_t)NBINS;
-        if (list_in_lds)
-            select_keys_block<NW, G, true>(ck, cq, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
-                                           k_eff_out + bh, sh, split, S, cb, gb);
-        else if (split == 0)  // the page list is not in LDS: one block does the whole key select
-            select_keys_block<NW, G, false>(ck, cq, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
-                                            k_eff_out + bh, sh, 0, 1, cb, gb);
-    }
+    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh, G,
+                        Hq, T, P, L, max_keep, top_k);
 }
 
-template <int NW, int G, bool PAGES, bool KEYS>
-hipError_t select_t(const DecodeArgs& a, int S, hipStream_t st) {
+// Fast select kernel: at most RUN * 1024 pages (one chunk, RUN items per
+// thread known at compile time), scores loaded before the length is known.
+template <int NW, int RUN, bool KEYS>
+__global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
+    const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
+    const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
+    int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, int S, int G, int Hq,
+    int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
+    __shared__ SelShared sh;
+    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const double* scp = score + bh * NPmax;
+    double raw[RUN];
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) {  // every load issued, unconditionally (clamped), before any use
+        const int64_t i = (int64_t)k * kSelThreads + threadIdx.x;
+        raw[k] = scp[i < NPmax ? i : NPmax - 1];
+    }
+    const int L = clamp_len(seq_len[b], T);
+    const int NP = (int)n_pages_of(L, P);
+    int keep = keep_pages[b];
+    keep = keep < 1 ? 1 : keep;
+    keep = keep > NP ? NP : keep;
+    keep = keep > max_keep ? max_keep : keep;
+    uint64_t key[RUN];
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) key[k] = order_key(raw[k]);
+    int32_t* pl = pages + bh * max_keep;
+    const int np = select_pages_fast<RUN>(scp, NP, keep, max_keep, pl, split == 0, sh, KEYS, key);
+    if (threadIdx.x == 0 && split == 0) n_pages[bh] = np;
+    __syncthreads();
+    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, KEYS && np <= kListLds, ham, sel, k_eff_out, cum, ghist, split, S,
+                        b, h, bh, G, Hq, T, P, L, max_keep, top_k);
+}
+
+template <typename Kernel>
+hipError_t select_launch(Kernel kernel, const DecodeArgs& a, int S, hipStream_t st) {
     const Shape& s = a.s;
-    hipLaunchKernelGGL((select_kernel<NW, G, PAGES, KEYS>), dim3(s.Hkv, s.B, S), dim3(kSelThreads), 0, st,
+    hipLaunchKernelGGL(kernel, dim3(s.Hkv, s.B, S), dim3(kSelThreads), 0, st,
                        reinterpret_cast<const double*>(a.ws + a.lay.score), a.keep_pages, a.codes,
                        reinterpret_cast<const uint64_t*>(a.ws + a.lay.code_q), a.seq_len,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.pages), reinterpret_cast<int32_t*>(a.ws + a.lay.n_pages),
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), reinterpret_cast<uint32_t*>(a.ws + a.lay.kcum),
-                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, S, s.Hq, s.Hkv, s.T, s.P,
-                       s.NPmax, a.max_keep, a.top_k);
+                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, S, s.G, s.Hq, s.Hkv, s.T,
+                       s.P, s.NPmax, a.max_keep, a.top_k);
     return hipGetLastError();
 }
 
-template <bool PAGES, bool KEYS, int NW>
-hipError_t select_nw(const DecodeArgs& a, int S, hipStream_t st) {
-    switch (a.s.G) {
-        case 1: return select_t<NW, 1, PAGES, KEYS>(a, S, st);
-        case 2: return select_t<NW, 2, PAGES, KEYS>(a, S, st);
-        case 3: return select_t<NW, 3, PAGES, KEYS>(a, S, st);
-        case 4: return select_t<NW, 4, PAGES, KEYS>(a, S, st);
-        case 5: return select_t<NW, 5, PAGES, KEYS>(a, S, st);
-        case 6: return select_t<NW, 6, PAGES, KEYS>(a, S, st);
-        case 7: return select_t<NW, 7, PAGES, KEYS>(a, S, st);
-        default: return select_t<NW, 8, PAGES, KEYS>(a, S, st);
-    }
-}
-
-template <bool PAGES, bool KEYS>
-hipError_t select_mode(const DecodeArgs& a, int S, hipStream_t st) {
-    return a.s.NW == 1 ? select_nw<PAGES, KEYS, 1>(a, S, st) : select_nw<PAGES, KEYS, 2>(a, S, st);
+// Page select (+ keys): the fast kernel when every page fits one chunk.
+template <int NW, bool KEYS>
+hipError_t select_pages_nw(const DecodeArgs& a, int S, hipStream_t st) {
+    const int64_t np = a.s.NPmax;
+    if (np <= 4 * kSelThreads) return select_launch(select_fast_kernel<NW, 4, KEYS>, a, S, st);
+    if (np <= 8 * kSelThreads) return select_launch(select_fast_kernel<NW, 8, KEYS>, a, S, st);
+    if (np <= kChunk) return select_launch(select_fast_kernel<NW, 16, KEYS>, a, S, st);
+    return select_launch(select_kernel<NW, true, KEYS>, a, S, st);
 }
 
 }  // namespace
 
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
-    return select_mode<true, true>(a, a.lay.sel_splits, st);
+    return a.s.NW == 1 ? select_pages_nw<1, true>(a, a.lay.sel_splits, st)
+                       : select_pages_nw<2, true>(a, a.lay.sel_splits, st);
 }
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t st) {
-    return select_nw<true, false, 1>(a, 1, st);  // the page half does not depend on the code width
+    return select_pages_nw<1, false>(a, 1, st);  // the page half does not depend on the code width
 }
-hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) { return select_mode<false, true>(a, 1, st); }
+hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) {
+    return a.s.NW == 1 ? select_launch(select_kernel<1, false, true>, a, 1, st)
+                       : select_launch(select_kernel<2, false, true>, a, 1, st);
+}
 
 }  // namespace hhr
