@@ -139,11 +139,28 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
     float Lacc = 0.f, Mrun = -__builtin_inff();
     for (int s0 = 0; s0 < used; s0 += kMergeRound) {
         const int ns = used - s0 < kMergeRound ? used - s0 : kMergeRound;
-        for (int x = tid; x < G * ns; x += NT) {
+        const float* po = part_o + ((q0 + qi) * stride + s0) * D + (c % (D / 4)) * 4;
+        // The round's (m, l) and the first batch of partials are loaded together.
+        float2 ml[(G * kMergeRound + NT - 1) / NT];
+#pragma unroll
+        for (int r = 0; r < (G * kMergeRound + NT - 1) / NT; ++r) {
+            const int x = tid + r * NT;
             const int i = x / ns, sI = x % ns;
-            const float2 ml = ld_agent2(part_ml + ((q0 + i) * stride + s0 + sI) * 2);
-            sh.cml[i][sI][0] = ml.x;
-            sh.cml[i][sI][1] = ml.y;
+            ml[r] = x < G * ns ? ld_agent2(part_ml + ((q0 + i) * stride + s0 + sI) * 2) : make_float2(0.f, 0.f);
+        }
+        float4 v[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int sI = g + u * NGR;
+            v[u] = act && sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < (G * kMergeRound + NT - 1) / NT; ++r) {
+            const int x = tid + r * NT;
+            if (x < G * ns) {
+                sh.cml[x / ns][x % ns][0] = ml[r].x;
+                sh.cml[x / ns][x % ns][1] = ml[r].y;
+            }
         }
         __syncthreads();
         if (act) {
@@ -153,13 +170,13 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
             acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
             Lacc *= f;
             Mrun = Mr;
-            const float* po = part_o + ((q0 + qi) * stride + s0) * D + (c % (D / 4)) * 4;
             for (int b0 = g; b0 < ns; b0 += NB * NGR) {
-                float4 v[NB];
+                if (b0 != g) {  // later batches (more splits per thread than NB)
 #pragma unroll
-                for (int u = 0; u < NB; ++u) {
-                    const int sI = b0 + u * NGR;
-                    v[u] = sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int u = 0; u < NB; ++u) {
+                        const int sI = b0 + u * NGR;
+                        v[u] = sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < NB; ++u) {

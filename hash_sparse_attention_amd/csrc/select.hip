@@ -743,7 +743,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 // Fast select kernel: at most RUN * 1024 pages (one chunk, RUN items per
-// thread known at compile time), scores loaded before the length is known.
+// thread known at compile time) and at most kListLds kept pages; scores are
+// loaded before the length is known.
 template <int NW, int RUN, bool KEYS>
 __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
@@ -774,8 +775,13 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     const int np = select_pages_fast<RUN>(scp, NP, keep, max_keep, pl, split == 0, sh, KEYS, key);
     if (threadIdx.x == 0 && split == 0) n_pages[bh] = np;
     __syncthreads();
-    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, KEYS && np <= kListLds, ham, sel, k_eff_out, cum, ghist, split, S,
-                        b, h, bh, G, Hq, T, P, L, max_keep, top_k);
+    if (KEYS) {  // max_keep <= kListLds here, so the page list is in LDS
+        const int NBINS = G * NW * 64 + 1;
+        select_keys_block<NW, true>(codes + bh * (int64_t)T * NW, code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW, G,
+                                    pl, np, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
+                                    sel + bh * top_k, k_eff_out + bh, sh, split, S, cum + bh * (int64_t)S * NBINS,
+                                    ghist + bh * (int64_t)NBINS);
+    }
 }
 
 template <typename Kernel>
@@ -796,6 +802,7 @@ hipError_t select_launch(Kernel kernel, const DecodeArgs& a, int S, hipStream_t 
 template <int NW, bool KEYS>
 hipError_t select_pages_nw(const DecodeArgs& a, int S, hipStream_t st) {
     const int64_t np = a.s.NPmax;
+    if (a.max_keep > kListLds) return select_launch(select_kernel<NW, true, KEYS>, a, S, st);
     if (np <= 4 * kSelThreads) return select_launch(select_fast_kernel<NW, 4, KEYS>, a, S, st);
     if (np <= 8 * kSelThreads) return select_launch(select_fast_kernel<NW, 8, KEYS>, a, S, st);
     if (np <= kChunk) return select_launch(select_fast_kernel<NW, 16, KEYS>, a, S, st);
