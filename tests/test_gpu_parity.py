@@ -159,6 +159,53 @@ def test_mistral7b_b8_ragged_sampled(dev):
     _sampled(wl, d, g, [0, 5], "mistral7b_b8")
 
 
+def test_qwen7b_b16_append_4096_sampled(dev):
+    """Qwen2.5-7B attention shape (28 query / 4 KV heads, G = 7), batch 16 at 128K, inputs drawn on the device:
+    encode all but the last 4096 tokens of each sequence, append those 4096 with hhr_encode_cache (the bulk
+    path), decode; the oracle (single-shot encode + decode) runs on sequences 0 and 11."""
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    from gpu_common import gpu_dims, to_dev
+    from synth import make_layer_torch
+    wl = WORKLOADS["qwen7b_b16"]
+    banner("qwen7b_b16: 4096-token append, oracle on sequences 0 and 11")
+    d = make_layer_torch(wl, 0, dev)
+    dims = gpu_dims(wl)
+    seq = d["seq_len_host"]
+    new = np.full(wl.batch, wl.append_tokens, np.int32)
+    pre = seq - new
+    meta, codes = hsa.alloc_cache(dims, dev)
+    meta.fill_(float("nan"))
+    codes.fill_(0x5A5A5A5A5A5A5A5A)
+    zero = to_dev(np.zeros(wl.batch, np.int32), dev)
+    hsa.encode_cache(dims, d["K"], d["R"], d["W"], zero, to_dev(pre, dev), wl.ctx, meta, codes)
+    hsa.encode_cache(dims, d["K"], d["R"], d["W"], to_dev(pre, dev), to_dev(new, dev), int(new.max()), meta, codes)
+    ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
+    ws.fill_(0xA5)
+    out = torch.full((wl.batch, wl.n_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device=dev)
+    sel = torch.full((wl.batch, wl.n_kv_heads, wl.top_k), -7, dtype=torch.int32, device=dev)
+    hsa.decode_step(dims, d["Q"], d["K"], d["V"], d["R"], d["W"], meta, codes, d["seq_len"], d["keep"],
+                    wl.max_keep, wl.top_k, out, ws, sel_idx=sel)
+    torch.cuda.synchronize()
+    v = hsa.workspace_view(dims, wl.max_keep, wl.top_k, ws)
+    g = dict(meta=hsa.meta_to_pages(meta, dims).cpu().numpy(),
+             codes=codes.cpu().numpy().view(np.uint64).reshape(wl.batch, wl.n_kv_heads, wl.ctx, 2),
+             q_rot=v.q_rot.cpu().numpy(), code_q=v.code_q.cpu().numpy().view(np.uint64),
+             score=v.score.cpu().numpy(), pages=v.pages.cpu().numpy(), n_pages=v.n_pages.cpu().numpy(),
+             ham=v.ham.cpu().numpy().view(np.uint16), sel=sel.cpu().numpy(), k_eff=v.k_eff.cpu().numpy(),
+             out=out.cpu().numpy())
+    batches = [0, 11]
+
+    def bits(x):
+        return x[batches].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    sl = dict(Q=bits(d["Q"]), K=bits(d["K"]), V=bits(d["V"]), R=d["R"].cpu().numpy(), W=d["W"].cpu().numpy(),
+              seq_len=seq[batches], keep=d["keep_host"][batches])
+    o = run_oracle(wl.with_(batch=len(batches)), sl)
+    compare(wl, seq, g, o, batches=batches, label="qwen7b_b16")
+
+
 def test_decode_step_append_matches_oracle(dev):
     """hhr_decode_step_append (fused append + query projection) equals the oracle's single-shot encode +
     decode, for a 1-token append, a ragged multi-token append, and an append larger than the fused limit."""
