@@ -52,6 +52,26 @@ __device__ __forceinline__ void load_slice(const void* base, int64_t row, int su
     }
 }
 
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2;
+
+// Dot product of this lane's slices of a query and a key: bf16 pairs through
+// the packed bf16 dot instruction with fp32 accumulation, fp32 by FMAs.
+template <int D, bool BF16>
+__device__ __forceinline__ float slice_dot(const uint32_t (&q)[BF16 ? D / 32 : D / 16],
+                                           const uint32_t (&k)[BF16 ? D / 32 : D / 16]) {
+    float a = 0.f;
+    if constexpr (BF16) {
+#pragma unroll
+        for (int w = 0; w < D / 32; ++w)
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[w]), __builtin_bit_cast(bf16x2, k[w]), a,
+                                                false);
+    } else {
+#pragma unroll
+        for (int d = 0; d < D / 16; ++d) a = __builtin_fmaf(__uint_as_float(q[d]), __uint_as_float(k[d]), a);
+    }
+    return a;
+}
+
 template <int D, bool BF16>
 __device__ __forceinline__ float slice_elem(const uint32_t* w, int d) {
     if (BF16) return __uint_as_float((d & 1) ? (w[d >> 1] & 0xffff0000u) : (w[d >> 1] << 16));
@@ -254,14 +274,9 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
     for (int j = 0; j < NI; ++j) load_slice<D, BF16>(K, kvb + t[j], sub, kw[j]);
 #pragma unroll
     for (int j = 0; j < NI; ++j) load_slice<D, BF16>(V, kvb + t[j], sub, vw[j]);
-    float qv[G][DPL];
+    uint32_t qw[G][NWD];  // this lane's slice of each query, raw
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        uint32_t qw[NWD];
-        load_slice<D, BF16>(Q, q0 + i, sub, qw);
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) qv[i][d] = slice_elem<D, BF16>(qw, d);
-    }
+    for (int i = 0; i < G; ++i) load_slice<D, BF16>(Q, q0 + i, sub, qw[i]);
 
     // Scores of the row's entries for the G heads.
     float sc[NI][G];
@@ -269,10 +284,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
     for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            float a = 0.f;
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) a = __builtin_fmaf(qv[i][d], slice_elem<D, BF16>(kw[j], d), a);
-            sc[j][i] = a;
+            sc[j][i] = slice_dot<D, BF16>(qw[i], kw[j]);
         }
 #pragma unroll
     for (int j = 0; j < NI; ++j)
@@ -483,14 +495,9 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
     const int L = clamp_len(seq_len[b], T);
     const int64_t kvb = bh * T;
-    float qv[G][DPL];
+    uint32_t qw[G][NWD];  // this lane's slice of each query, raw
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-        uint32_t qw[NWD];
-        load_slice<D, BF16>(Q, q0 + i, sub, qw);
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) qv[i][d] = slice_elem<D, BF16>(qw, d);
-    }
+    for (int i = 0; i < G; ++i) load_slice<D, BF16>(Q, q0 + i, sub, qw[i]);
     float m_i[G], l_i[G], o[G][DPL];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -520,10 +527,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
         for (int j = 0; j < NI; ++j)
 #pragma unroll
             for (int i = 0; i < G; ++i) {
-                float a = 0.f;
-#pragma unroll
-                for (int d = 0; d < DPL; ++d) a = __builtin_fmaf(qv[i][d], slice_elem<D, BF16>(kw[j], d), a);
-                sc[j][i] = a;
+                sc[j][i] = slice_dot<D, BF16>(qw[i], kw[j]);
             }
 #pragma unroll
         for (int j = 0; j < NI; ++j)
