@@ -92,6 +92,27 @@ def test_ties_zero_projection_and_duplicate_pages(dev):
     compare(wl, d["seq_len"], g, o, label="ties")
 
 
+def test_split_select_empty_ties_and_duplicates(dev):
+    """Enough candidate slots per KV head that the decode step splits the Hamming scan over several blocks:
+    empty, one-key and one-page sequences beside a full one, every distance tied (W = 0, so the first
+    k_eff candidates in key order win across block boundaries) and duplicated pages (tied page bounds)."""
+    import hash_sparse_attention_amd as hsa
+    from gpu_common import gpu_dims
+    wl = Workload("split_ties", 115, 4, 8, 2, 128, 4096, 16, 128, 50, 700, "bf16", outliers=2)
+    lay = hsa.workspace_layout(gpu_dims(wl), wl.max_keep, wl.top_k)
+    banner(f"split select: {lay.total} workspace bytes")
+    d = make_layer(wl, lengths=[0, 1, 16, 4096])
+    d["W"][:] = 0.0
+    K = d["K"]
+    for h in range(2):
+        for p in range(2, 256, 5):
+            K[3, h, p * 16:(p + 1) * 16] = K[3, h, 16:32]
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label="split ties")
+    assert (g["out"][0] == 0).all() and (g["sel"][0] == -1).all()
+
+
 def test_explicit_scale_and_workspace_sel(dev):
     wl = WORKLOADS["tiny"]
     banner("explicit softmax scale, selection left in the workspace")
