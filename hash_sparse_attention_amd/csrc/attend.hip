@@ -103,8 +103,38 @@ struct AttnShared {
     float wml[NR][G][2];    // row partials (m, l)
     float cml[G][kMergeRound][2];
     float lred[NR * 16];
+    float fr[NR][G];        // row weights exp(m_r - M) of the block combine
+    float bml[G][2];        // block (M, L) per query head
     int last_flag;
 };
+
+// Log-sum-exp weights of the block's NR row partials: per query head i,
+// M_i = max_r m_r, f_r = exp(m_r - M_i) (0 for a row without keys) and
+// L_i = sum_r f_r l_r, one thread per (i, r) with butterflies over the rows
+// (NR is a power of two, so a row group never straddles a wave).  Every
+// thread of the block calls it, after a barrier that follows the row writes.
+template <int D, int G, int NR>
+__device__ __forceinline__ void row_weights(AttnShared<D, G, NR>& sh) {
+    static_assert((NR & (NR - 1)) == 0 && NR <= 64, "row groups within a wave");
+    const int tid = threadIdx.x;
+    if (tid < G * NR) {
+        const int i = tid / NR, r = tid % NR;
+        const float m = sh.wml[r][i][0], l = sh.wml[r][i][1];
+        float M = m;
+#pragma unroll
+        for (int o = NR / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float f = l > 0.f ? __expf(m - M) : 0.f;
+        float L = f * l;
+#pragma unroll
+        for (int o = NR / 2; o > 0; o >>= 1) L += __shfl_xor(L, o);
+        sh.fr[r][i] = f;
+        if (r == 0) {
+            sh.bml[i][0] = M;
+            sh.bml[i][1] = L;
+        }
+    }
+    __syncthreads();
+}
 
 // The NT / 16 row partials of a block (m, l, o per query head, in LDS) merge
 // with a log-sum-exp into the block's split partial, published with
@@ -119,23 +149,17 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
                                              float* __restrict__ out) {
     constexpr int NP = NT / 16;
     const int tid = threadIdx.x;
+    row_weights<D, G, NP>(sh);
     if (has_keys) {
         for (int x = tid; x < G * D; x += NT) {
             const int i = x / D, d = x % D;
-            float M = -__builtin_inff();
+            float acc = 0.f;
 #pragma unroll
-            for (int r = 0; r < NP; ++r) M = fmaxf(M, sh.wml[r][i][0]);
-            float acc = 0.f, L = 0.f;
-#pragma unroll
-            for (int r = 0; r < NP; ++r) {
-                const float f = sh.wml[r][i][1] > 0.f ? __expf(sh.wml[r][i][0] - M) : 0.f;
-                acc = __builtin_fmaf(sh.wo[r][i][d], f, acc);
-                L = __builtin_fmaf(sh.wml[r][i][1], f, L);
-            }
+            for (int r = 0; r < NP; ++r) acc = __builtin_fmaf(sh.wo[r][i][d], sh.fr[r][i], acc);
             st_agent(part_o + ((q0 + i) * stride + split) * D + d, acc);
             if (d == 0) {
-                st_agent(part_ml + ((q0 + i) * stride + split) * 2, M);
-                st_agent(part_ml + ((q0 + i) * stride + split) * 2 + 1, L);
+                st_agent(part_ml + ((q0 + i) * stride + split) * 2, sh.bml[i][0]);
+                st_agent(part_ml + ((q0 + i) * stride + split) * 2 + 1, sh.bml[i][1]);
             }
         }
     }
@@ -232,6 +256,132 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
+}
+
+// Split merge of the compact+attend kernel.  Every block publishes its
+// split partial with agent-scope stores and, unless it is the merger, is
+// done: no store wait, no counter round trip.  The merger is the block that
+// took the head's last start ticket, so every block it waits for has
+// already started.  It loads all S partials and repeats the loads until none
+// still holds the sentinel the select kernel wrote for this step (each
+// 32-bit word is written once, so a word that is not the sentinel is final),
+// then merges them as merge_splits does.  The wait is bounded: after
+// kMaxPolls rounds the head's outputs are set to NaN rather than hang.
+constexpr int kMaxPolls = 1 << 20;
+
+template <int D, int G, int NT>
+__device__ __forceinline__ void merge_polled(AttnShared<D, G, NT / 16>& sh, int split, int stride, int S,
+                                             int64_t q0, float* __restrict__ part_o, float* __restrict__ part_ml,
+                                             float* __restrict__ out) {
+    constexpr int NP = NT / 16;
+    const int tid = threadIdx.x;
+    row_weights<D, G, NP>(sh);
+    for (int x = tid; x < G * D; x += NT) {
+        const int i = x / D, d = x % D;
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < NP; ++r) acc = __builtin_fmaf(sh.wo[r][i][d], sh.fr[r][i], acc);
+        st_agent(part_o + ((q0 + i) * stride + split) * D + d, acc);
+        if (d == 0) {
+            st_agent(part_ml + ((q0 + i) * stride + split) * 2, sh.bml[i][0]);
+            st_agent(part_ml + ((q0 + i) * stride + split) * 2 + 1, sh.bml[i][1]);
+        }
+    }
+    if (!sh.last_flag) return;
+
+    // Columns of 4 output floats; NGR groups of threads split the splits, NB
+    // loads each per round, so one batch covers a round of kMergeRound.
+    constexpr int NC = G * D / 4, NGR = NT / NC, NB = 16;
+    static_assert(NGR >= 1 && NB * NGR >= kMergeRound, "one batch per merge round");
+    constexpr int NML = (G * kMergeRound + NT - 1) / NT;
+    const int c = tid % NC, g = tid / NC, qi = c / (D / 4);
+    const bool act = g < NGR;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lacc = 0.f, Mrun = -__builtin_inff();
+    bool failed = false;
+    for (int s0 = 0; s0 < S && !failed; s0 += kMergeRound) {
+        const int ns = S - s0 < kMergeRound ? S - s0 : kMergeRound;
+        const float* po = part_o + ((q0 + qi) * stride + s0) * D + (c % (D / 4)) * 4;
+        float2 ml[NML];
+        float4 v[NB];
+        for (int poll = 0;; ++poll) {
+            bool pending = false;
+#pragma unroll
+            for (int r = 0; r < NML; ++r) {
+                const int x = tid + r * NT;
+                const int i = x / ns, sI = x % ns;
+                ml[r] = x < G * ns ? ld_agent2(part_ml + ((q0 + i) * stride + s0 + sI) * 2) : make_float2(0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int sI = g + u * NGR;
+                v[u] = act && sI < ns ? ld_agent4(po + (int64_t)sI * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int r = 0; r < NML; ++r)
+                pending |= __float_as_uint(ml[r].x) == kPartSentinel || __float_as_uint(ml[r].y) == kPartSentinel;
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+                pending |= __float_as_uint(v[u].x) == kPartSentinel || __float_as_uint(v[u].y) == kPartSentinel ||
+                           __float_as_uint(v[u].z) == kPartSentinel || __float_as_uint(v[u].w) == kPartSentinel;
+            if (!__syncthreads_or(pending)) break;
+            if (poll >= kMaxPolls) {
+                failed = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (failed) break;
+#pragma unroll
+        for (int r = 0; r < NML; ++r) {
+            const int x = tid + r * NT;
+            if (x < G * ns) {
+                sh.cml[x / ns][x % ns][0] = ml[r].x;
+                sh.cml[x / ns][x % ns][1] = ml[r].y;
+            }
+        }
+        __syncthreads();
+        if (act) {
+            float Mr = Mrun;
+            for (int sI = 0; sI < ns; ++sI) Mr = fmaxf(Mr, sh.cml[qi][sI][0]);
+            const float f = Mrun == -__builtin_inff() ? 0.f : __expf(Mrun - Mr);
+            acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+            Lacc *= f;
+            Mrun = Mr;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int sI = g + u * NGR;
+                if (sI < ns && sh.cml[qi][sI][1] > 0.f) {
+                    const float w = __expf(sh.cml[qi][sI][0] - Mr);
+                    acc.x = __builtin_fmaf(v[u].x, w, acc.x);
+                    acc.y = __builtin_fmaf(v[u].y, w, acc.y);
+                    acc.z = __builtin_fmaf(v[u].z, w, acc.z);
+                    acc.w = __builtin_fmaf(v[u].w, w, acc.w);
+                    Lacc = __builtin_fmaf(sh.cml[qi][sI][1], w, Lacc);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // Sum the groups and normalise.
+    float4* red = reinterpret_cast<float4*>(&sh.wo[0][0][0]);  // NGR * NC <= NP * G * D / 4 float4
+    if (act) {
+        red[g * NC + c] = acc;
+        sh.lred[g * NC + c] = Lacc;
+    }
+    __syncthreads();
+    if (act && g == 0) {
+        for (int r = 1; r < NGR; ++r) {
+            const float4 a = red[r * NC + c];
+            acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+            Lacc += sh.lred[r * NC + c];
+        }
+        const float inv = Lacc > 0.f ? 1.f / Lacc : 0.f;
+        const float nan = __builtin_nanf("");
+        *reinterpret_cast<float4*>(out + (q0 + qi) * D + (c % (D / 4)) * 4) =
+            failed ? make_float4(nan, nan, nan, nan)
+                   : make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
 }
 
 template <int D, bool BF16, int G>
@@ -393,6 +543,18 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
         hk[k] = hm[ss];
         pk[k] = pl[ss >> lp];
     }
+    // Start ticket of the head (the count is cleared by the step's query
+    // prep); the block that draws S - 1 merges the splits.  The result is
+    // only used at the end: the address carries the lane's mbcnt (0 for lane
+    // 0) so the compiler does not turn it into a wave-aggregated atomic whose
+    // result it reads back at once, which would stall the wave for the whole
+    // device-scope round trip here.  The last wave takes it: its next wait on
+    // memory is the K/V gather, by when the atomic has returned (wave 0 waits
+    // earlier, on the cumulative histograms).
+    uint32_t ticket = 0;
+    if (tid == NT - 64)
+        ticket = __hip_atomic_fetch_add(counters + bh + __builtin_amdgcn_mbcnt_lo(~0u, 0u), 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
     if (tid == 0) {
         thr[0] = nbins;
         thr[1] = 0;
@@ -426,19 +588,21 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     __syncthreads();
     const int hstar = thr[0], need = thr[1];
 
-    // Earlier blocks' counts below and at h* (one thread per block).
+    // Earlier blocks' counts below and at h* (one lane per block, S <= 64):
+    // both loads of every lane issued before either is used.
     if (tid < 64) {
+        const int i = tid <= split ? tid : split;
+        const uint32_t* ci = cum + (bh * S + i) * (int64_t)nbins;
+        const int ib = hstar <= 0 ? 0 : (hstar < nbins ? hstar - 1 : nbins - 1), ia = hstar < nbins ? hstar : 0;
+        const uint32_t c_at = ci[ia], c_below = ci[ib];
+        const int below = hstar > 0 ? (int)c_below : 0;
+        const int at = hstar < nbins ? (int)c_at - below : 0;
         int lt = 0, eq = 0, own_eq = 0;
-        for (int i = tid; i <= split; i += 64) {
-            const uint32_t* ci = cum + (bh * S + i) * (int64_t)nbins;
-            const int below = hstar > 0 ? (int)ci[(hstar < nbins ? hstar : nbins) - 1] : 0;
-            const int at = hstar < nbins ? (int)ci[hstar] - below : 0;
-            if (i < split) {
-                lt += below;
-                eq += at;
-            } else {
-                own_eq = at;
-            }
+        if (tid < split) {
+            lt = below;
+            eq = at;
+        } else if (tid == split) {
+            own_eq = at;
         }
         lt = wave_incl_scan(lt);
         eq = wave_incl_scan(eq);
@@ -563,8 +727,9 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             sh.wml[rw][i][1] = l_i[i];
         }
     }
+    if (tid == NT - 64) sh.last_flag = ticket == (uint32_t)(S - 1);
     __syncthreads();
-    merge_splits<D, G, NT>(sh, true, split, stride, S, S, q0, part_o, part_ml, counters + bh, out);
+    merge_polled<D, G, NT>(sh, split, stride, S, q0, part_o, part_ml, out);
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int n) {
@@ -603,6 +768,7 @@ template <int D, bool BF16, int G>
 hipError_t compact_g(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
     const int S = a.lay.sel_splits;
+    if (S < 2 || S > 64) return hipErrorInvalidValue;  // one lane per split in the offset scan
     float* po = reinterpret_cast<float*>(a.ws + a.lay.partial);
     float* pml = po + (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);

@@ -28,6 +28,10 @@ constexpr int kSelChunk = 16384;
 constexpr int kSelListLds = 8192;
 constexpr int kCompactSlots = 2048;
 
+// Bit pattern of a split attention partial not yet written in this step (a
+// NaN payload that arithmetic never produces).
+constexpr uint32_t kPartSentinel = 0x7fbadbadu;
+
 // Region offsets of the decode workspace (bytes, 256-aligned).  counters:
 // [0, B*Hkv) attention-split counters, then (sel_splits > 1) the per-(b, h)
 // Hamming histograms of the head, ghist_off u32 entries in; both are cleared
@@ -149,6 +153,21 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
     x |= (uint32_t)dpp_i<kRowBcast15, 0xa>(0, (int)x);
     x |= (uint32_t)dpp_i<kRowBcast31, 0xc>(0, (int)x);
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t x) {
+    x &= (uint32_t)dpp_i<kRowShr1, 0xf>(-1, (int)x);
+    x &= (uint32_t)dpp_i<kRowShr2, 0xf>(-1, (int)x);
+    x &= (uint32_t)dpp_i<kRowShr4, 0xf>(-1, (int)x);
+    x &= (uint32_t)dpp_i<kRowShr8, 0xf>(-1, (int)x);
+    x &= (uint32_t)dpp_i<kRowBcast15, 0xa>(-1, (int)x);
+    x &= (uint32_t)dpp_i<kRowBcast31, 0xc>(-1, (int)x);
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Lanes below this one whose bit is set in the wave mask m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Exclusive prefix sum of v over a block of NT threads (a multiple of 64, at

@@ -39,8 +39,10 @@ constexpr int kListLds = kSelListLds;       // kept-page ids staged in LDS
 static_assert(kChunk == kSelChunk, "chunk size");
 constexpr uint16_t kNoKey = 0xFFFF;         // distance of a slot past the sequence
 
+// Order-preserving key of a score; -0 is taken as +0 first (the two are the
+// same score, so they tie and the lower page wins).
 __device__ __forceinline__ uint64_t order_key(double s) {
-    const uint64_t u = (uint64_t)__double_as_longlong(s);
+    const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
@@ -51,7 +53,8 @@ struct SelShared {
     int hist[kBins];
     int scan[32];
     int found[3];
-    uint32_t red[2][16];
+    alignas(16) uint32_t red[4][16];        // per-wave OR / AND halves of the page keys (read as uint4)
+    int cnt[256];                           // (round, wave) kept counts, then their prefix
     int n_bucket;                           // boundary-bucket items gathered for the exact rank
     int bidx[kRefine + 8];                  // padded: the rank loop reads 8 entries per step
     uint64_t bkey[kRefine + 8];
@@ -286,66 +289,86 @@ __device__ __forceinline__ int select_pages_block(const double* __restrict__ sc,
 }
 
 // select_pages_block for at most RUN * 1024 pages, RUN known at compile time
-// and the keys already loaded (lane-strided, any value past NP): the same
-// selection with static loops and no chunking.
+// and the scores already loaded (lane-strided, any value past NP), with the
+// per-page work cut to a few instructions:
+//  - the radix passes run on 32-bit order keys of the scores rounded to fp32
+//    (a monotone map), so only pages tied with the threshold at fp32 need
+//    the fp64 scores: a bucket of at most kRefine of them is ranked exactly
+//    by one wave (64-bit keys, then page), which leaves a keep flag per
+//    bucket page in LDS.  A larger tied bucket (rare: over kRefine pages
+//    whose scores round to one fp32 value) falls back to the 64-bit select
+//    above, re-reading the scores.
+//  - page i = k * 1024 + tid sits in round k, wave tid / 64, lane tid % 64,
+//    so page order is (round, wave, lane) order: the ordered list comes from
+//    wave ballots and one prefix over the RUN x 16 (round, wave) counts; it
+//    is built in LDS and copied out with coalesced stores.
+// Needs max_keep <= kListLds.
 template <int RUN>
 __device__ __forceinline__ int select_pages_fast(const double* __restrict__ sc, int NP, int keep, int max_keep,
                                                  int32_t* __restrict__ out, bool write_out, SelShared& sh,
-                                                 bool to_lds, const uint64_t (&key)[RUN]) {
-    const int tid = threadIdx.x;
-    if (write_out)
-        for (int j = keep + tid; j < max_keep; j += kSelThreads) out[j] = -1;
+                                                 const double (&raw)[RUN]) {
+    constexpr int NWV = kSelThreads / 64;
+    static_assert(RUN * NWV <= 256, "one (round, wave) count per slot of sh.cnt");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (keep == NP) {  // every page is kept
-        for (int j = tid; j < NP; j += kSelThreads) {
-            if (write_out) out[j] = j;
-            if (to_lds && j < kListLds) sh.plist[j] = j;
+        for (int j = tid; j < max_keep; j += kSelThreads) {
+            if (write_out) out[j] = j < NP ? j : -1;
+            if (j < NP) sh.plist[j] = j;
         }
         return keep;
     }
     bool valid[RUN];
+    uint32_t key[RUN];
+    uint32_t kor = 0, kand = ~0u;
 #pragma unroll
-    for (int k = 0; k < RUN; ++k) valid[k] = k * kSelThreads + tid < NP;
-
-    // Bits every key shares: OR over all keys of (key ^ key of page 0).
-    const uint64_t ref = order_key(sc[0]);
-    uint64_t diff = 0;
-#pragma unroll
-    for (int k = 0; k < RUN; ++k) diff |= valid[k] ? key[k] ^ ref : 0;
-    const uint32_t dh = wave_or((uint32_t)(diff >> 32)), dl = wave_or((uint32_t)diff);
-    if ((tid & 63) == 0) {
-        sh.red[0][tid >> 6] = dh;
-        sh.red[1][tid >> 6] = dl;
+    for (int k = 0; k < RUN; ++k) {
+        valid[k] = k * kSelThreads + tid < NP;
+        const uint32_t u = __float_as_uint((float)(raw[k] + 0.0));  // -0 as +0, then round to fp32
+        key[k] = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+        kor |= valid[k] ? key[k] : 0u;
+        kand &= valid[k] ? key[k] : ~0u;
     }
+    // Bits every key shares: where the OR and the AND agree.  The first
+    // pass's histogram is cleared under the same barrier.
+    {
+        const uint32_t o = wave_or(kor), a = wave_and(kand);
+        if (lane == 0) {
+            sh.red[0][wave] = o;
+            sh.red[1][wave] = a;
+        }
+    }
+    for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
     if (tid == 0) sh.n_bucket = 0;
     __syncthreads();
-    diff = 0;
+    kor = 0;
+    kand = ~0u;
 #pragma unroll
-    for (int w = 0; w < kSelThreads / 64; ++w) diff |= ((uint64_t)sh.red[0][w] << 32) | sh.red[1][w];
-    uint64_t prefix, mask;
-    int shift;
-    if (diff == 0) {
-        mask = ~0ull;  // every score is equal: the first `keep` pages win
-        prefix = ref;
-        shift = 0;
-    } else {
-        const int top = 63 - __clzll(diff);
-        mask = top == 63 ? 0ull : ~0ull << (top + 1);
-        prefix = ref & mask;
-        shift = top + 1;
+    for (int w = 0; w < NWV; w += 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sh.red[0][w]);
+        const uint4 b = *reinterpret_cast<const uint4*>(&sh.red[1][w]);
+        kor |= a.x | a.y | a.z | a.w;
+        kand &= b.x & b.y & b.z & b.w;
     }
+    const uint32_t diff = kor ^ kand;
+    int shift = diff == 0 ? 0 : 32 - __clz(diff);
+    uint32_t mask = shift == 32 ? 0u : ~0u << shift, prefix = kand & mask;
     int need = keep;
-    bool all_in = false, by_pair = false;
-    uint64_t kt = 0;
-    int it = 0;
-    while (!all_in && !by_pair && shift > 0) {
+    int state = 0;  // 0: undecided, 1: every bucket page kept, 2: bucket decided by the flags
+    for (int pass = 0; state == 0 && shift > 0; ++pass) {
         const int width = shift < kBits ? shift : kBits;
         shift -= width;
         const int nb = 1 << width;
-        for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
-        __syncthreads();
+        if (pass == 0) {  // every valid key is in the bucket
 #pragma unroll
-        for (int k = 0; k < RUN; ++k)
-            if (valid[k] && (key[k] & mask) == prefix) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
+            for (int k = 0; k < RUN; ++k)
+                if (valid[k]) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
+        } else {
+            for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < RUN; ++k)
+                if (valid[k] && (key[k] & mask) == prefix) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1);
+        }
         __syncthreads();
         constexpr int DPT = kBins / kSelThreads;
         int cnt[DPT], sum = 0;
@@ -365,21 +388,32 @@ __device__ __forceinline__ int select_pages_fast(const double* __restrict__ sc, 
             above += cnt[j];
         }
         __syncthreads();
-        const int dig = sh.found[0];
         need -= sh.found[1];
         const int eq = sh.found[2];
-        prefix |= (uint64_t)dig << shift;
-        mask |= (uint64_t)(nb - 1) << shift;
+        prefix |= (uint32_t)sh.found[0] << shift;
+        mask |= (uint32_t)(nb - 1) << shift;
         if (eq == need) {
-            all_in = true;
+            state = 1;
         } else if (eq <= kRefine) {
+            // Gather the bucket (one LDS atomic per wave, slots from ballots),
+            // rank it exactly by (64-bit key desc, page asc) and flag the
+            // `need` first in LDS.
+            int base = 0, wn = 0;
 #pragma unroll
-            for (int k = 0; k < RUN; ++k)
-                if (valid[k] && (key[k] & mask) == prefix) {
-                    const int slot = atomicAdd(&sh.n_bucket, 1);
-                    sh.bkey[slot] = key[k];
+            for (int k = 0; k < RUN; ++k) wn += __popcll(__ballot(valid[k] && (key[k] & mask) == prefix));
+            if (lane == 0 && wn > 0) base = atomicAdd(&sh.n_bucket, wn);
+            base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+            for (int k = 0; k < RUN; ++k) {
+                const bool in = valid[k] && (key[k] & mask) == prefix;
+                const uint64_t bm = __ballot(in);
+                if (in) {
+                    const int slot = base + lanes_below(bm);
+                    sh.bkey[slot] = order_key(raw[k]);
                     sh.bidx[slot] = k * kSelThreads + tid;
                 }
+                base += __popcll(bm);
+            }
             __syncthreads();
             if (tid < 64) {
                 const int n = sh.n_bucket;
@@ -398,65 +432,53 @@ __device__ __forceinline__ int select_pages_fast(const double* __restrict__ sc, 
                     for (int u = 0; u < 8; ++u)
                         rank += j0 + u < n && (kj[u] > mk || (kj[u] == mk && ij[u] < mi));
                 }
-                if (tid < n && rank == need - 1) {
-                    sh.thr_key = mk;
-                    sh.thr_idx = mi;
-                }
+                if (tid < n) sh.u.pflag[mi] = rank < need;
             }
             __syncthreads();
-            kt = sh.thr_key;
-            it = sh.thr_idx;
-            by_pair = true;
+            state = 2;
         }
-        __syncthreads();
+    }
+    if (state == 0) {  // over kRefine pages tie at fp32 on the boundary
+        const uint64_t unused[kRun] = {};
+        return select_pages_block(sc, NP, keep, max_keep, out, write_out, sh, true, unused, false);
     }
 
-    const int cap = all_in ? 0x7fffffff : need;
+    // Kept pages: above the bucket, or in it and (all kept or flagged).
+    bool g[RUN];
 #pragma unroll
     for (int k = 0; k < RUN; ++k) {
-        const int i = k * kSelThreads + tid;
-        uint8_t f = 0;
-        if (valid[k]) {
-            if (by_pair) {
-                f = key[k] > kt || (key[k] == kt && i <= it);
-            } else {
-                const uint64_t mk = key[k] & mask;
-                f = (uint8_t)((mk > prefix) | ((mk == prefix) << 1));
-            }
-        }
-        sh.u.pflag[k * kSelThreads + tid] = f;
+        const uint32_t mk = key[k] & mask;
+        g[k] = valid[k] && (mk > prefix || (mk == prefix && (state == 1 || sh.u.pflag[k * kSelThreads + tid])));
+        const uint64_t bm = __ballot(g[k]);
+        if (lane == 0) sh.cnt[k * NWV + wave] = __popcll(bm);
     }
     __syncthreads();
-    // Thread tid now owns the contiguous items [tid * RUN, tid * RUN + RUN).
-    uint8_t f[RUN];
-    int n_gt = 0, n_eq = 0;
+    if (wave == 0) {  // exclusive prefix of the counts in (round, wave) order
+        constexpr int E = RUN * NWV, EPL = (E + 63) / 64;
+        int v[EPL], sum = 0;
 #pragma unroll
-    for (int k = 0; k < RUN; ++k) {
-        f[k] = sh.u.pflag[tid * RUN + k];
-        n_gt += f[k] & 1;
-        n_eq += f[k] >> 1;
-    }
-    int tot;
-    const int packed = block_excl_scan<kSelThreads>((n_gt << 16) | n_eq, sh.scan, tot);
-    int eq_rank = packed & 0xffff;
-    int pos = (packed >> 16) + (eq_rank < cap ? eq_rank : cap);
-#pragma unroll
-    for (int k = 0; k < RUN; ++k) {
-        bool in = f[k] & 1;
-        if (f[k] >> 1) {
-            in = eq_rank < cap;
-            ++eq_rank;
+        for (int e = 0; e < EPL; ++e) {
+            const int idx = lane * EPL + e;
+            v[e] = idx < E ? sh.cnt[idx] : 0;
+            sum += v[e];
         }
-        if (in) {
-            const int pg = tid * RUN + k;
-            if (pos < max_keep) {
-                if (write_out) out[pos] = pg;
-                if (to_lds && pos < kListLds) sh.plist[pos] = pg;
-            }
-            ++pos;
+        int run = wave_incl_scan(sum) - sum;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int idx = lane * EPL + e;
+            if (idx < E) sh.cnt[idx] = run;
+            run += v[e];
         }
     }
     __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RUN; ++k) {
+        const uint64_t bm = __ballot(g[k]);
+        if (g[k]) sh.plist[sh.cnt[k * NWV + wave] + lanes_below(bm)] = k * kSelThreads + tid;
+    }
+    __syncthreads();
+    if (write_out)
+        for (int j = tid; j < max_keep; j += kSelThreads) out[j] = j < keep ? sh.plist[j] : -1;
     return keep;
 }
 
@@ -703,14 +725,28 @@ __device__ __forceinline__ void keys_half(SelShared& sh, const uint64_t* __restr
                                      k_eff_out + bh, sh, 0, 1, cb, gb);
 }
 
+// With S > 1 the compact+attend kernel's merging block polls the split
+// partials until none holds the sentinel: each select block sets its own
+// split's (o, m, l) of the group's query heads to it, after its last load.
+__device__ __forceinline__ void mark_partials(float* __restrict__ part_o, float* __restrict__ part_ml, int64_t q0,
+                                              int G, int D, int split, int pstride) {
+    const float sent = __uint_as_float(kPartSentinel);
+    const int tid = threadIdx.x, n4 = D / 4;
+    for (int x = tid; x < G * n4; x += kSelThreads)
+        *reinterpret_cast<float4*>(part_o + ((q0 + x / n4) * pstride + split) * D + (x % n4) * 4) =
+            make_float4(sent, sent, sent, sent);
+    if (tid < 2 * G) part_ml[((q0 + tid / 2) * pstride + split) * 2 + (tid & 1)] = sent;
+}
+
 // General select kernel: any number of pages (chunks of 16K) and slots.
 template <int NW, bool PAGES, bool KEYS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
-    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, int S, int G, int Hq,
-    int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Hq, int Hkv, int T, int P, int64_t NPmax,
+    int max_keep, int top_k) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -740,6 +776,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh, G,
                         Hq, T, P, L, max_keep, top_k);
+    if (KEYS && S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
 }
 
 // Fast select kernel: at most RUN * 1024 pages (one chunk, RUN items per
@@ -750,8 +787,9 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
-    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, int S, int G, int Hq,
-    int Hkv, int T, int P, int64_t NPmax, int max_keep, int top_k) {
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Hq, int Hkv, int T, int P, int64_t NPmax,
+    int max_keep, int top_k) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -768,11 +806,8 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     keep = keep < 1 ? 1 : keep;
     keep = keep > NP ? NP : keep;
     keep = keep > max_keep ? max_keep : keep;
-    uint64_t key[RUN];
-#pragma unroll
-    for (int k = 0; k < RUN; ++k) key[k] = order_key(raw[k]);
     int32_t* pl = pages + bh * max_keep;
-    const int np = select_pages_fast<RUN>(scp, NP, keep, max_keep, pl, split == 0, sh, KEYS, key);
+    const int np = select_pages_fast<RUN>(scp, NP, keep, max_keep, pl, split == 0, sh, raw);
     if (threadIdx.x == 0 && split == 0) n_pages[bh] = np;
     __syncthreads();
     if (KEYS) {  // max_keep <= kListLds here, so the page list is in LDS
@@ -781,20 +816,23 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
                                     pl, np, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
                                     sel + bh * top_k, k_eff_out + bh, sh, split, S, cum + bh * (int64_t)S * NBINS,
                                     ghist + bh * (int64_t)NBINS);
+        if (S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
     }
 }
 
 template <typename Kernel>
 hipError_t select_launch(Kernel kernel, const DecodeArgs& a, int S, hipStream_t st) {
     const Shape& s = a.s;
+    float* po = reinterpret_cast<float*>(a.ws + a.lay.partial);
+    const size_t n_po = (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     hipLaunchKernelGGL(kernel, dim3(s.Hkv, s.B, S), dim3(kSelThreads), 0, st,
                        reinterpret_cast<const double*>(a.ws + a.lay.score), a.keep_pages, a.codes,
                        reinterpret_cast<const uint64_t*>(a.ws + a.lay.code_q), a.seq_len,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.pages), reinterpret_cast<int32_t*>(a.ws + a.lay.n_pages),
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), reinterpret_cast<uint32_t*>(a.ws + a.lay.kcum),
-                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, S, s.G, s.Hq, s.Hkv, s.T,
-                       s.P, s.NPmax, a.max_keep, a.top_k);
+                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, po, po + n_po,
+                       a.lay.part_splits, s.D, S, s.G, s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k);
     return hipGetLastError();
 }
 

@@ -69,8 +69,10 @@ def _load():
         lib.oracle_encode.argtypes = [ctypes.POINTER(_Dims), p, p, p, p, p, p, p]
         lib.oracle_decode.argtypes = [ctypes.POINTER(_Dims), p, p, p, p, p, p, p, p, p,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float] + [p] * 9
+        lib.oracle_select_pages.argtypes = [ctypes.POINTER(_Dims), p, p, p, ctypes.c_int32, p, p]
         lib.oracle_max_threads.argtypes = []
-        for f in (lib.oracle_project, lib.oracle_encode, lib.oracle_decode, lib.oracle_max_threads):
+        for f in (lib.oracle_project, lib.oracle_encode, lib.oracle_decode, lib.oracle_select_pages,
+                  lib.oracle_max_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -186,3 +188,18 @@ def decode(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max_keep
     if st:
         raise ValueError(f"oracle_decode failed ({st})")
     return r
+
+
+def select_pages(dims: Dims, score, seq_len, keep_pages, max_keep):
+    """The page select of `decode` alone, on given scores [B][Hkv][NPmax] fp64: returns (pages, n_pages)."""
+    score = _c(score, np.float64)
+    assert score.shape == (dims.batch, dims.n_kv_heads, dims.max_pages)
+    seq_len = _c(np.asarray(seq_len, np.int32), np.int32)
+    keep_pages = _c(np.asarray(keep_pages, np.int32), np.int32)
+    pages = np.zeros((dims.batch, dims.n_kv_heads, max_keep), np.int32)
+    n_pages = np.zeros((dims.batch, dims.n_kv_heads), np.int32)
+    st = _load().oracle_select_pages(ctypes.byref(dims.c()), _ptr(score), _ptr(seq_len), _ptr(keep_pages),
+                                     int(max_keep), _ptr(pages), _ptr(n_pages))
+    if st:
+        raise ValueError(f"oracle_select_pages failed ({st})")
+    return pages, n_pages

@@ -187,6 +187,21 @@ static int cmp_int(const void* a, const void* b) {
     return (x > y) - (x < y);
 }
 
+/* Page select of one (b, h) [ABS; BLOG, "Два уровня маршрутизации решают
+ * разные ошибки": pages with a low bound are dropped whole]: sort the NP
+ * (S, p) pairs by S descending, then p ascending (S compared as values, so
+ * -0 and +0 tie), take the first `keep`, list them ascending.  `pk` is
+ * reordered.  Returns keep after the clamp to [1, min(NP, max_keep)]. */
+static int64_t select_pages_one(page_key* pk, int64_t NP, int64_t keep, int32_t max_keep, int32_t* plist) {
+    if (keep < 1) keep = 1;
+    if (keep > NP) keep = NP;
+    if (keep > max_keep) keep = max_keep;
+    qsort(pk, NP, sizeof(page_key), cmp_page);
+    for (int64_t j = 0; j < keep; ++j) plist[j] = pk[j].p;
+    qsort(plist, keep, sizeof(int32_t), cmp_int);
+    return keep;
+}
+
 /*
  * One decode step for one layer: every sequence b, every KV head h, with the
  * G = Hq/Hkv query heads i = h*G .. h*G+G-1 that share KV head h.
@@ -292,13 +307,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
             }
 
             /* 3. page select */
-            int64_t keep = keep_pages[b];
-            if (keep < 1) keep = 1;
-            if (keep > NP) keep = NP;
-            if (keep > max_keep) keep = max_keep;
-            qsort(pk, NP, sizeof(page_key), cmp_page);
-            for (int64_t j = 0; j < keep; ++j) plist[j] = pk[j].p;
-            qsort(plist, keep, sizeof(int32_t), cmp_int);
+            const int64_t keep = select_pages_one(pk, NP, keep_pages[b], max_keep, plist);
             if (pages_out)
                 for (int64_t j = 0; j < max_keep; ++j) pages_out[bh * max_keep + j] = j < keep ? plist[j] : -1;
             if (npages_out) npages_out[bh] = (int32_t)keep;
@@ -369,4 +378,41 @@ int oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/*
+ * Step 3 of oracle_decode alone, on given page scores score [B][Hkv][NPmax]
+ * (entries p >= NP_b are ignored): pages [B][Hkv][max_keep] ascending, -1
+ * padded, and n_pages [B][Hkv].  Same rule and clamp as oracle_decode.
+ */
+int oracle_select_pages(const oracle_dims* dm, const double* score, const int32_t* seq_len,
+                        const int32_t* keep_pages, int32_t max_keep, int32_t* pages_out, int32_t* npages_out) {
+    if (!dims_ok(dm) || max_keep < 1) return ORACLE_BAD_DIMS;
+    const int B = dm->batch, Hkv = dm->n_kv_heads, P = dm->page_size;
+    const int64_t T = dm->max_ctx, NPmax = n_pages_of(T, P);
+    int status = ORACLE_OK;
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_len[b];
+            if (L < 0) L = 0;
+            if (L > T) L = T;
+            const int64_t NP = n_pages_of(L, P), bh = (int64_t)b * Hkv + h;
+            page_key* pk = malloc(sizeof(page_key) * (NP > 0 ? NP : 1));
+            int32_t* plist = malloc(sizeof(int32_t) * max_keep);
+            if (!pk || !plist) {
+                free(pk); free(plist);
+                status = ORACLE_NOMEM;
+                continue;
+            }
+            for (int64_t p = 0; p < NP; ++p) {
+                pk[p].s = score[bh * NPmax + p];
+                pk[p].p = (int32_t)p;
+            }
+            const int64_t keep = select_pages_one(pk, NP, keep_pages[b], max_keep, plist);
+            for (int64_t j = 0; j < max_keep; ++j) pages_out[bh * max_keep + j] = j < keep ? plist[j] : -1;
+            npages_out[bh] = (int32_t)keep;
+            free(pk); free(plist);
+        }
+    }
+    return status;
 }

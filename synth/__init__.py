@@ -7,6 +7,7 @@ makes.
 """
 from .workloads import (WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, keep_for,
                         make_layer, make_layer_torch)
+from .scores import tie_scores
 
 __all__ = ["WORKLOADS", "Workload", "make_layer", "make_layer_torch", "keep_for",
-           "f32_to_bf16_bits", "bf16_bits_to_f32"]
+           "f32_to_bf16_bits", "bf16_bits_to_f32", "tie_scores"]

@@ -387,3 +387,37 @@ def test_stages_from_oracle_intermediates(dev):
     hsa.stage_attend(dims, t["Q"], t["K"], t["V"], seq, mk, tk, out, ws, sel_idx=osel)
     torch.cuda.synchronize()
     assert np.abs(out.cpu().numpy().astype(np.float64) - o["out"]).max() <= 2e-3
+
+
+@pytest.mark.parametrize("npages,seq,keep,max_keep", [
+    (8192, (8192 * 16, 3001 * 16 - 7, 0), (700, 250, 5), 1024),       # fast select, 8 pages a thread
+    (4096, (4096 * 16, 2900 * 16, 17 * 16), (900, 300, 40), 1024),    # fast select, 4 pages a thread
+    (20000, (20000 * 16, 9000 * 16, 100), (700, 2500, 3), 4096),      # general select (chunked)
+    (12000, (12000 * 16, 11000 * 16, 1), (8500, 4000, 1), 9000),      # general select (list past LDS)
+])
+def test_page_select_stage_on_tied_scores(dev, npages, seq, keep, max_keep):
+    """The page-select stage on given fp64 scores with hard ties straddling the keep boundary (clusters
+    that tie only after rounding to fp32, more and fewer than 64 of them; exact duplicates; signed zeros
+    and denormals; all scores equal) equals the oracle's page-select step bit for bit."""
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    import oracle
+    from gpu_common import gpu_dims, oracle_dims, to_dev
+    from synth import tie_scores
+    wl = Workload("ties", 95, 3, 8, 2, 64, npages * 16, 16, 64, 25, 256, "fp32")
+    banner(f"page select on tied scores: {npages} pages, keep {keep}, max_keep {max_keep}")
+    seq = np.asarray(seq, np.int32)
+    keep = np.asarray(keep, np.int32)
+    NP = [-(-int(L) // 16) for L in seq]
+    S = tie_scores(int(npages) + int(max_keep), 3, 2, wl.max_pages, NP, keep)
+    dims = gpu_dims(wl)
+    ws = hsa.alloc_workspace(dims, max_keep, wl.top_k, dev)
+    ws.fill_(0x5C)
+    v = hsa.workspace_view(dims, max_keep, wl.top_k, ws)
+    v.score.copy_(torch.from_numpy(S).to(dev))
+    hsa.stage_select_pages(dims, to_dev(seq, dev), to_dev(keep, dev), max_keep, wl.top_k, ws)
+    torch.cuda.synchronize()
+    want_pages, want_n = oracle.select_pages(oracle_dims(wl), S, seq, keep, max_keep)
+    assert np.array_equal(v.n_pages.cpu().numpy(), want_n)
+    assert np.array_equal(v.pages.cpu().numpy(), want_pages)

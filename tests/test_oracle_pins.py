@@ -280,6 +280,41 @@ def test_page_select_ties_go_to_lower_index(oracle_mod):
     assert list(r["pages"][0, 0, :2]) == [3, 9]
 
 
+def test_page_select_step_is_brute_force_on_given_scores(oracle_mod):
+    """The page-select step alone, on scores with hard ties (fp32-tied clusters, exact duplicates, signed
+    zeros, denormals, all equal) and ragged lengths: the first keep of the pages sorted by (-S, p) in plain
+    Python (values compared as numbers, so -0 == +0), listed ascending and -1 padded; keep clamped."""
+    from synth import tie_scores
+    B, H, P, T = 3, 2, 16, 4096 * 16
+    NPmax = -(-T // P)
+    seq = np.array([T, 3001 * P - 7, 0], np.int32)
+    NP = [-(-int(L) // P) for L in seq]
+    keep = np.array([700, 250, 5], np.int32)
+    mk = 1024
+    S = tie_scores(11, B, H, NPmax, NP, keep)
+    dims = oracle_mod.Dims(B, 4 * H, H, 64, P, 64, T, False)
+    pages, n_pages = oracle_mod.select_pages(dims, S, seq, keep, mk)
+    for b in range(B):
+        for h in range(H):
+            kp = max(1, min(int(keep[b]), NP[b], mk))
+            if NP[b] == 0:
+                kp = 0
+            order = sorted(range(NP[b]), key=lambda p: (-float(S[b, h, p]), p))
+            want = sorted(order[:kp])
+            assert list(pages[b, h, :kp]) == want, (b, h)
+            assert (pages[b, h, kp:] == -1).all()
+            assert n_pages[b, h] == kp
+
+
+def test_page_select_step_matches_decode(oracle_mod):
+    """The page-select step on the decode step's own scores gives the decode step's page lists."""
+    wl = WORKLOADS["tiny"].with_(batch=2, ragged=(1000, 4096))
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    pages, n_pages = oracle_mod.select_pages(dims, r["score"], d["seq_len"], d["keep"], wl.max_keep)
+    assert np.array_equal(pages, r["pages"]) and np.array_equal(n_pages, r["n_pages"])
+
+
 def test_keep_is_clamped(oracle_mod):
     wl = WORKLOADS["tiny"]
     d = make_layer(wl)
