@@ -11,8 +11,9 @@
 // also feed the codes) or the G queries.  The block loads its 64 x D rows
 // with coalesced 16-byte loads into an LDS tile padded to D + 4 floats per
 // row (so a lane reading its own row hits distinct banks) and its vectors as
-// fp32; each wave then runs four vectors at a time as independent canonical
-// chains, lane = row: acc = fma(row[c], x[c], acc), c ascending from +0.
+// fp32; every wave loads its lane's row into registers and runs its share of
+// the vectors, two at a time, as independent canonical chains, lane = row:
+// acc = fma(row[c], x[c], acc), c ascending from +0.
 // Rows are independent (one rotated dimension, or one code bit), so no
 // result crosses blocks: hash rows ballot 64 sign bits into a code word and
 // rotation rows keep max/min over the page's keys, merged across waves in
@@ -23,7 +24,6 @@ namespace hhr {
 namespace {
 
 constexpr int kProjWaves = 8;
-constexpr int kChains = 4;   // vectors in flight per wave
 constexpr int kMaxVec = 64;  // vectors a block stages (P <= 64 keys, or G <= 8 queries)
 
 template <int D, int NB, bool BF16, bool KEYS, bool QUERIES>
@@ -102,61 +102,62 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     }
     __syncthreads();
 
-    // Wave w runs vector groups starting at w*kChains, (w + kProjWaves)*kChains, ...
+    // Wave w runs vectors w, w + kProjWaves, ... two chains at a time.  The
+    // lane's row of the group goes into registers in halves of up to 64
+    // columns (independent LDS reads, so their latency overlaps), and the
+    // chains run from registers, columns ascending.
     const int row = 64 * rg + lane;  // row of [R_h; W_h]
+    constexpr int HC = D < 64 ? D : 64;  // columns per half
     float mx = -__builtin_inff(), mn = __builtin_inff();
-    for (int j0 = w * kChains; j0 < nv; j0 += kProjWaves * kChains) {
-        float acc[kChains];
-        int vi[kChains];
-#pragma unroll
-        for (int u = 0; u < kChains; ++u) {
-            acc[u] = 0.f;
-            const int j = j0 + u;
-            vi[u] = v0 + (j < nv ? j : nv - 1);  // out-of-range chains recompute a valid vector; discarded
-        }
-#pragma unroll
-        for (int c = 0; c < D; c += 4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(&mt[lane * LDM + c]);
-            float4 x[kChains];
-#pragma unroll
-            for (int u = 0; u < kChains; ++u) x[u] = *reinterpret_cast<const float4*>(xs + vi[u] * D + c);
-#pragma unroll
-            for (int u = 0; u < kChains; ++u) {
-                acc[u] = __builtin_fmaf(m4.x, x[u].x, acc[u]);
-                acc[u] = __builtin_fmaf(m4.y, x[u].y, acc[u]);
-                acc[u] = __builtin_fmaf(m4.z, x[u].z, acc[u]);
-                acc[u] = __builtin_fmaf(m4.w, x[u].w, acc[u]);
-            }
-            // Pin the four chains to this step: left alone, the compiler
-            // finishes one chain before the next and keeps every loaded
-            // vector of the others live, which spills.
-            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])::"memory");
-        }
-#pragma unroll
-        for (int u = 0; u < kChains; ++u) {
-            const int j = j0 + u;
-            if (j >= nv) continue;  // wave-uniform
-            const int v = v0 + j;
-            if (qblock) {
-                const int64_t qi = q0 + v;
-                if (rot) {
-                    q_rot[qi * D + row] = acc[u];
-                    double* qsp = q_split + ((bh * D + row) * G + v) * 2;
-                    qsp[0] = acc[u] >= 0.f ? (double)acc[u] : 0.0;
-                    qsp[1] = acc[u] < 0.f ? (double)acc[u] : 0.0;
-                } else {
-                    const uint64_t word = __ballot(acc[u] > 0.f);
-                    if (lane == 0) code_q[qi * NW + (row - D) / 64] = word;
-                }
-            } else if (rot) {
-                const float vk = acc[u] == 0.f ? 0.f : acc[u];
-                mx = fmaxf(mx, vk);
-                mn = fminf(mn, vk);
+    auto emit = [&](int j, float a) {
+        const int v = v0 + j;
+        if (qblock) {
+            const int64_t qi = q0 + v;
+            if (rot) {
+                q_rot[qi * D + row] = a;
+                double* qsp = q_split + ((bh * D + row) * G + v) * 2;
+                qsp[0] = a >= 0.f ? (double)a : 0.0;
+                qsp[1] = a < 0.f ? (double)a : 0.0;
             } else {
-                const uint64_t word = __ballot(acc[u] > 0.f);
-                if (lane == 0) codes[(bh * T + lo + v) * NW + (row - D) / 64] = word;
+                const uint64_t word = __ballot(a > 0.f);
+                if (lane == 0) code_q[qi * NW + (row - D) / 64] = word;
+            }
+        } else if (rot) {
+            const float vk = a == 0.f ? 0.f : a;
+            mx = fmaxf(mx, vk);
+            mn = fminf(mn, vk);
+        } else {
+            const uint64_t word = __ballot(a > 0.f);
+            if (lane == 0) codes[(bh * T + lo + v) * NW + (row - D) / 64] = word;
+        }
+    };
+    for (int ja = w; ja < nv; ja += 2 * kProjWaves) {  // wave-uniform
+        const int jb = ja + kProjWaves;
+        const bool two = jb < nv;  // wave-uniform
+        const float4* xa = reinterpret_cast<const float4*>(xs + (v0 + ja) * D);
+        const float4* xb = reinterpret_cast<const float4*>(xs + (v0 + (two ? jb : ja)) * D);
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 1
+        for (int c0 = 0; c0 < D; c0 += HC) {
+            float4 mrow[HC / 4];
+#pragma unroll
+            for (int k = 0; k < HC / 4; ++k)
+                mrow[k] = *reinterpret_cast<const float4*>(&mt[lane * LDM + c0 + 4 * k]);
+#pragma unroll
+            for (int k = 0; k < HC / 4; ++k) {
+                const float4 x = xa[c0 / 4 + k], y = xb[c0 / 4 + k];
+                acc0 = __builtin_fmaf(mrow[k].x, x.x, acc0);
+                acc0 = __builtin_fmaf(mrow[k].y, x.y, acc0);
+                acc0 = __builtin_fmaf(mrow[k].z, x.z, acc0);
+                acc0 = __builtin_fmaf(mrow[k].w, x.w, acc0);
+                acc1 = __builtin_fmaf(mrow[k].x, y.x, acc1);
+                acc1 = __builtin_fmaf(mrow[k].y, y.y, acc1);
+                acc1 = __builtin_fmaf(mrow[k].z, y.z, acc1);
+                acc1 = __builtin_fmaf(mrow[k].w, y.w, acc1);
             }
         }
+        emit(ja, acc0);
+        if (two) emit(jb, acc1);
     }
     if (KEYS && !qblock && rot) {  // block-uniform
         red[w][lane][0] = mx;
