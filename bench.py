@@ -39,31 +39,35 @@ def algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total):
     """Bytes the method must move for one layer of one step (append + decode)."""
     B, Hkv, Hq, D, P, nb = wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.page_size, wl.hash_bits
     e = 2 if wl.dtype == "bf16" else 4
+    mb = 2 if wl.meta_bf16 else 4  # bytes per stored max or min
     tot = 0
     for b in range(B):
         L = int(seq[b])
         NP = -(-L // P)
         cand = int(keep[b]) * P  # every kept page is full at these lengths
-        tot += Hkv * (NP * 2 * D * 4 + cand * nb // 8)
+        tot += Hkv * (NP * 2 * D * mb + cand * nb // 8)
     tot += k_eff_total * (2 * D * e + 4)                       # gathered K and V rows + indices
     tot += Hkv * (D * D + nb * D) * 4                          # R_h, W_h
     tot += B * Hq * D * (e + 4)                                # q in, out
-    tot += B * Hkv * (P * D * e + 2 * D * 4 + nb // 8)         # append: page keys in, page meta + code out
+    tot += B * Hkv * (P * D * e + 2 * D * mb + nb // 8)        # append: page keys in, page meta + code out
     return tot
 
 
 def page_bound_bytes_per_launch(wl, seq):
-    """Per page: 2*D fp32 (max, min) read + one fp64 score written."""
+    """Per page: 2*D stored (max, min) read (fp32, or bf16 metadata) + one fp64 score written."""
     pages = sum(-(-int(L) // wl.page_size) for L in seq) * wl.n_kv_heads
-    return pages * (2 * wl.head_dim * 4 + 8), pages
+    return pages * (2 * wl.head_dim * (2 if wl.meta_bf16 else 4) + 8), pages
 
 
 def source_digest():
     return hashlib.sha256(open(BOUND_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per page-bound launch from the committed rocprofv3 --pmc summary, if the kernel is unchanged."""
+def traffic_from_profile(wl):
+    """HBM bytes per page-bound launch from the committed rocprofv3 --pmc summary (fp32 metadata), if the
+    kernel is unchanged."""
+    if wl.meta_bf16:
+        return None
     try:
         rec = json.load(open(PMC_FILE))
     except (OSError, ValueError):
@@ -79,7 +83,7 @@ def cpu_baseline(wl, host_layer, steps_note):
 
     import oracle
     od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                     wl.dtype == "bf16")
+                     wl.dtype == "bf16", wl.meta_bf16)
     t0 = time.perf_counter()
     meta, codes = oracle.encode(od, host_layer["K"], host_layer["R"], host_layer["W"], np.zeros(wl.batch, np.int32),
                                 host_layer["seq_len"])
@@ -119,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_128k")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
+    ap.add_argument("--meta", choices=("fp32", "bf16"), default="fp32",
+                    help="page metadata: fp32 (the workload as specified) or outward-rounded bf16")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bound-launches", type=int, default=96, help="page-bound launches timed for the roofline")
@@ -139,12 +145,13 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.layers:
         wl = wl.with_(layers=args.layers)
+    wl = wl.with_(meta_bf16=args.meta == "bf16")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, ctx={wl.ctx}, device {torch.cuda.get_device_name(0)}")
 
     dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                         wl.dtype == "bf16")
+                         wl.dtype == "bf16", meta_bf16=wl.meta_bf16)
     layers = []
     t0 = time.perf_counter()
     for l in range(wl.layers):
@@ -268,7 +275,8 @@ def main():
             "workload": (f"{wl.name}: Llama-3.1-8B-shaped decode step, {wl.layers} layers, batch {wl.batch}, "
                          f"{wl.n_q_heads}q/{wl.n_kv_heads}kv heads, head_dim {wl.head_dim}, context {wl.ctx}, "
                          f"page {wl.page_size}, {wl.hash_bits}-bit codes, keep {wl.keep_percent}% pages, "
-                         f"top-k {wl.top_k}; one step = per layer a 1-token append + decode"),
+                         f"top-k {wl.top_k}; page metadata {'bf16 (outward-rounded)' if wl.meta_bf16 else 'fp32'}; "
+                         f"one step = per layer a 1-token append + decode"),
             "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
         },
         "us_per_layer": us_layer,
@@ -283,7 +291,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic_from_profile(),
+            "traffic": traffic_from_profile(wl),
             "algorithmic_bytes_per_launch": bound_bytes,
             "pages_per_launch": n_pages,
             "us_per_launch": bound_us,

@@ -29,7 +29,8 @@ class HHRError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_dtype")]
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_dtype",
+        "meta_dtype")]
 
     def __repr__(self):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -100,9 +101,11 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def make_dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx, bf16: bool) -> Dims:
+def make_dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx, bf16: bool,
+              meta_bf16: bool = False) -> Dims:
+    """meta_bf16: store page metadata as outward-rounded bf16 (half the bytes of the page-bound stream)."""
     return Dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx,
-                HHR_BF16 if bf16 else HHR_F32)
+                HHR_BF16 if bf16 else HHR_F32, HHR_BF16 if meta_bf16 else HHR_F32)
 
 
 def dims_from(K, Q, W, page_size: int) -> Dims:
@@ -236,10 +239,16 @@ def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> Workspac
 
 
 def meta_to_pages(meta_flat, dims: Dims):
-    """Reshape the page-block-interleaved meta buffer to [B][Hkv][NPmax][D][2] (max, min); a host-side view helper."""
+    """Reshape the page-block-interleaved meta buffer to [B][Hkv][NPmax][D][2] (max, min) fp32 (bf16 metadata
+    widened exactly); a host-side view helper."""
+    import torch
     B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
     NP = -(-dims.max_ctx // dims.page_size)
     NPB = -(-NP // 64)
-    m = meta_flat.reshape(B, Hkv, NPB, D // 2, 64, 2, 2)      # [..][blk][pair][lane][dim-in-pair][max/min]
-    m = m.permute(0, 1, 2, 4, 3, 5, 6).reshape(B, Hkv, NPB * 64, D, 2)
+    if dims.meta_dtype == HHR_BF16:
+        m = meta_flat.view(torch.bfloat16).reshape(B, Hkv, NPB, D // 4, 64, 4, 2)  # [..][blk][quad][lane][dim][max/min]
+        m = m.permute(0, 1, 2, 4, 3, 5, 6).reshape(B, Hkv, NPB * 64, D, 2).float()
+    else:
+        m = meta_flat.reshape(B, Hkv, NPB, D // 2, 64, 2, 2)  # [..][blk][pair][lane][dim-in-pair][max/min]
+        m = m.permute(0, 1, 2, 4, 3, 5, 6).reshape(B, Hkv, NPB * 64, D, 2)
     return m[:, :, :NP]

@@ -54,6 +54,8 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
         return fail(HHR_E_SHAPE, "max_ctx must be in 1..2^26 (got %d)", d->max_ctx);
     if (d->kv_dtype != HHR_F32 && d->kv_dtype != HHR_BF16)
         return fail(HHR_E_DTYPE, "kv_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->kv_dtype);
+    if (d->meta_dtype != HHR_F32 && d->meta_dtype != HHR_BF16)
+        return fail(HHR_E_DTYPE, "meta_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->meta_dtype);
     s.B = d->batch;
     s.Hq = d->n_q_heads;
     s.Hkv = d->n_kv_heads;
@@ -66,6 +68,7 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
     s.NPmax = ((int64_t)s.T + s.P - 1) / s.P;
     s.NPB = (s.NPmax + 63) / 64;
     s.bf16 = d->kv_dtype == HHR_BF16;
+    s.meta16 = d->meta_dtype == HHR_BF16;
     return HHR_OK;
 }
 
@@ -172,7 +175,7 @@ extern "C" {
 size_t hhr_meta_bytes(const hhr_dims* dims) {
     Shape s;
     if (make_shape(dims, s) != HHR_OK) return 0;
-    return (size_t)s.B * s.Hkv * (size_t)s.NPB * 64 * s.D * 2 * sizeof(float);
+    return (size_t)s.B * s.Hkv * (size_t)s.NPB * 64 * s.D * 2 * (s.meta16 ? sizeof(uint16_t) : sizeof(float));
 }
 
 size_t hhr_codes_bytes(const hhr_dims* dims) {

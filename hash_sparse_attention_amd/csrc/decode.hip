@@ -4,6 +4,8 @@
 // rit.work HHR blog post, sections "Почему расстояние Хэмминга пропускает
 // важные ключи" and "Два уровня маршрутизации решают разные ошибки";
 // top-k selection as in Appendix Table 4 of the thelatestinai.com page.)
+#include <type_traits>
+
 #include "hhr_internal.h"
 
 namespace hhr {
@@ -40,14 +42,37 @@ __device__ __forceinline__ void bound_batch(const float4 (&v)[U], const double2*
     }
 }
 
-template <int D, int G, int U>
+// The same for bf16 metadata: one 16-byte slot holds a dimension quad
+// (max, min) x 4 as bf16, widened exactly to fp64.
+template <int G, int U>
+__device__ __forceinline__ void bound_batch16(const uint4 (&v)[U], const double2* __restrict__ qs, int j0,
+                                              double (&acc)[G]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int d = 4 * (j0 + u);
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double a = __uint_as_float(w[e] << 16), c = __uint_as_float(w[e] & 0xffff0000u);
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const double2 q = qs[(d + e) * G + i];
+                acc[i] = __builtin_fma(q.x, a, acc[i]);
+                acc[i] = __builtin_fma(q.y, c, acc[i]);
+            }
+        }
+    }
+}
+
+template <int D, int G, int U, bool M16>
 __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
                                                          int64_t NPB, int64_t NPmax) {
-    constexpr int NJ = D / 2;  // float4 per page
+    constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
+    using V4 = typename std::conditional<M16, uint4, float4>::type;
     __shared__ double2 qs[D * G];  // (max(q,0), min(q,0)) per dimension and query head
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -61,7 +86,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     __syncthreads();
     if (p >= NP) return;
 
-    const float4* mp = reinterpret_cast<const float4*>(meta) + (bh * NPB + p / 64) * (D / 2) * 64 + (p & 63);
+    const V4* mp = reinterpret_cast<const V4*>(meta) + (bh * NPB + p / 64) * NJ * 64 + (p & 63);
     double acc[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.0;
@@ -70,8 +95,8 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     // is summed.  The empty asm statements are compiler barriers for memory
     // operations, so the loads stay where they are written.
     constexpr int NBT = NJ / U;
-    float4 A[U], B[U];
-    auto load = [&](float4 (&v)[U], int k) {
+    V4 A[U], B[U];
+    auto load = [&](V4 (&v)[U], int k) {
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = mp[(int64_t)(k * U + u) * 64];
     };
@@ -81,11 +106,16 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     for (int k = 0; k < NBT; k += 2) {
         if (k + 1 < NBT) load(B, k + 1);
         asm volatile("" ::: "memory");
-        bound_batch<G, U>(A, qs, k * U, acc);
+        if constexpr (M16) bound_batch16<G, U>(A, qs, k * U, acc);
+        else bound_batch<G, U>(A, qs, k * U, acc);
         asm volatile("" ::: "memory");
         if (k + 2 < NBT) load(A, k + 2);
         asm volatile("" ::: "memory");
-        if (k + 1 < NBT) bound_batch<G, U>(B, qs, (k + 1) * U, acc);
+        if constexpr (M16) {
+            if (k + 1 < NBT) bound_batch16<G, U>(B, qs, (k + 1) * U, acc);
+        } else {
+            if (k + 1 < NBT) bound_batch<G, U>(B, qs, (k + 1) * U, acc);
+        }
         asm volatile("" ::: "memory");
     }
     double S = acc[0];
@@ -100,7 +130,9 @@ template <int D, int G>
 hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
     const dim3 grid((unsigned)((s.NPmax + 255) / 256), s.Hkv, s.B);
-    hipLaunchKernelGGL((page_bound_kernel<D, G, 8>), grid, dim3(256), 0, st, a.meta,
+    // Loads per lane per batch (two batches in flight), measured best per metadata type.
+    auto kern = s.meta16 ? page_bound_kernel<D, G, 8, true> : page_bound_kernel<D, G, 4, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
                        reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax);
     return hipGetLastError();

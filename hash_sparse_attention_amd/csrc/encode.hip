@@ -36,7 +36,7 @@ __device__ __forceinline__ EncRange enc_range(const int32_t* start, const int32_
 }
 
 // ------------------------------------------------------------------ bulk
-template <int D, int NB, bool BF16>
+template <int D, int NB, bool BF16, bool M16>
 __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict__ K, const float* __restrict__ R,
                                                           const float* __restrict__ W,
                                                           const int32_t* __restrict__ start,
@@ -84,6 +84,8 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
     const int p = t / P;
     const bool leader = (t - base) % P == 0 && valid;
     float4* mrow = reinterpret_cast<float4*>(meta) + (bh * NPB + p / 64) * (D / 2) * 64 + (p & 63);
+    // bf16 meta: dimension quad r/4 of page p is one 16-byte slot; a pair is its (r % 4) / 2 half.
+    uint2* mrow16 = reinterpret_cast<uint2*>(meta) + ((bh * NPB + p / 64) * (D / 4) * 64 + (p & 63)) * 2;
     for (int r = 0; r < D; r += 2) {
         float mx[2], mn[2];
 #pragma unroll
@@ -100,7 +102,12 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
                 mn[q] = fminf(mn[q], __shfl_xor(mn[q], o, 64));
             }
         }
-        if (leader) mrow[(r / 2) * 64] = make_float4(mx[0], mn[0], mx[1], mn[1]);
+        if (leader) {
+            if (M16)
+                mrow16[(r / 4) * 64 * 2 + (r % 4) / 2] = make_uint2(bf16_pair_out(mx[0], mn[0]), bf16_pair_out(mx[1], mn[1]));
+            else
+                mrow[(r / 2) * 64] = make_float4(mx[0], mn[0], mx[1], mn[1]);
+        }
     }
 
     // Hash rows: this lane's own code words.
@@ -121,11 +128,11 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
     }
 }
 
-template <int D, int NB, bool BF16>
+template <int D, int NB, bool BF16, bool M16>
 hipError_t launch_dnb(const Shape& s, const void* K, const float* R, const float* W, const int32_t* start,
                       const int32_t* count, int max_count, float* meta, uint64_t* codes, hipStream_t st) {
     const int tiles = (max_count + s.P - 1 + 255) / 256;  // keys [floor(s/P)P, e) in 256-key tiles
-    hipLaunchKernelGGL((encode_bulk_kernel<D, NB, BF16>), dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W,
+    hipLaunchKernelGGL((encode_bulk_kernel<D, NB, BF16, M16>), dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W,
                        start, count, max_count, meta, codes, s.Hkv, s.T, s.P, s.NPB);
     return hipGetLastError();
 }
@@ -133,8 +140,11 @@ hipError_t launch_dnb(const Shape& s, const void* K, const float* R, const float
 template <int D, int NB>
 hipError_t launch_dt(const Shape& s, const void* K, const float* R, const float* W, const int32_t* start,
                      const int32_t* count, int max_count, float* meta, uint64_t* codes, hipStream_t st) {
-    return s.bf16 ? launch_dnb<D, NB, true>(s, K, R, W, start, count, max_count, meta, codes, st)
-                  : launch_dnb<D, NB, false>(s, K, R, W, start, count, max_count, meta, codes, st);
+    if (s.meta16)
+        return s.bf16 ? launch_dnb<D, NB, true, true>(s, K, R, W, start, count, max_count, meta, codes, st)
+                      : launch_dnb<D, NB, false, true>(s, K, R, W, start, count, max_count, meta, codes, st);
+    return s.bf16 ? launch_dnb<D, NB, true, false>(s, K, R, W, start, count, max_count, meta, codes, st)
+                  : launch_dnb<D, NB, false, false>(s, K, R, W, start, count, max_count, meta, codes, st);
 }
 
 }  // namespace

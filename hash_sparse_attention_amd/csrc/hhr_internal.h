@@ -15,7 +15,8 @@ struct Shape {
     int B, Hq, Hkv, G, D, P, NB, NW, T;
     int64_t NPmax;  // pages of a full-capacity sequence
     int64_t NPB;    // 64-page blocks of meta per (b, h)
-    bool bf16;
+    bool bf16;      // Q, K, V are bf16
+    bool meta16;    // page metadata is bf16 (outward-rounded)
 };
 
 // Attention keys handled by one block (one split) of the attend kernel.
@@ -98,6 +99,22 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 // ---------------------------------------------------------------- device helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Outward rounding of page statistics to bf16 (bit patterns): the smallest
+// bf16 >= x for a max, the largest bf16 <= x for a min.  Dropping the low
+// half of the bits moves x toward zero, so a positive max (negative min)
+// with a nonzero low half goes one bf16 step further out.  Finite inputs,
+// -0 already read as +0.
+__device__ __forceinline__ uint32_t bf16_up(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u >> 16) + ((u & 0xffffu) != 0 && !(u >> 31) ? 1u : 0u);
+}
+__device__ __forceinline__ uint32_t bf16_down(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u >> 16) + ((u & 0xffffu) != 0 && (u >> 31) ? 1u : 0u);
+}
+// (max, min) of one dimension as the two bf16 of a 32-bit word, max first.
+__device__ __forceinline__ uint32_t bf16_pair_out(float mx, float mn) { return bf16_up(mx) | (bf16_down(mn) << 16); }
 
 __device__ __forceinline__ int clamp_len(int L, int T) { return L < 0 ? 0 : (L > T ? T : L); }
 

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     const float* __restrict__ W, const int32_t* __restrict__ start, const int32_t* __restrict__ count,
     int max_count, int key_blocks, float* __restrict__ meta, uint64_t* __restrict__ codes,
     float* __restrict__ q_rot, uint64_t* __restrict__ code_q, double* __restrict__ q_split,
-    uint32_t* __restrict__ counters, int n_counters, int Hq, int Hkv, int G, int T, int P, int64_t NPB) {
+    uint32_t* __restrict__ counters, int n_counters, int Hq, int Hkv, int G, int T, int P, int64_t NPB, bool meta16) {
     constexpr int RG = (D + NB) / 64;  // row groups of [R_h; W_h]
     constexpr int NW = NB / 64;
     constexpr int LDM = D + 4;         // padded row stride of the tile (floats)
@@ -169,8 +169,14 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
                 mx = fmaxf(mx, red[g][lane][0]);
                 mn = fminf(mn, red[g][lane][1]);
             }
-            float* mp = meta + (((bh * NPB + p / 64) * (D / 2) + row / 2) * 64 + (p & 63)) * 4 + (row & 1) * 2;
-            *reinterpret_cast<float2*>(mp) = make_float2(mx, mn);
+            if (meta16) {  // bf16 slot (dimension quad row / 4, page p), word row % 4
+                uint32_t* mp = reinterpret_cast<uint32_t*>(meta) +
+                               (((bh * NPB + p / 64) * (D / 4) + row / 4) * 64 + (p & 63)) * 4 + (row & 3);
+                *mp = bf16_pair_out(mx, mn);
+            } else {
+                float* mp = meta + (((bh * NPB + p / 64) * (D / 2) + row / 2) * 64 + (p & 63)) * 4 + (row & 1) * 2;
+                *reinterpret_cast<float2*>(mp) = make_float2(mx, mn);
+            }
         }
     }
 }
@@ -183,7 +189,7 @@ hipError_t project_t(const Shape& s, const ProjectArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((project_kernel<D, NB, BF16, KEYS, QUERIES>), dim3(s.Hkv, s.B, blocks),
                        dim3(kProjWaves * 64), 0, st, a.Q, a.K, a.R, a.W, a.start, a.count, a.max_count, key_blocks,
                        a.meta, a.codes, a.q_rot, a.code_q, a.q_split, a.counters, a.n_counters, s.Hq, s.Hkv, s.G,
-                       s.T, s.P, s.NPB);
+                       s.T, s.P, s.NPB, s.meta16);
     return hipGetLastError();
 }
 

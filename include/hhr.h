@@ -53,11 +53,17 @@
  *   R     [Hkv][D][D]  fp32   rotated_r = sum_c R[h][r][c] * x_c
  *   W     [Hkv][b][D]  fp32   bit j of a code = [ sum_c W[h][j][c] * x_c > 0 ]
  *   codes [B][Hkv][T][NW] uint64; bit j of a code is bit j%64 of word j/64
- *   meta  [B][Hkv][NPB][D/2][64][4] fp32, page-block interleaved: for page
- *         p = 64*blk + lane and dimension pair (2e, 2e+1) the four floats are
- *         (max_2e, min_2e, max_2e+1, min_2e+1) of the rotated keys of page p.
- *         A wave of 64 lanes, one page each, reads one dimension pair of 64
- *         pages as one contiguous 1 KiB span.
+ *   meta  meta_dtype HHR_F32: [B][Hkv][NPB][D/2][64][4] fp32, page-block
+ *         interleaved: for page p = 64*blk + lane and dimension pair
+ *         (2e, 2e+1) the four floats are (max_2e, min_2e, max_2e+1, min_2e+1)
+ *         of the rotated keys of page p.  A wave of 64 lanes, one page each,
+ *         reads one dimension pair of 64 pages as one contiguous 1 KiB span.
+ *         meta_dtype HHR_BF16: [B][Hkv][NPB][D/4][64][8] bf16 bit patterns,
+ *         the same interleave over dimension quads (max_4e, min_4e, ...,
+ *         max_4e+3, min_4e+3); each max is rounded up and each min down to
+ *         bf16 (outward), so the page bound below, computed from them, still
+ *         bounds every key of the page.  The pointer type stays float* in
+ *         the calls; the buffer holds hhr_meta_bytes(dims) bytes either way.
  *   out   [B][Hq][D] fp32
  *   sel_idx [B][Hkv][top_k] int32: the selected key positions, ascending,
  *         padded with -1.
@@ -68,7 +74,7 @@
  *     acc = +0.0f; for c = 0..D-1: acc = fmaf(M[r][c], x_c, acc)  (fp32, IEEE
  *     round-to-nearest-even, denormals kept).  bf16 inputs widen exactly.
  *   - A rotated key coordinate equal to -0 is stored as +0 before max/min.
- *   - The page bound of query head i is
+ *   - The page bound of query head i is (kmax, kmin as stored in meta)
  *       U_i(p) = sum over r ascending of max(qrot_i,r * kmax_r, qrot_i,r * kmin_r)
  *     evaluated in fp64 (each product of two fp32 values is exact in fp64);
  *     the score of the KV head's group is S(p) = max_i U_i(p), with -0 read
@@ -90,7 +96,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 1
+#define HHR_ABI_VERSION 2
 
 typedef enum {
     HHR_OK = 0,
@@ -115,6 +121,9 @@ typedef struct {
     int32_t hash_bits;  /* b                                              */
     int32_t max_ctx;    /* T: row capacity of K, V and codes              */
     int32_t kv_dtype;   /* hhr_dtype of Q, K and V                        */
+    int32_t meta_dtype; /* hhr_dtype of the page metadata: HHR_F32 (0, the
+                           default) or HHR_BF16 (outward-rounded, half the
+                           bytes; see "meta" under Layouts)               */
 } hhr_dims;
 
 /* Bytes of the meta and codes buffers for these dims (0 if the dims are invalid). */

@@ -52,7 +52,8 @@ def build(force: bool = True) -> str:
 
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_bf16")]
+        "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_bf16",
+        "meta_bf16")]
 
 
 def _load():
@@ -88,6 +89,7 @@ class Dims:
     hash_bits: int
     max_ctx: int
     kv_bf16: bool
+    meta_bf16: bool = False  # page max/min rounded outward to bf16 values
 
     @property
     def group(self) -> int:
@@ -103,7 +105,7 @@ class Dims:
 
     def c(self) -> _Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.page_size,
-                     self.hash_bits, self.max_ctx, int(self.kv_bf16))
+                     self.hash_bits, self.max_ctx, int(self.kv_bf16), int(self.meta_bf16))
 
 
 def _ptr(a):

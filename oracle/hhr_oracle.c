@@ -47,6 +47,7 @@ typedef struct {
     int32_t hash_bits;  /* b, a multiple of 64                 */
     int32_t max_ctx;    /* Tmax: row capacity of K, V, codes   */
     int32_t kv_bf16;    /* 1: Q, K, V hold bf16 bit patterns (uint16); 0: fp32 */
+    int32_t meta_bf16;  /* 1: page max/min are stored rounded outward to bf16 values */
 } oracle_dims;
 
 enum { ORACLE_OK = 0, ORACLE_BAD_DIMS = 1, ORACLE_NOMEM = 2 };
@@ -110,6 +111,39 @@ int oracle_project(int32_t D, int32_t nbits, const float* R, const float* W, con
     return ORACLE_OK;
 }
 
+/* bf16 neighbours of a finite fp32 x: bf16_trunc drops the low 16 bits
+ * (rounds toward zero); bf16_away is the next bf16 one step further from
+ * zero than the truncation. */
+static float bf16_trunc(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u &= 0xffff0000u;
+    float y;
+    memcpy(&y, &u, 4);
+    return y;
+}
+static float bf16_away(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    u = (u & 0xffff0000u) + 0x10000u;
+    float y;
+    memcpy(&y, &u, 4);
+    return y;
+}
+/* Outward rounding of a page statistic to bf16, so that the stored interval
+ * [kmin, kmax] still contains every key of the page ("store page bounds":
+ * the bound must stay an upper bound): the smallest bf16 >= x for a max, the
+ * largest bf16 <= x for a min.  x and its truncation enclose nothing but
+ * each other, and the truncation and bf16_away enclose x. */
+static float bf16_ceil(float x) {
+    const float t = bf16_trunc(x);
+    return t >= x ? t : bf16_away(x);
+}
+static float bf16_floor(float x) {
+    const float t = bf16_trunc(x);
+    return t <= x ? t : bf16_away(x);
+}
+
 /*
  * Encode keys [start[b], start[b]+count[b]) of every sequence b.
  *
@@ -119,6 +153,8 @@ int oracle_project(int32_t D, int32_t nbits, const float* R, const float* W, con
  *   for every page p the range touches, over that page's keys below
  *   start+count.  These are the stored page bounds [BLOG, "Когда HHR...";
  *   ABS].  A rotated value of -0 is taken as +0 so that max/min are unique.
+ *   With meta_bf16 the max is then rounded up and the min down to bf16
+ *   values (bf16_ceil / bf16_floor), kept here as fp32.
  * Layouts: K [B][Hkv][Tmax][D]; R [Hkv][D][D]; W [Hkv][b][D];
  *          meta [B][Hkv][ceil(Tmax/P)][D][2] fp32; codes [B][Hkv][Tmax][b/64].
  */
@@ -160,6 +196,11 @@ int oracle_encode(const oracle_dims* dm, const void* K, const float* R, const fl
                         if (t == lo || v < m[2 * r + 1]) m[2 * r + 1] = v;
                     }
                 }
+                if (dm->meta_bf16)
+                    for (int r = 0; r < D; ++r) {
+                        m[2 * r] = bf16_ceil(m[2 * r]);
+                        m[2 * r + 1] = bf16_floor(m[2 * r + 1]);
+                    }
             }
             free(x);
             free(xr);

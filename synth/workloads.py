@@ -43,6 +43,7 @@ class Workload:
     ragged: tuple | None = None  # (lo, hi): per-sequence lengths uniform in [lo, hi]
     append_tokens: int = 0       # size of the encode-append chunk timed for this workload
     planted: int = 8
+    meta_bf16: bool = False      # page metadata stored as outward-rounded bf16
 
     @property
     def group(self) -> int:

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(hsa):
 
 def test_version_and_status_strings(hsa):
     L = hsa.lib()
-    assert L.hhr_abi_version() == 1
+    assert L.hhr_abi_version() == 2
     for code, name in hsa.STATUS.items():
         assert L.hhr_status_str(code).decode() == name
 
@@ -77,6 +77,18 @@ def test_bad_dtype(hsa):
     d = dims()
     d.kv_dtype = 7
     assert call_decode(hsa, d, ws_bytes=1 << 30) == 3
+
+
+def test_bad_meta_dtype_and_meta_bytes(hsa):
+    L = hsa.lib()
+    d = dims()
+    d.meta_dtype = 5
+    assert call_decode(hsa, d, ws_bytes=1 << 30) == 3
+    assert L.hhr_meta_bytes(ctypes.byref(d)) == 0
+    f32, b16 = dims(), dims(meta_bf16=True)
+    # fp32 meta: B * Hkv * NPB * 64 pages * D * (max, min) * 4 bytes; bf16 meta is half of it
+    assert L.hhr_meta_bytes(ctypes.byref(f32)) == 1 * 8 * 128 * 64 * 128 * 2 * 4
+    assert L.hhr_meta_bytes(ctypes.byref(b16)) * 2 == L.hhr_meta_bytes(ctypes.byref(f32))
 
 
 def test_null_and_alignment(hsa):

@@ -48,6 +48,19 @@ def test_decode_parity_shapes(dev, name, wl):
     compare(wl, d["seq_len"], g, o, label=name)
 
 
+@pytest.mark.parametrize("name", ["tiny", "d64_b128_g1_p1", "d128_b128_g7_p16", "d64_b64_g8_p64", "llama8b_32k"])
+def test_bf16_meta_parity(dev, name):
+    """Outward-rounded bf16 page metadata: meta (widened), scores, pages, distances, selections bit for bit and
+    attention within the bar, against the oracle run with the same metadata rule."""
+    wl = WORKLOADS[name] if name in WORKLOADS else dict(SHAPES)[name]
+    wl = (WORKLOADS["tiny"] if wl is None else wl).with_(meta_bf16=True)
+    banner(f"bf16 meta parity {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=f"{name} bf16 meta")
+
+
 def test_empty_and_tiny_sequences(dev):
     wl = Workload("edge", 110, 4, 8, 2, 128, 600, 16, 128, 25, 40, "bf16")
     banner("empty and tiny sequences")
@@ -227,14 +240,15 @@ def test_qwen7b_b16_append_4096_sampled(dev):
     compare(wl, seq, g, o, batches=batches, label="qwen7b_b16")
 
 
-def test_decode_step_append_matches_oracle(dev):
+@pytest.mark.parametrize("meta_bf16", [False, True], ids=["fp32_meta", "bf16_meta"])
+def test_decode_step_append_matches_oracle(dev, meta_bf16):
     """hhr_decode_step_append (fused append + query projection) equals the oracle's single-shot encode +
     decode, for a 1-token append, a ragged multi-token append, and an append larger than the fused limit."""
     import torch
 
     import hash_sparse_attention_amd as hsa
     from gpu_common import gpu_dims, to_dev
-    wl = Workload("fused", 114, 3, 12, 3, 128, 700, 16, 128, 20, 48, "bf16", outliers=2)
+    wl = Workload("fused", 114, 3, 12, 3, 128, 700, 16, 128, 20, 48, "bf16", outliers=2, meta_bf16=meta_bf16)
     d = make_layer(wl, lengths=[700, 650, 333])
     o = run_oracle(wl, d)
     for new in ([1, 1, 1], [5, 17, 1], [70, 3, 100]):

@@ -35,7 +35,7 @@ def bits_of(codes):
 
 def dims_for(o, wl: Workload):
     return o.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits,
-                  wl.ctx, wl.dtype == "bf16")
+                  wl.ctx, wl.dtype == "bf16", wl.meta_bf16)
 
 
 def f32(x, wl):
@@ -246,6 +246,80 @@ def test_page_bound_is_upper_bound_of_every_logit(oracle_mod, G, P):
                 assert S >= (raw[:, sl] - 1e-5 * qn * kn[:, sl]).max()
                 if P == 1:
                     assert abs(S - lt[:, sl].max()) <= 1e-12 * mag.max()
+
+
+def _bf16_step(v, down: bool):
+    """The bf16 value adjacent to the bf16 value v (fp32 array, low 16 bits zero), toward -inf (down) or +inf;
+    from the IEEE bit layout, independent of the oracle's code."""
+    u = np.asarray(v, np.float32).view(np.uint32).astype(np.int64)
+    neg = (u >> 31) == 1
+    mag_up = (neg & down) | (~neg & ~down)  # moving away from zero
+    zero = (u & 0x7FFFFFFF) == 0
+    out = np.where(mag_up, u + 0x10000, u - 0x10000)
+    out = np.where(zero, np.where(down, 0x80010000, 0x00010000), out)
+    return out.astype(np.uint32).view(np.float32)
+
+
+def test_bf16_meta_is_outward_rounding_of_fp32_meta(oracle_mod):
+    """With bf16 metadata every stored max is the smallest bf16 value >= the page's true max and every min the
+    largest bf16 value <= its true min (the true values: the fp32-metadata encode of the same keys)."""
+    wl = WORKLOADS["tiny"].with_(batch=2, ragged=(1000, 4096))
+    d = make_layer(wl)
+    seq = d["seq_len"]
+    dm32 = dims_for(oracle_mod, wl)
+    dm16 = dims_for(oracle_mod, wl.with_(meta_bf16=True))
+    m32, _ = oracle_mod.encode(dm32, d["K"], d["R"], d["W"], np.zeros(wl.batch, np.int32), seq)
+    m16, _ = oracle_mod.encode(dm16, d["K"], d["R"], d["W"], np.zeros(wl.batch, np.int32), seq)
+    for b in range(wl.batch):
+        NP = -(-int(seq[b]) // wl.page_size)
+        mx32, mn32 = m32[b, :, :NP, :, 0], m32[b, :, :NP, :, 1]
+        mx16, mn16 = m16[b, :, :NP, :, 0], m16[b, :, :NP, :, 1]
+        assert (mx16.view(np.uint32) & 0xFFFF == 0).all() and (mn16.view(np.uint32) & 0xFFFF == 0).all()
+        assert (mx16 >= mx32).all() and (mn16 <= mn32).all()
+        assert (_bf16_step(mx16, down=True) < mx32).all()     # nothing bf16 in [true max, stored max)
+        assert (_bf16_step(mn16, down=False) > mn32).all()    # nothing bf16 in (stored min, true min]
+        assert (mx16 > mx32).any()  # the rounding is not vacuous on these keys
+
+
+def test_bf16_meta_rounding_special_values(oracle_mod):
+    """Hand cases through a one-key page: values already bf16 stay; positive and negative values round
+    outward; +0 stays +0 (the rotation is the identity, so the page max/min are the key itself)."""
+    D = 32
+    vals = np.zeros(D, np.float32)
+    vals[:8] = [1.0, -1.0, 1.0 + 2.0 ** -10, -(1.0 + 2.0 ** -10), 3.0e-39, -3.0e-39, 0.0, 65504.0]
+    K = vals[None, None, None, :]
+    R = np.eye(D, dtype=np.float32)[None]
+    W = np.eye(64, D, dtype=np.float32)[None]
+    dm = oracle_mod.Dims(1, 1, 1, D, 1, 64, 1, False, True)
+    m, _ = oracle_mod.encode(dm, K, R, W, np.array([0], np.int32), np.array([1], np.int32))
+    mx, mn = m[0, 0, 0, :8, 0], m[0, 0, 0, :8, 1]
+    up = [1.0, -1.0, 1.0 + 2.0 ** -7, -1.0, None, None, 0.0, 65536.0]
+    dn = [1.0, -1.0, 1.0, -(1.0 + 2.0 ** -7), None, None, 0.0, 65504.0 - 224.0]
+    for i in (0, 1, 2, 3, 6):
+        assert mx[i] == np.float32(up[i]) and mn[i] == np.float32(dn[i]), i
+    # 3e-39 (an fp32 denormal): the max rounds up to a bf16 denormal above it, the min down to below it
+    assert mx[4] >= vals[4] and mn[4] <= vals[4] and mx[5] >= vals[5] and mn[5] <= vals[5]
+    assert mx[7] == np.float32(65536.0) and mn[7] == np.float32(65280.0)
+
+
+@pytest.mark.parametrize("G,P", [(4, 4), (2, 16)])
+def test_bf16_meta_bound_still_bounds_every_logit(oracle_mod, G, P):
+    """The page bound from bf16 metadata is >= the bound from fp32 metadata of the same keys, hence >= every
+    rotated logit of the page."""
+    wl = Workload("pin_ub16", 92, 2, 2 * G, 2, 32, 200, P, 64, 30, 32, "bf16", outliers=2, ragged=(150, 200))
+    d = make_layer(wl)
+    _, _, _, r32 = run(oracle_mod, wl, d, max_keep=-(-200 // P))
+    _, _, _, r16 = run(oracle_mod, wl.with_(meta_bf16=True), d, max_keep=-(-200 // P))
+    Kf = f32(d["K"], wl)
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        NP = -(-L // P)
+        assert (r16["score"][b, :, :NP] >= r32["score"][b, :, :NP]).all()
+        for h in range(wl.n_kv_heads):
+            kr, _ = oracle_mod.project(d["R"][h], d["W"][h], Kf[b, h, :L])
+            lt = r16["q_rot"][b, h * G:(h + 1) * G].astype(np.float64) @ kr.astype(np.float64).T
+            for p in range(NP):
+                assert r16["score"][b, h, p] >= lt[:, p * P:min((p + 1) * P, L)].max() - 1e-9
 
 
 def test_page_select_is_lexsort_of_scores(oracle_mod):
