@@ -435,3 +435,19 @@ def test_page_select_stage_on_tied_scores(dev, npages, seq, keep, max_keep):
     want_pages, want_n = oracle.select_pages(oracle_dims(wl), S, seq, keep, max_keep)
     assert np.array_equal(v.n_pages.cpu().numpy(), want_n)
     assert np.array_equal(v.pages.cpu().numpy(), want_pages)
+
+
+def test_fidelity_harness_matches_oracle_selection(dev):
+    """The retrieval-fidelity harness, run through the library, reports the same key recall, page coverage,
+    attention mass and planted recall as on the oracle's selections (the selections are equal)."""
+    from hash_sparse_attention_amd.fidelity import metrics, run_library
+    wl = WORKLOADS["tiny"].with_(batch=2, ragged=(2000, 4096))
+    banner("fidelity harness")
+    d = make_layer(wl)
+    out, sel, pages, n_pages = run_library(wl, d, dev)
+    g = metrics(wl, d, sel, out, pages, n_pages)
+    o = run_oracle(wl, d)
+    m = metrics(wl, d, o["sel"], o["out"], o["pages"], o["n_pages"])
+    for k in ("key_recall", "page_coverage", "attention_mass", "planted_recall"):
+        assert g[k] == m[k], k
+    assert abs(g["out_max_err"] - m["out_max_err"]) <= 2e-3

@@ -579,3 +579,45 @@ def test_planted_keys_in_kept_pages_are_selected(oracle_mod):
         assert surv <= set(r["sel"][0, h])
         hits += len(surv)
     assert hits > 0
+
+
+# ----------------------------------------------------------------------------- fidelity harness metrics
+
+def test_fidelity_metrics_on_oracle_selections(oracle_mod):
+    """The harness's metrics on known selections: selecting every key of every page (keep all, top_k >= L)
+    gives recall, coverage, mass and planted recall 1 and full attention's output; the oracle's sparse
+    selection gives values in [0, 1] and selects the planted keys of kept pages."""
+    from hash_sparse_attention_amd.fidelity import metrics
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    NPg = wl.max_pages
+    dims, meta, codes, r = run(oracle_mod, wl, d, keep=[NPg], max_keep=NPg, top_k=wl.ctx)
+    m = metrics(wl, d, r["sel"], r["out"], r["pages"], r["n_pages"])
+    assert m["key_recall"] == 1.0 and m["page_coverage"] == 1.0 and m["planted_recall"] == 1.0
+    assert abs(m["attention_mass"] - 1.0) < 1e-12 and m["out_max_err"] < 1e-9
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    m = metrics(wl, d, r["sel"], r["out"], r["pages"], r["n_pages"])
+    for k in ("key_recall", "page_coverage", "attention_mass", "planted_recall"):
+        assert 0.0 <= m[k] <= 1.0, k
+    assert m["key_recall"] <= m["page_coverage"] + 1e-12  # a key the page stage dropped cannot be selected
+
+
+def test_fidelity_recall_counts_the_exact_top_k(oracle_mod):
+    """Hand-built selections: the exact top-k itself has recall 1; its first half padded with keys outside
+    it has recall 1/2 (recall is measured at the selection's own size)."""
+    from hash_sparse_attention_amd.fidelity import metrics
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    G, L = wl.group, int(d["seq_len"][0])
+    sel = np.full_like(r["sel"], -1)
+    half = np.full_like(r["sel"], -1)
+    for h in range(wl.n_kv_heads):
+        q = f32(d["Q"], wl)[0, h * G:(h + 1) * G].astype(np.float64)
+        s = (q @ f32(d["K"], wl)[0, h, :L].astype(np.float64).T).max(axis=0)
+        order = np.lexsort((np.arange(L), -s))
+        k = 64
+        sel[0, h, :k] = np.sort(order[:k])
+        half[0, h, :k] = np.sort(np.concatenate([order[:k // 2], order[L - k // 2:]]))
+    assert metrics(wl, d, sel, r["out"], r["pages"], r["n_pages"])["key_recall"] == 1.0
+    assert metrics(wl, d, half, r["out"], r["pages"], r["n_pages"])["key_recall"] == 0.5
