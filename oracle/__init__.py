@@ -71,9 +71,10 @@ def _load():
         lib.oracle_decode.argtypes = [ctypes.POINTER(_Dims), p, p, p, p, p, p, p, p, p,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float] + [p] * 9
         lib.oracle_select_pages.argtypes = [ctypes.POINTER(_Dims), p, p, p, ctypes.c_int32, p, p]
+        lib.oracle_topk.argtypes = [ctypes.POINTER(_Dims), p, p, p, p, ctypes.c_int32, ctypes.c_float] + [p] * 4
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_project, lib.oracle_encode, lib.oracle_decode, lib.oracle_select_pages,
-                  lib.oracle_max_threads):
+                  lib.oracle_topk, lib.oracle_max_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -205,3 +206,21 @@ def select_pages(dims: Dims, score, seq_len, keep_pages, max_keep):
     if st:
         raise ValueError(f"oracle_select_pages failed ({st})")
     return pages, n_pages
+
+
+def topk(dims: Dims, Q, K, V, seq_len, top_k, scale=0.0):
+    """TopK (Oracle) step: keys by exact logit, then attention; returns dict(score, sel, k_eff, out).
+
+    score [B][Hkv][Tmax] fp64 is the group-max logit z(t) (0 for t >= L); only batch, heads,
+    head_dim, max_ctx and the kv dtype of `dims` matter.
+    """
+    B, Hq, Hkv, D = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    Q = _kv(Q, dims); K = _kv(K, dims); V = _kv(V, dims)
+    seq_len = _c(np.asarray(seq_len, np.int32), np.int32)
+    r = dict(score=np.zeros((B, Hkv, dims.max_ctx), np.float64), sel=np.zeros((B, Hkv, top_k), np.int32),
+             k_eff=np.zeros((B, Hkv), np.int32), out=np.zeros((B, Hq, D), np.float64))
+    st = _load().oracle_topk(ctypes.byref(dims.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(seq_len), int(top_k),
+                             float(scale), *(_ptr(r[k]) for k in ("score", "sel", "k_eff", "out")))
+    if st:
+        raise ValueError(f"oracle_topk failed ({st})")
+    return r

@@ -243,6 +243,41 @@ static int64_t select_pages_one(page_key* pk, int64_t NP, int64_t keep, int32_t 
     return keep;
 }
 
+/* Softmax scale: the caller's when positive, else 1/sqrt(D). */
+static double softmax_scale(float scale_in, int D) {
+    return scale_in > 0.0f ? (double)scale_in : 1.0 / sqrt((double)D);
+}
+
+/* Attention of the G query heads q [G][D] (fp32 values) over the keff keys
+ * sel[] of one (b, h), whose rows start at row0 of K and V: out_i =
+ * sum_j softmax_j(scale * q_i . k_j) v_j, all in fp64 (the logit summed with
+ * d ascending, the softmax shifted by its maximum) [ABS: attention over the
+ * retrieved keys].  out [G][D]; zero when keff = 0.  sc holds >= keff doubles. */
+static void attend_selected(const float* q, int G, int D, const void* K, const void* V, int64_t row0, int bf,
+                            const int32_t* sel, int64_t keff, double scale, double* sc, double* out) {
+    for (int i = 0; i < G; ++i) {
+        double* o = out + (int64_t)i * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (keff == 0) continue;
+        double mx = 0.0;
+        for (int64_t j = 0; j < keff; ++j) {
+            const int64_t row = (row0 + sel[j]) * D;
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(K, row + d, bf);
+            sc[j] = s * scale;
+            if (j == 0 || sc[j] > mx) mx = sc[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < keff; ++j) {
+            const double wgt = exp(sc[j] - mx);
+            const int64_t row = (row0 + sel[j]) * D;
+            l += wgt;
+            for (int d = 0; d < D; ++d) o[d] += wgt * (double)elem(V, row + d, bf);
+        }
+        for (int d = 0; d < D; ++d) o[d] /= l;
+    }
+}
+
 /*
  * One decode step for one layer: every sequence b, every KV head h, with the
  * G = Hq/Hkv query heads i = h*G .. h*G+G-1 that share KV head h.
@@ -288,7 +323,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
     const int D = dm->head_dim, P = dm->page_size, nb = dm->hash_bits, NW = nb / 64;
     const int64_t T = dm->max_ctx, NPmax = n_pages_of(T, P);
     const int bf = dm->kv_bf16;
-    const double scale = scale_in > 0.0f ? (double)scale_in : 1.0 / sqrt((double)D);
+    const double scale = softmax_scale(scale_in, D);
     int status = ORACLE_OK;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -382,30 +417,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
             if (keff_out) keff_out[bh] = (int32_t)keff;
 
             /* 7. attention over the selected keys */
-            if (out) {
-                for (int i = 0; i < G; ++i) {
-                    const int64_t qi = (int64_t)b * Hq + h * G + i;
-                    double* o = out + qi * D;
-                    for (int d = 0; d < D; ++d) o[d] = 0.0;
-                    if (keff == 0) continue;
-                    double mx = 0.0;
-                    for (int64_t j = 0; j < keff; ++j) {
-                        const int64_t row = (bh * T + sel[j]) * D;
-                        double s = 0.0;
-                        for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(K, row + d, bf);
-                        sc[j] = s * scale;
-                        if (j == 0 || sc[j] > mx) mx = sc[j];
-                    }
-                    double l = 0.0;
-                    for (int64_t j = 0; j < keff; ++j) {
-                        const double wgt = exp(sc[j] - mx);
-                        const int64_t row = (bh * T + sel[j]) * D;
-                        l += wgt;
-                        for (int d = 0; d < D; ++d) o[d] += wgt * (double)elem(V, row + d, bf);
-                    }
-                    for (int d = 0; d < D; ++d) o[d] /= l;
-                }
-            }
+            if (out) attend_selected(q, G, D, K, V, bh * T, bf, sel, keff, scale, sc, out + ((int64_t)b * Hq + h * G) * D);
             free(q); free(qr); free(cq); free(pk); free(plist); free(cand); free(sel); free(sc);
         }
     }
@@ -453,6 +465,83 @@ int oracle_select_pages(const oracle_dims* dm, const double* score, const int32_
             for (int64_t j = 0; j < max_keep; ++j) pages_out[bh * max_keep + j] = j < keep ? plist[j] : -1;
             npages_out[bh] = (int32_t)keep;
             free(pk); free(plist);
+        }
+    }
+    return status;
+}
+
+/*
+ * TopK (Oracle): the comparison row of the pages that keeps the keys with the
+ * largest exact attention logit, with no bounds and no codes [FIG, the
+ * "TopK (Oracle)" rows of Table 1 and Table 2, and "TopK-1.5%" in Appendix
+ * Table 4; BLOG, "Когда HHR меняет планы запуска модели": selection by exact
+ * scores].  For every sequence b and KV head h, the G query heads of h
+ * sharing one selection as in oracle_decode:
+ *  1. z(t) = max_i sum_d q_i,d * k_t,d for t < L, in fp64, d ascending from
+ *     +0: a product of two fp32 numbers is exact in fp64, so only the
+ *     additions round.  -0 is read as +0.  The group max mirrors the page
+ *     score S(p) = max_i U_i(p) of the HHR path.
+ *  2. key select: the k_eff = min(top_k, L) keys with the largest z, equal z
+ *     going to the lower t; listed ascending, padded with -1.
+ *  3. attention over them, as step 7 of oracle_decode.
+ * Outputs (NULL skips): score [B][Hkv][Tmax] fp64 (z; +0 for t >= L),
+ * sel [B][Hkv][top_k], k_eff [B][Hkv], out [B][Hq][D] fp64.
+ */
+int oracle_topk(const oracle_dims* dm, const void* Q, const void* K, const void* V, const int32_t* seq_len,
+                int32_t top_k, float scale_in, double* score_out, int32_t* sel_out, int32_t* keff_out,
+                double* out) {
+    if (!dims_ok(dm) || top_k < 1) return ORACLE_BAD_DIMS;
+    const int B = dm->batch, Hq = dm->n_q_heads, Hkv = dm->n_kv_heads, G = Hq / Hkv, D = dm->head_dim;
+    const int64_t T = dm->max_ctx;
+    const int bf = dm->kv_bf16;
+    const double scale = softmax_scale(scale_in, D);
+    int status = ORACLE_OK;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hkv; ++h) {
+            int64_t L = seq_len[b];
+            if (L < 0) L = 0;
+            if (L > T) L = T;
+            const int64_t bh = (int64_t)b * Hkv + h;
+            float* q = malloc(sizeof(float) * G * D);
+            page_key* zk = malloc(sizeof(page_key) * (L > 0 ? L : 1));
+            int32_t* sel = malloc(sizeof(int32_t) * top_k);
+            double* sc = malloc(sizeof(double) * top_k);
+            if (!q || !zk || !sel || !sc) {
+                free(q); free(zk); free(sel); free(sc);
+#pragma omp atomic write
+                status = ORACLE_NOMEM;
+                continue;
+            }
+            for (int i = 0; i < G; ++i)
+                for (int d = 0; d < D; ++d) q[i * D + d] = elem(Q, ((int64_t)b * Hq + h * G + i) * D + d, bf);
+
+            /* 1. exact logits, max over the group */
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t row = (bh * T + t) * D;
+                double z = 0.0;
+                for (int i = 0; i < G; ++i) {
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(K, row + d, bf);
+                    if (i == 0 || s > z) z = s;
+                }
+                if (z == 0.0) z = 0.0;
+                zk[t].s = z;
+                zk[t].p = (int32_t)t;
+            }
+            if (score_out)
+                for (int64_t t = 0; t < T; ++t) score_out[bh * T + t] = t < L ? zk[t].s : 0.0;
+
+            /* 2. key select: the same order as the page select, over keys */
+            const int64_t keff = select_pages_one(zk, L, top_k, top_k, sel);
+            if (sel_out)
+                for (int64_t j = 0; j < top_k; ++j) sel_out[bh * top_k + j] = j < keff ? sel[j] : -1;
+            if (keff_out) keff_out[bh] = (int32_t)keff;
+
+            /* 3. attention over the selected keys */
+            if (out) attend_selected(q, G, D, K, V, bh * T, bf, sel, keff, scale, sc, out + ((int64_t)b * Hq + h * G) * D);
+            free(q); free(zk); free(sel); free(sc);
         }
     }
     return status;

@@ -34,6 +34,11 @@ MUTANTS = {
     "meta_from_start_not_page_start": ("const int64_t lo = p * P,", "const int64_t lo = p * P < s ? s : p * P,"),
     "candidates_past_length": ("if (t >= L) continue;", "if (t >= T) continue;"),
     "keep_not_clamped_to_one": ("if (keep < 1) keep = 1;", ""),
+    "topk_group_min_not_max": ("if (i == 0 || s > z) z = s;", "if (i == 0 || s < z) z = s;"),
+    "topk_logit_from_value_rows": ("double s = 0.0;\n                    for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(K",
+                                   "double s = 0.0;\n                    for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(V"),
+    "topk_first_head_only": ("double z = 0.0;\n                for (int i = 0; i < G; ++i) {",
+                             "double z = 0.0;\n                for (int i = 0; i < 1; ++i) {"),
     "value_from_key_rows": ("o[d] += wgt * (double)elem(V, row + d, bf);", "o[d] += wgt * (double)elem(K, row + d, bf);"),
 }
 

@@ -621,3 +621,106 @@ def test_fidelity_recall_counts_the_exact_top_k(oracle_mod):
         half[0, h, :k] = np.sort(np.concatenate([order[:k // 2], order[L - k // 2:]]))
     assert metrics(wl, d, sel, r["out"], r["pages"], r["n_pages"])["key_recall"] == 1.0
     assert metrics(wl, d, half, r["out"], r["pages"], r["n_pages"])["key_recall"] == 0.5
+
+
+# ----------------------------------------------------------------------------- TopK (Oracle) selection
+
+def _int_layer(seed, B, Hq, Hkv, D, T, lo=-3, hi=3, bf16=False):
+    """Integer-valued Q, K, V: every logit is an exact integer whatever the summation order."""
+    rng = np.random.default_rng(seed)
+    Q = rng.integers(lo, hi + 1, (B, Hq, D)).astype(np.float32)
+    K = rng.integers(lo, hi + 1, (B, Hkv, T, D)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    if bf16:
+        return f32_to_bf16_bits(Q), f32_to_bf16_bits(K), f32_to_bf16_bits(V)
+    return Q, K, V
+
+
+@pytest.mark.parametrize("G,D,bf16", [(1, 16, False), (4, 16, True), (3, 64, False), (8, 8, True)])
+def test_topk_select_is_lexsort_of_integer_logits(oracle_mod, G, D, bf16):
+    """TopK (Oracle) keeps the keys of largest exact group-max logit, ties to the lower key: with
+    integer-valued inputs the logits are exact integers, so numpy's int64 products and lexsort
+    state the expected selection exactly (and the small range makes ties common)."""
+    B, Hkv, T, top_k = 2, 2, 203, 37
+    Q, K, V = _int_layer(11 + G + D, B, G * Hkv, Hkv, D, T, bf16=bf16)
+    seq = np.array([203, 29], np.int32)  # the second is shorter than top_k
+    dims = oracle_mod.Dims(B, G * Hkv, Hkv, D, 16, 64, T, bf16)
+    r = oracle_mod.topk(dims, Q, K, V, seq, top_k)
+    Qi = (bf16_bits_to_f32(Q) if bf16 else Q).astype(np.int64)
+    Ki = (bf16_bits_to_f32(K) if bf16 else K).astype(np.int64)
+    for b in range(B):
+        L = int(seq[b])
+        for h in range(Hkv):
+            z = (Qi[b, h * G:(h + 1) * G] @ Ki[b, h, :L].T).max(axis=0)
+            keff = min(top_k, L)
+            want = np.sort(np.lexsort((np.arange(L), -z))[:keff])
+            assert r["k_eff"][b, h] == keff
+            assert (r["sel"][b, h, :keff] == want).all()
+            assert (r["sel"][b, h, keff:] == -1).all()
+            assert (r["score"][b, h, :L] == z.astype(np.float64)).all()
+            assert (r["score"][b, h, L:] == 0).all()
+
+
+def test_topk_ties_go_to_lower_key(oracle_mod):
+    """All logits equal (zero query): the first top_k keys are kept."""
+    B, Hkv, G, D, T = 1, 1, 2, 8, 100
+    Q, K, V = _int_layer(5, B, G * Hkv, Hkv, D, T)
+    Q[:] = 0
+    dims = oracle_mod.Dims(B, G * Hkv, Hkv, D, 16, 64, T, False)
+    r = oracle_mod.topk(dims, Q, K, V, [T], 10)
+    assert (r["sel"][0, 0] == np.arange(10)).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "bf16_ragged"])
+def test_topk_all_keys_is_full_attention(oracle_mod, name):
+    """top_k >= L keeps every key: the output is exact softmax attention (numpy fp64)."""
+    wl = WORKLOADS["tiny"].with_(ctx=1024) if name == "tiny" else \
+        Workload("pin_topk_full", 95, 2, 6, 3, 32, 300, 16, 64, 100, 300, "bf16", outliers=2, ragged=(1, 300))
+    d = make_layer(wl)
+    r = oracle_mod.topk(dims_for(oracle_mod, wl), d["Q"], d["K"], d["V"], d["seq_len"], wl.ctx)
+    Qf, Kf, Vf = (f32(d[k], wl).astype(np.float64) for k in ("Q", "K", "V"))
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        assert (r["sel"][b, :, :L] == np.arange(L)).all() and (r["k_eff"][b] == L).all()
+        for i in range(wl.n_q_heads):
+            h = i // wl.group
+            ref = _softmax_attention(Qf[b, i], Kf[b, h, :L], Vf[b, h, :L], 1 / np.sqrt(wl.head_dim))
+            assert np.abs(r["out"][b, i] - ref).max() <= 1e-9 * max(1.0, np.abs(ref).max())
+
+
+def test_topk_logits_near_fp64_dot(oracle_mod):
+    """The group-max logit of random fp32 data is the fp64 dot product up to fp64 rounding."""
+    wl = WORKLOADS["tiny"].with_(ctx=512)
+    d = make_layer(wl)
+    r = oracle_mod.topk(dims_for(oracle_mod, wl), d["Q"], d["K"], d["V"], d["seq_len"], 64)
+    Q, K = np.asarray(d["Q"], np.float64), np.asarray(d["K"], np.float64)
+    G = wl.group
+    for h in range(wl.n_kv_heads):
+        z = (Q[0, h * G:(h + 1) * G] @ K[0, h].T).max(axis=0)
+        bound = wl.head_dim * 2.0 ** -52 * (np.abs(Q[0, h * G:(h + 1) * G]) @ np.abs(K[0, h]).T).max(axis=0)
+        assert (np.abs(r["score"][0, h] - z) <= bound).all()
+
+
+def test_topk_equals_hhr_path_at_page_size_one_without_rotation(oracle_mod):
+    """With one key per page, R_h = I and every candidate kept by the Hamming stage, the page bound
+    of a page is its key's exact logit, so the HHR step selects what TopK (Oracle) selects."""
+    wl = Workload("pin_topk_p1", 96, 2, 8, 2, 32, 160, 1, 64, 25, 24, "bf16", outliers=2, ragged=(50, 160))
+    d = make_layer(wl)
+    d["R"] = np.stack([np.eye(wl.head_dim, dtype=np.float32)] * wl.n_kv_heads)
+    top_k = 24
+    t = oracle_mod.topk(dims_for(oracle_mod, wl), d["Q"], d["K"], d["V"], d["seq_len"], top_k)
+    dims, meta, codes, r = run(oracle_mod, wl, d, keep=[top_k] * wl.batch, max_keep=top_k, top_k=top_k)
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        assert (r["score"][b, :, :L] == t["score"][b, :, :L]).all()
+    assert (r["pages"] == t["sel"]).all() and (r["sel"] == t["sel"]).all()
+    assert np.abs(r["out"] - t["out"]).max() == 0.0
+
+
+def test_topk_recalls_planted_keys(oracle_mod):
+    """The planted keys sit well above the random keys' logits: a top-k of 16 holds all 8."""
+    wl = WORKLOADS["tiny"]
+    d = make_layer(wl)
+    r = oracle_mod.topk(dims_for(oracle_mod, wl), d["Q"], d["K"], d["V"], d["seq_len"], 16)
+    for h in range(wl.n_kv_heads):
+        assert np.isin(d["planted"][0, h], r["sel"][0, h]).all()
