@@ -116,6 +116,149 @@ def _cpu_model():
     return "unknown"
 
 
+def main_topk(args):
+    """The TopK (Oracle) comparison step on the same workload: per layer, hhr_topk_decode_step (exact fp64
+    logits over every key, top-k by logit, gather attention).  Roofline of its dominant kernel, the logit
+    stream over K; CPU baseline: the oracle's TopK step on layer 0."""
+    import numpy as np
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    import oracle
+    from synth import WORKLOADS, make_layer_torch
+
+    wl = WORKLOADS[args.workload]
+    if args.layers:
+        wl = wl.with_(layers=args.layers)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"topk mode, workload {wl.name}: {wl.layers} layers, B={wl.batch}, ctx={wl.ctx}")
+    dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
+                         wl.dtype == "bf16")
+    layers = []
+    for l in range(wl.layers):
+        d = make_layer_torch(wl, l, dev)
+        d["out"] = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+        d["sel"] = torch.empty((wl.batch, wl.n_kv_heads, wl.top_k), dtype=torch.int32, device=dev)
+        layers.append(d)
+    ws = hsa.alloc_topk_workspace(dims, wl.top_k, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for d in layers:
+            hsa.topk_decode_step(dims, d["Q"], d["K"], d["V"], d["seq_len"], wl.top_k, d["out"], ws, sel_idx=d["sel"])
+
+    step()
+    torch.cuda.synchronize()
+    ref_out = torch.stack([d["out"].clone() for d in layers])
+    ref_sel = torch.stack([d["sel"].clone() for d in layers])
+    graph = None
+    if not args.no_graph:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step()
+        torch.cuda.current_stream().wait_stream(stream)
+        for rep in range(3):
+            for d in layers:
+                d["out"].fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(torch.stack([d["out"] for d in layers]), ref_out), f"graph replay {rep} differs"
+            assert torch.equal(torch.stack([d["sel"] for d in layers]), ref_sel), f"graph replay {rep} differs"
+        log("graph captured; 3 replays equal the eager step")
+    run = graph.replay if graph is not None else step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    us_layer = ms_per_step * 1e3 / wl.layers
+    seq = layers[0]["seq_len_host"]
+    e = 2 if wl.dtype == "bf16" else 4
+    keys = int(sum(int(L) for L in seq)) * wl.n_kv_heads
+    k_eff = int(sum(min(wl.top_k, int(L)) for L in seq)) * wl.n_kv_heads
+    log(f"{args.steps} steps: {ms_per_step:.3f} ms/step, {us_layer:.2f} us/layer")
+
+    # Dominant kernel: the logit stream (all of K once, one fp64 logit written per key), launched back to
+    # back from a captured graph cycling the layers.
+    n_b = args.bound_launches
+    bstream = torch.cuda.Stream()
+    bstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(bstream):
+        for d in layers:
+            hsa.stage_topk_logits(dims, d["K"], d["seq_len"], wl.top_k, ws, stream=bstream)
+        bgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bgraph, stream=bstream):
+            for i in range(n_b):
+                d = layers[i % len(layers)]
+                hsa.stage_topk_logits(dims, d["K"], d["seq_len"], wl.top_k, ws, stream=bstream)
+        bgraph.replay()
+        bstream.synchronize()
+        e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_start.record(bstream)
+        bgraph.replay()
+        e_stop.record(bstream)
+    torch.cuda.synchronize()
+    logit_us = e_start.elapsed_time(e_stop) / n_b * 1e3
+    logit_bytes = keys * (wl.head_dim * e + 8)
+    achieved = logit_bytes / (logit_us * 1e-6) / 1e9
+    log(f"logit kernel: {logit_us:.2f} us/launch, {achieved:.0f} GB/s")
+    step_bytes = logit_bytes + keys * 8 + k_eff * (2 * wl.head_dim * e + 4) + wl.batch * wl.n_q_heads * wl.head_dim * (e + 4)
+
+    line = {
+        "metric": METRIC + " [TopK (Oracle) comparison step]",
+        "value": keys * wl.layers / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (seeded; lognormal channel scales, 2 outlier key channels, planted keys)",
+        "config": {
+            "workload": (f"{wl.name}: TopK (Oracle) decode step, {wl.layers} layers, batch {wl.batch}, "
+                         f"{wl.n_q_heads}q/{wl.n_kv_heads}kv heads, head_dim {wl.head_dim}, context {wl.ctx}, "
+                         f"top-k {wl.top_k} by exact fp64 logit (group max), bf16 K/V"),
+            "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
+        },
+        "us_per_layer": us_layer,
+        "hbm_algorithmic_bytes_per_layer": step_bytes,
+        "hbm_GBps": step_bytes / (us_layer * 1e-6) / 1e9,
+        "roofline": {
+            "kernel": "topk_logit_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "algorithmic_bytes_per_launch": logit_bytes, "keys_per_launch": keys, "us_per_launch": logit_us,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        d0 = layers[0]
+        host = {k: d0[k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ("Q", "K", "V")}
+        od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
+                         True)
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            r = oracle.topk(od, host["Q"], host["K"], host["V"], d0["seq_len_host"], wl.top_k)
+            times.append(time.perf_counter() - t0)
+        t = sorted(times)[1]
+        err = float(np.abs(ref_out[0].cpu().numpy().astype(np.float64) - r["out"]).max())
+        sel_ok = bool(np.array_equal(ref_sel[0].cpu().numpy(), r["sel"]))
+        line["cpu_baseline"] = dict(
+            value=keys / t, unit="keys/s", cores=min(oracle.max_threads(), wl.batch * wl.n_kv_heads), kind="oracle",
+            us_per_layer=t * 1e6, cpu=_cpu_model(),
+            sample=(f"layer 0 of {wl.layers}: oracle TopK step (all {wl.n_kv_heads} KV heads, {int(seq[0])} keys), "
+                    f"median of 3 ({t:.3f} s each)"),
+            layer0_parity={"selected_keys_equal": sel_ok, "attention_max_abs_diff": err})
+        log(f"cpu baseline {keys / t:.3g} keys/s; layer-0 parity sel={sel_ok} err={err:.2e}")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,11 +273,17 @@ def main():
     ap.add_argument("--bound-launches", type=int, default=96, help="page-bound launches timed for the roofline")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run N plain 1 GiB-in/1 GiB-out negations (for rocprofv3 --pmc calibration)")
+    ap.add_argument("--mode", choices=("hhr", "topk"), default="hhr",
+                    help="hhr: the HHR decode step (default); topk: the TopK (Oracle) comparison step "
+                         "(keys by exact logit over all of K, then the same attention)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N > 1 is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "topk":
+        main_topk(args)
+        return
 
     import numpy as np
     import torch

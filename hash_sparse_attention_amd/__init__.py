@@ -42,6 +42,10 @@ class WorkspaceLayout(ctypes.Structure):
         "counters", "total")] + [("n_splits", ctypes.c_int32)]
 
 
+class TopkLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("score", "sel", "k_eff", "total")]
+
+
 _lib = None
 
 
@@ -63,6 +67,10 @@ def lib():
             "hhr_decode_step": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, i32, f32, p, p, p, sz, p]),
             "hhr_decode_step_append": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, p, p, i32, i32, f32, p, p,
                                                       p, sz, p]),
+            "hhr_topk_workspace_layout": (ctypes.c_int, [D, i32, ctypes.POINTER(TopkLayout)]),
+            "hhr_topk_workspace_bytes": (sz, [D, i32]),
+            "hhr_topk_decode_step": (ctypes.c_int, [D, p, p, p, p, i32, f32, p, p, p, sz, p]),
+            "hhr_stage_topk_logits": (ctypes.c_int, [D, p, p, i32, p, sz, p]),
             "hhr_stage_qprep": (ctypes.c_int, [D, p, p, p, i32, i32, p, sz, p]),
             "hhr_stage_page_bounds": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
             "hhr_stage_select_pages": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
@@ -80,7 +88,9 @@ def lib():
 
 
 EXPORTED = ("hhr_meta_bytes", "hhr_codes_bytes", "hhr_encode_cache", "hhr_decode_workspace_bytes",
-            "hhr_decode_workspace_layout", "hhr_decode_step", "hhr_decode_step_append", "hhr_stage_qprep", "hhr_stage_page_bounds",
+            "hhr_decode_workspace_layout", "hhr_decode_step", "hhr_decode_step_append", "hhr_topk_workspace_layout",
+            "hhr_topk_workspace_bytes", "hhr_topk_decode_step", "hhr_stage_topk_logits", "hhr_stage_qprep",
+            "hhr_stage_page_bounds",
             "hhr_stage_select_pages", "hhr_stage_select_keys", "hhr_stage_attend", "hhr_status_str",
             "hhr_last_error", "hhr_abi_version")
 
@@ -169,6 +179,47 @@ def decode_step_append(dims: Dims, Q, K, V, R, W, meta, codes, append_start, app
                                         _ptr(seq_len), _ptr(keep_pages), int(max_keep), int(top_k), float(scale),
                                         _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
                                         _stream(stream)))
+
+
+def topk_workspace_layout(dims: Dims, top_k: int) -> TopkLayout:
+    lay = TopkLayout()
+    _check(lib().hhr_topk_workspace_layout(ctypes.byref(dims), int(top_k), ctypes.byref(lay)))
+    return lay
+
+
+def alloc_topk_workspace(dims: Dims, top_k: int, device="cuda"):
+    import torch
+    return torch.empty(topk_workspace_layout(dims, top_k).total, dtype=torch.uint8, device=device)
+
+
+def topk_decode_step(dims: Dims, Q, K, V, seq_len, top_k: int, out, workspace, sel_idx=None, scale: float = 0.0,
+                     stream=None):
+    """TopK (Oracle) step: keys by exact logit (fp64), then the same gather attention."""
+    _check(lib().hhr_topk_decode_step(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(seq_len), int(top_k),
+                                      float(scale), _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+
+
+def stage_topk_logits(dims: Dims, K, seq_len, top_k: int, workspace, stream=None):
+    """The logit kernel of the TopK (Oracle) step alone (after one full step on the same workspace)."""
+    _check(lib().hhr_stage_topk_logits(ctypes.byref(dims), _ptr(K), _ptr(seq_len), int(top_k), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
+
+
+def topk_workspace_view(dims: Dims, top_k: int, workspace):
+    """(score fp64 [B][Hkv][max_ctx], sel int32 [B][Hkv][top_k], k_eff int32 [B][Hkv]) views of a TopK workspace."""
+    import torch
+    lay = topk_workspace_layout(dims, top_k)
+    B, Hkv, T = dims.batch, dims.n_kv_heads, dims.max_ctx
+
+    def region(off, dtype, shape, esize):
+        n = esize
+        for x in shape:
+            n *= x
+        return workspace[off:off + n].view(dtype).view(*shape)
+
+    return (region(lay.score, torch.float64, (B, Hkv, T), 8), region(lay.sel, torch.int32, (B, Hkv, top_k), 4),
+            region(lay.k_eff, torch.int32, (B, Hkv), 4))
 
 
 def stage_qprep(dims, Q, R, W, max_keep, top_k, workspace, stream=None):

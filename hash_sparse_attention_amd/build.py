@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhhr.so")
-SOURCES = ["api.hip", "encode.hip", "project.hip", "decode.hip", "select.hip", "attend.hip"]
+SOURCES = ["api.hip", "encode.hip", "project.hip", "decode.hip", "select.hip", "attend.hip", "topk.hip"]
 ARCH = os.environ.get("HHR_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -166,6 +166,35 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     return l;
 }
 
+void topk_layout(const Shape& s, int top_k, WsLayout& l, TopkLayout& t) {
+    l = WsLayout{};
+    t = TopkLayout{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t BH = (size_t)s.B * s.Hkv, BQ = (size_t)s.B * s.Hq;
+    t.nblk = (s.T + kTopkBlk - 1) / kTopkBlk;
+    t.score = take(BH * (size_t)s.T * sizeof(double));
+    l.sel = take(BH * (size_t)top_k * sizeof(int32_t));
+    l.k_eff = take(BH * sizeof(int32_t));
+    t.q64 = take(BH * s.D * s.G * sizeof(double));
+    t.hist = take(BH * kTopkBins * sizeof(uint32_t));
+    t.info = take(BH * 16 * sizeof(uint32_t));
+    t.bkey = take(BH * kTopkCap * sizeof(uint64_t));
+    t.bidx = take(BH * kTopkCap * sizeof(int32_t));
+    t.ocnt = take(BH * (size_t)t.nblk * sizeof(int32_t));
+    t.off = take(BH * (size_t)t.nblk * sizeof(int32_t));
+    l.n_splits = (top_k + kAttnChunk - 1) / kAttnChunk;
+    l.part_splits = l.n_splits;
+    l.sel_splits = 1;
+    l.partial = take(BQ * (size_t)l.part_splits * (s.D + 2) * sizeof(float));
+    l.counters = take(2 * BH * sizeof(uint32_t));
+    l.total = off;
+}
+
 }  // namespace hhr
 
 using namespace hhr;
@@ -434,6 +463,82 @@ hhr_status hhr_stage_attend(const hhr_dims* dims, const void* Q, const void* K, 
     a.scale = resolve_scale(softmax_scale, a.s.D);
     if (sel_idx) a.sel = const_cast<int32_t*>(sel_idx);
     HHR_TRY(hip_check(launch_attend(a, true, static_cast<hipStream_t>(stream)), "attention launch"));
+    return ok();
+}
+
+hhr_status hhr_topk_workspace_layout(const hhr_dims* dims, int32_t top_k, hhr_topk_layout* layout) {
+    Shape s;
+    HHR_TRY(make_shape(dims, s));
+    if (top_k < 1 || top_k > (1 << 24)) return fail(HHR_E_RANGE, "top_k must be in 1..2^24 (got %d)", top_k);
+    if (!layout) return fail(HHR_E_NULL, "layout is NULL");
+    WsLayout l;
+    TopkLayout t;
+    topk_layout(s, top_k, l, t);
+    layout->score = t.score;
+    layout->sel = l.sel;
+    layout->k_eff = l.k_eff;
+    layout->total = l.total;
+    return ok();
+}
+
+size_t hhr_topk_workspace_bytes(const hhr_dims* dims, int32_t top_k) {
+    hhr_topk_layout l;
+    if (hhr_topk_workspace_layout(dims, top_k, &l) != HHR_OK) return 0;
+    return l.total;
+}
+
+namespace {
+// Common front of the TopK (Oracle) entry points.
+hhr_status topk_prepare(const hhr_dims* dims, int top_k, void* workspace, size_t workspace_bytes, TopkArgs& a) {
+    HHR_TRY(make_shape(dims, a.d.s));
+    if (top_k < 1 || top_k > (1 << 24)) return fail(HHR_E_RANGE, "top_k must be in 1..2^24 (got %d)", top_k);
+    HHR_TRY(check_ptr(workspace, "workspace", 256));
+    topk_layout(a.d.s, top_k, a.d.lay, a.tl);
+    if (workspace_bytes < a.d.lay.total)
+        return fail(HHR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, a.d.lay.total);
+    a.d.ws = static_cast<char*>(workspace);
+    a.d.top_k = top_k;
+    a.d.max_keep = 1;
+    a.d.sel = reinterpret_cast<int32_t*>(a.d.ws + a.d.lay.sel);
+    return HHR_OK;
+}
+}  // namespace
+
+hhr_status hhr_stage_topk_logits(const hhr_dims* dims, const void* K, const int32_t* seq_len, int32_t top_k,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    TopkArgs a{};
+    HHR_TRY(topk_prepare(dims, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(K, "K"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    a.d.K = K;
+    a.d.seq_len = seq_len;
+    HHR_TRY(hip_check(launch_topk_logits(a, static_cast<hipStream_t>(stream)), "logit launch"));
+    return ok();
+}
+
+hhr_status hhr_topk_decode_step(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                                const int32_t* seq_len, int32_t top_k, float softmax_scale, float* out,
+                                int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+    TopkArgs a{};
+    HHR_TRY(topk_prepare(dims, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(Q, "Q"));
+    HHR_TRY(check_ptr(K, "K"));
+    HHR_TRY(check_ptr(V, "V"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    HHR_TRY(check_ptr(out, "out"));
+    if (sel_idx) HHR_TRY(check_ptr(sel_idx, "sel_idx", 4));
+    a.d.Q = Q;
+    a.d.K = K;
+    a.d.V = V;
+    a.d.seq_len = seq_len;
+    a.d.out = out;
+    a.d.scale = resolve_scale(softmax_scale, a.d.s.D);
+    if (sel_idx) a.d.sel = sel_idx;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_TRY(hip_check(launch_topk_prep(a, st), "top-k prep launch"));
+    HHR_TRY(hip_check(launch_topk_logits(a, st), "logit launch"));
+    HHR_TRY(hip_check(launch_topk_select(a, st), "top-k select launch"));
+    HHR_TRY(hip_check(launch_attend(a.d, false, st), "attention launch"));
     return ok();
 }
 

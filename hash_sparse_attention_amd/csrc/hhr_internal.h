@@ -67,6 +67,22 @@ struct DecodeArgs {
     WsLayout lay;
 };
 
+// TopK (Oracle) path: 12-bit histogram digits of the exact logits, keys per
+// collect / write block, the largest boundary bucket ranked in registers,
+// and the most collect blocks one (b, h) can have (max_ctx <= 2^26).
+constexpr int kTopkBins = 4096;
+constexpr int kTopkBlk = 4096;
+constexpr int kTopkCap = 16384;
+constexpr int kTopkMaxBlk = (1 << 26) / kTopkBlk;
+
+// Workspace regions of the TopK (Oracle) step beyond those it shares with
+// the decode step's layout (sel, k_eff, partial, counters: counters holds
+// B*Hkv attention tickets, then B*Hkv bucket fill counts).
+struct TopkLayout {
+    size_t score, q64, hist, info, bkey, bidx, ocnt, off;
+    int nblk;  // collect / write blocks per (b, h)
+};
+
 // Projection of a few vectors (appended keys and/or the queries) by [R_h; W_h].
 struct ProjectArgs {
     bool keys, queries;
@@ -96,6 +112,15 @@ hipError_t launch_attend(const DecodeArgs& a, bool zero_counters, hipStream_t st
 hipError_t launch_compact_attend(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 
+struct TopkArgs {
+    DecodeArgs d;  // Q, K, V, seq_len, top_k, scale, out, sel, ws and the shared layout
+    TopkLayout tl;
+};
+void topk_layout(const Shape& s, int top_k, WsLayout& lay, TopkLayout& tl);
+hipError_t launch_topk_prep(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_topk_logits(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t stream);  // collect, threshold, ordered write
+
 // ---------------------------------------------------------------- device helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
@@ -115,6 +140,14 @@ __device__ __forceinline__ uint32_t bf16_down(float x) {
 }
 // (max, min) of one dimension as the two bf16 of a 32-bit word, max first.
 __device__ __forceinline__ uint32_t bf16_pair_out(float mx, float mn) { return bf16_up(mx) | (bf16_down(mn) << 16); }
+
+// 12-bit digit of a logit for the TopK (Oracle) histogram: the top bits of
+// the order-preserving 32-bit key of its fp32 rounding (a monotone map, so a
+// higher digit means a larger logit).
+__device__ __forceinline__ uint32_t topk_bin(double z) {
+    const uint32_t u = __float_as_uint((float)z);
+    return ((u >> 31) ? ~u : (u | 0x80000000u)) >> 20;
+}
 
 __device__ __forceinline__ int clamp_len(int L, int T) { return L < 0 ? 0 : (L > T ? T : L); }
 

@@ -847,7 +847,363 @@ hipError_t select_pages_nw(const DecodeArgs& a, int S, hipStream_t st) {
     return select_launch(select_kernel<NW, true, KEYS>, a, S, st);
 }
 
+// ============================================================== TopK (Oracle) key select
+// The keys of one (b, h) with the largest exact logit z (fp64, from the
+// logit kernel), equal z to the lower key, listed ascending.  The logit
+// kernel leaves a histogram of topk_bin(z), a monotone 12-bit digit of z, so:
+//  - collect (many blocks per (b, h)): finds the boundary digit d1 whose bin
+//    holds the k_eff-th largest z, counts each block's keys above it and
+//    appends the bin's keys (64-bit order key, index) to a bucket;
+//  - threshold (one block per (b, h)): ranks the bucket exactly -- a radix
+//    select on the order keys, then, among keys tied at the boundary value,
+//    on the index -- and turns each block's count into its output offset;
+//  - write (many blocks): every block compacts its selected keys in order.
+// A bucket over kTopkCap keys (heavy ties) falls back to the block select
+// above on all the scores.
+
+// Boundary digit of the `need` largest: found[0] = d1, found[1] = keys in
+// higher bins, found[2] = keys in bin d1.  `need` >= 1 and <= the total.
+template <int NT>
+__device__ __forceinline__ void topk_boundary(const uint32_t* __restrict__ gh, int need, int* scan, int* found) {
+    constexpr int BPT = kTopkBins / NT;
+    const int tid = threadIdx.x;
+    int c[BPT], sum = 0;
+#pragma unroll
+    for (int m = 0; m < BPT; ++m) {
+        c[m] = (int)gh[kTopkBins - 1 - BPT * tid - m];
+        sum += c[m];
+    }
+    int tot;
+    int above = block_excl_scan<NT>(sum, scan, tot);
+#pragma unroll
+    for (int m = 0; m < BPT; ++m) {
+        if (above < need && above + c[m] >= need) {
+            found[0] = kTopkBins - 1 - BPT * tid - m;
+            found[1] = above;
+            found[2] = c[m];
+        }
+        above += c[m];
+    }
+    __syncthreads();
+}
+
+// MSB-first radix select (descending) over the block's N-per-thread values
+// v (valid where ok; `count` valid in all, 1 <= need): on return the values
+// with (v & mask) > prefix rank above the boundary bucket {(v & mask) ==
+// prefix}, `need` of which are taken, and all_in says that is all of it.
+// Bits every valid value shares are skipped first.
+template <int N>
+__device__ __forceinline__ void radix_desc(const uint64_t (&v)[N], const bool (&ok)[N], int count, int& need,
+                                           uint64_t& prefix, uint64_t& mask, bool& all_in, SelShared& sh) {
+    const int tid = threadIdx.x;
+    if (need >= count) {  // block-uniform
+        prefix = 0;
+        mask = 0;
+        all_in = true;
+        return;
+    }
+    uint64_t o = 0, a = ~0ull;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        if (ok[k]) {
+            o |= v[k];
+            a &= v[k];
+        }
+    const uint32_t oh = wave_or((uint32_t)(o >> 32)), ol = wave_or((uint32_t)o);
+    const uint32_t ah = wave_and((uint32_t)(a >> 32)), al = wave_and((uint32_t)a);
+    if ((tid & 63) == 0) {
+        sh.red[0][tid >> 6] = oh;
+        sh.red[1][tid >> 6] = ol;
+        sh.red[2][tid >> 6] = ah;
+        sh.red[3][tid >> 6] = al;
+    }
+    __syncthreads();
+    o = 0;
+    a = ~0ull;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+        o |= ((uint64_t)sh.red[0][w] << 32) | sh.red[1][w];
+        a &= ((uint64_t)sh.red[2][w] << 32) | sh.red[3][w];
+    }
+    __syncthreads();
+    const uint64_t diff = o ^ a;
+    all_in = false;
+    if (diff == 0) {  // every valid value is equal
+        prefix = a;
+        mask = ~0ull;
+        return;
+    }
+    const int top = 63 - __clzll(diff);
+    mask = top == 63 ? 0ull : ~0ull << (top + 1);
+    prefix = a & mask;
+    int shift = top + 1;
+    while (!all_in && shift > 0) {
+        const int width = shift < kBits ? shift : kBits;
+        shift -= width;
+        const int nb = 1 << width;
+        for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if (ok[k] && (v[k] & mask) == prefix) atomicAdd(&sh.hist[(v[k] >> shift) & (nb - 1)], 1);
+        __syncthreads();
+        constexpr int DPT = kBins / kSelThreads;
+        int cnt[DPT], sum = 0;
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            const int d = nb - 1 - DPT * tid - j;
+            cnt[j] = d >= 0 ? sh.hist[d] : 0;
+            sum += cnt[j];
+        }
+        int tot;
+        int above = block_excl_scan<kSelThreads>(sum, sh.scan, tot);
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            if (above < need && above + cnt[j] >= need) {
+                sh.found[0] = nb - 1 - DPT * tid - j;
+                sh.found[1] = above;
+                sh.found[2] = cnt[j];
+            }
+            above += cnt[j];
+        }
+        __syncthreads();
+        need -= sh.found[1];
+        prefix |= (uint64_t)sh.found[0] << shift;
+        mask |= (uint64_t)(nb - 1) << shift;
+        all_in = sh.found[2] == need;
+        __syncthreads();
+    }
+}
+
+// Selection rule of a boundary-bin key with order key v and index t.
+__device__ __forceinline__ bool topk_in_bucket(uint64_t v, int t, uint64_t p1, uint64_t m1, uint64_t p2,
+                                               uint64_t m2) {
+    const uint64_t w = (uint64_t)(0xffffffffu - (uint32_t)t);
+    return (v & m1) > p1 || ((v & m1) == p1 && (w & m2) >= p2);
+}
+
+constexpr int kTopkRun = kTopkBlk / 256;  // keys per thread of a collect / write block
+
+__global__ __launch_bounds__(256) void topk_collect_kernel(const double* __restrict__ score,
+                                                           const uint32_t* __restrict__ hist,
+                                                           const int32_t* __restrict__ seq_len,
+                                                           uint32_t* __restrict__ bfill, uint64_t* __restrict__ bkey,
+                                                           int32_t* __restrict__ bidx, int32_t* __restrict__ ocnt,
+                                                           int Hkv, int T, int top_k, int nblk_max) {
+    __shared__ int scan[32];
+    __shared__ int found[3];
+    __shared__ uint32_t bbase;
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int L = clamp_len(seq_len[b], T);
+    const int base = j * kTopkBlk;
+    if (base >= L) return;  // block-uniform
+    const int keff = top_k < L ? top_k : L;
+    const double* sc = score + bh * T;
+    double s[kTopkRun];
+#pragma unroll
+    for (int k = 0; k < kTopkRun; ++k) {
+        const int i = base + k * 256 + tid;
+        s[k] = sc[i < L ? i : L - 1];
+    }
+    topk_boundary<256>(hist + bh * kTopkBins, keff, scan, found);
+    const uint32_t d1 = (uint32_t)found[0];
+    const int e1 = found[2];
+    int n_out = 0, n_b = 0;
+    bool isb[kTopkRun];
+#pragma unroll
+    for (int k = 0; k < kTopkRun; ++k) {
+        const bool valid = base + k * 256 + tid < L;
+        const uint32_t bin = topk_bin(s[k]);
+        n_out += valid && bin > d1;
+        isb[k] = valid && bin == d1;
+        n_b += isb[k];
+    }
+    int tot;
+    block_excl_scan<256>(n_out, scan, tot);
+    if (tid == 0) ocnt[bh * nblk_max + j] = tot;
+    if (e1 > kTopkCap) return;  // the threshold kernel falls back to the full select
+    int totb;
+    int pos = block_excl_scan<256>(n_b, scan, totb);
+    if (tid == 0 && totb > 0) bbase = atomicAdd(&bfill[bh], (uint32_t)totb);
+    __syncthreads();
+    if (n_b == 0) return;
+    pos += (int)bbase;
+#pragma unroll
+    for (int k = 0; k < kTopkRun; ++k)
+        if (isb[k]) {
+            if (pos < kTopkCap) {
+                bkey[bh * kTopkCap + pos] = order_key(s[k]);
+                bidx[bh * kTopkCap + pos] = base + k * 256 + tid;
+            }
+            ++pos;
+        }
+}
+
+// info per (b, h), 16 words: [0] 0 = rule below, 1 = list already written;
+// [1] d1; [2..3] p1; [4..5] m1; [6..7] p2; [8..9] m2 (low word first).
+constexpr int kTopkBucketRun = kTopkCap / kSelThreads;
+
+__global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
+    const double* __restrict__ score, const uint32_t* __restrict__ hist, const uint64_t* __restrict__ bkey,
+    const int32_t* __restrict__ bidx, const int32_t* __restrict__ ocnt, int32_t* __restrict__ off,
+    uint32_t* __restrict__ info, int32_t* __restrict__ sel, int32_t* __restrict__ k_eff,
+    const int32_t* __restrict__ seq_len, int Hkv, int T, int top_k, int nblk_max) {
+    __shared__ SelShared sh;
+    __shared__ int cntb[kTopkMaxBlk];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int L = clamp_len(seq_len[b], T);
+    const int keff = top_k < L ? top_k : L;
+    int32_t* so = sel + bh * top_k;
+    uint32_t* inf = info + bh * 16;
+    for (int x = keff + tid; x < top_k; x += kSelThreads) so[x] = -1;
+    if (tid == 0) k_eff[bh] = keff;
+    if (keff == 0) {  // block-uniform
+        if (tid == 0) inf[0] = 1u;
+        return;
+    }
+    topk_boundary<kSelThreads>(hist + bh * kTopkBins, keff, sh.scan, sh.found);
+    const uint32_t d1 = (uint32_t)sh.found[0];
+    const int c_above = sh.found[1], e1 = sh.found[2];
+    __syncthreads();
+    if (e1 > kTopkCap) {  // block-uniform: heavy ties; select on every score
+        uint64_t pre[kRun];
+        select_pages_block(score + bh * T, L, keff, top_k, so, true, sh, false, pre, false);
+        if (tid == 0) inf[0] = 1u;
+        return;
+    }
+    uint64_t v[kTopkBucketRun];
+    int32_t ix[kTopkBucketRun];
+    bool ok[kTopkBucketRun];
+#pragma unroll
+    for (int k = 0; k < kTopkBucketRun; ++k) {
+        const int slot = k * kSelThreads + tid;
+        ok[k] = slot < e1;
+        v[k] = ok[k] ? bkey[bh * kTopkCap + slot] : 0ull;
+        ix[k] = ok[k] ? bidx[bh * kTopkCap + slot] : 0;
+    }
+    int need = keff - c_above;
+    uint64_t p1, m1, p2 = 0, m2 = 0;
+    bool all1;
+    radix_desc<kTopkBucketRun>(v, ok, e1, need, p1, m1, all1, sh);
+    if (!all1) {  // `need` of the keys whose order key is exactly p1: the lowest indices
+        uint64_t w[kTopkBucketRun];
+        bool okt[kTopkBucketRun];
+        int nt = 0;
+#pragma unroll
+        for (int k = 0; k < kTopkBucketRun; ++k) {
+            okt[k] = ok[k] && v[k] == p1;
+            w[k] = (uint64_t)(0xffffffffu - (uint32_t)ix[k]);
+            nt += okt[k];
+        }
+        int ntie;
+        block_excl_scan<kSelThreads>(nt, sh.scan, ntie);
+        bool all2;
+        radix_desc<kTopkBucketRun>(w, okt, ntie, need, p2, m2, all2, sh);
+    }
+    if (tid == 0) {
+        inf[0] = 0u;
+        inf[1] = d1;
+        inf[2] = (uint32_t)p1;
+        inf[3] = (uint32_t)(p1 >> 32);
+        inf[4] = (uint32_t)m1;
+        inf[5] = (uint32_t)(m1 >> 32);
+        inf[6] = (uint32_t)p2;
+        inf[7] = (uint32_t)(p2 >> 32);
+        inf[8] = (uint32_t)m2;
+        inf[9] = (uint32_t)(m2 >> 32);
+    }
+    // Each collect block's output offset: its keys above d1 plus its taken
+    // bucket keys, summed over the blocks before it.
+    const int nblk = (L + kTopkBlk - 1) / kTopkBlk;
+    for (int x = tid; x < nblk; x += kSelThreads) cntb[x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTopkBucketRun; ++k)
+        if (ok[k] && (uint32_t)ix[k] < (uint32_t)L && topk_in_bucket(v[k], ix[k], p1, m1, p2, m2))
+            atomicAdd(&cntb[ix[k] / kTopkBlk], 1);
+    __syncthreads();
+    int run = 0;
+    for (int x0 = 0; x0 < nblk; x0 += kSelThreads) {
+        const int x = x0 + tid;
+        const int c = x < nblk ? ocnt[bh * nblk_max + x] + cntb[x] : 0;
+        int tot;
+        const int pre = block_excl_scan<kSelThreads>(c, sh.scan, tot);
+        if (x < nblk) off[bh * nblk_max + x] = run + pre;
+        run += tot;
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_write_kernel(const double* __restrict__ score,
+                                                         const uint32_t* __restrict__ info,
+                                                         const int32_t* __restrict__ off,
+                                                         const int32_t* __restrict__ seq_len,
+                                                         int32_t* __restrict__ sel, int Hkv, int T, int top_k,
+                                                         int nblk_max) {
+    __shared__ int scan[32];
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int L = clamp_len(seq_len[b], T);
+    const int base = j * kTopkBlk;
+    if (base >= L) return;  // block-uniform
+    const uint32_t* inf = info + bh * 16;
+    if (inf[0] != 0u) return;
+    const uint32_t d1 = inf[1];
+    const uint64_t p1 = ((uint64_t)inf[3] << 32) | inf[2], m1 = ((uint64_t)inf[5] << 32) | inf[4];
+    const uint64_t p2 = ((uint64_t)inf[7] << 32) | inf[6], m2 = ((uint64_t)inf[9] << 32) | inf[8];
+    const int t0 = base + tid * kTopkRun;  // this thread's contiguous keys
+    const double* sc = score + bh * T;
+    double s[kTopkRun];
+#pragma unroll
+    for (int m = 0; m < kTopkRun; ++m) s[m] = t0 + m < L ? sc[t0 + m] : 0.0;
+    bool in[kTopkRun];
+    int n = 0;
+#pragma unroll
+    for (int m = 0; m < kTopkRun; ++m) {
+        const uint32_t bin = topk_bin(s[m]);
+        in[m] = t0 + m < L &&
+                (bin > d1 || (bin == d1 && topk_in_bucket(order_key(s[m]), t0 + m, p1, m1, p2, m2)));
+        n += in[m];
+    }
+    int tot;
+    int pos = off[bh * nblk_max + j] + block_excl_scan<256>(n, scan, tot);
+    int32_t* so = sel + bh * top_k;
+#pragma unroll
+    for (int m = 0; m < kTopkRun; ++m)
+        if (in[m]) {
+            if (pos < top_k) so[pos] = t0 + m;
+            ++pos;
+        }
+}
+
 }  // namespace
+
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
+    const Shape& s = a.d.s;
+    const TopkLayout& t = a.tl;
+    char* ws = a.d.ws;
+    const dim3 grid((unsigned)t.nblk, s.Hkv, s.B);
+    uint32_t* bfill = reinterpret_cast<uint32_t*>(ws + a.d.lay.counters) + (size_t)s.B * s.Hkv;
+    hipLaunchKernelGGL(topk_collect_kernel, grid, dim3(256), 0, st, reinterpret_cast<const double*>(ws + t.score),
+                       reinterpret_cast<const uint32_t*>(ws + t.hist), a.d.seq_len, bfill,
+                       reinterpret_cast<uint64_t*>(ws + t.bkey), reinterpret_cast<int32_t*>(ws + t.bidx),
+                       reinterpret_cast<int32_t*>(ws + t.ocnt), s.Hkv, s.T, a.d.top_k, t.nblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(s.Hkv, s.B), dim3(kSelThreads), 0, st,
+                       reinterpret_cast<const double*>(ws + t.score), reinterpret_cast<const uint32_t*>(ws + t.hist),
+                       reinterpret_cast<const uint64_t*>(ws + t.bkey), reinterpret_cast<const int32_t*>(ws + t.bidx),
+                       reinterpret_cast<const int32_t*>(ws + t.ocnt), reinterpret_cast<int32_t*>(ws + t.off),
+                       reinterpret_cast<uint32_t*>(ws + t.info), a.d.sel,
+                       reinterpret_cast<int32_t*>(ws + a.d.lay.k_eff), a.d.seq_len, s.Hkv, s.T, a.d.top_k, t.nblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_write_kernel, grid, dim3(256), 0, st, reinterpret_cast<const double*>(ws + t.score),
+                       reinterpret_cast<const uint32_t*>(ws + t.info), reinterpret_cast<const int32_t*>(ws + t.off),
+                       a.d.seq_len, a.d.sel, s.Hkv, s.T, a.d.top_k, t.nblk);
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
     return a.s.NW == 1 ? select_pages_nw<1, true>(a, a.lay.sel_splits, st)

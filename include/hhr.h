@@ -96,7 +96,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 2
+#define HHR_ABI_VERSION 3
 
 typedef enum {
     HHR_OK = 0,
@@ -231,6 +231,55 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
                                   const int32_t* seq_len, const int32_t* keep_pages, int32_t max_keep_pages,
                                   int32_t top_k, float softmax_scale, float* out, int32_t* sel_idx, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * hhr_topk_decode_step -- the TopK (Oracle) comparison step: keys chosen by
+ * their exact attention logit, with no page bounds and no codes (the
+ * "TopK (Oracle)" rows of Table 1 and Table 2 and "TopK-1.5%" in Appendix
+ * Table 4 on the thelatestinai.com page for arXiv 2610.01230; rit.work HHR
+ * blog post, section "Когда HHR меняет планы запуска модели").
+ *
+ * For every sequence b (length L = seq_len[b]) and KV head h, with the G
+ * query heads of h sharing one selection as in hhr_decode_step:
+ *   1. z(t) = max over the G heads of sum_d q_i,d * k_t,d for t < L, in fp64
+ *      with d ascending from +0 (each product of two fp32 values is exact in
+ *      fp64, so z is reproducible bit for bit); -0 is read as +0;
+ *   2. the k_eff = min(top_k, L) keys with the largest z, equal z going to
+ *      the lower t, written ascending to sel_idx (or the workspace), -1
+ *      padded;
+ *   3. out_i = sum_t softmax_t(scale * q_i . k_t) v_t over them, as step 7
+ *      of hhr_decode_step.
+ * Only batch, n_q_heads, n_kv_heads, head_dim, max_ctx and kv_dtype matter;
+ * the other dims fields must still hold valid values.  The step reads all of
+ * K (it is the exact reference, not a fast path).  A boundary bin of more
+ * than 16384 keys tied within fp32 rounding (e.g. a constant query) takes a
+ * slower single-block select; the result is the same.
+ *   Q, K, V         device, read (layouts as for hhr_decode_step)
+ *   seq_len         device int32 [B], read
+ *   top_k >= 1      host
+ *   out             device fp32 [B][Hq][D], written
+ *   sel_idx         device int32 [B][Hkv][top_k], written, or NULL
+ *   workspace       device scratch >= hhr_topk_workspace_bytes; afterwards
+ *                   it holds z (fp64 [B][Hkv][max_ctx] at `score`; entries
+ *                   t >= L unspecified), the selection (at `sel` when sel_idx
+ *                   is NULL) and k_eff (int32 [B][Hkv] at `k_eff`)
+ * Errors as for hhr_decode_step; nothing is enqueued on failure.
+ */
+typedef struct {
+    size_t score, sel, k_eff, total;
+} hhr_topk_layout;
+
+hhr_status hhr_topk_workspace_layout(const hhr_dims* dims, int32_t top_k, hhr_topk_layout* layout);
+size_t hhr_topk_workspace_bytes(const hhr_dims* dims, int32_t top_k);  /* 0 on invalid arguments */
+hhr_status hhr_topk_decode_step(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                                const int32_t* seq_len, int32_t top_k, float softmax_scale, float* out,
+                                int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream);
+/* Stage entry point for timing and tests: step 1's logit kernel alone, on a
+ * workspace a full hhr_topk_decode_step with the same dims, Q and top_k has
+ * used (it reads the widened queries that step left).  Rewrites z at `score`
+ * and adds to a histogram that only the full step uses and clears. */
+hhr_status hhr_stage_topk_logits(const hhr_dims* dims, const void* K, const int32_t* seq_len, int32_t top_k,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Stage entry points: each runs one stage of hhr_decode_step on the same

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(hsa):
 
 def test_version_and_status_strings(hsa):
     L = hsa.lib()
-    assert L.hhr_abi_version() == 2
+    assert L.hhr_abi_version() == 3
     for code, name in hsa.STATUS.items():
         assert L.hhr_status_str(code).decode() == name
 
@@ -167,3 +167,30 @@ def test_workspace_layout_regions(hsa):
     assert spans[-1][1] <= lay.total
     assert 1 <= lay.n_splits <= 300
     assert hsa.workspace_bytes(d, 17, 300) == lay.total
+
+
+def test_topk_entry_validates_before_launch(hsa):
+    """hhr_topk_decode_step rejects bad arguments on the host; the layout covers every region."""
+    L = hsa.lib()
+    d = dims()
+    lay = hsa.TopkLayout()
+    assert L.hhr_topk_workspace_layout(ctypes.byref(d), 4096, ctypes.byref(lay)) == 0
+    B, Hkv, T = 1, 8, 131072
+    assert lay.score % 256 == 0 and lay.sel % 256 == 0 and lay.k_eff % 256 == 0
+    assert lay.total >= lay.score + B * Hkv * T * 8 and lay.total >= lay.sel + B * Hkv * 4096 * 4
+    assert L.hhr_topk_workspace_bytes(ctypes.byref(d), 4096) == lay.total
+    assert L.hhr_topk_workspace_bytes(ctypes.byref(d), 0) == 0
+
+    def call(top_k=4096, ws_bytes=None, q=FAKE, ws=FAKE, sel=None):
+        n = lay.total if ws_bytes is None else ws_bytes
+        return L.hhr_topk_decode_step(ctypes.byref(d), q, FAKE, FAKE, FAKE, top_k, 0.0, FAKE, sel, ws, n, None)
+
+    assert call(top_k=0) == 6
+    assert call(q=None) == 1
+    assert call(ws_bytes=lay.total - 1) == 5
+    assert "workspace" in L.hhr_last_error().decode()
+    assert call(ws=FAKE_ODD) == 4
+    assert call(sel=ctypes.c_void_p(0x10002)) == 4
+    bad = dims(head_dim=96)
+    assert L.hhr_topk_decode_step(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 16, 0.0, FAKE, None, FAKE, 1 << 40,
+                                  None) == 7
