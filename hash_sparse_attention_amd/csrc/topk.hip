@@ -7,8 +7,8 @@
 // модели": the evaluation includes selection by exact scores).
 //
 // This file holds the front of that path:
-//  - prep: the group's queries widened to fp64, [D][G] per (b, h) so the
-//    logit kernel reads them with uniform (scalar) loads, and the per-step
+//  - prep: the group's queries widened to fp64, [D][G] per (b, h), which the
+//    logit kernel reads with uniform (scalar) loads, and the per-step
 //    counters cleared;
 //  - logits: z(t) = max over the G query heads of sum_d q_i,d k_t,d in fp64,
 //    d ascending from +0 (each product of two fp32 values is exact in fp64,
@@ -79,8 +79,11 @@ __device__ __forceinline__ void logit_chunk(const u32x4 (&v)[8], u32x4* st, int 
 #pragma unroll
         for (int i = 0; i < G; ++i) acc[i] = 0.0;
     }
-#pragma unroll
+    // Slots one per iteration (not unrolled): each iteration holds one slot's
+    // queries (EPS * G doubles, uniform loads) instead of the whole chunk's.
+#pragma unroll 1
     for (int s = 0; s < 8; ++s) {
+        const double* __restrict__ qd = qc + s * EPS * G;
         const u32x4 w = st[lane * 8 + (s ^ (lane & 7))];
 #pragma unroll
         for (int e = 0; e < EPS; ++e) {
@@ -88,9 +91,8 @@ __device__ __forceinline__ void logit_chunk(const u32x4 (&v)[8], u32x4* st, int 
             if constexpr (BF16) kf = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
             else kf = __uint_as_float(w[e]);
             const double kd = (double)kf;
-            const int d = s * EPS + e;  // dimension within the chunk
 #pragma unroll
-            for (int i = 0; i < G; ++i) acc[i] = __builtin_fma(qc[d * G + i], kd, acc[i]);
+            for (int i = 0; i < G; ++i) acc[i] = __builtin_fma(qd[e * G + i], kd, acc[i]);
         }
     }
 }
@@ -130,9 +132,9 @@ __global__ __launch_bounds__(256) void topk_logit_kernel(const void* __restrict_
     if (tb >= L) return;  // block-uniform
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int x = tid; x < kTopkBins; x += 256) lh[x] = 0u;
+    const double* __restrict__ qh = q64 + bh * D * G;
 
     const char* kbase = static_cast<const char*>(K) + bh * (int64_t)T * (D * ES);
-    const double* __restrict__ qh = q64 + bh * D * G;
     double* __restrict__ sc = score + bh * T;
     u32x4* st = stage[wave];
     const int lrow = lane >> 3, lslot = lane & 7;
