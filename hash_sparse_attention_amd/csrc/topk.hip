@@ -39,13 +39,13 @@ __global__ __launch_bounds__(256) void topk_prep_kernel(const void* __restrict__
 }
 
 // One block: 4 waves, each wave 64 keys per tile (one lane per key, which
-// fixes the order of its sums), kLogitTiles tiles per wave.  A tile's rows
+// fixes the order of its sums), `tiles` tiles per wave, chosen on the host so
+// the whole grid is resident at once (no tail wave of blocks).  A tile's rows
 // arrive with 1 KiB-contiguous loads (8 lanes per 128-byte row chunk) and go
 // through a wave-private LDS tile (16-byte slots XOR-swizzled by row) so each
 // lane can read its own row.  The next chunk's loads are in flight while the
 // current one is summed.
-constexpr int kLogitTiles = 4;
-constexpr int kLogitKeys = 4 * 64 * kLogitTiles;
+constexpr int kLogitResident = 4 * 256;  // blocks the GPU holds at once (LDS: 4 per CU)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a native vector: kept in registers
 
@@ -64,17 +64,20 @@ __device__ __forceinline__ void tile_load(u32x4 (&v)[8], const char* __restrict_
 
 // Stage one tile chunk through the wave's LDS tile and add it to the lane's
 // G running sums (d ascending within the chunk; chunks arrive in order).
-template <int D, bool BF16, int G>
-__device__ __forceinline__ void logit_chunk(const u32x4 (&v)[8], u32x4* st, int lane, int lrow, int lslot,
-                                            const double* __restrict__ qc, bool first, double (&acc)[G]) {
-    constexpr int EPS = BF16 ? 8 : 4;  // elements per 16-byte slot
-    __syncthreads();                   // the previous chunk's LDS reads are done
+__device__ __forceinline__ void stage_chunk(const u32x4 (&v)[8], u32x4* st, int lrow, int lslot) {
+    __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int r = 8 * j + lrow;
         st[r * 8 + (lslot ^ (r & 7))] = v[j];
     }
     __syncthreads();
+}
+
+template <int D, bool BF16, int G>
+__device__ __forceinline__ void logit_chunk(const u32x4* st, int lane, const double* __restrict__ qc, bool first,
+                                            double (&acc)[G]) {
+    constexpr int EPS = BF16 ? 8 : 4;  // elements per 16-byte slot
     if (first) {
 #pragma unroll
         for (int i = 0; i < G; ++i) acc[i] = 0.0;
@@ -97,18 +100,23 @@ __device__ __forceinline__ void logit_chunk(const u32x4 (&v)[8], u32x4* st, int 
     }
 }
 
-// z of the lane's key: the group max, -0 read as +0; stored and counted in
-// the block histogram when the key is inside the sequence.
+// z of the lane's key: the group max, -0 read as +0; counted in the block
+// histogram (two 16-bit bins per word) when inside the sequence.  The store
+// is unconditional, so the compiler can count outstanding memory operations
+// exactly and keep the next chunk's loads in flight: a key in [L, T) leaves
+// an unspecified entry, and a lane past the capacity (its row clamped to
+// T - 1) writes z(T - 1) itself to entry T - 1.
 template <int G>
-__device__ __forceinline__ void logit_finish(const double (&acc)[G], int t, int L, double* __restrict__ sc,
+__device__ __forceinline__ void logit_finish(const double (&acc)[G], int t, int L, int T, double* __restrict__ sc,
                                              uint32_t* lh) {
     double z = acc[0];
 #pragma unroll
     for (int i = 1; i < G; ++i) z = acc[i] > z ? acc[i] : z;
     if (z == 0.0) z = 0.0;
+    sc[t < T ? t : T - 1] = z;
     if (t < L) {
-        sc[t] = z;
-        atomicAdd(&lh[topk_bin(z)], 1u);
+        const uint32_t bin = topk_bin(z);
+        atomicAdd(&lh[bin >> 1], 1u << (16 * (bin & 1)));
     }
 }
 
@@ -116,22 +124,22 @@ template <int D, bool BF16, int G>
 __global__ __launch_bounds__(256) void topk_logit_kernel(const void* __restrict__ K, const double* __restrict__ q64,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, uint32_t* __restrict__ hist,
-                                                         int Hkv, int T) {
+                                                         int Hkv, int T, int tiles) {
     constexpr int ES = BF16 ? 2 : 4;        // bytes per element
     constexpr int NC = D * ES / 128;        // 128-byte chunks per row
     constexpr int CD = 128 / ES;            // dimensions per chunk
-    constexpr int NS = kLogitTiles * NC;    // (tile, chunk) steps per wave
-    static_assert(NC >= 1 && NS % 2 == 0, "row chunks");
+    static_assert(NC >= 1, "row chunks");
+    const int NS = tiles * NC;              // (tile, chunk) steps per wave; even (the host rounds tiles)
     __shared__ u32x4 stage[4][64 * 8];
-    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t lh[kTopkBins / 2];  // a block counts at most 65535 keys per bin
 
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
-    const int tb = blockIdx.x * kLogitKeys;
+    const int tb = blockIdx.x * 256 * tiles;
     if (tb >= L) return;  // block-uniform
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int x = tid; x < kTopkBins; x += 256) lh[x] = 0u;
+    for (int x = tid; x < kTopkBins / 2; x += 256) lh[x] = 0u;
     const double* __restrict__ qh = q64 + bh * D * G;
 
     const char* kbase = static_cast<const char*>(K) + bh * (int64_t)T * (D * ES);
@@ -142,36 +150,56 @@ __global__ __launch_bounds__(256) void topk_logit_kernel(const void* __restrict_
 
     // Steps (tile, chunk) in order, two at a time with fixed buffers: the
     // loads of the next step are in flight while this one is summed.
+    // Steps (tile, chunk) in order, two per iteration with fixed register
+    // buffers A and B: B's loads go out at the top of the iteration and A is
+    // refilled (two steps ahead) as soon as it is in LDS, so loads stay in
+    // flight while a chunk is summed.  Every load is unconditional (the last
+    // ones re-load a chunk already read) and A's loads are always older than
+    // B's, so the compiler can wait for exactly the buffer it needs.
     u32x4 A[8], B[8];
     double acc[G];
-    tile_load<D * ES>(A, kbase, tw, T, 0, lrow, lslot);
+    auto t_of = [&](int step) { return tw + (step / NC) * 256; };
+    tile_load<D * ES>(A, kbase, t_of(0), T, 0, lrow, lslot);
 #pragma unroll 1
     for (int step = 0; step < NS; step += 2) {
-        const int ta = step / NC, ca = step % NC, tb2 = (step + 1) / NC, cb = (step + 1) % NC;
-        tile_load<D * ES>(B, kbase, tw + tb2 * 256, T, cb, lrow, lslot);
-        logit_chunk<D, BF16, G>(A, st, lane, lrow, lslot, qh + ca * CD * G, ca == 0, acc);
-        if (ca == NC - 1) logit_finish<G>(acc, tw + ta * 256 + lane, L, sc, lh);
-        if (step + 2 < NS)
-            tile_load<D * ES>(A, kbase, tw + ((step + 2) / NC) * 256, T, (step + 2) % NC, lrow, lslot);
-        logit_chunk<D, BF16, G>(B, st, lane, lrow, lslot, qh + cb * CD * G, cb == 0, acc);
-        if (cb == NC - 1) logit_finish<G>(acc, tw + tb2 * 256 + lane, L, sc, lh);
+        const int ca = step % NC, cb = (step + 1) % NC;
+        if (tb + (step / NC) * 256 >= L) break;  // block-uniform: the rest of the block is past the sequence
+        const int na = step + 2 < NS ? step + 2 : step;
+        tile_load<D * ES>(B, kbase, t_of(step + 1), T, cb, lrow, lslot);
+        stage_chunk(A, st, lrow, lslot);
+        tile_load<D * ES>(A, kbase, t_of(na), T, na % NC, lrow, lslot);
+        logit_chunk<D, BF16, G>(st, lane, qh + ca * CD * G, ca == 0, acc);
+        if constexpr (NC == 1) logit_finish<G>(acc, t_of(step) + lane, L, T, sc, lh);
+        else if constexpr (NC > 2) {
+            if (ca == NC - 1) logit_finish<G>(acc, t_of(step) + lane, L, T, sc, lh);
+        }
+        stage_chunk(B, st, lrow, lslot);
+        logit_chunk<D, BF16, G>(st, lane, qh + cb * CD * G, cb == 0, acc);
+        if constexpr (NC <= 2) logit_finish<G>(acc, t_of(step + 1) + lane, L, T, sc, lh);
+        else if (cb == NC - 1) logit_finish<G>(acc, t_of(step + 1) + lane, L, T, sc, lh);
     }
     __syncthreads();
     uint32_t* gh = hist + bh * kTopkBins;
-    for (int x = tid; x < kTopkBins; x += 256) {
+    for (int x = tid; x < kTopkBins / 2; x += 256) {
         const uint32_t n = lh[x];
-        if (n) atomicAdd(&gh[x], n);
+        if (n & 0xffffu) atomicAdd(&gh[2 * x], n & 0xffffu);
+        if (n >> 16) atomicAdd(&gh[2 * x + 1], n >> 16);
     }
 }
 
 template <int D, bool BF16, int G>
 hipError_t logits_g(const TopkArgs& a, hipStream_t st) {
     const Shape& s = a.d.s;
-    const dim3 grid((unsigned)((s.T + kLogitKeys - 1) / kLogitKeys), s.Hkv, s.B);
+    // Tiles per wave: enough that the grid fits the resident block slots, even.
+    const int64_t heads = (int64_t)s.B * s.Hkv;
+    const int64_t per_head = kLogitResident / heads > 0 ? kLogitResident / heads : 1;
+    int tiles = (int)((s.T + 256 * per_head - 1) / (256 * per_head));
+    tiles = tiles < 2 ? 2 : tiles + (tiles & 1);
+    const dim3 grid((unsigned)((s.T + 256 * tiles - 1) / (256 * tiles)), s.Hkv, s.B);
     hipLaunchKernelGGL((topk_logit_kernel<D, BF16, G>), grid, dim3(256), 0, st, a.d.K,
                        reinterpret_cast<const double*>(a.d.ws + a.tl.q64), a.d.seq_len,
                        reinterpret_cast<double*>(a.d.ws + a.tl.score),
-                       reinterpret_cast<uint32_t*>(a.d.ws + a.tl.hist), s.Hkv, s.T);
+                       reinterpret_cast<uint32_t*>(a.d.ws + a.tl.hist), s.Hkv, s.T, tiles);
     return hipGetLastError();
 }
 
