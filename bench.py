@@ -29,6 +29,8 @@ METRIC = "decode-step latency (µs/layer) + keys scanned/s + HBM GB/s (% peak) a
 HBM_PEAK_GBPS = 8000.0
 PMC_FILE = os.path.join(ROOT, "profiles", "page_bound_llama8b_128k_pmc.json")
 BOUND_SRC = os.path.join(ROOT, "hash_sparse_attention_amd", "csrc", "decode.hip")
+TOPK_PMC_FILE = os.path.join(ROOT, "profiles", "topk_logit_llama8b_128k_pmc.json")
+TOPK_SRC = os.path.join(ROOT, "hash_sparse_attention_amd", "csrc", "topk.hip")
 
 
 def log(msg):
@@ -59,8 +61,19 @@ def page_bound_bytes_per_launch(wl, seq):
     return pages * (2 * wl.head_dim * (2 if wl.meta_bf16 else 4) + 8), pages
 
 
-def source_digest():
-    return hashlib.sha256(open(BOUND_SRC, "rb").read()).hexdigest()[:16]
+def source_digest(path=BOUND_SRC):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def pmc_traffic(pmc_file, src):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if the kernel source is unchanged."""
+    try:
+        rec = json.load(open(pmc_file))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_digest(src):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def traffic_from_profile(wl):
@@ -211,6 +224,13 @@ def main_topk(args):
     logit_bytes = keys * (wl.head_dim * e + 8)
     achieved = logit_bytes / (logit_us * 1e-6) / 1e9
     log(f"logit kernel: {logit_us:.2f} us/launch, {achieved:.0f} GB/s")
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.calibrate_copy):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     step_bytes = logit_bytes + keys * 8 + k_eff * (2 * wl.head_dim * e + 4) + wl.batch * wl.n_q_heads * wl.head_dim * (e + 4)
 
     line = {
@@ -231,7 +251,7 @@ def main_topk(args):
         "hbm_GBps": step_bytes / (us_layer * 1e-6) / 1e9,
         "roofline": {
             "kernel": "topk_logit_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": pmc_traffic(TOPK_PMC_FILE, TOPK_SRC),
             "algorithmic_bytes_per_launch": logit_bytes, "keys_per_launch": keys, "us_per_launch": logit_us,
         },
         "cpu_baseline": None,
