@@ -22,10 +22,19 @@ query heads i of the group and the keys t < L:
 Reported per setting as the mean over (sequence, KV head), the output error
 as the max.
 
+The Hamming-versus-logit view (thelatestinai.com page, Figure 2 caption:
+Hamming distances of a random orthogonal projection followed by sign, set
+against the query-key logits): for every query head i and key t < L of one
+KV head, H_i(t) = popcount(code(q_i) XOR code(k_t)) from the library's own
+codes against z_i(t) = q_i . k_t, tabulated by distance bin, with the rank
+correlation between -H and z and the share of the exact top 1% keys that
+the Hamming order also puts in its top 1%.
+
 The exact references are plain fp64 numpy on the host: this is a
 measurement tool, not a path of the library.  `python -m
 hash_sparse_attention_amd.fidelity --workload llama8b_32k` runs a sweep of
-keep percentages and code lengths on the GPU and prints one table.
+keep percentages and code lengths on the GPU and prints one table;
+`--scatter` prints the Hamming-versus-logit table instead.
 """
 from __future__ import annotations
 
@@ -81,8 +90,81 @@ def metrics(wl, d: dict, sel: np.ndarray, out: np.ndarray, pages: np.ndarray, n_
                 planted_recall=mean(plant), units=len(rec))
 
 
-def run_library(wl, d: dict, dev, scale: float = 0.0):
-    """Encode and one decode step of the layer through the library; returns (out, sel, pages, n_pages)."""
+def popcount64(x: np.ndarray) -> np.ndarray:
+    """Bits set in each uint64 (SWAR, on the host)."""
+    x = np.asarray(x, np.uint64)
+    m1, m2, m4 = np.uint64(0x5555555555555555), np.uint64(0x3333333333333333), np.uint64(0x0F0F0F0F0F0F0F0F)
+    x = x - ((x >> np.uint64(1)) & m1)
+    x = (x & m2) + ((x >> np.uint64(2)) & m2)
+    x = (x + (x >> np.uint64(4))) & m4
+    return ((x * np.uint64(0x0101010101010101)) >> np.uint64(56)).astype(np.int64)
+
+
+def _ranks(a: np.ndarray) -> np.ndarray:
+    """Ranks 1..n with ties given their mean rank."""
+    order = np.argsort(a, kind="stable")
+    r = np.empty(len(a), np.float64)
+    r[order] = np.arange(1, len(a) + 1)
+    uniq, inv, cnt = np.unique(a, return_inverse=True, return_counts=True)
+    sums = np.bincount(inv, weights=r)
+    return (sums / cnt)[inv]
+
+
+def hamming_logit(wl, d: dict, codes: np.ndarray, code_q: np.ndarray, b: int = 0, h: int = 0,
+                  n_bins: int = 16) -> dict:
+    """Hamming distance against logit on KV head h of sequence b, over every query head of its group.
+
+    codes [B][Hkv][T][W] and code_q [B][Hq][W] (uint64) are the library's codes of the keys and queries.
+    Returns rows (lo, hi, keys, mean z, p10 z, p90 z, max z) per distance bin [lo, hi], the Spearman
+    correlation of -H with z (per query head, averaged), and the top-1% overlap (averaged).
+    """
+    bf16 = wl.dtype == "bf16"
+    G, nb = wl.group, wl.hash_bits
+    L = int(d["seq_len"][b])
+    Q, K = _f32(d["Q"], bf16), _f32(d["K"], bf16)
+    ck = np.asarray(codes[b, h, :L]).view(np.uint64)
+    Hs, Zs, rho, top = [], [], [], []
+    for i in range(h * G, (h + 1) * G):
+        cq = np.asarray(code_q[b, i]).view(np.uint64)
+        H = popcount64(ck ^ cq[None, :]).sum(axis=1)
+        z = K[b, h, :L].astype(np.float64) @ Q[b, i].astype(np.float64)
+        Hs.append(H)
+        Zs.append(z)
+        rz, rh = _ranks(z), _ranks(-H.astype(np.float64))
+        rho.append(float(np.corrcoef(rz, rh)[0, 1]))
+        k = max(1, L // 100)
+        exact = np.lexsort((np.arange(L), -z))[:k]
+        by_h = np.lexsort((np.arange(L), H))[:k]
+        top.append(float(np.isin(exact, by_h).mean()))
+    H, z = np.concatenate(Hs), np.concatenate(Zs)
+    edges = np.linspace(0, nb, n_bins + 1)
+    rows = []
+    for j in range(n_bins):
+        lo, hi = int(np.ceil(edges[j])), int(np.ceil(edges[j + 1])) - (1 if j + 1 < n_bins else 0)
+        m = (H >= lo) & (H <= hi)
+        if m.any():
+            zz = z[m]
+            rows.append((lo, hi, int(m.sum()), float(zz.mean()), float(np.percentile(zz, 10)),
+                         float(np.percentile(zz, 90)), float(zz.max())))
+        else:
+            rows.append((lo, hi, 0, float("nan"), float("nan"), float("nan"), float("nan")))
+    return dict(rows=rows, spearman=float(np.mean(rho)), top1_overlap=float(np.mean(top)), keys=int(len(z)))
+
+
+def hamming_table(res: dict) -> str:
+    lines = ["| H from | H to | keys | mean logit | p10 | p90 | max |", "|---|---|---|---|---|---|---|"]
+    for lo, hi, n, mu, p10, p90, mx in res["rows"]:
+        if n:
+            lines.append(f"| {lo} | {hi} | {n} | {mu:.2f} | {p10:.2f} | {p90:.2f} | {mx:.2f} |")
+    lines.append("")
+    lines.append(f"Spearman(-H, logit) = {res['spearman']:.3f}; exact top-1% keys also in the Hamming top 1%: "
+                 f"{res['top1_overlap']:.3f} ({res['keys']} (query head, key) pairs)")
+    return "\n".join(lines)
+
+
+def run_library(wl, d: dict, dev, scale: float = 0.0, want_codes: bool = False):
+    """Encode and one decode step of the layer through the library; returns (out, sel, pages, n_pages), plus
+    (codes, code_q) as host arrays when want_codes."""
     import torch
 
     import hash_sparse_attention_amd as hsa
@@ -106,7 +188,12 @@ def run_library(wl, d: dict, dev, scale: float = 0.0):
                     out, ws, sel_idx=sel, scale=scale)
     torch.cuda.synchronize()
     v = hsa.workspace_view(dims, wl.max_keep, wl.top_k, ws)
-    return out.cpu().numpy(), sel.cpu().numpy(), v.pages.cpu().numpy(), v.n_pages.cpu().numpy()
+    res = (out.cpu().numpy(), sel.cpu().numpy(), v.pages.cpu().numpy(), v.n_pages.cpu().numpy())
+    if want_codes:
+        nw = wl.hash_bits // 64
+        cd = codes.view(wl.batch, wl.n_kv_heads, wl.ctx, nw).cpu().numpy().view(np.uint64)
+        res = res + (cd, v.code_q.cpu().numpy().view(np.uint64))
+    return res
 
 
 def sweep(workload: str, keeps, bits, layer: int = 0, dev=None, meta_bf16: bool = False) -> list:
@@ -148,7 +235,28 @@ def main(argv=None):
     ap.add_argument("--layer", type=int, default=0)
     ap.add_argument("--meta", choices=("fp32", "bf16"), default="fp32")
     ap.add_argument("--json", default="", help="also write the rows to this file")
+    ap.add_argument("--scatter", action="store_true", help="Hamming-versus-logit table instead of the sweep")
+    ap.add_argument("--orthogonal-w", action="store_true",
+                    help="with --scatter: codes from W_h = R_h (a random orthogonal projection, b = D)")
+    ap.add_argument("--head", type=int, default=0)
     a = ap.parse_args(argv)
+    if a.scatter:
+        import torch
+
+        from synth import WORKLOADS, make_layer
+        nb = [int(x) for x in a.bits.split(",")][0]
+        wl = WORKLOADS[a.workload].with_(hash_bits=nb, meta_bf16=a.meta == "bf16")
+        d = make_layer(wl, layer=a.layer)
+        if a.orthogonal_w:
+            if nb != wl.head_dim:
+                raise SystemExit("--orthogonal-w needs --bits equal to the head size")
+            d["W"] = d["R"].copy()
+        *_, cd, cq = run_library(wl, d, torch.device("cuda:0"), want_codes=True)
+        res = hamming_logit(wl, d, cd, cq, h=a.head)
+        print(hamming_table(res))
+        if a.json:
+            json.dump(res, open(a.json, "w"), indent=1)
+        return
     rows = sweep(a.workload, [int(x) for x in a.keep.split(",")], [int(x) for x in a.bits.split(",")], a.layer,
                  meta_bf16=a.meta == "bf16")
     print(table(rows))

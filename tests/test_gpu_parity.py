@@ -451,3 +451,20 @@ def test_fidelity_harness_matches_oracle_selection(dev):
     for k in ("key_recall", "page_coverage", "attention_mass", "planted_recall"):
         assert g[k] == m[k], k
     assert abs(g["out_max_err"] - m["out_max_err"]) <= 2e-3
+
+
+def test_hamming_logit_table_matches_oracle_codes(dev):
+    """The Hamming-versus-logit table from the library's key and query codes equals the one from the
+    oracle's codes (the codes are bit-exact), with W_h = R_h as in the pages' random-orthogonal setup."""
+    from hash_sparse_attention_amd.fidelity import hamming_logit, run_library
+    wl = WORKLOADS["tiny"].with_(hash_bits=64)
+    banner("hamming vs logit table")
+    d = make_layer(wl)
+    d["W"] = d["R"].copy()
+    *_, cd, cq = run_library(wl, d, dev, want_codes=True)
+    o = run_oracle(wl, d)
+    for h in range(wl.n_kv_heads):
+        g = hamming_logit(wl, d, cd, cq, h=h)
+        m = hamming_logit(wl, d, o["codes"], o["code_q"], h=h)
+        assert np.array_equal(np.array(g["rows"], float), np.array(m["rows"], float), equal_nan=True)  # empty bins: NaN
+        assert g["spearman"] == m["spearman"] and g["top1_overlap"] == m["top1_overlap"]

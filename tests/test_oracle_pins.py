@@ -724,3 +724,24 @@ def test_topk_recalls_planted_keys(oracle_mod):
     r = oracle_mod.topk(dims_for(oracle_mod, wl), d["Q"], d["K"], d["V"], d["seq_len"], 16)
     for h in range(wl.n_kv_heads):
         assert np.isin(d["planted"][0, h], r["sel"][0, h]).all()
+
+
+def test_hamming_logit_table_on_known_codes():
+    """Four keys whose Hamming distances to the query are 0, 10, 20, 64 and whose logits fall 3, 2, 1, 0:
+    each lands in its distance bin, the rank correlation of -H with the logit is 1 (and -1 reversed), and
+    the exact top key is the Hamming top key."""
+    from hash_sparse_attention_amd.fidelity import hamming_logit, popcount64
+    wl = Workload("ham_pin", 97, 1, 1, 1, 2, 4, 1, 64, 100, 4, "fp32")
+    K = np.zeros((1, 1, 4, 2), np.float32)
+    K[0, 0, :, 0] = [3, 2, 1, 0]
+    d = dict(Q=np.array([[[1.0, 0.0]]], np.float32), K=K, seq_len=np.array([4], np.int32))
+    cq = np.zeros((1, 1, 1), np.uint64)
+    ck = np.array([0, (1 << 10) - 1, (1 << 20) - 1, 2 ** 64 - 1], np.uint64).reshape(1, 1, 4, 1)
+    assert list(popcount64(ck.ravel())) == [0, 10, 20, 64]
+    r = hamming_logit(wl, d, ck, cq)
+    got = {(lo, hi): (n, mu) for lo, hi, n, mu, *_ in r["rows"] if n}
+    assert got == {(0, 3): (1, 3.0), (8, 11): (1, 2.0), (20, 23): (1, 1.0), (60, 64): (1, 0.0)}
+    assert r["spearman"] == pytest.approx(1.0) and r["top1_overlap"] == 1.0 and r["keys"] == 4
+    d["K"] = K[:, :, ::-1].copy()
+    r = hamming_logit(wl, d, ck, cq)
+    assert r["spearman"] == pytest.approx(-1.0) and r["top1_overlap"] == 0.0
