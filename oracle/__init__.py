@@ -53,7 +53,7 @@ def build(force: bool = True) -> str:
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_bf16",
-        "meta_bf16")]
+        "meta_bf16", "sink_tokens", "local_window")]
 
 
 def _load():
@@ -91,6 +91,8 @@ class Dims:
     max_ctx: int
     kv_bf16: bool
     meta_bf16: bool = False  # page max/min rounded outward to bf16 values
+    sink_tokens: int = 0     # decode: the first sink_tokens keys are always attended
+    local_window: int = 0    # decode: the last local_window keys are always attended
 
     @property
     def group(self) -> int:
@@ -106,7 +108,8 @@ class Dims:
 
     def c(self) -> _Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.page_size,
-                     self.hash_bits, self.max_ctx, int(self.kv_bf16), int(self.meta_bf16))
+                     self.hash_bits, self.max_ctx, int(self.kv_bf16), int(self.meta_bf16), int(self.sink_tokens),
+                     int(self.local_window))
 
 
 def _ptr(a):
@@ -166,7 +169,8 @@ def encode(dims: Dims, K, R, W, start, count, meta=None, codes=None):
 
 
 def decode(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max_keep, top_k, scale=0.0):
-    """One decode step; returns a dict of every intermediate and the fp64 output."""
+    """One decode step; returns a dict of every intermediate and the fp64 output (sel holds
+    top_k + sink_tokens + local_window entries per head)."""
     B, Hq, Hkv, D, P = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.page_size
     Q = _kv(Q, dims); K = _kv(K, dims); V = _kv(V, dims)
     R = _c(R, np.float32); W = _c(W, np.float32)
@@ -180,7 +184,7 @@ def decode(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max_keep
         pages=np.zeros((B, Hkv, max_keep), np.int32),
         n_pages=np.zeros((B, Hkv), np.int32),
         ham=np.zeros((B, Hkv, max_keep * P), np.uint16),
-        sel=np.zeros((B, Hkv, top_k), np.int32),
+        sel=np.zeros((B, Hkv, top_k + dims.sink_tokens + dims.local_window), np.int32),
         k_eff=np.zeros((B, Hkv), np.int32),
         out=np.zeros((B, Hq, D), np.float64),
     )

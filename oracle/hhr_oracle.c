@@ -48,6 +48,8 @@ typedef struct {
     int32_t max_ctx;    /* Tmax: row capacity of K, V, codes   */
     int32_t kv_bf16;    /* 1: Q, K, V hold bf16 bit patterns (uint16); 0: fp32 */
     int32_t meta_bf16;  /* 1: page max/min are stored rounded outward to bf16 values */
+    int32_t sink_tokens;  /* decode: the first sink_tokens keys are always attended    */
+    int32_t local_window; /* decode: the last local_window keys are always attended    */
 } oracle_dims;
 
 enum { ORACLE_OK = 0, ORACLE_BAD_DIMS = 1, ORACLE_NOMEM = 2 };
@@ -57,6 +59,7 @@ static int dims_ok(const oracle_dims* d) {
     if (d->n_q_heads % d->n_kv_heads) return 0;
     if (d->head_dim < 1 || d->page_size < 1 || d->max_ctx < 0) return 0;
     if (d->hash_bits < 64 || d->hash_bits % 64) return 0;
+    if (d->sink_tokens < 0 || d->local_window < 0) return 0;
     return 1;
 }
 
@@ -302,13 +305,22 @@ static void attend_selected(const float* q, int G, int D, const void* K, const v
  *     the selected t, fp64; scale = 1/sqrt(D) when scale <= 0.
  * An empty sequence (L = 0) yields out = 0, no pages, no keys.
  *
+ * Sink tokens and a local window (a variant; the HHR pages use none, the
+ * baselines they compare against do [FIG, Appendix Table 4: 4 sink tokens
+ * and a local window of 64 keys]): with sink_tokens = s and local_window =
+ * w, the forced keys F = {t < min(s, L)} and {max(min(s, L), L - w) <= t < L}
+ * are always attended; steps 4-6 run on the candidates outside F, and the
+ * selection lists the sinks, then the step-6 keys, then the window keys
+ * (ascending, since the step-6 keys lie between them).  k_eff = |F| + the
+ * step-6 count; the list holds top_k + s + w entries.
+ *
  * Outputs (any pointer may be NULL to skip it):
  *   qrot  [B][Hq][D] fp32        code_q [B][Hq][b/64]
  *   score [B][Hkv][NPmax] fp64   (+0.0 for p >= NP)
  *   pages [B][Hkv][max_keep] int32 ascending, -1 padded; n_pages [B][Hkv]
  *   ham   [B][Hkv][max_keep*P] uint16: H of candidate slot j*P + r = key
- *         pages[j]*P + r; 0xFFFF where that key is >= L or the slot is unused
- *   sel   [B][Hkv][top_k] int32 ascending, -1 padded; k_eff [B][Hkv]
+ *         pages[j]*P + r; 0xFFFF where that key is >= L, forced, or the slot is unused
+ *   sel   [B][Hkv][top_k + s + w] int32 ascending, -1 padded; k_eff [B][Hkv]
  *   out   [B][Hq][D] fp64
  */
 int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const void* V,
@@ -324,6 +336,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
     const int64_t T = dm->max_ctx, NPmax = n_pages_of(T, P);
     const int bf = dm->kv_bf16;
     const double scale = softmax_scale(scale_in, D);
+    const int64_t cap = (int64_t)top_k + dm->sink_tokens + dm->local_window;  /* sel row length */
     int status = ORACLE_OK;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -333,6 +346,9 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
             if (L < 0) L = 0;
             if (L > T) L = T;
             const int64_t NP = n_pages_of(L, P);
+            /* forced keys: [0, s_end) and [w_start, L) */
+            const int64_t s_end = dm->sink_tokens < L ? dm->sink_tokens : L;
+            const int64_t w_start = L - dm->local_window > s_end ? L - dm->local_window : s_end;
             const int64_t bh = (int64_t)b * Hkv + h;
             const float* Rh = R + (int64_t)h * D * D;
             const float* Wh = W + (int64_t)h * nb * D;
@@ -343,8 +359,8 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
             page_key* pk = malloc(sizeof(page_key) * (NP > 0 ? NP : 1));
             int32_t* plist = malloc(sizeof(int32_t) * max_keep);
             key_key* cand = malloc(sizeof(key_key) * (int64_t)max_keep * P);
-            int32_t* sel = malloc(sizeof(int32_t) * top_k);
-            double* sc = malloc(sizeof(double) * top_k);
+            int32_t* sel = malloc(sizeof(int32_t) * cap);
+            double* sc = malloc(sizeof(double) * cap);
             if (!q || !qr || !cq || !pk || !plist || !cand || !sel || !sc) {
                 free(q); free(qr); free(cq); free(pk); free(plist); free(cand); free(sel); free(sc);
 #pragma omp atomic write
@@ -395,7 +411,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
             for (int64_t j = 0; j < keep; ++j) {
                 for (int r = 0; r < P; ++r) {
                     const int64_t t = (int64_t)plist[j] * P + r;
-                    if (t >= L) continue;
+                    if (t >= L || t < s_end || t >= w_start) continue;
                     int32_t H = 0;
                     for (int i = 0; i < G; ++i)
                         for (int w = 0; w < NW; ++w)
@@ -407,13 +423,16 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
                 }
             }
 
-            /* 6. key select */
-            const int64_t keff = nc < top_k ? nc : top_k;
+            /* 6. key select, then the forced keys around it */
+            const int64_t kh = nc < top_k ? nc : top_k;
             qsort(cand, nc, sizeof(key_key), cmp_key);
-            for (int64_t j = 0; j < keff; ++j) sel[j] = cand[j].t;
-            qsort(sel, keff, sizeof(int32_t), cmp_int);
+            for (int64_t j = 0; j < kh; ++j) sel[s_end + j] = cand[j].t;
+            qsort(sel + s_end, kh, sizeof(int32_t), cmp_int);
+            for (int64_t t = 0; t < s_end; ++t) sel[t] = (int32_t)t;
+            for (int64_t t = w_start; t < L; ++t) sel[s_end + kh + (t - w_start)] = (int32_t)t;
+            const int64_t keff = s_end + kh + (L - w_start);
             if (sel_out)
-                for (int64_t j = 0; j < top_k; ++j) sel_out[bh * top_k + j] = j < keff ? sel[j] : -1;
+                for (int64_t j = 0; j < cap; ++j) sel_out[bh * cap + j] = j < keff ? sel[j] : -1;
             if (keff_out) keff_out[bh] = (int32_t)keff;
 
             /* 7. attention over the selected keys */

@@ -44,6 +44,8 @@ class Workload:
     append_tokens: int = 0       # size of the encode-append chunk timed for this workload
     planted: int = 8
     meta_bf16: bool = False      # page metadata stored as outward-rounded bf16
+    sink_tokens: int = 0         # decode variant: first keys always attended
+    local_window: int = 0        # decode variant: last keys always attended
 
     @property
     def group(self) -> int:

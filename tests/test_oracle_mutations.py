@@ -39,6 +39,8 @@ MUTANTS = {
                                    "double s = 0.0;\n                    for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(V"),
     "topk_first_head_only": ("double z = 0.0;\n                for (int i = 0; i < G; ++i) {",
                              "double z = 0.0;\n                for (int i = 0; i < 1; ++i) {"),
+    "forced_keys_compete": ("if (t >= L || t < s_end || t >= w_start) continue;", "if (t >= L) continue;"),
+    "window_one_short": ("for (int64_t t = w_start; t < L; ++t) sel[", "for (int64_t t = w_start + 1; t < L; ++t) sel["),
     "value_from_key_rows": ("o[d] += wgt * (double)elem(V, row + d, bf);", "o[d] += wgt * (double)elem(K, row + d, bf);"),
 }
 

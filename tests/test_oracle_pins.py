@@ -35,7 +35,7 @@ def bits_of(codes):
 
 def dims_for(o, wl: Workload):
     return o.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits,
-                  wl.ctx, wl.dtype == "bf16", wl.meta_bf16)
+                  wl.ctx, wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window)
 
 
 def f32(x, wl):
@@ -745,3 +745,58 @@ def test_hamming_logit_table_on_known_codes():
     d["K"] = K[:, :, ::-1].copy()
     r = hamming_logit(wl, d, ck, cq)
     assert r["spearman"] == pytest.approx(-1.0) and r["top1_overlap"] == 0.0
+
+
+# ----------------------------------------------------------------------------- sink tokens and a local window
+
+def _popcount(x):
+    return bin(int(x)).count("1")
+
+
+@pytest.mark.parametrize("sinks,window,ragged", [(4, 64, None), (1, 0, (100, 4096)), (0, 17, (1, 4096)),
+                                                  (7, 300, (50, 400))])
+def test_forced_keys_plus_hamming_top_k_of_the_rest(oracle_mod, sinks, window, ragged):
+    """With sinks s and window w: the page list is the plain step's; the selection is [0, s), then the
+    top_k of the kept pages' other keys by (H, t) (brute-force popcount, numpy lexsort), then the last w keys."""
+    wl = WORKLOADS["tiny"].with_(batch=3 if ragged else 1, ragged=ragged, sink_tokens=sinks, local_window=window)
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    plain = run(oracle_mod, wl.with_(sink_tokens=0, local_window=0), d)[3]
+    assert (r["pages"] == plain["pages"]).all() and (r["n_pages"] == plain["n_pages"]).all()
+    G, P, cap = wl.group, wl.page_size, wl.top_k + sinks + window
+    assert r["sel"].shape[-1] == cap
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        s_end = min(sinks, L)
+        w_start = max(s_end, L - window)
+        for h in range(wl.n_kv_heads):
+            cand = [p * P + j for p in r["pages"][b, h, :r["n_pages"][b, h]] for j in range(P)]
+            cand = np.array([t for t in cand if t < L and s_end <= t < w_start], np.int64)
+            H = np.array([sum(_popcount(r["code_q"][b, i, w] ^ codes[b, h, t, w]) for i in range(h * G, (h + 1) * G)
+                               for w in range(wl.hash_bits // 64)) for t in cand], np.int64)
+            pick = np.sort(cand[np.lexsort((cand, H))[:wl.top_k]]) if len(cand) else np.zeros(0, np.int64)
+            want = np.concatenate([np.arange(s_end), pick, np.arange(w_start, L)])
+            assert r["k_eff"][b, h] == len(want)
+            assert (r["sel"][b, h, :len(want)] == want).all() and (r["sel"][b, h, len(want):] == -1).all()
+            ham = r["ham"][b, h]
+            for j, p in enumerate(r["pages"][b, h, :r["n_pages"][b, h]]):
+                for q in range(P):
+                    t = p * P + q
+                    if t < L and (t < s_end or t >= w_start):
+                        assert ham[j * P + q] == 0xFFFF
+
+
+def test_window_covering_the_sequence_is_full_attention(oracle_mod):
+    """A local window at least as long as the sequence forces every key: exact softmax attention (numpy
+    fp64) whatever keep and top_k are, with no key listed twice."""
+    wl = WORKLOADS["tiny"].with_(batch=2, ctx=1024, ragged=(10, 1024), sink_tokens=5, local_window=1024, top_k=3)
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl, d)
+    Qf, Kf, Vf = (np.asarray(d[k], np.float64) for k in ("Q", "K", "V"))
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        assert (r["k_eff"][b] == L).all() and (r["sel"][b, :, :L] == np.arange(L)).all()
+        for i in range(wl.n_q_heads):
+            ref = _softmax_attention(Qf[b, i], Kf[b, i // wl.group, :L], Vf[b, i // wl.group, :L],
+                                     1 / np.sqrt(wl.head_dim))
+            assert np.abs(r["out"][b, i] - ref).max() <= 1e-9 * max(1.0, np.abs(ref).max())
