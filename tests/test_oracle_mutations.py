@@ -32,7 +32,7 @@ MUTANTS = {
     "key_ties_high_first": ("return (x->t > y->t) - (x->t < y->t);", "return (x->t < y->t) - (x->t > y->t);"),
     "scale_without_sqrt": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),
     "meta_from_start_not_page_start": ("const int64_t lo = p * P,", "const int64_t lo = p * P < s ? s : p * P,"),
-    "candidates_past_length": ("if (t >= L || t < s_end", "if (t >= T || t < s_end"),
+    "candidates_past_length": ("? L - dm->local_window : s_end;", "? T - dm->local_window : s_end;"),
     "keep_not_clamped_to_one": ("if (keep < 1) keep = 1;", ""),
     "topk_group_min_not_max": ("if (i == 0 || s > z) z = s;", "if (i == 0 || s < z) z = s;"),
     "topk_logit_from_value_rows": ("double s = 0.0;\n                    for (int d = 0; d < D; ++d) s += (double)q[i * D + d] * (double)elem(K",
