@@ -96,7 +96,7 @@ def cpu_baseline(wl, host_layer, steps_note):
 
     import oracle
     od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                     wl.dtype == "bf16", wl.meta_bf16)
+                     wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window)
     t0 = time.perf_counter()
     meta, codes = oracle.encode(od, host_layer["K"], host_layer["R"], host_layer["W"], np.zeros(wl.batch, np.int32),
                                 host_layer["seq_len"])
@@ -293,6 +293,8 @@ def main():
     ap.add_argument("--bound-launches", type=int, default=96, help="page-bound launches timed for the roofline")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="also run N plain 1 GiB-in/1 GiB-out negations (for rocprofv3 --pmc calibration)")
+    ap.add_argument("--sinks", type=int, default=0, help="hhr mode: sink tokens always attended (a variant; 0 = off)")
+    ap.add_argument("--window", type=int, default=0, help="hhr mode: local window always attended (0 = off)")
     ap.add_argument("--mode", choices=("hhr", "topk"), default="hhr",
                     help="hhr: the HHR decode step (default); topk: the TopK (Oracle) comparison step "
                          "(keys by exact logit over all of K, then the same attention)")
@@ -314,13 +316,14 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.layers:
         wl = wl.with_(layers=args.layers)
-    wl = wl.with_(meta_bf16=args.meta == "bf16")
+    wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, ctx={wl.ctx}, device {torch.cuda.get_device_name(0)}")
 
     dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                         wl.dtype == "bf16", meta_bf16=wl.meta_bf16)
+                         wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
+                         local_window=wl.local_window)
     layers = []
     t0 = time.perf_counter()
     for l in range(wl.layers):
@@ -330,7 +333,7 @@ def main():
         hsa.encode_cache(dims, d["K"], d["R"], d["W"], zero, d["seq_len"], wl.ctx, meta, codes)
         d.update(meta=meta, codes=codes)
         d["out"] = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
-        d["sel"] = torch.empty((wl.batch, wl.n_kv_heads, wl.top_k), dtype=torch.int32, device=dev)
+        d["sel"] = torch.empty((wl.batch, wl.n_kv_heads, hsa.sel_cap(dims, wl.top_k)), dtype=torch.int32, device=dev)
         d["app_start"] = (d["seq_len"] - 1).contiguous()
         d["app_count"] = torch.ones(wl.batch, dtype=torch.int32, device=dev)
         layers.append(d)
@@ -445,7 +448,9 @@ def main():
                          f"{wl.n_q_heads}q/{wl.n_kv_heads}kv heads, head_dim {wl.head_dim}, context {wl.ctx}, "
                          f"page {wl.page_size}, {wl.hash_bits}-bit codes, keep {wl.keep_percent}% pages, "
                          f"top-k {wl.top_k}; page metadata {'bf16 (outward-rounded)' if wl.meta_bf16 else 'fp32'}; "
-                         f"one step = per layer a 1-token append + decode"),
+                         + (f"{wl.sink_tokens} sink tokens and a {wl.local_window}-key local window always "
+                            f"attended; " if wl.sink_tokens or wl.local_window else "") +
+                         "one step = per layer a 1-token append + decode"),
             "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
         },
         "us_per_layer": us_layer,

@@ -30,7 +30,7 @@ class HHRError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_dtype",
-        "meta_dtype")]
+        "meta_dtype", "sink_tokens", "local_window")]
 
     def __repr__(self):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -112,10 +112,18 @@ def _stream(stream):
 
 
 def make_dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx, bf16: bool,
-              meta_bf16: bool = False) -> Dims:
-    """meta_bf16: store page metadata as outward-rounded bf16 (half the bytes of the page-bound stream)."""
+              meta_bf16: bool = False, sink_tokens: int = 0, local_window: int = 0) -> Dims:
+    """meta_bf16: store page metadata as outward-rounded bf16 (half the bytes of the page-bound stream).
+    sink_tokens, local_window: keys always attended by the decode step (the first and the last ones); its
+    selection rows then hold top_k + sink_tokens + local_window entries (`sel_cap`)."""
     return Dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx,
-                HHR_BF16 if bf16 else HHR_F32, HHR_BF16 if meta_bf16 else HHR_F32)
+                HHR_BF16 if bf16 else HHR_F32, HHR_BF16 if meta_bf16 else HHR_F32, int(sink_tokens),
+                int(local_window))
+
+
+def sel_cap(dims: Dims, top_k: int) -> int:
+    """Entries per (sequence, KV head) row of the decode step's selection."""
+    return int(top_k) + dims.sink_tokens + dims.local_window
 
 
 def dims_from(K, Q, W, page_size: int) -> Dims:
@@ -284,7 +292,7 @@ def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> Workspac
         pages=region(lay.pages, torch.int32, (B, Hkv, max_keep)),
         n_pages=region(lay.n_pages, torch.int32, (B, Hkv)),
         ham=region(lay.ham, torch.int16, (B, Hkv, max_keep * P)),
-        sel=region(lay.sel, torch.int32, (B, Hkv, top_k)),
+        sel=region(lay.sel, torch.int32, (B, Hkv, sel_cap(dims, top_k))),
         k_eff=region(lay.k_eff, torch.int32, (B, Hkv)),
     )
 

@@ -56,6 +56,9 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
         return fail(HHR_E_DTYPE, "kv_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->kv_dtype);
     if (d->meta_dtype != HHR_F32 && d->meta_dtype != HHR_BF16)
         return fail(HHR_E_DTYPE, "meta_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->meta_dtype);
+    if (d->sink_tokens < 0 || d->sink_tokens > d->max_ctx || d->local_window < 0 || d->local_window > d->max_ctx)
+        return fail(HHR_E_RANGE, "sink_tokens (%d) and local_window (%d) must be in 0..max_ctx", d->sink_tokens,
+                    d->local_window);
     s.B = d->batch;
     s.Hq = d->n_q_heads;
     s.Hkv = d->n_kv_heads;
@@ -69,6 +72,8 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
     s.NPB = (s.NPmax + 63) / 64;
     s.bf16 = d->kv_dtype == HHR_BF16;
     s.meta16 = d->meta_dtype == HHR_BF16;
+    s.nsink = d->sink_tokens;
+    s.window = d->local_window;
     return HHR_OK;
 }
 
@@ -105,6 +110,7 @@ hhr_status prepare(const hhr_dims* dims, int max_keep, int top_k, void* workspac
     HHR_TRY(check_ptr(workspace, "workspace", 256));
     a.max_keep = max_keep;
     a.top_k = top_k;
+    a.sel_cap = top_k + a.s.nsink + a.s.window;
     a.lay = ws_layout(a.s, max_keep, top_k);
     if (ws_bytes < a.lay.total)
         return fail(HHR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, a.lay.total);
@@ -132,7 +138,9 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
         return o;
     };
     const size_t BH = (size_t)s.B * s.Hkv, BQ = (size_t)s.B * s.Hq;
-    l.n_splits = (top_k + kAttnChunk - 1) / kAttnChunk;
+    const bool forced = s.nsink + s.window > 0;  // sinks / window: the single-block key select
+    const int sel_cap = top_k + s.nsink + s.window;
+    l.n_splits = (sel_cap + kAttnChunk - 1) / kAttnChunk;
     l.q_rot = take(BQ * s.D * sizeof(float));
     l.code_q = take(BQ * s.NW * sizeof(uint64_t));
     l.q_split = take(BH * s.D * s.G * 2 * sizeof(double));
@@ -140,7 +148,7 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     l.pages = take(BH * (size_t)max_keep * sizeof(int32_t));
     l.n_pages = take(BH * sizeof(int32_t));
     l.ham = take(BH * (size_t)max_keep * s.P * sizeof(uint16_t));
-    l.sel = take(BH * (size_t)top_k * sizeof(int32_t));
+    l.sel = take(BH * (size_t)sel_cap * sizeof(int32_t));
     l.k_eff = take(BH * sizeof(int32_t));
     // Split key select: about 512 candidate slots per block, at most
     // kCompactSlots, and no more blocks than the GPU holds at once (each one
@@ -148,7 +156,7 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     const size_t slots = (size_t)max_keep * s.P;
     const size_t BHs = BH > 0 ? BH : 1;
     int S = 1;
-    if (slots <= (size_t)kSelChunk && max_keep <= kSelListLds) {
+    if (!forced && slots <= (size_t)kSelChunk && max_keep <= kSelListLds) {
         size_t want = (slots + 511) / 512, cap = 256 / BHs;
         want = want < cap ? want : cap;
         want = want > 64 ? 64 : want;
@@ -498,6 +506,7 @@ hhr_status topk_prepare(const hhr_dims* dims, int top_k, void* workspace, size_t
         return fail(HHR_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, a.d.lay.total);
     a.d.ws = static_cast<char*>(workspace);
     a.d.top_k = top_k;
+    a.d.sel_cap = top_k;  // no forced keys on this path
     a.d.max_keep = 1;
     a.d.sel = reinterpret_cast<int32_t*>(a.d.ws + a.d.lay.sel);
     return HHR_OK;

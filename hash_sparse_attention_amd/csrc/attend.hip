@@ -745,7 +745,7 @@ hipError_t attend_g(const DecodeArgs& a, hipStream_t st) {
     float* pml = po + (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     hipLaunchKernelGGL((attend_kernel<D, BF16, G>), grid, dim3(256), 0, st, a.Q, a.K, a.V, a.sel,
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.k_eff), po, pml,
-                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters), a.out, s.Hq, s.Hkv, s.T, a.top_k,
+                       reinterpret_cast<uint32_t*>(a.ws + a.lay.counters), a.out, s.Hq, s.Hkv, s.T, a.sel_cap,
                        a.lay.n_splits, a.lay.part_splits, a.scale);
     return hipGetLastError();
 }

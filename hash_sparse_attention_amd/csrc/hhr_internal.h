@@ -17,6 +17,7 @@ struct Shape {
     int64_t NPB;    // 64-page blocks of meta per (b, h)
     bool bf16;      // Q, K, V are bf16
     bool meta16;    // page metadata is bf16 (outward-rounded)
+    int nsink, window;  // keys always attended: the first nsink and the last window
 };
 
 // Attention keys handled by one block (one split) of the attend kernel.
@@ -56,6 +57,7 @@ hipError_t launch_encode(const Shape& s, const void* K, const float* R, const fl
 struct DecodeArgs {
     Shape s;
     int max_keep, top_k;
+    int sel_cap;  // entries per (b, h) row of sel: top_k plus the forced keys' room
     float scale;
     const void *Q, *K, *V;
     const float *R, *W, *meta;

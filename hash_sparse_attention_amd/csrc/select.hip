@@ -501,16 +501,23 @@ __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t
 // their distances, their cumulative histogram (cum) and add their histogram
 // into the head's (ghist).  The threshold, the ordered compaction and the
 // attention then run in the compact+attend kernel.
+//
+// Forced keys (nsink, window > 0, single-block path only): the keys
+// [0, s_end) and [w_start, L) take no part in the ranking (distance 0xFFFF)
+// and are listed around the ranked ones: so = sinks, ranked, window.
 template <int NW, bool LDSLIST>
 __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ ck, const uint64_t* __restrict__ cqg,
                                                   int G, const int32_t* __restrict__ pl, int np, int L,
                                                   int P, int max_keep, int top_k, uint16_t* __restrict__ hm,
                                                   int32_t* __restrict__ so, int32_t* __restrict__ keff_out,
                                                   SelShared& sh, int split, int S, uint32_t* __restrict__ cum,
-                                                  uint32_t* __restrict__ ghist) {
+                                                  uint32_t* __restrict__ ghist, int nsink = 0, int window = 0) {
     constexpr int NB = NW * 64;
     const int NBINS = G * NB + 1;
     const int tid = threadIdx.x;
+    const int s_end = nsink < L ? nsink : L;
+    const int w_start = L - window > s_end ? L - window : s_end;  // ranked keys: [s_end, w_start)
+    const int sel_cap = top_k + nsink + window;
     const int nslots = np * P;
     const int lp = 31 - __clz(P);  // P is a power of two
     uint64_t cq[kMaxGroup * NW];
@@ -534,7 +541,7 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
                 const int s = c * kChunk + k * kSelThreads + tid;
                 const int ss = s < nslots ? s : 0;
                 const int t = page_of(ss) * P + (ss & (P - 1));
-                Hreg[k] = (s < nslots && t >= 0 && t < L) ? t : -1;
+                Hreg[k] = (s < nslots && t >= s_end && t < w_start) ? t : -1;
             }
         }
 #pragma unroll
@@ -571,7 +578,7 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
                 const int s = lo + k * kSelThreads + tid;
                 const int ss = s < hi ? s : 0;
                 const int t = sh.plist[ss >> lp] * P + (ss & (P - 1));
-                Hreg[k] = (s < hi && t >= 0 && t < L) ? t : -1;
+                Hreg[k] = (s < hi && t >= s_end && t < w_start) ? t : -1;
             }
         }
 #pragma unroll
@@ -690,7 +697,7 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
             }
             if (in) {
                 const int s = c * kChunk + tid * run + k;
-                if (pos < top_k) so[pos] = pg[k] * P + (s & (P - 1));
+                if (pos < top_k) so[s_end + pos] = pg[k] * P + (s & (P - 1));
                 ++pos;
             }
         }
@@ -698,8 +705,11 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
         eq_base += tot & 0xffff;
         __syncthreads();  // dist is rewritten by the next chunk
     }
-    for (int j = keff + tid; j < top_k; j += kSelThreads) so[j] = -1;
-    if (tid == 0) *keff_out = keff;
+    for (int j = tid; j < s_end; j += kSelThreads) so[j] = j;
+    for (int j = tid; j < L - w_start; j += kSelThreads) so[s_end + keff + j] = w_start + j;
+    const int listed = s_end + keff + (L - w_start);
+    for (int j = listed + tid; j < sel_cap; j += kSelThreads) so[j] = -1;
+    if (tid == 0) *keff_out = listed;
 }
 
 // Key half of the select kernels, after the page list (LDS or workspace).
@@ -709,7 +719,8 @@ __device__ __forceinline__ void keys_half(SelShared& sh, const uint64_t* __restr
                                           bool list_in_lds, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
                                           int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum,
                                           uint32_t* __restrict__ ghist, int split, int S, int b, int h, int64_t bh,
-                                          int G, int Hq, int T, int P, int L, int max_keep, int top_k) {
+                                          int G, int Hq, int T, int P, int L, int max_keep, int top_k, int nsink,
+                                          int window) {
     if (!KEYS) return;
     const uint64_t* ck = codes + bh * (int64_t)T * NW;
     const uint64_t* cq = code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW;
@@ -717,12 +728,13 @@ __device__ __forceinline__ void keys_half(SelShared& sh, const uint64_t* __restr
     const int NBINS = G * NW * 64 + 1;
     uint32_t* cb = cum + bh * (int64_t)S * NBINS;
     uint32_t* gb = ghist + bh * (int64_t)NBINS;
+    const int64_t cap = (int64_t)top_k + nsink + window;
     if (list_in_lds)
-        select_keys_block<NW, true>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k, k_eff_out + bh,
-                                    sh, split, S, cb, gb);
+        select_keys_block<NW, true>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * cap, k_eff_out + bh,
+                                    sh, split, S, cb, gb, nsink, window);
     else if (split == 0)  // the page list is not in LDS: one block does the whole key select
-        select_keys_block<NW, false>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * top_k,
-                                     k_eff_out + bh, sh, 0, 1, cb, gb);
+        select_keys_block<NW, false>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * cap,
+                                     k_eff_out + bh, sh, 0, 1, cb, gb, nsink, window);
 }
 
 // With S > 1 the compact+attend kernel's merging block polls the split
@@ -746,7 +758,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
     int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Hq, int Hkv, int T, int P, int64_t NPmax,
-    int max_keep, int top_k) {
+    int max_keep, int top_k, int nsink, int window) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -775,7 +787,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         __syncthreads();
     }
     keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh, G,
-                        Hq, T, P, L, max_keep, top_k);
+                        Hq, T, P, L, max_keep, top_k, nsink, window);
     if (KEYS && S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
 }
 
@@ -789,7 +801,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
     int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Hq, int Hkv, int T, int P, int64_t NPmax,
-    int max_keep, int top_k) {
+    int max_keep, int top_k, int nsink, int window) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -814,8 +826,8 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
         const int NBINS = G * NW * 64 + 1;
         select_keys_block<NW, true>(codes + bh * (int64_t)T * NW, code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW, G,
                                     pl, np, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
-                                    sel + bh * top_k, k_eff_out + bh, sh, split, S, cum + bh * (int64_t)S * NBINS,
-                                    ghist + bh * (int64_t)NBINS);
+                                    sel + bh * ((int64_t)top_k + nsink + window), k_eff_out + bh, sh, split, S,
+                                    cum + bh * (int64_t)S * NBINS, ghist + bh * (int64_t)NBINS, nsink, window);
         if (S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
     }
 }
@@ -832,7 +844,8 @@ hipError_t select_launch(Kernel kernel, const DecodeArgs& a, int S, hipStream_t 
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), reinterpret_cast<uint32_t*>(a.ws + a.lay.kcum),
                        reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, po, po + n_po,
-                       a.lay.part_splits, s.D, S, s.G, s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k);
+                       a.lay.part_splits, s.D, S, s.G, s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k, s.nsink,
+                       s.window);
     return hipGetLastError();
 }
 

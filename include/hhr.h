@@ -96,7 +96,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 3
+#define HHR_ABI_VERSION 4
 
 typedef enum {
     HHR_OK = 0,
@@ -124,6 +124,10 @@ typedef struct {
     int32_t meta_dtype; /* hhr_dtype of the page metadata: HHR_F32 (0, the
                            default) or HHR_BF16 (outward-rounded, half the
                            bytes; see "meta" under Layouts)               */
+    int32_t sink_tokens;  /* decode variant, 0..max_ctx (0 = off): the first
+                             sink_tokens keys are always attended          */
+    int32_t local_window; /* decode variant, 0..max_ctx (0 = off): the last
+                             local_window keys are always attended         */
 } hhr_dims;
 
 /* Bytes of the meta and codes buffers for these dims (0 if the dims are invalid). */
@@ -198,8 +202,14 @@ hhr_status hhr_decode_workspace_layout(const hhr_dims* dims, int32_t max_keep_pa
  *      the largest S, equal S going to the lower page index;
  *   4. candidates: keys t < L of the kept pages;
  *   5. H(t) = group Hamming distance;
- *   6. the k_eff = min(top_k, #candidates) candidates with the smallest
- *      (H(t), t), written ascending to sel_idx (or the workspace), -1 padded;
+ *   6. the min(top_k, #candidates) candidates with the smallest (H(t), t),
+ *      written ascending to sel_idx (or the workspace), -1 padded;
+ *      with sink_tokens s or local_window w nonzero (the baselines' sink
+ *      tokens and local window, Appendix Table 4 of the thelatestinai.com
+ *      page), the keys t < min(s, L) and t >= max(min(s, L), L - w) are
+ *      always selected and take no part in steps 4-6, and the list is the
+ *      sink keys, then the step-6 keys, then the window keys (ascending);
+ *      k_eff = the number listed, sel_idx rows hold top_k + s + w entries;
  *   7. out_i = sum_t softmax_t(scale * q_i . k_t) v_t over the selected t,
  *      scale = softmax_scale if > 0, else 1/sqrt(D).
  * L = 0 gives out = 0, no pages and no keys.
@@ -207,7 +217,7 @@ hhr_status hhr_decode_workspace_layout(const hhr_dims* dims, int32_t max_keep_pa
  *   seq_len, keep_pages             device int32 [B], read
  *   max_keep_pages >= 1, top_k >= 1 host; they size the workspace
  *   out                             device fp32 [B][Hq][D], written
- *   sel_idx                         device int32 [B][Hkv][top_k], written, or NULL
+ *   sel_idx                         device int32 [B][Hkv][top_k + s + w], written, or NULL
  *   workspace, workspace_bytes      device scratch >= hhr_decode_workspace_bytes
  */
 hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, const void* V,

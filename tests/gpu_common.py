@@ -26,13 +26,14 @@ def to_dev(a, dev):
 def gpu_dims(wl: Workload):
     import hash_sparse_attention_amd as hsa
     return hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                         wl.dtype == "bf16", meta_bf16=wl.meta_bf16)
+                         wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
+                         local_window=wl.local_window)
 
 
 def oracle_dims(wl: Workload):
     import oracle
     return oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                       wl.dtype == "bf16", wl.meta_bf16)
+                       wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window)
 
 
 def run_gpu(wl: Workload, d: dict, dev, keep=None, max_keep=None, top_k=None, seq=None, chunks=None,
@@ -59,7 +60,8 @@ def run_gpu(wl: Workload, d: dict, dev, keep=None, max_keep=None, top_k=None, se
     ws = hsa.alloc_workspace(dims, max_keep, top_k, dev)
     ws.fill_(0xA5)
     out = torch.full((wl.batch, wl.n_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device=dev)
-    sel = torch.full((wl.batch, wl.n_kv_heads, top_k), -7, dtype=torch.int32, device=dev) if use_sel_out else None
+    cap = hsa.sel_cap(dims, top_k)
+    sel = torch.full((wl.batch, wl.n_kv_heads, cap), -7, dtype=torch.int32, device=dev) if use_sel_out else None
     hsa.decode_step(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], meta, codes, seq_t, keep_t, max_keep, top_k, out,
                     ws, sel_idx=sel, scale=scale)
     torch.cuda.synchronize()

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(hsa):
 
 def test_version_and_status_strings(hsa):
     L = hsa.lib()
-    assert L.hhr_abi_version() == 3
+    assert L.hhr_abi_version() == 4
     for code, name in hsa.STATUS.items():
         assert L.hhr_status_str(code).decode() == name
 
@@ -194,3 +194,20 @@ def test_topk_entry_validates_before_launch(hsa):
     bad = dims(head_dim=96)
     assert L.hhr_topk_decode_step(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 16, 0.0, FAKE, None, FAKE, 1 << 40,
                                   None) == 7
+
+
+def test_forced_key_fields_are_validated_and_size_the_selection(hsa):
+    """sink_tokens and local_window must lie in 0..max_ctx; they widen the workspace's selection rows."""
+    L = hsa.lib()
+    base = dims()
+    wide = dims(sink_tokens=4, local_window=64)
+    lay0, lay1 = hsa.WorkspaceLayout(), hsa.WorkspaceLayout()
+    assert L.hhr_decode_workspace_layout(ctypes.byref(base), 820, 4096, ctypes.byref(lay0)) == 0
+    assert L.hhr_decode_workspace_layout(ctypes.byref(wide), 820, 4096, ctypes.byref(lay1)) == 0
+    assert lay1.k_eff - lay1.sel >= 8 * (4096 + 68) * 4 and lay1.n_splits == -(-(4096 + 68) // 128)
+    assert hsa.sel_cap(wide, 4096) == 4096 + 68
+    for bad in (dict(sink_tokens=-1), dict(local_window=-3), dict(local_window=131073)):
+        d = dims(**bad)
+        assert L.hhr_decode_workspace_bytes(ctypes.byref(d), 820, 4096) == 0
+        assert call_decode(hsa, d, ws_bytes=1 << 40) == 6
+        assert "sink_tokens" in L.hhr_last_error().decode()

@@ -468,3 +468,27 @@ def test_hamming_logit_table_matches_oracle_codes(dev):
         m = hamming_logit(wl, d, o["codes"], o["code_q"], h=h)
         assert np.array_equal(np.array(g["rows"], float), np.array(m["rows"], float), equal_nan=True)  # empty bins: NaN
         assert g["spearman"] == m["spearman"] and g["top1_overlap"] == m["top1_overlap"]
+
+
+FORCED = [
+    # sink tokens / local window (keys always attended; the rest ranked by the Hamming stage)
+    ("tiny_s4_w64", WORKLOADS["tiny"].with_(sink_tokens=4, local_window=64)),
+    ("bf16_b3_ragged_s1", Workload("fk1", 150, 3, 8, 2, 128, 5000, 16, 128, 10, 300, "bf16", outliers=2,
+                                   ragged=(1, 5000), sink_tokens=1)),
+    ("g7_w17", Workload("fk2", 151, 2, 14, 2, 128, 2000, 16, 128, 10, 150, "bf16", outliers=2, ragged=(1, 2000),
+                        local_window=17)),
+    ("p1_s7_w300", Workload("fk3", 152, 2, 2, 2, 64, 700, 1, 128, 20, 17, "fp32", ragged=(50, 700),
+                            sink_tokens=7, local_window=300)),
+    ("window_covers_all", Workload("fk4", 153, 2, 8, 2, 64, 1024, 16, 64, 25, 3, "fp32", ragged=(10, 1024),
+                                   sink_tokens=5, local_window=1024)),
+    ("llama8b_32k_s4_w64", WORKLOADS["llama8b_32k"].with_(sink_tokens=4, local_window=64)),
+]
+
+
+@pytest.mark.parametrize("name,wl", FORCED, ids=[f[0] for f in FORCED])
+def test_sinks_and_local_window_parity(dev, name, wl):
+    banner(f"forced keys {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
