@@ -53,7 +53,7 @@ def build(force: bool = True) -> str:
 class _Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_bf16",
-        "meta_bf16", "sink_tokens", "local_window")]
+        "meta_bf16", "sink_tokens", "local_window", "page_group", "hamming_group")]
 
 
 def _load():
@@ -93,6 +93,8 @@ class Dims:
     meta_bf16: bool = False  # page max/min rounded outward to bf16 values
     sink_tokens: int = 0     # decode: the first sink_tokens keys are always attended
     local_window: int = 0    # decode: the last local_window keys are always attended
+    page_group: int = 0      # decode: page score over the group, 0 = max, 1 = min
+    hamming_group: int = 0   # decode: 0 = H summed over the group's codes, 1 = H to the mean query's code
 
     @property
     def group(self) -> int:
@@ -109,7 +111,7 @@ class Dims:
     def c(self) -> _Dims:
         return _Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.page_size,
                      self.hash_bits, self.max_ctx, int(self.kv_bf16), int(self.meta_bf16), int(self.sink_tokens),
-                     int(self.local_window))
+                     int(self.local_window), int(self.page_group), int(self.hamming_group))
 
 
 def _ptr(a):

@@ -50,6 +50,9 @@ typedef struct {
     int32_t meta_bf16;  /* 1: page max/min are stored rounded outward to bf16 values */
     int32_t sink_tokens;  /* decode: the first sink_tokens keys are always attended    */
     int32_t local_window; /* decode: the last local_window keys are always attended    */
+    int32_t page_group;    /* decode: 0 = page score max over the group's heads, 1 = min    */
+    int32_t hamming_group; /* decode: 0 = H summed over the group's query codes,
+                              1 = H against the code of the group's mean query            */
 } oracle_dims;
 
 enum { ORACLE_OK = 0, ORACLE_BAD_DIMS = 1, ORACLE_NOMEM = 2 };
@@ -60,6 +63,7 @@ static int dims_ok(const oracle_dims* d) {
     if (d->head_dim < 1 || d->page_size < 1 || d->max_ctx < 0) return 0;
     if (d->hash_bits < 64 || d->hash_bits % 64) return 0;
     if (d->sink_tokens < 0 || d->local_window < 0) return 0;
+    if ((d->page_group != 0 && d->page_group != 1) || (d->hamming_group != 0 && d->hamming_group != 1)) return 0;
     return 1;
 }
 
@@ -314,6 +318,13 @@ static void attend_selected(const float* q, int G, int D, const void* K, const v
  * (ascending, since the step-6 keys lie between them).  k_eff = |F| + the
  * step-6 count; the list holds top_k + s + w entries.
  *
+ * Group aggregation variants (the pages leave the GQA grouping open; see
+ * [FIG, Figure 4]: recall is measured per KV head): page_group = 1 scores a
+ * page by the min over the group of U_i(p) instead of the max;
+ * hamming_group = 1 replaces step 5's sum by H(t) = popcount(code(qm) XOR
+ * code_t), where qm is the group's mean query, qm_d = (sum_i q_i,d) / G in
+ * fp32 (i ascending, then one division), coded by the same canonical chain.
+ *
  * Outputs (any pointer may be NULL to skip it):
  *   qrot  [B][Hq][D] fp32        code_q [B][Hq][b/64]
  *   score [B][Hkv][NPmax] fp64   (+0.0 for p >= NP)
@@ -355,7 +366,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
 
             float* q = malloc(sizeof(float) * G * D);
             float* qr = malloc(sizeof(float) * G * D);
-            uint64_t* cq = malloc(sizeof(uint64_t) * G * NW);
+            uint64_t* cq = malloc(sizeof(uint64_t) * (G + 1) * NW);  /* the group's codes, then the mean query's */
             page_key* pk = malloc(sizeof(page_key) * (NP > 0 ? NP : 1));
             int32_t* plist = malloc(sizeof(int32_t) * max_keep);
             key_key* cand = malloc(sizeof(key_key) * (int64_t)max_keep * P);
@@ -376,6 +387,21 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
                 if (qrot_out) memcpy(qrot_out + qi * D, qr + i * D, sizeof(float) * D);
                 if (codeq_out) memcpy(codeq_out + qi * NW, cq + i * NW, sizeof(uint64_t) * NW);
             }
+            if (dm->hamming_group) {  /* the group's mean query and its code */
+                float* qm = malloc(sizeof(float) * D * 2);
+                if (qm) {
+                    for (int d = 0; d < D; ++d) {
+                        float acc = 0.0f;
+                        for (int i = 0; i < G; ++i) acc += q[i * D + d];
+                        qm[d] = acc / (float)G;
+                    }
+                    project(D, nb, Rh, Wh, qm, qm + D, cq + G * NW);
+                    free(qm);
+                } else {
+#pragma omp atomic write
+                    status = ORACLE_NOMEM;
+                }
+            }
 
             /* 2. page bounds */
             for (int64_t p = 0; p < NP; ++p) {
@@ -388,7 +414,7 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
                         double c = (double)qr[i * D + r] * (double)m[2 * r + 1];
                         U += a > c ? a : c;
                     }
-                    if (i == 0 || U > S) S = U;
+                    if (i == 0 || (dm->page_group ? U < S : U > S)) S = U;
                 }
                 if (S == 0.0) S = 0.0; /* -0 and +0 are the same score */
                 pk[p].s = S;
@@ -413,9 +439,14 @@ int oracle_decode(const oracle_dims* dm, const void* Q, const void* K, const voi
                     const int64_t t = (int64_t)plist[j] * P + r;
                     if (t >= L || t < s_end || t >= w_start) continue;
                     int32_t H = 0;
-                    for (int i = 0; i < G; ++i)
+                    if (dm->hamming_group) {
                         for (int w = 0; w < NW; ++w)
-                            H += __builtin_popcountll(cq[i * NW + w] ^ codes[(bh * T + t) * NW + w]);
+                            H += __builtin_popcountll(cq[G * NW + w] ^ codes[(bh * T + t) * NW + w]);
+                    } else {
+                        for (int i = 0; i < G; ++i)
+                            for (int w = 0; w < NW; ++w)
+                                H += __builtin_popcountll(cq[i * NW + w] ^ codes[(bh * T + t) * NW + w]);
+                    }
                     if (ham_out) ham_out[bh * (int64_t)max_keep * P + j * P + r] = (uint16_t)H;
                     cand[nc].h = H;
                     cand[nc].t = (int32_t)t;

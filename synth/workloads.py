@@ -46,6 +46,8 @@ class Workload:
     meta_bf16: bool = False      # page metadata stored as outward-rounded bf16
     sink_tokens: int = 0         # decode variant: first keys always attended
     local_window: int = 0        # decode variant: last keys always attended
+    page_group: int = 0          # decode variant: page score over the group, 0 = max, 1 = min
+    hamming_group: int = 0       # decode variant: 0 = H summed over the group, 1 = H to the mean query's code
 
     @property
     def group(self) -> int:

@@ -24,10 +24,12 @@ MUTANTS = {
                             "xrot[r] = dot_canon(t_, x, D); }"),
     "bound_min_not_max": ("U += a > c ? a : c;", "U += a < c ? a : c;"),
     "bound_always_kmax": ("U += a > c ? a : c;", "U += a;"),
-    "group_min_not_max": ("if (i == 0 || U > S) S = U;", "if (i == 0 || U < S) S = U;"),
+    "group_min_not_max": ("(dm->page_group ? U < S : U > S)", "(dm->page_group ? U < S : U < S)"),
+    "group_min_mode_is_max": ("(dm->page_group ? U < S : U > S)", "(dm->page_group ? U > S : U > S)"),
+    "mean_query_first_head": ("for (int i = 0; i < G; ++i) acc += q[i * D + d];", "for (int i = 0; i < 1; ++i) acc += q[i * D + d];"),
     "page_ties_high_first": ("return (x->p > y->p) - (x->p < y->p);", "return (x->p < y->p) - (x->p > y->p);"),
     "hamming_and": ("__builtin_popcountll(cq[i * NW + w] ^ codes", "__builtin_popcountll(cq[i * NW + w] & codes"),
-    "hamming_first_head_only": ("for (int i = 0; i < G; ++i)\n                        for (int w = 0; w < NW; ++w)",
+    "hamming_first_head_only": ("for (int i = 0; i < G; ++i)\n                            for (int w = 0; w < NW; ++w)",
                                 "for (int i = 0; i < 1; ++i)\n                        for (int w = 0; w < NW; ++w)"),
     "key_ties_high_first": ("return (x->t > y->t) - (x->t < y->t);", "return (x->t < y->t) - (x->t > y->t);"),
     "scale_without_sqrt": ("1.0 / sqrt((double)D)", "1.0 / (double)D"),

@@ -35,7 +35,8 @@ def bits_of(codes):
 
 def dims_for(o, wl: Workload):
     return o.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits,
-                  wl.ctx, wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window)
+                  wl.ctx, wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window, wl.page_group,
+                  wl.hamming_group)
 
 
 def f32(x, wl):
@@ -800,3 +801,66 @@ def test_window_covering_the_sequence_is_full_attention(oracle_mod):
             ref = _softmax_attention(Qf[b, i], Kf[b, i // wl.group, :L], Vf[b, i // wl.group, :L],
                                      1 / np.sqrt(wl.head_dim))
             assert np.abs(r["out"][b, i] - ref).max() <= 1e-9 * max(1.0, np.abs(ref).max())
+
+
+# ----------------------------------------------------------------------------- group aggregation variants
+
+@pytest.mark.parametrize("name", ["tiny", "bf16_g7"])
+def test_page_group_min_is_min_of_single_head_scores(oracle_mod, name):
+    """page_group = 1: S(p) is the min over the group of U_i(p); each U_i(p) is the score of a run with
+    one query head per KV head (G = 1), so the min of those runs' scores must equal it exactly."""
+    wl = WORKLOADS["tiny"] if name == "tiny" else \
+        Workload("pin_g7", 98, 2, 14, 2, 64, 600, 8, 64, 20, 40, "bf16", outliers=2, ragged=(100, 600))
+    d = make_layer(wl)
+    r = run(oracle_mod, wl.with_(page_group=1), d)[3]
+    G = wl.group
+    per = []
+    for j in range(G):
+        d1 = dict(d)
+        d1["Q"] = np.ascontiguousarray(d["Q"][:, j::G])
+        per.append(run(oracle_mod, wl.with_(n_q_heads=wl.n_kv_heads), d1)[3]["score"])
+    want = np.minimum.reduce(per)
+    for b in range(wl.batch):
+        NP = -(-int(d["seq_len"][b]) // wl.page_size)
+        assert (r["score"][b, :, :NP] == want[b, :, :NP]).all()
+
+
+def _f32_mean(q):
+    """fp32 mean over axis 0: sequential fp32 sum (rows ascending), then one fp32 division."""
+    acc = np.zeros(q.shape[1], np.float32)
+    for row in q:
+        acc = (acc + row.astype(np.float32)).astype(np.float32)
+    return (acc / np.float32(q.shape[0])).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "bf16_g7"])
+def test_hamming_group_mean_uses_the_mean_query_code(oracle_mod, name):
+    """hamming_group = 1: every candidate's H is the popcount of code(mean query) XOR its code, the mean
+    query's code coming from the pinned projection of a numpy fp32 mean."""
+    wl = WORKLOADS["tiny"] if name == "tiny" else \
+        Workload("pin_g7m", 99, 2, 14, 2, 64, 600, 8, 128, 20, 40, "bf16", outliers=2, ragged=(100, 600))
+    d = make_layer(wl)
+    dims, meta, codes, r = run(oracle_mod, wl.with_(hamming_group=1), d)
+    G, P, NW = wl.group, wl.page_size, wl.hash_bits // 64
+    Qf = f32(d["Q"], wl)
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        for h in range(wl.n_kv_heads):
+            qm = _f32_mean(Qf[b, h * G:(h + 1) * G])
+            _, cm = oracle_mod.project(d["R"][h], d["W"][h], qm[None, :])
+            for j, p in enumerate(r["pages"][b, h, :r["n_pages"][b, h]]):
+                for q in range(P):
+                    t = int(p) * P + q
+                    want = sum(_popcount(cm[0, w] ^ codes[b, h, t, w]) for w in range(NW)) if t < L else 0xFFFF
+                    assert r["ham"][b, h, j * P + q] == want
+
+
+def test_hamming_group_mean_with_one_head_is_the_plain_step(oracle_mod):
+    """With G = 1 the mean query is the query: both aggregations give the same distances and keys."""
+    wl = WORKLOADS["tiny"].with_(n_q_heads=2)
+    d = make_layer(wl)
+    d["Q"] = np.ascontiguousarray(d["Q"][:, :2])
+    a = run(oracle_mod, wl, d)[3]
+    m = run(oracle_mod, wl.with_(hamming_group=1, page_group=1), d)[3]
+    for k in ("score", "pages", "ham", "sel", "k_eff"):
+        assert (a[k] == m[k]).all(), k
