@@ -56,6 +56,9 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
         return fail(HHR_E_DTYPE, "kv_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->kv_dtype);
     if (d->meta_dtype != HHR_F32 && d->meta_dtype != HHR_BF16)
         return fail(HHR_E_DTYPE, "meta_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->meta_dtype);
+    if ((d->page_group != 0 && d->page_group != 1) || (d->hamming_group != 0 && d->hamming_group != 1))
+        return fail(HHR_E_RANGE, "page_group (%d) and hamming_group (%d) must be 0 or 1", d->page_group,
+                    d->hamming_group);
     if (d->sink_tokens < 0 || d->sink_tokens > d->max_ctx || d->local_window < 0 || d->local_window > d->max_ctx)
         return fail(HHR_E_RANGE, "sink_tokens (%d) and local_window (%d) must be in 0..max_ctx", d->sink_tokens,
                     d->local_window);
@@ -74,6 +77,9 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
     s.meta16 = d->meta_dtype == HHR_BF16;
     s.nsink = d->sink_tokens;
     s.window = d->local_window;
+    s.pg_min = d->page_group == 1;
+    s.ham_mean = d->hamming_group == 1;
+    s.Gh = s.ham_mean ? 1 : s.G;
     return HHR_OK;
 }
 
@@ -143,6 +149,7 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     l.n_splits = (sel_cap + kAttnChunk - 1) / kAttnChunk;
     l.q_rot = take(BQ * s.D * sizeof(float));
     l.code_q = take(BQ * s.NW * sizeof(uint64_t));
+    l.code_qm = take(s.ham_mean ? BH * s.NW * sizeof(uint64_t) : 0);
     l.q_split = take(BH * s.D * s.G * 2 * sizeof(double));
     l.score = take(BH * (size_t)s.NPmax * sizeof(double));
     l.pages = take(BH * (size_t)max_keep * sizeof(int32_t));
@@ -163,7 +170,7 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
         if (want >= 2 && (slots + want - 1) / want <= (size_t)kCompactSlots) S = (int)want;
     }
     l.sel_splits = S;
-    l.nbins = s.G * s.NB + 1;
+    l.nbins = s.Gh * s.NB + 1;
     l.part_splits = l.n_splits > S ? l.n_splits : S;
     l.partial = take(BQ * (size_t)l.part_splits * (s.D + 2) * sizeof(float));
     l.ghist_off = BH;
@@ -376,6 +383,7 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         p.codes = codes;
         p.q_rot = reinterpret_cast<float*>(a.ws + a.lay.q_rot);
         p.code_q = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_q);
+        p.code_qm = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_qm);
         p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
         p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
         p.n_counters = a.lay.n_clear;

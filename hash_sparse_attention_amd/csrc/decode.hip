@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
-                                                         int64_t NPB, int64_t NPmax) {
+                                                         int64_t NPB, int64_t NPmax, int pg_min) {
     constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
     using V4 = typename std::conditional<M16, uint4, float4>::type;
@@ -118,9 +118,14 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
         }
         asm volatile("" ::: "memory");
     }
-    double S = acc[0];
+    double S = acc[0];  // the group's max, or its min (a variant)
+    if (pg_min) {
 #pragma unroll
-    for (int i = 1; i < G; ++i) S = acc[i] > S ? acc[i] : S;
+        for (int i = 1; i < G; ++i) S = acc[i] < S ? acc[i] : S;
+    } else {
+#pragma unroll
+        for (int i = 1; i < G; ++i) S = acc[i] > S ? acc[i] : S;
+    }
     if (S == 0.0) S = 0.0;
     score[bh * NPmax + p] = S;
 }
@@ -134,7 +139,8 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     auto kern = s.meta16 ? page_bound_kernel<D, G, 8, true> : page_bound_kernel<D, G, 4, false>;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
-                       reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax);
+                       reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax,
+                       s.pg_min ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -162,6 +168,7 @@ hipError_t launch_qprep(const DecodeArgs& a, hipStream_t st) {
     p.W = a.W;
     p.q_rot = reinterpret_cast<float*>(a.ws + a.lay.q_rot);
     p.code_q = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_q);
+    p.code_qm = reinterpret_cast<uint64_t*>(a.ws + a.lay.code_qm);
     p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
     p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
     p.n_counters = a.lay.n_clear;

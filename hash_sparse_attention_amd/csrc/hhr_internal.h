@@ -18,6 +18,9 @@ struct Shape {
     bool bf16;      // Q, K, V are bf16
     bool meta16;    // page metadata is bf16 (outward-rounded)
     int nsink, window;  // keys always attended: the first nsink and the last window
+    bool pg_min;        // page score = min over the group (else max)
+    bool ham_mean;      // Hamming against the group's mean-query code (else summed over the group)
+    int Gh;             // query codes per KV head in the Hamming stage: 1 with ham_mean, else G
 };
 
 // Attention keys handled by one block (one split) of the attend kernel.
@@ -42,6 +45,7 @@ constexpr uint32_t kPartSentinel = 0x7fbadbadu;
 // part_splits: split stride of the attention partials.
 struct WsLayout {
     size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters, kcum, total;
+    size_t code_qm;  // the group's mean-query code [B][Hkv][NW] (ham_mean)
     int n_splits, sel_splits, part_splits, nbins;
     size_t ghist_off;  // u32 entries from counters to the head histograms
     int n_clear;       // u32 entries the query prep clears from counters
@@ -96,6 +100,7 @@ struct ProjectArgs {
     uint64_t* codes;
     float* q_rot;
     uint64_t* code_q;
+    uint64_t* code_qm;  // with ham_mean: the group's mean-query code
     double* q_split;
     uint32_t* counters;
     int n_counters;

@@ -14,6 +14,9 @@
 // fp32; every wave loads its lane's row into registers and runs its share of
 // the vectors, two at a time, as independent canonical chains, lane = row:
 // acc = fma(row[c], x[c], acc), c ascending from +0.
+// With the mean-query variant the query block adds one vector, the group's
+// mean qm_d = (sum_i q_i,d) / G in fp32 (heads ascending, one division),
+// which only goes through the hash rows; its code goes to code_qm.
 // Rows are independent (one rotated dimension, or one code bit), so no
 // result crosses blocks: hash rows ballot 64 sign bits into a code word and
 // rotation rows keep max/min over the page's keys, merged across waves in
@@ -31,8 +34,9 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     const void* __restrict__ Q, const void* __restrict__ K, const float* __restrict__ R,
     const float* __restrict__ W, const int32_t* __restrict__ start, const int32_t* __restrict__ count,
     int max_count, int key_blocks, float* __restrict__ meta, uint64_t* __restrict__ codes,
-    float* __restrict__ q_rot, uint64_t* __restrict__ code_q, double* __restrict__ q_split,
-    uint32_t* __restrict__ counters, int n_counters, int Hq, int Hkv, int G, int T, int P, int64_t NPB, bool meta16) {
+    float* __restrict__ q_rot, uint64_t* __restrict__ code_q, uint64_t* __restrict__ code_qm,
+    double* __restrict__ q_split, uint32_t* __restrict__ counters, int n_counters, int Hq, int Hkv, int G, int T,
+    int P, int64_t NPB, bool meta16, bool qmean) {
     constexpr int RG = (D + NB) / 64;  // row groups of [R_h; W_h]
     constexpr int NW = NB / 64;
     constexpr int LDM = D + 4;         // padded row stride of the tile (floats)
@@ -53,10 +57,12 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
 
     // This block's vectors: n_rot through the rotation rows, of which the
     // last ones (from hfirst) also through the hash rows.
-    int lo = 0, p = 0, n_rot = 0, hfirst = 0;
+    int lo = 0, p = 0, n_rot = 0, hfirst = 0, n_load = 0, n_vec = 0;
     int64_t xrow0 = 0;
     if (qblock) {
         n_rot = G;
+        n_load = G;
+        n_vec = G + (qmean ? 1 : 0);  // the mean query goes through the hash rows only
         xrow0 = q0;
     } else if (KEYS) {
         int s = start[b];
@@ -71,9 +77,10 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
         n_rot = (c > 0 && lo < e) ? (lo + P < e ? lo + P : e) - lo : 0;
         hfirst = s - lo > 0 ? s - lo : 0;
         xrow0 = bh * T + lo;
+        n_load = n_vec = n_rot;
     }
     const int v0 = rot ? 0 : hfirst;
-    const int nv = n_rot - v0;
+    const int nv = (rot ? n_rot : n_vec) - v0;
     if (nv <= 0) return;  // block-uniform
 
     // The 64 rows of this group (coalesced) and the vectors (as fp32).
@@ -86,14 +93,14 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     const void* src = qblock ? Q : K;
     if (BF16) {
         const uint32_t* x2 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(src) + xrow0 * D);
-        for (int i = tid; i < n_rot * D / 2; i += kProjWaves * 64) {
+        for (int i = tid; i < n_load * D / 2; i += kProjWaves * 64) {
             const uint32_t u = x2[i];
             xs[2 * i] = __uint_as_float(u << 16);
             xs[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
         }
     } else {
         const float* xf = static_cast<const float*>(src) + xrow0 * D;
-        for (int i = tid; i < n_rot * D; i += kProjWaves * 64) xs[i] = xf[i];
+        for (int i = tid; i < n_load * D; i += kProjWaves * 64) xs[i] = xf[i];
     }
 #pragma unroll
     for (int k = 0; k < F4PT; ++k) {
@@ -101,6 +108,14 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
         *reinterpret_cast<float4*>(&mt[(f / (D / 4)) * LDM + (f % (D / 4)) * 4]) = mv[k];
     }
     __syncthreads();
+    if (n_vec > n_load) {  // block-uniform: the group's mean query, after the staged queries
+        for (int d = tid; d < D; d += kProjWaves * 64) {
+            float acc = 0.f;
+            for (int i = 0; i < G; ++i) acc += xs[i * D + d];
+            xs[G * D + d] = acc / (float)G;
+        }
+        __syncthreads();
+    }
 
     // Wave w runs vectors w, w + kProjWaves, ... two chains at a time.  The
     // lane's row of the group goes into registers in halves of up to 64
@@ -120,7 +135,10 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
                 qsp[1] = a < 0.f ? (double)a : 0.0;
             } else {
                 const uint64_t word = __ballot(a > 0.f);
-                if (lane == 0) code_q[qi * NW + (row - D) / 64] = word;
+                if (lane == 0) {
+                    if (v < G) code_q[qi * NW + (row - D) / 64] = word;
+                    else code_qm[bh * NW + (row - D) / 64] = word;
+                }
             }
         } else if (rot) {
             const float vk = a == 0.f ? 0.f : a;
@@ -188,8 +206,8 @@ hipError_t project_t(const Shape& s, const ProjectArgs& a, hipStream_t st) {
     const int blocks = (key_blocks + (QUERIES ? 1 : 0)) * RG;
     hipLaunchKernelGGL((project_kernel<D, NB, BF16, KEYS, QUERIES>), dim3(s.Hkv, s.B, blocks),
                        dim3(kProjWaves * 64), 0, st, a.Q, a.K, a.R, a.W, a.start, a.count, a.max_count, key_blocks,
-                       a.meta, a.codes, a.q_rot, a.code_q, a.q_split, a.counters, a.n_counters, s.Hq, s.Hkv, s.G,
-                       s.T, s.P, s.NPB, s.meta16);
+                       a.meta, a.codes, a.q_rot, a.code_q, a.code_qm, a.q_split, a.counters, a.n_counters, s.Hq,
+                       s.Hkv, s.G, s.T, s.P, s.NPB, s.meta16, a.queries && s.ham_mean);
     return hipGetLastError();
 }
 

@@ -719,21 +719,21 @@ __device__ __forceinline__ void keys_half(SelShared& sh, const uint64_t* __restr
                                           bool list_in_lds, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
                                           int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum,
                                           uint32_t* __restrict__ ghist, int split, int S, int b, int h, int64_t bh,
-                                          int G, int Hq, int T, int P, int L, int max_keep, int top_k, int nsink,
+                                          int Gh, int T, int P, int L, int max_keep, int top_k, int nsink,
                                           int window) {
     if (!KEYS) return;
     const uint64_t* ck = codes + bh * (int64_t)T * NW;
-    const uint64_t* cq = code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW;
+    const uint64_t* cq = code_q + bh * Gh * NW;  // the group's Gh query codes
     uint16_t* hm = ham + bh * (int64_t)max_keep * P;
-    const int NBINS = G * NW * 64 + 1;
+    const int NBINS = Gh * NW * 64 + 1;
     uint32_t* cb = cum + bh * (int64_t)S * NBINS;
     uint32_t* gb = ghist + bh * (int64_t)NBINS;
     const int64_t cap = (int64_t)top_k + nsink + window;
     if (list_in_lds)
-        select_keys_block<NW, true>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * cap, k_eff_out + bh,
+        select_keys_block<NW, true>(ck, cq, Gh, pl, np, L, P, max_keep, top_k, hm, sel + bh * cap, k_eff_out + bh,
                                     sh, split, S, cb, gb, nsink, window);
     else if (split == 0)  // the page list is not in LDS: one block does the whole key select
-        select_keys_block<NW, false>(ck, cq, G, pl, np, L, P, max_keep, top_k, hm, sel + bh * cap,
+        select_keys_block<NW, false>(ck, cq, Gh, pl, np, L, P, max_keep, top_k, hm, sel + bh * cap,
                                      k_eff_out + bh, sh, 0, 1, cb, gb, nsink, window);
 }
 
@@ -757,7 +757,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
     int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Hq, int Hkv, int T, int P, int64_t NPmax,
+    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
     int max_keep, int top_k, int nsink, int window) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
@@ -786,8 +786,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         __syncthreads();
     }
-    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh, G,
-                        Hq, T, P, L, max_keep, top_k, nsink, window);
+    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh, Gh,
+                        T, P, L, max_keep, top_k, nsink, window);
     if (KEYS && S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
 }
 
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
     int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Hq, int Hkv, int T, int P, int64_t NPmax,
+    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
     int max_keep, int top_k, int nsink, int window) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
@@ -823,8 +823,8 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     if (threadIdx.x == 0 && split == 0) n_pages[bh] = np;
     __syncthreads();
     if (KEYS) {  // max_keep <= kListLds here, so the page list is in LDS
-        const int NBINS = G * NW * 64 + 1;
-        select_keys_block<NW, true>(codes + bh * (int64_t)T * NW, code_q + ((int64_t)b * Hq + (int64_t)h * G) * NW, G,
+        const int NBINS = Gh * NW * 64 + 1;
+        select_keys_block<NW, true>(codes + bh * (int64_t)T * NW, code_q + bh * Gh * NW, Gh,
                                     pl, np, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
                                     sel + bh * ((int64_t)top_k + nsink + window), k_eff_out + bh, sh, split, S,
                                     cum + bh * (int64_t)S * NBINS, ghist + bh * (int64_t)NBINS, nsink, window);
@@ -839,13 +839,13 @@ hipError_t select_launch(Kernel kernel, const DecodeArgs& a, int S, hipStream_t 
     const size_t n_po = (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     hipLaunchKernelGGL(kernel, dim3(s.Hkv, s.B, S), dim3(kSelThreads), 0, st,
                        reinterpret_cast<const double*>(a.ws + a.lay.score), a.keep_pages, a.codes,
-                       reinterpret_cast<const uint64_t*>(a.ws + a.lay.code_q), a.seq_len,
+                       reinterpret_cast<const uint64_t*>(a.ws + (s.ham_mean ? a.lay.code_qm : a.lay.code_q)), a.seq_len,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.pages), reinterpret_cast<int32_t*>(a.ws + a.lay.n_pages),
                        reinterpret_cast<uint16_t*>(a.ws + a.lay.ham), a.sel,
                        reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), reinterpret_cast<uint32_t*>(a.ws + a.lay.kcum),
                        reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, po, po + n_po,
-                       a.lay.part_splits, s.D, S, s.G, s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k, s.nsink,
-                       s.window);
+                       a.lay.part_splits, s.D, S, s.G, s.Gh, s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k,
+                       s.nsink, s.window);
     return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 4
+#define HHR_ABI_VERSION 5
 
 typedef enum {
     HHR_OK = 0,
@@ -128,6 +128,11 @@ typedef struct {
                              sink_tokens keys are always attended          */
     int32_t local_window; /* decode variant, 0..max_ctx (0 = off): the last
                              local_window keys are always attended         */
+    int32_t page_group;    /* decode variant: page score over the GQA group,
+                              0 = max of the heads' bounds (default), 1 = min */
+    int32_t hamming_group; /* decode variant: 0 = distance summed over the
+                              group's query codes (default), 1 = distance to
+                              the code of the group's mean query           */
 } hhr_dims;
 
 /* Bytes of the meta and codes buffers for these dims (0 if the dims are invalid). */
@@ -197,11 +202,15 @@ hhr_status hhr_decode_workspace_layout(const hhr_dims* dims, int32_t max_keep_pa
  * For every sequence b (length L = seq_len[b]) and KV head h, with the G
  * query heads of h sharing one selection:
  *   1. qrot_i = R_h q_i and code_q,i (canonical chains);
- *   2. S(p) for p < NP(L) (fp64, see above);
+ *   2. S(p) for p < NP(L) (fp64, see above); with page_group = 1 the min
+ *      over the group's heads instead of the max;
  *   3. keep = clamp(keep_pages[b], 1, min(NP(L), max_keep_pages)) pages with
  *      the largest S, equal S going to the lower page index;
  *   4. candidates: keys t < L of the kept pages;
- *   5. H(t) = group Hamming distance;
+ *   5. H(t) = group Hamming distance; with hamming_group = 1, H(t) =
+ *      popcount(code(qm) XOR code_t) for the group's mean query qm, qm_d =
+ *      (sum_i q_i,d) / G in fp32 (heads ascending, one division), coded by
+ *      the same canonical chain;
  *   6. the min(top_k, #candidates) candidates with the smallest (H(t), t),
  *      written ascending to sel_idx (or the workspace), -1 padded;
  *      with sink_tokens s or local_window w nonzero (the baselines' sink

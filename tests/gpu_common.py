@@ -27,13 +27,14 @@ def gpu_dims(wl: Workload):
     import hash_sparse_attention_amd as hsa
     return hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                          wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
-                         local_window=wl.local_window)
+                         local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group)
 
 
 def oracle_dims(wl: Workload):
     import oracle
     return oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                       wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window)
+                       wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window, wl.page_group,
+                       wl.hamming_group)
 
 
 def run_gpu(wl: Workload, d: dict, dev, keep=None, max_keep=None, top_k=None, seq=None, chunks=None,

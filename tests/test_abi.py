@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(hsa):
 
 def test_version_and_status_strings(hsa):
     L = hsa.lib()
-    assert L.hhr_abi_version() == 4
+    assert L.hhr_abi_version() == 5
     for code, name in hsa.STATUS.items():
         assert L.hhr_status_str(code).decode() == name
 
@@ -211,3 +211,15 @@ def test_forced_key_fields_are_validated_and_size_the_selection(hsa):
         assert L.hhr_decode_workspace_bytes(ctypes.byref(d), 820, 4096) == 0
         assert call_decode(hsa, d, ws_bytes=1 << 40) == 6
         assert "sink_tokens" in L.hhr_last_error().decode()
+
+
+def test_group_variant_fields_are_validated(hsa):
+    """page_group and hamming_group accept 0 or 1 only, checked before anything is enqueued."""
+    L = hsa.lib()
+    for ok in (dict(page_group=1), dict(hamming_group=1), dict(page_group=1, hamming_group=1)):
+        assert L.hhr_decode_workspace_bytes(ctypes.byref(dims(**ok)), 820, 4096) > 0
+    for bad in (dict(page_group=2), dict(hamming_group=-1)):
+        d = dims(**bad)
+        assert L.hhr_decode_workspace_bytes(ctypes.byref(d), 820, 4096) == 0
+        assert call_decode(hsa, d, ws_bytes=1 << 40) == 6
+        assert "page_group" in L.hhr_last_error().decode()

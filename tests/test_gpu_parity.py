@@ -492,3 +492,25 @@ def test_sinks_and_local_window_parity(dev, name, wl):
     g = run_gpu(wl, d, dev)
     o = run_oracle(wl, d)
     compare(wl, d["seq_len"], g, o, label=name)
+
+
+GROUPED = [
+    # group aggregation variants: min page score over the GQA group, Hamming to the mean query's code
+    ("tiny_min", WORKLOADS["tiny"].with_(page_group=1)),
+    ("tiny_mean", WORKLOADS["tiny"].with_(hamming_group=1)),
+    ("g7_min_mean_ragged", Workload("gv1", 160, 3, 14, 2, 128, 2000, 16, 128, 10, 150, "bf16", outliers=2,
+                                    ragged=(1, 2000), page_group=1, hamming_group=1)),
+    ("g8_mean_d64_p64", Workload("gv2", 161, 1, 16, 2, 64, 3000, 64, 64, 30, 400, "bf16", hamming_group=1)),
+    ("g3_mean_fp32_sinks", Workload("gv3", 162, 2, 6, 2, 128, 777, 32, 128, 40, 64, "fp32", ragged=(700, 777),
+                                    hamming_group=1, sink_tokens=4, local_window=16)),
+    ("llama8b_32k_mean", WORKLOADS["llama8b_32k"].with_(hamming_group=1)),
+]
+
+
+@pytest.mark.parametrize("name,wl", GROUPED, ids=[g[0] for g in GROUPED])
+def test_group_aggregation_variants_parity(dev, name, wl):
+    banner(f"group variant {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
