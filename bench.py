@@ -96,7 +96,8 @@ def cpu_baseline(wl, host_layer, steps_note):
 
     import oracle
     od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
-                     wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window)
+                     wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window, wl.page_group,
+                     wl.hamming_group)
     t0 = time.perf_counter()
     meta, codes = oracle.encode(od, host_layer["K"], host_layer["R"], host_layer["W"], np.zeros(wl.batch, np.int32),
                                 host_layer["seq_len"])
@@ -295,6 +296,10 @@ def main():
                     help="also run N plain 1 GiB-in/1 GiB-out negations (for rocprofv3 --pmc calibration)")
     ap.add_argument("--sinks", type=int, default=0, help="hhr mode: sink tokens always attended (a variant; 0 = off)")
     ap.add_argument("--window", type=int, default=0, help="hhr mode: local window always attended (0 = off)")
+    ap.add_argument("--page-group", type=int, choices=(0, 1), default=0,
+                    help="hhr mode: page score over the GQA group, 0 = max (default), 1 = min (a variant)")
+    ap.add_argument("--hamming-group", type=int, choices=(0, 1), default=0,
+                    help="hhr mode: 0 = distance summed over the group's codes, 1 = to the mean query's code")
     ap.add_argument("--mode", choices=("hhr", "topk"), default="hhr",
                     help="hhr: the HHR decode step (default); topk: the TopK (Oracle) comparison step "
                          "(keys by exact logit over all of K, then the same attention)")
@@ -316,14 +321,15 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.layers:
         wl = wl.with_(layers=args.layers)
-    wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window)
+    wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window,
+                  page_group=args.page_group, hamming_group=args.hamming_group)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, ctx={wl.ctx}, device {torch.cuda.get_device_name(0)}")
 
     dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                          wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
-                         local_window=wl.local_window)
+                         local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group)
     layers = []
     t0 = time.perf_counter()
     for l in range(wl.layers):
@@ -450,6 +456,8 @@ def main():
                          f"top-k {wl.top_k}; page metadata {'bf16 (outward-rounded)' if wl.meta_bf16 else 'fp32'}; "
                          + (f"{wl.sink_tokens} sink tokens and a {wl.local_window}-key local window always "
                             f"attended; " if wl.sink_tokens or wl.local_window else "") +
+                         ("page score = min over the group; " if wl.page_group else "") +
+                         ("Hamming to the group's mean-query code; " if wl.hamming_group else "") +
                          "one step = per layer a 1-token append + decode"),
             "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
         },
