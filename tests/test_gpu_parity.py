@@ -240,15 +240,19 @@ def test_qwen7b_b16_append_4096_sampled(dev):
     compare(wl, seq, g, o, batches=batches, label="qwen7b_b16")
 
 
-@pytest.mark.parametrize("meta_bf16", [False, True], ids=["fp32_meta", "bf16_meta"])
-def test_decode_step_append_matches_oracle(dev, meta_bf16):
+@pytest.mark.parametrize("meta_bf16,variant", [(False, {}), (True, {}),
+                                               (False, dict(sink_tokens=3, local_window=40, hamming_group=1)),
+                                               (True, dict(page_group=1))],
+                         ids=["fp32_meta", "bf16_meta", "sinks_window_mean_code", "bf16_meta_min_page"])
+def test_decode_step_append_matches_oracle(dev, meta_bf16, variant):
     """hhr_decode_step_append (fused append + query projection) equals the oracle's single-shot encode +
     decode, for a 1-token append, a ragged multi-token append, and an append larger than the fused limit."""
     import torch
 
     import hash_sparse_attention_amd as hsa
     from gpu_common import gpu_dims, to_dev
-    wl = Workload("fused", 114, 3, 12, 3, 128, 700, 16, 128, 20, 48, "bf16", outliers=2, meta_bf16=meta_bf16)
+    wl = Workload("fused", 114, 3, 12, 3, 128, 700, 16, 128, 20, 48, "bf16", outliers=2, meta_bf16=meta_bf16,
+                  **variant)
     d = make_layer(wl, lengths=[700, 650, 333])
     o = run_oracle(wl, d)
     for new in ([1, 1, 1], [5, 17, 1], [70, 3, 100]):
@@ -263,7 +267,7 @@ def test_decode_step_append_matches_oracle(dev, meta_bf16):
                          int(pre.max()), meta, codes)
         ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
         out = torch.empty((3, 12, 128), dtype=torch.float32, device=dev)
-        sel = torch.empty((3, 3, wl.top_k), dtype=torch.int32, device=dev)
+        sel = torch.empty((3, 3, hsa.sel_cap(dims, wl.top_k)), dtype=torch.int32, device=dev)
         hsa.decode_step_append(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], meta, codes, to_dev(pre, dev),
                                to_dev(new, dev), int(new.max()), to_dev(seq, dev), to_dev(d["keep"], dev),
                                wl.max_keep, wl.top_k, out, ws, sel_idx=sel)

@@ -189,3 +189,41 @@ def test_topk_selection_is_exact_top_k_at_scale(dev, name):
             tied_out = np.nonzero(~mask & (z == zmin))[0]
             tied_in = sel[z[sel] == zmin]
             assert len(tied_out) == 0 or tied_out.min() > tied_in.max()
+
+
+def test_topk_graph_replay_matches_eager(dev):
+    """A captured HIP graph of the TopK step replays to the eager result every time, with eager work and
+    synchronizations between replays (the step clears its own counters with a kernel, not a memset)."""
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    wl = WORKLOADS["llama8b_32k"]
+    banner("topk graph capture and replay")
+    d = make_layer(wl)
+    dims = gpu_dims(wl)
+    t = {k: to_dev(d[k], dev) for k in ("Q", "K", "V")}
+    seq = to_dev(d["seq_len"], dev)
+    ws = hsa.alloc_topk_workspace(dims, wl.top_k, dev)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev)
+    sel = torch.empty((1, 8, wl.top_k), dtype=torch.int32, device=dev)
+
+    def step():
+        hsa.topk_decode_step(dims, t["Q"], t["K"], t["V"], seq, wl.top_k, out, ws, sel_idx=sel)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel = out.clone(), sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-9)
+        _ = (t["K"][0, 0, :8].float() * 2).sum().item()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(sel, ref_sel), f"replay {rep}"
