@@ -296,6 +296,10 @@ def main():
                     help="also run N plain 1 GiB-in/1 GiB-out negations (for rocprofv3 --pmc calibration)")
     ap.add_argument("--sinks", type=int, default=0, help="hhr mode: sink tokens always attended (a variant; 0 = off)")
     ap.add_argument("--window", type=int, default=0, help="hhr mode: local window always attended (0 = off)")
+    ap.add_argument("--keep-percent", type=int, default=0,
+                    help="hhr mode: pages kept, percent (0 = the workload's; 100 = LHP-only, Hamming over every key)")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="hhr mode: keys selected (0 = the workload's; >= the candidates = GKR-only attention)")
     ap.add_argument("--page-group", type=int, choices=(0, 1), default=0,
                     help="hhr mode: page score over the GQA group, 0 = max (default), 1 = min (a variant)")
     ap.add_argument("--hamming-group", type=int, choices=(0, 1), default=0,
@@ -323,6 +327,10 @@ def main():
         wl = wl.with_(layers=args.layers)
     wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window,
                   page_group=args.page_group, hamming_group=args.hamming_group)
+    if args.keep_percent:
+        wl = wl.with_(keep_percent=args.keep_percent)
+    if args.top_k:
+        wl = wl.with_(top_k=args.top_k)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, ctx={wl.ctx}, device {torch.cuda.get_device_name(0)}")

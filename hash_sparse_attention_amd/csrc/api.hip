@@ -157,15 +157,19 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     l.ham = take(BH * (size_t)max_keep * s.P * sizeof(uint16_t));
     l.sel = take(BH * (size_t)sel_cap * sizeof(int32_t));
     l.k_eff = take(BH * sizeof(int32_t));
-    // Split key select: about 512 candidate slots per block, at most
-    // kCompactSlots, and no more blocks than the GPU holds at once (each one
-    // repeats the page select).
+    // Split key select: about 512 candidate slots per block, and no more
+    // blocks than the GPU holds at once (each one repeats the page select),
+    // unless more are needed for the compaction's kCompactSlots per block;
+    // at most 64 blocks per head (then they run in rounds: the merge never
+    // waits for a block that has not started).
     const size_t slots = (size_t)max_keep * s.P;
     const size_t BHs = BH > 0 ? BH : 1;
     int S = 1;
-    if (!forced && slots <= (size_t)kSelChunk && max_keep <= kSelListLds) {
+    if (!forced && max_keep <= kSelListLds) {
         size_t want = (slots + 511) / 512, cap = 256 / BHs;
         want = want < cap ? want : cap;
+        const size_t need = (slots + kCompactSlots - 1) / kCompactSlots;
+        want = want < need ? need : want;
         want = want > 64 ? 64 : want;
         if (want >= 2 && (slots + want - 1) / want <= (size_t)kCompactSlots) S = (int)want;
     }

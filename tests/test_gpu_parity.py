@@ -518,3 +518,19 @@ def test_group_aggregation_variants_parity(dev, name, wl):
     g = run_gpu(wl, d, dev)
     o = run_oracle(wl, d)
     compare(wl, d["seq_len"], g, o, label=name)
+
+
+
+@pytest.mark.parametrize("name,wl", [
+    ("lhp_only_40k", Workload("lhp1", 170, 1, 8, 2, 128, 40000, 16, 128, 100, 2048, "bf16", outliers=2)),
+    ("lhp_only_ragged_b2", Workload("lhp2", 171, 2, 8, 2, 64, 70000, 16, 64, 100, 900, "bf16",
+                                    ragged=(30000, 70000))),
+], ids=["lhp_only_40k", "lhp_only_ragged_b2"])
+def test_lhp_only_many_candidates(dev, name, wl):
+    """LHP-only (every page kept, so the Hamming stage ranks every key): more candidate slots than one
+    select chunk, spread over up to 64 split blocks per head."""
+    banner(f"LHP-only {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
