@@ -95,6 +95,7 @@ class Dims:
     local_window: int = 0    # decode: the last local_window keys are always attended
     page_group: int = 0      # decode: page score over the group, 0 = max, 1 = min
     hamming_group: int = 0   # decode: 0 = H summed over the group's codes, 1 = H to the mean query's code
+    per_head: bool = False   # decode: one selection per query head instead of one per KV head
 
     @property
     def group(self) -> int:
@@ -172,7 +173,18 @@ def encode(dims: Dims, K, R, W, start, count, meta=None, codes=None):
 
 def decode(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max_keep, top_k, scale=0.0):
     """One decode step; returns a dict of every intermediate and the fp64 output (sel holds
-    top_k + sink_tokens + local_window entries per head)."""
+    top_k + sink_tokens + local_window entries per head).
+
+    per_head: every query head selects for itself.  By definition that is the shared-selection step on the
+    same inputs with each KV head's data (K, V, R_h, W_h, metadata, codes) repeated for its G query heads,
+    which is what is run: the per-(b, h) outputs then hold one row per query head."""
+    if dims.per_head and dims.group > 1:
+        from dataclasses import replace
+        G = dims.group
+        rep = lambda a, axis: np.ascontiguousarray(np.repeat(np.asarray(a), G, axis=axis))
+        de = replace(dims, n_kv_heads=dims.n_q_heads, per_head=False)
+        return decode(de, Q, rep(K, 1), rep(V, 1), rep(R, 0), rep(W, 0), rep(meta, 1), rep(codes, 1), seq_len,
+                      keep_pages, max_keep, top_k, scale)
     B, Hq, Hkv, D, P = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.page_size
     Q = _kv(Q, dims); K = _kv(K, dims); V = _kv(V, dims)
     R = _c(R, np.float32); W = _c(W, np.float32)

@@ -48,6 +48,7 @@ class Workload:
     local_window: int = 0        # decode variant: last keys always attended
     page_group: int = 0          # decode variant: page score over the group, 0 = max, 1 = min
     hamming_group: int = 0       # decode variant: 0 = H summed over the group, 1 = H to the mean query's code
+    per_head: bool = False       # decode variant: one selection per query head
 
     @property
     def group(self) -> int:

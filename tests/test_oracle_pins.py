@@ -36,7 +36,7 @@ def bits_of(codes):
 def dims_for(o, wl: Workload):
     return o.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits,
                   wl.ctx, wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window, wl.page_group,
-                  wl.hamming_group)
+                  wl.hamming_group, wl.per_head)
 
 
 def f32(x, wl):
@@ -863,4 +863,53 @@ def test_hamming_group_mean_with_one_head_is_the_plain_step(oracle_mod):
     a = run(oracle_mod, wl, d)[3]
     m = run(oracle_mod, wl.with_(hamming_group=1, page_group=1), d)[3]
     for k in ("score", "pages", "ham", "sel", "k_eff"):
+        assert (a[k] == m[k]).all(), k
+
+
+# ----------------------------------------------------------------------------- per-query-head selection
+
+PH = Workload("pin_ph", 100, 2, 8, 2, 64, 700, 8, 128, 100, 5000, "bf16", outliers=2, ragged=(200, 700))
+
+
+def test_per_head_scores_max_to_the_shared_score(oracle_mod):
+    """The shared page score is the max over the group of the bounds, so it equals the max of the per-head
+    scores exactly, page by page."""
+    wl = WORKLOADS["tiny"].with_(batch=2, ragged=(1000, 4096))
+    d = make_layer(wl)
+    shared = run(oracle_mod, wl, d)[3]
+    ph = run(oracle_mod, wl.with_(per_head=True), d)[3]
+    G = wl.group
+    assert ph["score"].shape[1] == wl.n_q_heads and ph["sel"].shape[1] == wl.n_q_heads
+    for b in range(wl.batch):
+        NP = -(-int(d["seq_len"][b]) // wl.page_size)
+        for h in range(wl.n_kv_heads):
+            assert (ph["score"][b, h * G:(h + 1) * G, :NP].max(axis=0) == shared["score"][b, h, :NP]).all()
+
+
+def test_per_head_distances_sum_to_the_shared_distance(oracle_mod):
+    """With every page kept the candidate slots line up, and the shared Hamming distance is the sum of the
+    group's per-head distances; with top_k >= L both are full attention, head by head."""
+    wl = PH
+    d = make_layer(wl)
+    npg = wl.max_pages
+    kw = dict(keep=[npg] * wl.batch, max_keep=npg, top_k=wl.ctx)
+    shared = run(oracle_mod, wl, d, **kw)[3]
+    ph = run(oracle_mod, wl.with_(per_head=True), d, **kw)[3]
+    G = wl.group
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            grp = ph["ham"][b, h * G:(h + 1) * G].astype(np.int64)
+            valid = shared["ham"][b, h] != 0xFFFF
+            assert ((grp == 0xFFFF).all(axis=0) == ~valid).all()
+            assert (grp[:, valid].sum(axis=0) == shared["ham"][b, h, valid]).all()
+    assert np.abs(ph["out"] - shared["out"]).max() <= 1e-12
+
+
+def test_per_head_with_one_head_per_group_is_the_plain_step(oracle_mod):
+    wl = WORKLOADS["tiny"].with_(n_q_heads=2)
+    d = make_layer(wl)
+    d["Q"] = np.ascontiguousarray(d["Q"][:, :2])
+    a = run(oracle_mod, wl, d)[3]
+    m = run(oracle_mod, wl.with_(per_head=True), d)[3]
+    for k in ("score", "pages", "ham", "sel", "k_eff", "out"):
         assert (a[k] == m[k]).all(), k
