@@ -97,7 +97,7 @@ def cpu_baseline(wl, host_layer, steps_note):
     import oracle
     od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                      wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window, wl.page_group,
-                     wl.hamming_group)
+                     wl.hamming_group, wl.per_head)
     t0 = time.perf_counter()
     meta, codes = oracle.encode(od, host_layer["K"], host_layer["R"], host_layer["W"], np.zeros(wl.batch, np.int32),
                                 host_layer["seq_len"])
@@ -300,6 +300,8 @@ def main():
                     help="hhr mode: pages kept, percent (0 = the workload's; 100 = LHP-only, Hamming over every key)")
     ap.add_argument("--top-k", type=int, default=0,
                     help="hhr mode: keys selected (0 = the workload's; >= the candidates = GKR-only attention)")
+    ap.add_argument("--per-head", action="store_true",
+                    help="hhr mode: one selection per query head instead of one per KV head (a variant)")
     ap.add_argument("--page-group", type=int, choices=(0, 1), default=0,
                     help="hhr mode: page score over the GQA group, 0 = max (default), 1 = min (a variant)")
     ap.add_argument("--hamming-group", type=int, choices=(0, 1), default=0,
@@ -326,7 +328,7 @@ def main():
     if args.layers:
         wl = wl.with_(layers=args.layers)
     wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window,
-                  page_group=args.page_group, hamming_group=args.hamming_group)
+                  page_group=args.page_group, hamming_group=args.hamming_group, per_head=args.per_head)
     if args.keep_percent:
         wl = wl.with_(keep_percent=args.keep_percent)
     if args.top_k:
@@ -337,7 +339,8 @@ def main():
 
     dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                          wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
-                         local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group)
+                         local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group,
+                         per_head=wl.per_head)
     layers = []
     t0 = time.perf_counter()
     for l in range(wl.layers):
@@ -347,7 +350,8 @@ def main():
         hsa.encode_cache(dims, d["K"], d["R"], d["W"], zero, d["seq_len"], wl.ctx, meta, codes)
         d.update(meta=meta, codes=codes)
         d["out"] = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
-        d["sel"] = torch.empty((wl.batch, wl.n_kv_heads, hsa.sel_cap(dims, wl.top_k)), dtype=torch.int32, device=dev)
+        d["sel"] = torch.empty((wl.batch, hsa.sel_units(dims), hsa.sel_cap(dims, wl.top_k)), dtype=torch.int32,
+                               device=dev)
         d["app_start"] = (d["seq_len"] - 1).contiguous()
         d["app_count"] = torch.ones(wl.batch, dtype=torch.int32, device=dev)
         layers.append(d)
@@ -466,6 +470,7 @@ def main():
                             f"attended; " if wl.sink_tokens or wl.local_window else "") +
                          ("page score = min over the group; " if wl.page_group else "") +
                          ("Hamming to the group's mean-query code; " if wl.hamming_group else "") +
+                         ("one selection per query head; " if wl.per_head else "") +
                          "one step = per layer a 1-token append + decode"),
             "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
         },

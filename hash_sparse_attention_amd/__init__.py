@@ -30,7 +30,7 @@ class HHRError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_dtype",
-        "meta_dtype", "sink_tokens", "local_window", "page_group", "hamming_group")]
+        "meta_dtype", "sink_tokens", "local_window", "page_group", "hamming_group", "per_head")]
 
     def __repr__(self):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -113,15 +113,21 @@ def _stream(stream):
 
 def make_dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx, bf16: bool,
               meta_bf16: bool = False, sink_tokens: int = 0, local_window: int = 0, page_group: int = 0,
-              hamming_group: int = 0) -> Dims:
+              hamming_group: int = 0, per_head: bool = False) -> Dims:
     """meta_bf16: store page metadata as outward-rounded bf16 (half the bytes of the page-bound stream).
     sink_tokens, local_window: keys always attended by the decode step (the first and the last ones); its
     selection rows then hold top_k + sink_tokens + local_window entries (`sel_cap`).
     page_group = 1 scores a page by the min over the GQA group (default 0: max); hamming_group = 1 ranks keys
-    by the distance to the code of the group's mean query (default 0: summed over the group's codes)."""
+    by the distance to the code of the group's mean query (default 0: summed over the group's codes).
+    per_head: one selection per query head instead of one per KV head (per-(b, h) rows become per query head)."""
     return Dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx,
                 HHR_BF16 if bf16 else HHR_F32, HHR_BF16 if meta_bf16 else HHR_F32, int(sink_tokens),
-                int(local_window), int(page_group), int(hamming_group))
+                int(local_window), int(page_group), int(hamming_group), int(bool(per_head)))
+
+
+def sel_units(dims: Dims) -> int:
+    """Selection rows per sequence: query heads with per-query-head selection, else KV heads."""
+    return dims.n_q_heads if dims.per_head else dims.n_kv_heads
 
 
 def sel_cap(dims: Dims, top_k: int) -> int:
@@ -276,7 +282,8 @@ class WorkspaceView:
 def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> WorkspaceView:
     import torch
     lay = workspace_layout(dims, max_keep, top_k)
-    B, Hq, Hkv, D, P = dims.batch, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.page_size
+    B, Hq, D, P = dims.batch, dims.n_q_heads, dims.head_dim, dims.page_size
+    Hkv = sel_units(dims)  # per-(b, h) rows: query heads with per-query-head selection
     G, NW = Hq // Hkv, dims.hash_bits // 64
     NP = -(-dims.max_ctx // P)
 

@@ -56,6 +56,8 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
         return fail(HHR_E_DTYPE, "kv_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->kv_dtype);
     if (d->meta_dtype != HHR_F32 && d->meta_dtype != HHR_BF16)
         return fail(HHR_E_DTYPE, "meta_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->meta_dtype);
+    if (d->per_head != 0 && d->per_head != 1)
+        return fail(HHR_E_RANGE, "per_head must be 0 or 1 (got %d)", d->per_head);
     if ((d->page_group != 0 && d->page_group != 1) || (d->hamming_group != 0 && d->hamming_group != 1))
         return fail(HHR_E_RANGE, "page_group (%d) and hamming_group (%d) must be 0 or 1", d->page_group,
                     d->hamming_group);
@@ -80,6 +82,8 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
     s.pg_min = d->page_group == 1;
     s.ham_mean = d->hamming_group == 1;
     s.Gh = s.ham_mean ? 1 : s.G;
+    s.share = 1;
+    s.per_head = d->per_head == 1;
     return HHR_OK;
 }
 
@@ -111,7 +115,8 @@ hhr_status hip_check(hipError_t e, const char* what) {
 // Common front half of the decode step and its stages.
 hhr_status prepare(const hhr_dims* dims, int max_keep, int top_k, void* workspace, size_t ws_bytes,
                    DecodeArgs& a) {
-    HHR_TRY(make_shape(dims, a.s));
+    HHR_TRY(make_shape(dims, a.sd));
+    a.s = selection_shape(a.sd);
     HHR_TRY(check_sel(a.s, max_keep, top_k));
     HHR_TRY(check_ptr(workspace, "workspace", 256));
     a.max_keep = max_keep;
@@ -267,15 +272,18 @@ hhr_status hhr_encode_cache(const hhr_dims* dims, const void* K, const float* R,
 }
 
 size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, int32_t top_k) {
-    Shape s;
-    if (make_shape(dims, s) != HHR_OK || check_sel(s, max_keep_pages, top_k) != HHR_OK) return 0;
+    Shape d;
+    if (make_shape(dims, d) != HHR_OK) return 0;
+    const Shape s = selection_shape(d);
+    if (check_sel(s, max_keep_pages, top_k) != HHR_OK) return 0;
     return ws_layout(s, max_keep_pages, top_k).total;
 }
 
 hhr_status hhr_decode_workspace_layout(const hhr_dims* dims, int32_t max_keep_pages, int32_t top_k,
                                        hhr_workspace_layout* layout) {
-    Shape s;
-    HHR_TRY(make_shape(dims, s));
+    Shape d;
+    HHR_TRY(make_shape(dims, d));
+    const Shape s = selection_shape(d);
     HHR_TRY(check_sel(s, max_keep_pages, top_k));
     if (!layout) return fail(HHR_E_NULL, "layout is NULL");
     const WsLayout l = ws_layout(s, max_keep_pages, top_k);
@@ -391,10 +399,12 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
         p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
         p.n_counters = a.lay.n_clear;
-        HHR_TRY(hip_check(launch_project(a.s, p, st), "append + qprep launch"));
+        p.qmean = a.s.ham_mean;
+        p.qs_unit = a.s.share > 1;
+        HHR_TRY(hip_check(launch_project(a.sd, p, st), "append + qprep launch"));
     } else {
         if (max_append > 0)
-            HHR_TRY(hip_check(launch_encode(a.s, K, R, W, append_start, append_count, max_append, meta, codes, st),
+            HHR_TRY(hip_check(launch_encode(a.sd, K, R, W, append_start, append_count, max_append, meta, codes, st),
                               "encode launch"));
         HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
     }
@@ -511,6 +521,8 @@ namespace {
 // Common front of the TopK (Oracle) entry points.
 hhr_status topk_prepare(const hhr_dims* dims, int top_k, void* workspace, size_t workspace_bytes, TopkArgs& a) {
     HHR_TRY(make_shape(dims, a.d.s));
+    a.d.s.per_head = false;  // the TopK step always shares one selection per KV head
+    a.d.sd = a.d.s;
     if (top_k < 1 || top_k > (1 << 24)) return fail(HHR_E_RANGE, "top_k must be in 1..2^24 (got %d)", top_k);
     HHR_TRY(check_ptr(workspace, "workspace", 256));
     topk_layout(a.d.s, top_k, a.d.lay, a.tl);

@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
                                                      const int32_t* __restrict__ k_eff, float* __restrict__ part_o,
                                                      float* __restrict__ part_ml, uint32_t* __restrict__ counters,
                                                      float* __restrict__ out, int Hq, int Hkv, int T, int top_k,
-                                                     int n_splits, int stride, float scale) {
+                                                     int n_splits, int stride, float scale, int share) {
     constexpr int NI = 8;                     // entries per row
     constexpr int CH = 16 * NI;               // entries per block (4 waves x 4 rows)
     static_assert(CH == kAttnChunk, "split size");
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
         tj = (tj < 0 || tj >= T) ? 0 : tj;
         t[j] = tj;
     }
-    const int64_t kvb = bh * T;
+    const int64_t kvb = ((int64_t)b * (Hkv / share) + h / share) * T;  // rows of the unit's data head
     uint32_t kw[NI][NWD], vw[NI][NWD];
 #pragma unroll
     for (int j = 0; j < NI; ++j) load_slice<D, BF16>(K, kvb + t[j], sub, kw[j]);
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     const uint32_t* __restrict__ cum, const uint32_t* __restrict__ ghist, const int32_t* __restrict__ seq_len,
     int32_t* __restrict__ sel, int32_t* __restrict__ k_eff_out, float* __restrict__ part_o,
     float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out, int Hq, int Hkv, int T,
-    int P, int max_keep, int top_k, int S, int stride, int nbins, float scale) {
+    int P, int max_keep, int top_k, int S, int stride, int nbins, float scale, int share) {
     constexpr int NT = kCompactThreads;
     constexpr int NR = NT / 16;               // 16-lane rows
     constexpr int SPT = kCompactSlots / NT;   // slots per thread
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
 
     // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
     const int L = clamp_len(seq_len[b], T);
-    const int64_t kvb = bh * T;
+    const int64_t kvb = ((int64_t)b * (Hkv / share) + h / share) * T;  // rows of the unit's data head
     uint32_t qw[G][NWD];  // this lane's slice of each query, raw
 #pragma unroll
     for (int i = 0; i < G; ++i) load_slice<D, BF16>(Q, q0 + i, sub, qw[i]);
@@ -746,7 +746,7 @@ hipError_t attend_g(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((attend_kernel<D, BF16, G>), grid, dim3(256), 0, st, a.Q, a.K, a.V, a.sel,
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.k_eff), po, pml,
                        reinterpret_cast<uint32_t*>(a.ws + a.lay.counters), a.out, s.Hq, s.Hkv, s.T, a.sel_cap,
-                       a.lay.n_splits, a.lay.part_splits, a.scale);
+                       a.lay.n_splits, a.lay.part_splits, a.scale, s.share);
     return hipGetLastError();
 }
 
@@ -779,7 +779,7 @@ hipError_t compact_g(const DecodeArgs& a, hipStream_t st) {
                        reinterpret_cast<const uint16_t*>(a.ws + a.lay.ham),
                        reinterpret_cast<const uint32_t*>(a.ws + a.lay.kcum), counters + a.lay.ghist_off, a.seq_len,
                        a.sel, reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), po, pml, counters, a.out, s.Hq, s.Hkv,
-                       s.T, s.P, a.max_keep, a.top_k, S, a.lay.part_splits, a.lay.nbins, a.scale);
+                       s.T, s.P, a.max_keep, a.top_k, S, a.lay.part_splits, a.lay.nbins, a.scale, s.share);
     return hipGetLastError();
 }
 

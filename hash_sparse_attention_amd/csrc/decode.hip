@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
-                                                         int64_t NPB, int64_t NPmax, int pg_min) {
+                                                         int64_t NPB, int64_t NPmax, int pg_min, int share) {
     constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
     using V4 = typename std::conditional<M16, uint4, float4>::type;
@@ -86,7 +86,8 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     __syncthreads();
     if (p >= NP) return;
 
-    const V4* mp = reinterpret_cast<const V4*>(meta) + (bh * NPB + p / 64) * NJ * 64 + (p & 63);
+    const int64_t bhd = (int64_t)b * (Hkv / share) + h / share;  // the unit's data head
+    const V4* mp = reinterpret_cast<const V4*>(meta) + (bhd * NPB + p / 64) * NJ * 64 + (p & 63);
     double acc[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) acc[i] = 0.0;
@@ -140,7 +141,7 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
                        reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax,
-                       s.pg_min ? 1 : 0);
+                       s.pg_min ? 1 : 0, s.share);
     return hipGetLastError();
 }
 
@@ -172,7 +173,9 @@ hipError_t launch_qprep(const DecodeArgs& a, hipStream_t st) {
     p.q_split = reinterpret_cast<double*>(a.ws + a.lay.q_split);
     p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
     p.n_counters = a.lay.n_clear;
-    return launch_project(a.s, p, st);
+    p.qmean = a.s.ham_mean;
+    p.qs_unit = a.s.share > 1;
+    return launch_project(a.sd, p, st);  // per KV head of the cache
 }
 
 hipError_t launch_page_bounds(const DecodeArgs& a, hipStream_t st) {

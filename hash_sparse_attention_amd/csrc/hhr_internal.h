@@ -21,7 +21,24 @@ struct Shape {
     bool pg_min;        // page score = min over the group (else max)
     bool ham_mean;      // Hamming against the group's mean-query code (else summed over the group)
     int Gh;             // query codes per KV head in the Hamming stage: 1 with ham_mean, else G
+    int share;          // selection units per data head: 1, or G with per-query-head selection
+                        // (then Hkv counts units, G = 1, and a unit's data head is unit / share)
+    bool per_head;      // per-query-head selection was asked for
 };
+
+// The shape the selection stages run on: with per-query-head selection one
+// unit per query head (Hkv := Hq, G := 1), reading data head unit / share.
+inline Shape selection_shape(const Shape& d) {
+    if (!d.per_head || d.G == 1) return d;
+    Shape s = d;
+    s.share = d.G;
+    s.Hkv = d.Hq;
+    s.G = 1;
+    s.Gh = 1;
+    s.ham_mean = false;  // the mean of one query is that query
+    s.pg_min = false;    // the min over one head is that head's bound
+    return s;
+}
 
 // Attention keys handled by one block (one split) of the attend kernel.
 constexpr int kAttnChunk = 128;
@@ -59,7 +76,8 @@ hipError_t launch_encode(const Shape& s, const void* K, const float* R, const fl
                          hipStream_t stream);
 
 struct DecodeArgs {
-    Shape s;
+    Shape s;   // selection shape (units)
+    Shape sd;  // data shape (the KV heads of the cache): projection and append
     int max_keep, top_k;
     int sel_cap;  // entries per (b, h) row of sel: top_k plus the forced keys' room
     float scale;
@@ -104,6 +122,8 @@ struct ProjectArgs {
     double* q_split;
     uint32_t* counters;
     int n_counters;
+    bool qmean;    // also code the group's mean query into code_qm (queries only)
+    bool qs_unit;  // q_split per query head [B][Hq][D][1][2] (per-query-head selection)
 };
 // Appends of at most this many keys per sequence go through the projection kernel.
 constexpr int kAppendMax = 64;

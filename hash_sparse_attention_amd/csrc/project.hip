@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     int max_count, int key_blocks, float* __restrict__ meta, uint64_t* __restrict__ codes,
     float* __restrict__ q_rot, uint64_t* __restrict__ code_q, uint64_t* __restrict__ code_qm,
     double* __restrict__ q_split, uint32_t* __restrict__ counters, int n_counters, int Hq, int Hkv, int G, int T,
-    int P, int64_t NPB, bool meta16, bool qmean) {
+    int P, int64_t NPB, bool meta16, bool qmean, bool qs_unit) {
     constexpr int RG = (D + NB) / 64;  // row groups of [R_h; W_h]
     constexpr int NW = NB / 64;
     constexpr int LDM = D + 4;         // padded row stride of the tile (floats)
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
             const int64_t qi = q0 + v;
             if (rot) {
                 q_rot[qi * D + row] = a;
-                double* qsp = q_split + ((bh * D + row) * G + v) * 2;
+                double* qsp = q_split + (qs_unit ? (qi * D + row) : ((bh * D + row) * G + v)) * 2;
                 qsp[0] = a >= 0.f ? (double)a : 0.0;
                 qsp[1] = a < 0.f ? (double)a : 0.0;
             } else {
@@ -207,7 +207,7 @@ hipError_t project_t(const Shape& s, const ProjectArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((project_kernel<D, NB, BF16, KEYS, QUERIES>), dim3(s.Hkv, s.B, blocks),
                        dim3(kProjWaves * 64), 0, st, a.Q, a.K, a.R, a.W, a.start, a.count, a.max_count, key_blocks,
                        a.meta, a.codes, a.q_rot, a.code_q, a.code_qm, a.q_split, a.counters, a.n_counters, s.Hq,
-                       s.Hkv, s.G, s.T, s.P, s.NPB, s.meta16, a.queries && s.ham_mean);
+                       s.Hkv, s.G, s.T, s.P, s.NPB, s.meta16, a.queries && a.qmean, a.qs_unit);
     return hipGetLastError();
 }
 

@@ -719,10 +719,10 @@ __device__ __forceinline__ void keys_half(SelShared& sh, const uint64_t* __restr
                                           bool list_in_lds, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
                                           int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum,
                                           uint32_t* __restrict__ ghist, int split, int S, int b, int h, int64_t bh,
-                                          int Gh, int T, int P, int L, int max_keep, int top_k, int nsink,
-                                          int window) {
+                                          int64_t bhd, int Gh, int T, int P, int L, int max_keep, int top_k,
+                                          int nsink, int window) {
     if (!KEYS) return;
-    const uint64_t* ck = codes + bh * (int64_t)T * NW;
+    const uint64_t* ck = codes + bhd * (int64_t)T * NW;  // the unit's data head
     const uint64_t* cq = code_q + bh * Gh * NW;  // the group's Gh query codes
     uint16_t* hm = ham + bh * (int64_t)max_keep * P;
     const int NBINS = Gh * NW * 64 + 1;
@@ -758,10 +758,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
     int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
-    int max_keep, int top_k, int nsink, int window) {
+    int max_keep, int top_k, int nsink, int window, int share) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t bhd = (int64_t)b * (Hkv / share) + h / share;  // the unit's data head
     uint64_t pre[kRun];  // unused here: the general page select loads its chunks itself
     const int L = clamp_len(seq_len[b], T);
     const int NP = (int)n_pages_of(L, P);
@@ -786,8 +787,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         __syncthreads();
     }
-    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh, Gh,
-                        T, P, L, max_keep, top_k, nsink, window);
+    keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh,
+                        bhd, Gh, T, P, L, max_keep, top_k, nsink, window);
     if (KEYS && S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
 }
 
@@ -801,10 +802,11 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
     int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
-    int max_keep, int top_k, int nsink, int window) {
+    int max_keep, int top_k, int nsink, int window, int share) {
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t bhd = (int64_t)b * (Hkv / share) + h / share;  // the unit's data head
     const double* scp = score + bh * NPmax;
     double raw[RUN];
 #pragma unroll
@@ -824,7 +826,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     __syncthreads();
     if (KEYS) {  // max_keep <= kListLds here, so the page list is in LDS
         const int NBINS = Gh * NW * 64 + 1;
-        select_keys_block<NW, true>(codes + bh * (int64_t)T * NW, code_q + bh * Gh * NW, Gh,
+        select_keys_block<NW, true>(codes + bhd * (int64_t)T * NW, code_q + bh * Gh * NW, Gh,
                                     pl, np, L, P, max_keep, top_k, ham + bh * (int64_t)max_keep * P,
                                     sel + bh * ((int64_t)top_k + nsink + window), k_eff_out + bh, sh, split, S,
                                     cum + bh * (int64_t)S * NBINS, ghist + bh * (int64_t)NBINS, nsink, window);
@@ -845,7 +847,7 @@ hipError_t select_launch(Kernel kernel, const DecodeArgs& a, int S, hipStream_t 
                        reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), reinterpret_cast<uint32_t*>(a.ws + a.lay.kcum),
                        reinterpret_cast<uint32_t*>(a.ws + a.lay.counters) + a.lay.ghist_off, po, po + n_po,
                        a.lay.part_splits, s.D, S, s.G, s.Gh, s.Hq, s.Hkv, s.T, s.P, s.NPmax, a.max_keep, a.top_k,
-                       s.nsink, s.window);
+                       s.nsink, s.window, s.share);
     return hipGetLastError();
 }
 

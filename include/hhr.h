@@ -96,7 +96,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 5
+#define HHR_ABI_VERSION 6
 
 typedef enum {
     HHR_OK = 0,
@@ -133,6 +133,12 @@ typedef struct {
     int32_t hamming_group; /* decode variant: 0 = distance summed over the
                               group's query codes (default), 1 = distance to
                               the code of the group's mean query           */
+    int32_t per_head;      /* decode variant: 0 = one selection per KV head,
+                              shared by its G query heads (default); 1 = one
+                              selection per query head: every per-(b, h)
+                              workspace row and sel_idx row is then per
+                              query head ([B][Hq]...), as if each KV head
+                              were repeated for its G query heads          */
 } hhr_dims;
 
 /* Bytes of the meta and codes buffers for these dims (0 if the dims are invalid). */

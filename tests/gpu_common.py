@@ -27,14 +27,15 @@ def gpu_dims(wl: Workload):
     import hash_sparse_attention_amd as hsa
     return hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                          wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
-                         local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group)
+                         local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group,
+                         per_head=wl.per_head)
 
 
 def oracle_dims(wl: Workload):
     import oracle
     return oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                        wl.dtype == "bf16", wl.meta_bf16, wl.sink_tokens, wl.local_window, wl.page_group,
-                       wl.hamming_group)
+                       wl.hamming_group, wl.per_head)
 
 
 def run_gpu(wl: Workload, d: dict, dev, keep=None, max_keep=None, top_k=None, seq=None, chunks=None,
@@ -62,7 +63,7 @@ def run_gpu(wl: Workload, d: dict, dev, keep=None, max_keep=None, top_k=None, se
     ws.fill_(0xA5)
     out = torch.full((wl.batch, wl.n_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device=dev)
     cap = hsa.sel_cap(dims, top_k)
-    sel = torch.full((wl.batch, wl.n_kv_heads, cap), -7, dtype=torch.int32, device=dev) if use_sel_out else None
+    sel = torch.full((wl.batch, hsa.sel_units(dims), cap), -7, dtype=torch.int32, device=dev) if use_sel_out else None
     hsa.decode_step(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], meta, codes, seq_t, keep_t, max_keep, top_k, out,
                     ws, sel_idx=sel, scale=scale)
     torch.cuda.synchronize()
@@ -105,6 +106,8 @@ def compare(wl: Workload, seq, g: dict, o: dict, batches=None, label=""):
             assert np.array_equal(g["codes"][b, h, :L], o["codes"][ob, h, :L]), f"codes {tag}"
             assert np.array_equal(g["meta"][b, h, :NP].view(np.uint32), o["meta"][ob, h, :NP].view(np.uint32)), \
                 f"meta {tag}"
+        for h in range(wl.n_q_heads if wl.per_head else wl.n_kv_heads):  # selection rows
+            tag = f"{label} b={b} unit={h}"
             assert np.array_equal(g["score"][b, h, :NP].view(np.uint64), o["score"][ob, h, :NP].view(np.uint64)), \
                 f"page scores {tag}"
             assert np.array_equal(g["pages"][b, h], o["pages"][ob, h]), f"pages {tag}"

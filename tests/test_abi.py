@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(hsa):
 
 def test_version_and_status_strings(hsa):
     L = hsa.lib()
-    assert L.hhr_abi_version() == 5
+    assert L.hhr_abi_version() == 6
     for code, name in hsa.STATUS.items():
         assert L.hhr_status_str(code).decode() == name
 

@@ -242,8 +242,8 @@ def test_qwen7b_b16_append_4096_sampled(dev):
 
 @pytest.mark.parametrize("meta_bf16,variant", [(False, {}), (True, {}),
                                                (False, dict(sink_tokens=3, local_window=40, hamming_group=1)),
-                                               (True, dict(page_group=1))],
-                         ids=["fp32_meta", "bf16_meta", "sinks_window_mean_code", "bf16_meta_min_page"])
+                                               (True, dict(page_group=1)), (False, dict(per_head=True))],
+                         ids=["fp32_meta", "bf16_meta", "sinks_window_mean_code", "bf16_meta_min_page", "per_head"])
 def test_decode_step_append_matches_oracle(dev, meta_bf16, variant):
     """hhr_decode_step_append (fused append + query projection) equals the oracle's single-shot encode +
     decode, for a 1-token append, a ragged multi-token append, and an append larger than the fused limit."""
@@ -267,7 +267,7 @@ def test_decode_step_append_matches_oracle(dev, meta_bf16, variant):
                          int(pre.max()), meta, codes)
         ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
         out = torch.empty((3, 12, 128), dtype=torch.float32, device=dev)
-        sel = torch.empty((3, 3, hsa.sel_cap(dims, wl.top_k)), dtype=torch.int32, device=dev)
+        sel = torch.empty((3, hsa.sel_units(dims), hsa.sel_cap(dims, wl.top_k)), dtype=torch.int32, device=dev)
         hsa.decode_step_append(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], meta, codes, to_dev(pre, dev),
                                to_dev(new, dev), int(new.max()), to_dev(seq, dev), to_dev(d["keep"], dev),
                                wl.max_keep, wl.top_k, out, ws, sel_idx=sel)
@@ -530,6 +530,28 @@ def test_lhp_only_many_candidates(dev, name, wl):
     """LHP-only (every page kept, so the Hamming stage ranks every key): more candidate slots than one
     select chunk, spread over up to 64 split blocks per head."""
     banner(f"LHP-only {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
+
+
+PER_HEAD = [
+    # one selection per query head (the group does not share)
+    ("tiny_per_head", WORKLOADS["tiny"].with_(per_head=True)),
+    ("g7_per_head_ragged", Workload("ph1", 180, 3, 14, 2, 128, 2000, 16, 128, 10, 150, "bf16", outliers=2,
+                                    ragged=(1, 2000), per_head=True)),
+    ("g8_per_head_bf16meta_sinks", Workload("ph2", 181, 2, 16, 2, 64, 3000, 64, 64, 30, 400, "bf16",
+                                            meta_bf16=True, sink_tokens=2, local_window=33, per_head=True)),
+    ("g4_per_head_mean_min_fp32", Workload("ph3", 182, 2, 8, 2, 64, 1500, 8, 128, 15, 90, "fp32",
+                                           ragged=(700, 1500), per_head=True, page_group=1, hamming_group=1)),
+    ("llama8b_32k_per_head", WORKLOADS["llama8b_32k"].with_(per_head=True)),
+]
+
+
+@pytest.mark.parametrize("name,wl", PER_HEAD, ids=[p[0] for p in PER_HEAD])
+def test_per_query_head_selection_parity(dev, name, wl):
+    banner(f"per-head selection {name}")
     d = make_layer(wl)
     g = run_gpu(wl, d, dev)
     o = run_oracle(wl, d)
