@@ -47,7 +47,8 @@ def algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total):
         L = int(seq[b])
         NP = -(-L // P)
         cand = int(keep[b]) * P  # every kept page is full at these lengths
-        tot += Hkv * (NP * 2 * D * mb + cand * nb // 8)
+        units = Hq if wl.per_head else Hkv  # selections: each reads its head's metadata and candidates' codes
+        tot += units * (NP * 2 * D * mb + cand * nb // 8)
     tot += k_eff_total * (2 * D * e + 4)                       # gathered K and V rows + indices
     tot += Hkv * (D * D + nb * D) * 4                          # R_h, W_h
     tot += B * Hq * D * (e + 4)                                # q in, out
@@ -57,7 +58,8 @@ def algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total):
 
 def page_bound_bytes_per_launch(wl, seq):
     """Per page: 2*D stored (max, min) read (fp32, or bf16 metadata) + one fp64 score written."""
-    pages = sum(-(-int(L) // wl.page_size) for L in seq) * wl.n_kv_heads
+    units = wl.n_q_heads if wl.per_head else wl.n_kv_heads  # selections, each streaming its head's metadata
+    pages = sum(-(-int(L) // wl.page_size) for L in seq) * units
     return pages * (2 * wl.head_dim * (2 if wl.meta_bf16 else 4) + 8), pages
 
 

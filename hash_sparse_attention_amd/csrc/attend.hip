@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
         tj = (tj < 0 || tj >= T) ? 0 : tj;
         t[j] = tj;
     }
-    const int64_t kvb = ((int64_t)b * (Hkv / share) + h / share) * T;  // rows of the unit's data head
+    const int64_t kvb = data_head(b, h, Hkv, share) * T;  // rows of the unit's data head
     uint32_t kw[NI][NWD], vw[NI][NWD];
 #pragma unroll
     for (int j = 0; j < NI; ++j) load_slice<D, BF16>(K, kvb + t[j], sub, kw[j]);
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
 
     // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
     const int L = clamp_len(seq_len[b], T);
-    const int64_t kvb = ((int64_t)b * (Hkv / share) + h / share) * T;  // rows of the unit's data head
+    const int64_t kvb = data_head(b, h, Hkv, share) * T;  // rows of the unit's data head
     uint32_t qw[G][NWD];  // this lane's slice of each query, raw
 #pragma unroll
     for (int i = 0; i < G; ++i) load_slice<D, BF16>(Q, q0 + i, sub, qw[i]);

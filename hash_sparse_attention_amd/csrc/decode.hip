@@ -64,12 +64,12 @@ __device__ __forceinline__ void bound_batch16(const uint4 (&v)[U], const double2
     }
 }
 
-template <int D, int G, int U, bool M16>
+template <int D, int G, int U, bool M16, bool PGMIN>
 __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
-                                                         int64_t NPB, int64_t NPmax, int pg_min, int share) {
+                                                         int64_t NPB, int64_t NPmax, int share) {
     constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
     using V4 = typename std::conditional<M16, uint4, float4>::type;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     __syncthreads();
     if (p >= NP) return;
 
-    const int64_t bhd = (int64_t)b * (Hkv / share) + h / share;  // the unit's data head
+    const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     const V4* mp = reinterpret_cast<const V4*>(meta) + (bhd * NPB + p / 64) * NJ * 64 + (p & 63);
     double acc[G];
 #pragma unroll
@@ -120,13 +120,8 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
         asm volatile("" ::: "memory");
     }
     double S = acc[0];  // the group's max, or its min (a variant)
-    if (pg_min) {
 #pragma unroll
-        for (int i = 1; i < G; ++i) S = acc[i] < S ? acc[i] : S;
-    } else {
-#pragma unroll
-        for (int i = 1; i < G; ++i) S = acc[i] > S ? acc[i] : S;
-    }
+    for (int i = 1; i < G; ++i) S = PGMIN ? (acc[i] < S ? acc[i] : S) : (acc[i] > S ? acc[i] : S);
     if (S == 0.0) S = 0.0;
     score[bh * NPmax + p] = S;
 }
@@ -137,11 +132,12 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
     const dim3 grid((unsigned)((s.NPmax + 255) / 256), s.Hkv, s.B);
     // Loads per lane per batch (two batches in flight), measured best per metadata type.
-    auto kern = s.meta16 ? page_bound_kernel<D, G, 8, true> : page_bound_kernel<D, G, 4, false>;
+    auto kern = s.meta16 ? (s.pg_min ? page_bound_kernel<D, G, 8, true, true> : page_bound_kernel<D, G, 8, true, false>)
+                         : (s.pg_min ? page_bound_kernel<D, G, 4, false, true> : page_bound_kernel<D, G, 4, false, false>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
                        reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax,
-                       s.pg_min ? 1 : 0, s.share);
+                       s.share);
     return hipGetLastError();
 }
 

@@ -178,7 +178,13 @@ __device__ __forceinline__ uint32_t topk_bin(double z) {
 
 __device__ __forceinline__ int clamp_len(int L, int T) { return L < 0 ? 0 : (L > T ? T : L); }
 
-__device__ __forceinline__ int64_t n_pages_of(int64_t L, int P) { return (L + P - 1) / P; }
+// P is a power of two (validated on the host): a shift, not a 64-bit division.
+__device__ __forceinline__ int64_t n_pages_of(int64_t L, int P) { return (L + P - 1) >> __builtin_ctz((unsigned)P); }
+
+// Data head of selection unit h of sequence b (share > 1 only with per-query-head selection).
+__device__ __forceinline__ int64_t data_head(int b, int h, int Hunits, int share) {
+    return share == 1 ? (int64_t)b * Hunits + h : (int64_t)b * (Hunits / share) + h / share;
+}
 
 // ---- wave64 primitives on DPP (row shifts within 16-lane rows, then row
 // broadcasts across rows).  A DPP step is a VALU op: far cheaper than a

@@ -762,7 +762,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
-    const int64_t bhd = (int64_t)b * (Hkv / share) + h / share;  // the unit's data head
+    const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     uint64_t pre[kRun];  // unused here: the general page select loads its chunks itself
     const int L = clamp_len(seq_len[b], T);
     const int NP = (int)n_pages_of(L, P);
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     __shared__ SelShared sh;
     const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
-    const int64_t bhd = (int64_t)b * (Hkv / share) + h / share;  // the unit's data head
+    const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     const double* scp = score + bh * NPmax;
     double raw[RUN];
 #pragma unroll
