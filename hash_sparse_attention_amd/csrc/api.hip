@@ -149,7 +149,7 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
         return o;
     };
     const size_t BH = (size_t)s.B * s.Hkv, BQ = (size_t)s.B * s.Hq;
-    const bool forced = s.nsink + s.window > 0;  // sinks / window: the single-block key select
+    const size_t forced = (size_t)s.nsink + s.window;  // sink / window keys block 0 of a split also attends
     const int sel_cap = top_k + s.nsink + s.window;
     l.n_splits = (sel_cap + kAttnChunk - 1) / kAttnChunk;
     l.q_rot = take(BQ * s.D * sizeof(float));
@@ -170,13 +170,14 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     const size_t slots = (size_t)max_keep * s.P;
     const size_t BHs = BH > 0 ? BH : 1;
     int S = 1;
-    if (!forced && max_keep <= kSelListLds) {
+    if (max_keep <= kSelListLds && forced < (size_t)kCompactSlots) {
         size_t want = (slots + 511) / 512, cap = 256 / BHs;
         want = want < cap ? want : cap;
-        const size_t need = (slots + kCompactSlots - 1) / kCompactSlots;
+        const size_t room = kCompactSlots - forced;  // candidate slots a block can take
+        const size_t need = (slots + room - 1) / room;
         want = want < need ? need : want;
         want = want > 64 ? 64 : want;
-        if (want >= 2 && (slots + want - 1) / want <= (size_t)kCompactSlots) S = (int)want;
+        if (want >= 2 && (slots + want - 1) / want <= room) S = (int)want;
     }
     l.sel_splits = S;
     l.nbins = s.Gh * s.NB + 1;

@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     const uint32_t* __restrict__ cum, const uint32_t* __restrict__ ghist, const int32_t* __restrict__ seq_len,
     int32_t* __restrict__ sel, int32_t* __restrict__ k_eff_out, float* __restrict__ part_o,
     float* __restrict__ part_ml, uint32_t* __restrict__ counters, float* __restrict__ out, int Hq, int Hkv, int T,
-    int P, int max_keep, int top_k, int S, int stride, int nbins, float scale, int share) {
+    int P, int max_keep, int top_k, int S, int stride, int nbins, float scale, int share, int nsink, int window) {
     constexpr int NT = kCompactThreads;
     constexpr int NR = NT / 16;               // 16-lane rows
     constexpr int SPT = kCompactSlots / NT;   // slots per thread
@@ -635,7 +635,13 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     const int packed = block_excl_scan<NT>((n_lt << 16) | n_eq, scan, tot);
     int eq_rank = packed & 0xffff;
     int pos = (packed >> 16) + (eq_rank < incl ? eq_rank : incl);
-    int32_t* so = sel + bh * (int64_t)top_k;
+    // Forced keys (sink tokens, local window): [0, s_end) and [w_start, L),
+    // listed around the ranked ones; block 0 also attends them.
+    const int L = clamp_len(seq_len[b], T);
+    const int s_end = nsink < L ? nsink : L;
+    const int w_start = L - window > s_end ? L - window : s_end;
+    const int nforced = s_end + (L - w_start);
+    int32_t* so = sel + bh * ((int64_t)top_k + nsink + window);
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
         bool in = hv[k] < hstar;
@@ -644,20 +650,25 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             ++eq_rank;
         }
         if (in) {
-            if (offset + pos < top_k) so[offset + pos] = tv[k];
+            if (offset + pos < top_k) so[s_end + offset + pos] = tv[k];
             list[pos] = tv[k];
             ++pos;
         }
     }
-    const int cnt = (tot >> 16) + ((tot & 0xffff) < incl ? (tot & 0xffff) : incl);
+    int cnt = (tot >> 16) + ((tot & 0xffff) < incl ? (tot & 0xffff) : incl);
     if (split == 0) {
-        for (int j = keff + tid; j < top_k; j += NT) so[j] = -1;
-        if (tid == 0) k_eff_out[bh] = keff;
+        const int listed = keff + nforced;
+        for (int j = tid; j < s_end; j += NT) so[j] = j;
+        for (int j = tid; j < L - w_start; j += NT) so[s_end + keff + j] = w_start + j;
+        for (int j = listed + tid; j < top_k + nsink + window; j += NT) so[j] = -1;
+        for (int j = tid; j < nforced && cnt + j < kCompactSlots; j += NT)
+            list[cnt + j] = j < s_end ? j : w_start + (j - s_end);
+        cnt = cnt + nforced < kCompactSlots ? cnt + nforced : kCompactSlots;  // the layout keeps it in range
+        if (tid == 0) k_eff_out[bh] = listed;
     }
     __syncthreads();
 
     // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
-    const int L = clamp_len(seq_len[b], T);
     const int64_t kvb = data_head(b, h, Hkv, share) * T;  // rows of the unit's data head
     uint32_t qw[G][NWD];  // this lane's slice of each query, raw
 #pragma unroll
@@ -779,7 +790,8 @@ hipError_t compact_g(const DecodeArgs& a, hipStream_t st) {
                        reinterpret_cast<const uint16_t*>(a.ws + a.lay.ham),
                        reinterpret_cast<const uint32_t*>(a.ws + a.lay.kcum), counters + a.lay.ghist_off, a.seq_len,
                        a.sel, reinterpret_cast<int32_t*>(a.ws + a.lay.k_eff), po, pml, counters, a.out, s.Hq, s.Hkv,
-                       s.T, s.P, a.max_keep, a.top_k, S, a.lay.part_splits, a.lay.nbins, a.scale, s.share);
+                       s.T, s.P, a.max_keep, a.top_k, S, a.lay.part_splits, a.lay.nbins, a.scale, s.share, s.nsink,
+                       s.window);
     return hipGetLastError();
 }
 
