@@ -314,7 +314,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus N > 1 is not supported", file=sys.stderr)
+        print("bench.py: the decode step is measured on exactly one GPU; --gpus N > 1 is not supported", file=sys.stderr)
         sys.exit(2)
     if args.mode == "topk":
         main_topk(args)

@@ -106,7 +106,7 @@ typedef enum {
     HHR_E_ALIGN = 4,       /* a pointer is not aligned as required          */
     HHR_E_WORKSPACE = 5,   /* workspace smaller than required               */
     HHR_E_RANGE = 6,       /* a scalar argument is out of range             */
-    HHR_E_UNSUPPORTED = 7, /* valid but not supported by this build         */
+    HHR_E_UNSUPPORTED = 7, /* valid but not supported by this library      */
     HHR_E_HIP = 8          /* a HIP launch failed                           */
 } hhr_status;
 
