@@ -1,0 +1,85 @@
+"""Host-side logic of bench.py, on the CPU: the byte model behind the roofline
+figures, the rule that counter-derived traffic is reported only for the kernel
+source it was measured on, the committed counter summaries against that model,
+and the one-GPU guard."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402  (imports no GPU code at module level)
+from synth.workloads import WORKLOADS  # noqa: E402
+
+
+def test_page_bound_bytes_per_launch():
+    """One page costs its 2*D stored bounds (4 or 2 bytes each) plus its fp64 score."""
+    wl = WORKLOADS["llama8b_128k"]
+    seq = [wl.ctx] * wl.batch
+    b, pages = bench.page_bound_bytes_per_launch(wl, seq)
+    assert pages == 8 * (131072 // 16)
+    assert b == pages * (2 * 128 * 4 + 8) == 67_633_152
+    b16, pages16 = bench.page_bound_bytes_per_launch(wl.with_(meta_bf16=True), seq)
+    assert pages16 == pages and b16 == pages * (2 * 128 * 2 + 8)
+    # One selection per query head streams its KV head's metadata once per query head.
+    bph, pph = bench.page_bound_bytes_per_launch(wl.with_(per_head=True), seq)
+    assert pph == 4 * pages and bph == 4 * b
+
+
+def test_page_count_rounds_partial_pages_up():
+    wl = WORKLOADS["mistral7b_b8"]  # page 32, 8 KV heads
+    _, pages = bench.page_bound_bytes_per_launch(wl, [1, 32, 33, 64])
+    assert pages == 8 * (1 + 1 + 2 + 2)
+
+
+def test_bf16_metadata_saves_exactly_half_the_bound_reads():
+    wl = WORKLOADS["llama8b_128k"]
+    seq, keep = [wl.ctx], [wl.max_keep]
+    full = bench.algorithmic_bytes_per_layer(wl, seq, keep, 4096 * 8)
+    half = bench.algorithmic_bytes_per_layer(wl.with_(meta_bf16=True), seq, keep, 4096 * 8)
+    n_pages = wl.ctx // wl.page_size
+    # The whole stream's bounds (8 heads) plus the appended page's bounds.
+    assert full - half == 8 * n_pages * 2 * 128 * 2 + 8 * 2 * 128 * 2
+
+
+def test_counter_traffic_only_for_the_profiled_source(tmp_path):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel, first version\n")
+    rec = tmp_path / "pmc.json"
+    rec.write_text(json.dumps({"source_sha256_16": bench.source_digest(str(src)), "bytes_per_launch": 1234.5}))
+    assert bench.pmc_traffic(str(rec), str(src)) == 1234.5
+    src.write_text("// kernel, edited\n")
+    assert bench.pmc_traffic(str(rec), str(src)) is None
+    assert bench.pmc_traffic(str(tmp_path / "absent.json"), str(src)) is None
+    rec.write_text("not json")
+    assert bench.pmc_traffic(str(rec), str(src)) is None
+
+
+@pytest.mark.parametrize("path", [bench.PMC_FILE, bench.TOPK_PMC_FILE])
+def test_committed_counter_summaries_against_the_byte_model(path):
+    """Each committed summary states the algorithmic bytes of the launch it
+    measured (the same model bench.py uses) and HBM traffic within 15% above it."""
+    rec = json.load(open(path))
+    wl = WORKLOADS["llama8b_128k"]
+    if "page_bound" in rec["kernel"]:
+        alg, _ = bench.page_bound_bytes_per_launch(wl, [wl.ctx])
+    else:  # one fp64 logit written per key of K (bf16 keys)
+        keys = wl.n_kv_heads * wl.ctx
+        alg = keys * (wl.head_dim * 2 + 8)
+    assert rec["algorithmic_bytes_per_launch"] == alg
+    assert rec["fetch_bytes"] + rec["write_bytes"] == pytest.approx(rec["bytes_per_launch"])
+    assert 1.0 <= rec["bytes_per_launch"] / alg < 1.15
+    assert len(rec["source_sha256_16"]) == 16 and rec["command"]
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                       timeout=120, env={**os.environ, **env})
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
