@@ -140,7 +140,6 @@ def main_topk(args):
     import torch
 
     import hash_sparse_attention_amd as hsa
-    import oracle
     from synth import WORKLOADS, make_layer_torch
 
     wl = WORKLOADS[args.workload]
@@ -259,7 +258,8 @@ def main_topk(args):
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline:  # the CPU baseline leg: the only place this mode touches the oracle
+        import oracle
         d0 = layers[0]
         host = {k: d0[k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ("Q", "K", "V")}
         od = oracle.Dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,

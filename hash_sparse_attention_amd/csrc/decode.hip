@@ -22,7 +22,8 @@ namespace {
 //
 // The order of the sum ties each page to one lane, so a launch has one wave
 // per SIMD at 64K pages; the stream stays busy because every lane keeps the
-// next batch of U float4 loads in flight while it sums the current one.  The
+// next batch of U 16-byte loads in flight while it sums the current one.  The
+// loads carry the nontemporal hint: every metadata line is read once.  The
 // query terms are staged once per block in LDS and read as broadcasts.
 template <int G, int U>
 __device__ __forceinline__ void bound_batch(const float4 (&v)[U], const double2* __restrict__ qs, int j0,
@@ -99,7 +100,11 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     V4 A[U], B[U];
     auto load = [&](V4 (&v)[U], int k) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = mp[(int64_t)(k * U + u) * 64];
+        for (int u = 0; u < U; ++u) {
+            const u32x4 r = load_stream16(mp + (int64_t)(k * U + u) * 64);
+            if constexpr (M16) v[u] = make_uint4(r.x, r.y, r.z, r.w);
+            else v[u] = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w));
+        }
     };
     load(A, 0);
     asm volatile("" ::: "memory");

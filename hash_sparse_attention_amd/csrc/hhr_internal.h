@@ -150,6 +150,18 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t stream);  // collec
 
 // ---------------------------------------------------------------- device helpers
 
+// A native vector of four 32-bit words: the compiler keeps it in registers
+// (the HIP struct vector types can go to scratch when indexed in a rolled loop).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the nontemporal hint, for data a launch streams exactly
+// once: the page metadata of the bound pass and the keys of the exact-logit
+// pass.  Measured on gfx950 at 128K context, the bound stream ran 4.7 TB/s
+// with it against 4.2 TB/s with plain loads, the logit stream 4.8 against 4.4.
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // Outward rounding of page statistics to bf16 (bit patterns): the smallest

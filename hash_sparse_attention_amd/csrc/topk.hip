@@ -47,7 +47,6 @@ __global__ __launch_bounds__(256) void topk_prep_kernel(const void* __restrict__
 // current one is summed.
 constexpr int kLogitResident = 4 * 256;  // blocks the GPU holds at once (LDS: 4 per CU)
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a native vector: kept in registers
 
 // The 8 16-byte pieces this lane loads of one 64-row tile chunk: rows
 // t0 + 8j + lrow, bytes [c*128 + lslot*16, +16) of each row.
@@ -58,7 +57,7 @@ __device__ __forceinline__ void tile_load(u32x4 (&v)[8], const char* __restrict_
     for (int j = 0; j < 8; ++j) {
         int t = t0 + 8 * j + lrow;
         t = t < T ? t : T - 1;  // rows past the capacity are never used
-        v[j] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)t * RB + c * 128 + lslot * 16);
+        v[j] = load_stream16(kbase + (int64_t)t * RB + c * 128 + lslot * 16);  // K is read once
     }
 }
 
