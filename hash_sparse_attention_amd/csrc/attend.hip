@@ -46,7 +46,7 @@ __device__ __forceinline__ void load_slice(const void* base, int64_t row, int su
     } else {
 #pragma unroll
         for (int x = 0; x < NWD; x += 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(p + x);
+            const u32x4 v = load_stream16(p + x);  // a gathered row is read once
             w[x] = v.x; w[x + 1] = v.y; w[x + 2] = v.z; w[x + 3] = v.w;
         }
     }

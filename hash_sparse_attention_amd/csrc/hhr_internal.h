@@ -154,10 +154,15 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t stream);  // collec
 // (the HIP struct vector types can go to scratch when indexed in a rolled loop).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte load with the nontemporal hint, for data a launch streams exactly
-// once: the page metadata of the bound pass and the keys of the exact-logit
-// pass.  Measured on gfx950 at 128K context, the bound stream ran 4.7 TB/s
-// with it against 4.2 TB/s with plain loads, the logit stream 4.8 against 4.4.
+// 16-byte load with the nontemporal hint, for data a step reads exactly once:
+// the page metadata of the bound pass, the keys of the exact-logit pass, the
+// candidates' codes, the gathered K/V rows and the projection rows.  Measured
+// on gfx950 at 128K context: the bound stream ran 4.7 TB/s with it against
+// 4.2 TB/s with plain loads, the logit stream 4.8 against 4.4, and the hinted
+// code loads and row gathers took the decode step from 53.4 to 51.4 us per
+// layer.  Data the previous launch wrote is read with plain loads (hinting
+// the select outputs that compaction reads back made the step slower); the
+// page scores are the one exception, measured slightly faster hinted.
 __device__ __forceinline__ u32x4 load_stream16(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }

@@ -89,7 +89,10 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     constexpr int F4PT = 64 * D / 4 / (kProjWaves * 64);
     float4 mv[F4PT];
 #pragma unroll
-    for (int k = 0; k < F4PT; ++k) mv[k] = mg[tid + k * kProjWaves * 64];
+    for (int k = 0; k < F4PT; ++k) {  // the rows are read once per step
+        const u32x4 r = load_stream16(mg + tid + k * kProjWaves * 64);
+        mv[k] = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w));
+    }
     const void* src = qblock ? Q : K;
     if (BF16) {
         const uint32_t* x2 = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(src) + xrow0 * D);

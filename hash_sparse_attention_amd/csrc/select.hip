@@ -485,7 +485,7 @@ __device__ __forceinline__ int select_pages_fast(const double* __restrict__ sc, 
 template <int NW>
 __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t, uint64_t (&kc)[NW]) {
     if constexpr (NW == 2) {
-        const uint4 v = *reinterpret_cast<const uint4*>(ck + (int64_t)t * 2);
+        const u32x4 v = load_stream16(ck + (int64_t)t * 2);  // each candidate's code is read once
         kc[0] = ((uint64_t)v.y << 32) | v.x;
         kc[1] = ((uint64_t)v.w << 32) | v.z;
     } else {
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
 #pragma unroll
     for (int k = 0; k < RUN; ++k) {  // every load issued, unconditionally (clamped), before any use
         const int64_t i = (int64_t)k * kSelThreads + threadIdx.x;
-        raw[k] = scp[i < NPmax ? i : NPmax - 1];
+        raw[k] = __builtin_nontemporal_load(scp + (i < NPmax ? i : NPmax - 1));  // measured faster hinted
     }
     const int L = clamp_len(seq_len[b], T);
     const int NP = (int)n_pages_of(L, P);
