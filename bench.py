@@ -142,7 +142,7 @@ def main_topk(args):
     import hash_sparse_attention_amd as hsa
     from synth import WORKLOADS, make_layer_torch
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[args.workload or "llama8b_128k"]
     if args.layers:
         wl = wl.with_(layers=args.layers)
     dev = torch.device("cuda:0")
@@ -282,12 +282,128 @@ def main_topk(args):
     print(json.dumps(line), flush=True)
 
 
+# fp32 vector peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2 (packed/dual issue) FMAs x 2 FLOP x 2.4 GHz.
+# Without packed fp32 ops (this library compiles them out) a lane retires one FMA per cycle: half of it.
+FP32_PEAK_TFLOPS = 157.3
+FP32_PEAK_UNPACKED_TFLOPS = 78.6
+
+
+def main_encode(args):
+    """hhr_encode_cache on the append of a chunk of new keys per sequence (default: the Qwen2.5-7B attention
+    shape, batch 16 at 128K context, 4096 new tokens per sequence): rotation, page max/min and codes of every
+    new key.  Bound by fp32 VALU (each key runs (D + b) canonical chains of D FMAs); the HBM bytes are reported
+    beside it.  CPU baseline: the oracle's encode of the same chunk on a bounded sample of sequences, which also
+    checks the GPU's codes and page bounds there bit for bit."""
+    import numpy as np
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    from synth import WORKLOADS, make_layer_torch
+
+    wl = WORKLOADS[args.workload or "qwen7b_b16"]
+    n_new = wl.append_tokens or 4096
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"encode mode, workload {wl.name}: B={wl.batch}, {wl.n_kv_heads} KV heads, ctx={wl.ctx}, "
+        f"append {n_new} tokens per sequence")
+    dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
+                         wl.dtype == "bf16", meta_bf16=wl.meta_bf16)
+    d = make_layer_torch(wl, 0, dev)
+    seq = np.asarray(d["seq_len_host"], np.int64)
+    new = np.minimum(seq, n_new).astype(np.int32)
+    pre = (seq - new).astype(np.int32)
+    meta, codes = hsa.alloc_cache(dims, dev)
+    start = torch.tensor(pre, dtype=torch.int32, device=dev)
+    count = torch.tensor(new, dtype=torch.int32, device=dev)
+    max_count = int(new.max())
+
+    def run():
+        hsa.encode_cache(dims, d["K"], d["R"], d["W"], start, count, max_count, meta, codes)
+
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        run()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) / args.steps * 1e3
+    D, nb, P = wl.head_dim, wl.hash_bits, wl.page_size
+    e = 2 if wl.dtype == "bf16" else 4
+    mb = 2 if wl.meta_bf16 else 4
+    keys = int(new.sum()) * wl.n_kv_heads
+    flops = keys * (D + nb) * D * 2
+    pages = int(sum(-(-int(s1) // P) - int(s0) // P for s0, s1 in zip(pre, seq))) * wl.n_kv_heads
+    hbm = keys * (D * e + nb // 8) + pages * 2 * D * mb + wl.n_kv_heads * (D + nb) * D * 4
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"{args.steps} launches: {us:.2f} us each, {tflops:.1f} TFLOP/s fp32, {hbm / (us * 1e-6) / 1e9:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:  # the CPU baseline leg: the only place this mode touches the oracle
+        import oracle
+        sample = [0, wl.batch - 1] if wl.batch > 1 else [0]
+        od = oracle.Dims(len(sample), wl.n_q_heads, wl.n_kv_heads, D, P, nb, wl.ctx, wl.dtype == "bf16",
+                         meta_bf16=wl.meta_bf16)
+        Kh = d["K"][sample].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        Rh, Wh = d["R"].cpu().numpy(), d["W"].cpu().numpy()
+        times = []
+        for _ in range(3):
+            om, oc = oracle.alloc_cache(od)
+            t0 = time.perf_counter()
+            oracle.encode(od, Kh, Rh, Wh, pre[sample], new[sample], om, oc)
+            times.append(time.perf_counter() - t0)
+        t = sorted(times)[1]
+        gm = hsa.meta_to_pages(meta, dims)[sample].cpu().numpy()
+        gc = codes.view(-1).cpu().numpy().view(np.uint64).reshape(wl.batch, wl.n_kv_heads, wl.ctx, nb // 64)[sample]
+        ok = True
+        for i in range(len(sample)):
+            s0, s1 = int(pre[sample[i]]), int(seq[sample[i]])
+            ok &= bool(np.array_equal(gc[i, :, s0:s1], oc[i, :, s0:s1]))
+            ok &= bool(np.array_equal(gm[i, :, s0 // P:-(-s1 // P)], om[i, :, s0 // P:-(-s1 // P)]))
+        sample_keys = int(new[sample].sum()) * wl.n_kv_heads
+        cpu = dict(value=sample_keys / t, unit="keys/s", cores=min(oracle.max_threads(), len(sample) * wl.n_kv_heads),
+                   kind="oracle",
+                   sample=(f"sequences {sample} of {wl.batch} ({sample_keys} new keys over {wl.n_kv_heads} KV heads): "
+                           f"oracle encode of the same chunk, median of 3 ({t:.3f} s each)"),
+                   cpu=_cpu_model(), parity={"codes_and_page_bounds_equal": ok})
+        log(f"cpu baseline {sample_keys / t:.3g} keys/s; GPU encode equals the oracle on the sample: {ok}")
+
+    line = {
+        "metric": "hhr_encode_cache append throughput (keys encoded/s) [a0 encode]",
+        "value": keys / (us * 1e-6),
+        "unit": "keys/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": us * 1e-3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; lognormal channel scales, 2 outlier key channels, planted keys)",
+        "config": {
+            "workload": (f"{wl.name}: hhr_encode_cache appending {n_new} tokens to each of {wl.batch} sequences "
+                         f"at context {wl.ctx}, {wl.n_kv_heads} KV heads, head_dim {D}, {nb}-bit codes, page {P}, "
+                         f"{wl.dtype} K, {'bf16' if wl.meta_bf16 else 'fp32'} page metadata"),
+            "global_batch": wl.batch, "seq_len": wl.ctx, "append_tokens": n_new,
+        },
+        "us_per_launch": us,
+        "hbm_algorithmic_bytes_per_launch": hbm,
+        "hbm_GBps": hbm / (us * 1e-6) / 1e9,
+        "roofline": {
+            "kernel": "encode_bulk_kernel", "bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS, "traffic": None,
+            "peak_without_packed_fp32": FP32_PEAK_UNPACKED_TFLOPS, "flops_per_launch": flops,
+            "keys_per_launch": keys, "us_per_launch": us,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama8b_128k")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: llama8b_128k; qwen7b_b16 for --mode encode)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--meta", choices=("fp32", "bf16"), default="fp32",
                     help="page metadata: fp32 (the workload as specified) or outward-rounded bf16")
@@ -308,9 +424,10 @@ def main():
                     help="hhr mode: page score over the GQA group, 0 = max (default), 1 = min (a variant)")
     ap.add_argument("--hamming-group", type=int, choices=(0, 1), default=0,
                     help="hhr mode: 0 = distance summed over the group's codes, 1 = to the mean query's code")
-    ap.add_argument("--mode", choices=("hhr", "topk"), default="hhr",
+    ap.add_argument("--mode", choices=("hhr", "topk", "encode"), default="hhr",
                     help="hhr: the HHR decode step (default); topk: the TopK (Oracle) comparison step "
-                         "(keys by exact logit over all of K, then the same attention)")
+                         "(keys by exact logit over all of K, then the same attention); encode: "
+                         "hhr_encode_cache on a 4096-token append per sequence")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -319,6 +436,9 @@ def main():
     if args.mode == "topk":
         main_topk(args)
         return
+    if args.mode == "encode":
+        main_encode(args)
+        return
 
     import numpy as np
     import torch
@@ -326,7 +446,7 @@ def main():
     import hash_sparse_attention_amd as hsa
     from synth import WORKLOADS, make_layer_torch
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[args.workload or "llama8b_128k"]
     if args.layers:
         wl = wl.with_(layers=args.layers)
     wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window,
