@@ -10,8 +10,8 @@
 //
 // This file holds the bulk mapping on gfx950 (wave64), used for many keys:
 // one lane per key.  The key row sits in VGPRs as fp32; the rows of
-// [R_h; W_h] are wave-uniform, so they come in through scalar loads and feed
-// v_fma as SGPR operands.  A page is P adjacent lanes: its max/min is a
+// [R_h; W_h] are wave-uniform, so they come in through scalar loads, one
+// chunk ahead, and feed v_fma as SGPR operands.  A page is P adjacent lanes: its max/min is a
 // butterfly over P lanes.  Each lane packs its own code words and stores
 // them contiguously.  Appends of a few keys (the token just generated) use
 // the row-per-lane projection kernel instead.
@@ -80,20 +80,58 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
         for (int i = 0; i < D; ++i) k[i] = 0.f;
     }
 
+    // Rows of [R_h; W_h] stream in as wave-uniform chunks of CH columns:
+    // scalar loads into SGPRs, which feed v_fma as operands.  Scalar loads
+    // can return out of order, so a wait can only be for all of them; one
+    // chunk is kept in flight: wait for the current chunk, issue the next
+    // one, then run the CH FMAs of the current one, which cover its latency
+    // (across row boundaries too).  Each chain is the canonical one: acc = +0,
+    // c ascending.
+    constexpr int CH = 32;       // columns per chunk
+    constexpr int NCH = D / CH;  // chunks per row: even, so buffer A holds a row's first chunk on entry
+    static_assert(NCH % 2 == 0, "chunks per row");
+    const float* Rh = R + (int64_t)h * D * D;
+    const float* Wh = W + (int64_t)h * NB * D;
+    float A[CH], Bc[CH];
+    auto load = [&](float (&c)[CH], const float* p) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) c[i] = p[i];
+    };
+    // The chain of the row at p_row; leaves the first chunk of the row at p_next in A.
+    auto row_chain = [&](const float* p_row, const float* p_next) {
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            float(&cur)[CH] = (q & 1) ? Bc : A;
+            float(&nxt)[CH] = (q & 1) ? A : Bc;
+            // Wait for chunk q (then the only scalar load in flight), then issue
+            // chunk q + 1, so the wait never covers the chunk just issued.
+            // 0xc07f: lgkmcnt(0), vmcnt and expcnt left at their maximum.
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_sched_barrier(0);
+            load(nxt, q + 1 < NCH ? p_row + (q + 1) * CH : p_next);
+            __builtin_amdgcn_sched_barrier(0);  // the loads (and their address math) stay ahead of the FMAs
+#pragma unroll
+            for (int i = 0; i < CH; ++i) acc = __builtin_fmaf(cur[i], k[q * CH + i], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return acc;
+    };
+    load(A, Rh);
+
     // Rotation rows, two at a time so a page leader stores one float4 per pair.
     const int p = t / P;
     const bool leader = (t - base) % P == 0 && valid;
     float4* mrow = reinterpret_cast<float4*>(meta) + (bh * NPB + p / 64) * (D / 2) * 64 + (p & 63);
     // bf16 meta: dimension quad r/4 of page p is one 16-byte slot; a pair is its (r % 4) / 2 half.
     uint2* mrow16 = reinterpret_cast<uint2*>(meta) + ((bh * NPB + p / 64) * (D / 4) * 64 + (p & 63)) * 2;
+#pragma unroll 1
     for (int r = 0; r < D; r += 2) {
         float mx[2], mn[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const float* Mr = R + ((int64_t)h * D + r + q) * D;
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < D; ++c) acc = __builtin_fmaf(Mr[c], k[c], acc);
+            const float* row = Rh + (int64_t)(r + q) * D;
+            const float acc = row_chain(row, r + q + 1 < D ? row + D : Wh);  // then hash row 0
             const float v = acc == 0.f ? 0.f : acc;
             mx[q] = valid ? v : -__builtin_inff();
             mn[q] = valid ? v : __builtin_inff();
@@ -114,11 +152,10 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
     uint64_t code[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) code[w] = 0;
+#pragma unroll 1
     for (int j = 0; j < NB; ++j) {
-        const float* Mr = W + ((int64_t)h * NB + j) * D;
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < D; ++c) acc = __builtin_fmaf(Mr[c], k[c], acc);
+        const float* row = Wh + (int64_t)j * D;
+        const float acc = row_chain(row, j + 1 < NB ? row + D : row);  // the last row reloads itself (in bounds)
         if (acc > 0.f) code[j >> 6] |= 1ull << (j & 63);
     }
     if (valid && t >= rg.s) {
