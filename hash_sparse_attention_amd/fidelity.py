@@ -1,6 +1,6 @@
 """Retrieval fidelity of the HHR selection on seeded synthetic inputs.
 
-The pages judge HHR's two-stage retrieval by how much of the exact attention
+The pages evaluate HHR's two-stage retrieval by how much of the exact attention
 it keeps: recall of the keys exact attention ranks highest, and the effect
 of the candidate budget and the code length ("HHR: Hierarchical Hash
 Retrieval for Efficient LLM Generation", Abstract; thelatestinai.com page,
