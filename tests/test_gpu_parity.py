@@ -35,6 +35,8 @@ SHAPES = [
     ("d128_b128_g4_p8_b3", Workload("b3", 106, 3, 8, 2, 128, 5000, 8, 128, 10, 333, "bf16", outliers=2,
                                     ragged=(4000, 5000))),
     ("d64_b128_g5_p2", Workload("g5", 107, 1, 5, 1, 64, 1500, 2, 128, 5, 70, "fp32")),
+    ("d128_b64_g6_p16", Workload("g6", 108, 2, 12, 2, 128, 2500, 16, 64, 20, 120, "fp32", outliers=2,
+                                 ragged=(900, 2500))),
 ]
 
 
