@@ -141,10 +141,17 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
             }
         }
         if (leader) {
-            if (M16)
-                mrow16[(r / 4) * 64 * 2 + (r % 4) / 2] = make_uint2(bf16_pair_out(mx[0], mn[0]), bf16_pair_out(mx[1], mn[1]));
-            else
-                mrow[(r / 2) * 64] = make_float4(mx[0], mn[0], mx[1], mn[1]);
+            // The outputs are read by later steps, not by this launch or the
+            // next: stored with the nontemporal hint (measured 2-3% faster).
+            if (M16) {
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                const u2v m2 = {bf16_pair_out(mx[0], mn[0]), bf16_pair_out(mx[1], mn[1])};
+                __builtin_nontemporal_store(m2, reinterpret_cast<u2v*>(mrow16 + (r / 4) * 64 * 2 + (r % 4) / 2));
+            } else {
+                typedef float f4v __attribute__((ext_vector_type(4)));
+                const f4v m4 = {mx[0], mn[0], mx[1], mn[1]};
+                __builtin_nontemporal_store(m4, reinterpret_cast<f4v*>(mrow + (r / 2) * 64));
+            }
         }
     }
 
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
     if (valid && t >= rg.s) {
         uint64_t* cp = codes + (bh * T + t) * NW;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) cp[w] = code[w];
+        for (int w = 0; w < NW; ++w) __builtin_nontemporal_store(code[w], cp + w);
     }
 }
 
