@@ -288,6 +288,21 @@ FP32_PEAK_TFLOPS = 157.3
 FP32_PEAK_UNPACKED_TFLOPS = 78.6
 
 
+def encode_model(wl, pre, seq):
+    """Work of one hhr_encode_cache launch that encodes keys [pre[b], seq[b]) of every sequence: the keys, the
+    fp32 FLOPs of their (D + b) canonical chains of D FMAs, the pages touched, and the HBM bytes (K read, codes
+    and the touched pages' bounds written, R_h and W_h read once)."""
+    D, nb, P = wl.head_dim, wl.hash_bits, wl.page_size
+    e = 2 if wl.dtype == "bf16" else 4
+    mb = 2 if wl.meta_bf16 else 4
+    keys = int(sum(int(s1) - int(s0) for s0, s1 in zip(pre, seq))) * wl.n_kv_heads
+    pages = int(sum(-(-int(s1) // P) - int(s0) // P for s0, s1 in zip(pre, seq) if s1 > s0)) * wl.n_kv_heads
+    parts = {"k_read": keys * D * e, "codes_written": keys * nb // 8, "meta_written": pages * 2 * D * mb,
+             "rw_read": wl.n_kv_heads * (D + nb) * D * 4}
+    return {"keys": keys, "flops": keys * (D + nb) * D * 2, "pages": pages, "hbm_bytes": sum(parts.values()),
+            **parts}
+
+
 def main_encode(args):
     """hhr_encode_cache on the append of a chunk of new keys per sequence (default: the Qwen2.5-7B attention
     shape, batch 16 at 128K context, 4096 new tokens per sequence): rotation, page max/min and codes of every
@@ -331,12 +346,8 @@ def main_encode(args):
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) / args.steps * 1e3
     D, nb, P = wl.head_dim, wl.hash_bits, wl.page_size
-    e = 2 if wl.dtype == "bf16" else 4
-    mb = 2 if wl.meta_bf16 else 4
-    keys = int(new.sum()) * wl.n_kv_heads
-    flops = keys * (D + nb) * D * 2
-    pages = int(sum(-(-int(s1) // P) - int(s0) // P for s0, s1 in zip(pre, seq))) * wl.n_kv_heads
-    hbm = keys * (D * e + nb // 8) + pages * 2 * D * mb + wl.n_kv_heads * (D + nb) * D * 4
+    m = encode_model(wl, pre, seq)
+    keys, flops, hbm = m["keys"], m["flops"], m["hbm_bytes"]
     tflops = flops / (us * 1e-6) / 1e12
     log(f"{args.steps} launches: {us:.2f} us each, {tflops:.1f} TFLOP/s fp32, {hbm / (us * 1e-6) / 1e9:.0f} GB/s")
 

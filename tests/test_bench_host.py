@@ -83,3 +83,27 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_encode_append_work_model():
+    """The 4096-token append to 16 sequences x 4 KV heads at 128K (head_dim 128, 128-bit codes, page 16, bf16 K,
+    fp32 bounds): 262,144 keys, each (128 + 128) chains of 128 FMAs; K read, 16-byte codes and the 16,384 touched
+    pages' bounds written, R_h and W_h read once."""
+    import numpy as np
+    wl = WORKLOADS["qwen7b_b16"]
+    seq = np.full(wl.batch, wl.ctx)
+    m = bench.encode_model(wl, seq - wl.append_tokens, seq)
+    assert m["keys"] == 16 * 4 * 4096 == 262_144
+    assert m["flops"] == 262_144 * 256 * 128 * 2 == 17_179_869_184
+    assert m["pages"] == 16 * 4 * (4096 // 16)
+    assert m["k_read"] == 262_144 * 128 * 2 and m["codes_written"] == 262_144 * 16
+    assert m["meta_written"] == 16_384 * 2 * 128 * 4
+    assert m["hbm_bytes"] == 67_108_864 + 4_194_304 + 16_777_216 + 4 * 256 * 128 * 4
+
+
+def test_encode_model_counts_partial_pages_once():
+    """A chunk that starts and ends inside pages touches every page it overlaps once; an empty chunk nothing."""
+    wl = WORKLOADS["tiny"]  # page 16, 2 KV heads
+    m = bench.encode_model(wl, [5, 7], [40, 7])
+    assert m["keys"] == 35 * 2
+    assert m["pages"] == 3 * 2  # pages 0, 1, 2 of the first sequence
