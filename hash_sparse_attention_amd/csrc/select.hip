@@ -33,7 +33,7 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kRun = 16;                    // items per thread per chunk
 constexpr int kChunk = kSelThreads * kRun;  // items per chunk
-constexpr int kBits = 12;                   // radix digit width of the page select
+constexpr int kBits = 11;                   // radix digit width of the page select (measured: 11 beats 10 and 12)
 constexpr int kBins = 1 << kBits;
 constexpr int kListLds = kSelListLds;       // kept-page ids staged in LDS
 static_assert(kChunk == kSelChunk, "chunk size");
@@ -71,7 +71,7 @@ struct SelShared {
 // into LDS.  Returns the number kept.  `pre` holds the keys of the first
 // chunk when the caller loaded them (lane-strided, any value past NP).
 //
-// One 12-bit radix pass below the bits all keys share usually leaves a
+// One 11-bit radix pass below the bits all keys share usually leaves a
 // boundary bucket of a few pages.  If it has at most 64, one wave ranks them
 // exactly by (key desc, page asc) and the keep-th of that order, (kt, it),
 // decides every page: kept iff key > kt or (key == kt and page <= it).
