@@ -104,6 +104,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, n: int, what: str):
+    """Raise before any launch if tensor t (when given) holds fewer than n elements."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements, the call writes {n}")
+
+
+def _check_outputs(dims: "Dims", top_k: int, out, sel_idx):
+    _need(out, dims.batch * dims.n_q_heads * dims.head_dim, "out")
+    _need(sel_idx, dims.batch * sel_units(dims) * sel_cap(dims, top_k), "sel_idx")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -182,6 +193,7 @@ def alloc_workspace(dims: Dims, max_keep: int, top_k: int, device="cuda"):
 
 def decode_step(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max_keep: int, top_k: int,
                 out, workspace, sel_idx=None, scale: float = 0.0, stream=None):
+    _check_outputs(dims, top_k, out, sel_idx)
     _check(lib().hhr_decode_step(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(R), _ptr(W), _ptr(meta),
                                  _ptr(codes), _ptr(seq_len), _ptr(keep_pages), int(max_keep), int(top_k),
                                  float(scale), _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
@@ -191,6 +203,7 @@ def decode_step(dims: Dims, Q, K, V, R, W, meta, codes, seq_len, keep_pages, max
 def decode_step_append(dims: Dims, Q, K, V, R, W, meta, codes, append_start, append_count, max_append: int,
                        seq_len, keep_pages, max_keep: int, top_k: int, out, workspace, sel_idx=None,
                        scale: float = 0.0, stream=None):
+    _check_outputs(dims, top_k, out, sel_idx)
     _check(lib().hhr_decode_step_append(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(R), _ptr(W), _ptr(meta),
                                         _ptr(codes), _ptr(append_start), _ptr(append_count), int(max_append),
                                         _ptr(seq_len), _ptr(keep_pages), int(max_keep), int(top_k), float(scale),
@@ -212,6 +225,8 @@ def alloc_topk_workspace(dims: Dims, top_k: int, device="cuda"):
 def topk_decode_step(dims: Dims, Q, K, V, seq_len, top_k: int, out, workspace, sel_idx=None, scale: float = 0.0,
                      stream=None):
     """TopK (Oracle) step: keys by exact logit (fp64), then the same gather attention."""
+    _need(out, dims.batch * dims.n_q_heads * dims.head_dim, "out")
+    _need(sel_idx, dims.batch * dims.n_kv_heads * int(top_k), "sel_idx")
     _check(lib().hhr_topk_decode_step(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(seq_len), int(top_k),
                                       float(scale), _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
                                       _stream(stream)))
@@ -255,11 +270,13 @@ def stage_select_pages(dims, seq_len, keep_pages, max_keep, top_k, workspace, st
 
 
 def stage_select_keys(dims, codes, seq_len, max_keep, top_k, workspace, sel_idx=None, stream=None):
+    _need(sel_idx, dims.batch * sel_units(dims) * sel_cap(dims, top_k), "sel_idx")
     _check(lib().hhr_stage_select_keys(ctypes.byref(dims), _ptr(codes), _ptr(seq_len), int(max_keep), int(top_k),
                                        _ptr(sel_idx), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def stage_attend(dims, Q, K, V, seq_len, max_keep, top_k, out, workspace, sel_idx=None, scale=0.0, stream=None):
+    _check_outputs(dims, top_k, out, sel_idx)
     _check(lib().hhr_stage_attend(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(seq_len), int(max_keep),
                                   int(top_k), float(scale), _ptr(sel_idx), _ptr(out), _ptr(workspace),
                                   workspace.numel(), _stream(stream)))

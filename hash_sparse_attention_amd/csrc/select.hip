@@ -17,8 +17,8 @@
 // k * 1024 + tid) so every global load and store of a wave is contiguous, and
 // all of them are issued up front.  Page scores are fp64 turned into
 // order-preserving 64-bit keys; a block OR of (key ^ key of page 0) finds the
-// bits they all share, so the MSB-first radix select starts below them, 12
-// bits (4096 LDS bins) per pass.  Hamming distances are small integers: one
+// bits they all share, so the MSB-first radix select starts below them, 11
+// bits (2048 LDS bins) per pass.  Hamming distances are small integers: one
 // LDS histogram and one scan find the threshold.  The ordered compaction
 // reads per-item flags (pages) or distances (keys) back from LDS as a
 // contiguous run per thread, so a single block scan of packed (before,
@@ -48,6 +48,9 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 
 constexpr int kRefine = 64;                 // boundary-bucket size ranked exactly by one wave
 constexpr int kMaxGroup = 8;                // query heads per KV head
+// sh.hist also holds the Hamming histogram (G * b + 1 bins, at most 8 * 128 + 1),
+// and the split scan gives each thread two bins.
+static_assert(kBins >= kMaxGroup * 128 + 1 && 2 * kSelThreads >= kMaxGroup * 128 + 1, "Hamming bins");
 
 struct SelShared {
     int hist[kBins];

@@ -65,8 +65,10 @@
  *         bounds every key of the page.  The pointer type stays float* in
  *         the calls; the buffer holds hhr_meta_bytes(dims) bytes either way.
  *   out   [B][Hq][D] fp32
- *   sel_idx [B][Hkv][top_k] int32: the selected key positions, ascending,
- *         padded with -1.
+ *   sel_idx [B][U][top_k + sink_tokens + local_window] int32, U = Hkv (or Hq
+ *         with per_head = 1): the selected key positions, ascending, padded
+ *         with -1.  A row holds top_k entries when both forced-key variants
+ *         are off.
  *
  * Arithmetic (what makes codes and selections reproducible bit for bit)
  * ---------------------------------------------------------------------
@@ -185,7 +187,8 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, 
  *   ham     uint16 [B][Hkv][max_keep*P] Hamming distance of candidate slot
  *                  j*P + r, i.e. key pages[j]*P + r; 0xFFFF if that key is
  *                  past the sequence or the slot is unused
- *   sel     int32  [B][Hkv][top_k] selected keys (when sel_idx is NULL)
+ *   sel     int32  [B][Hkv][top_k + sink_tokens + local_window] selected
+ *                  keys (when sel_idx is NULL)
  *   k_eff   int32  [B][Hkv] number of selected keys
  *   partial, counters: internal (private scratch may follow; total covers it)
  */
