@@ -50,7 +50,8 @@ def test_decode_parity_shapes(dev, name, wl):
     compare(wl, d["seq_len"], g, o, label=name)
 
 
-@pytest.mark.parametrize("name", ["tiny", "d64_b128_g1_p1", "d128_b128_g7_p16", "d64_b64_g8_p64", "llama8b_32k"])
+@pytest.mark.parametrize("name", ["tiny", "d64_b128_g1_p1", "d128_b128_g7_p16", "d64_b64_g8_p64", "llama8b_32k",
+                                  "llama8b_128k"])
 def test_bf16_meta_parity(dev, name):
     """Outward-rounded bf16 page metadata: meta (widened), scores, pages, distances, selections bit for bit and
     attention within the bar, against the oracle run with the same metadata rule."""
@@ -555,6 +556,33 @@ PER_HEAD = [
 def test_per_query_head_selection_parity(dev, name, wl):
     banner(f"per-head selection {name}")
     d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
+
+
+# Paths the shapes above do not reach (each is named by the kernel path it takes at these sizes).
+PATH_SHAPES = [
+    # D = 128 with G = 8: the largest attention tiles (8 query heads x 128 dims per row) on the split select.
+    ("d128_g8_split_64q8kv", Workload("g8s", 180, 1, 64, 8, 128, 8192, 16, 128, 25, 512, "bf16", outliers=2)),
+    ("d128_g8_split_16q2kv", Workload("g8t", 181, 1, 16, 2, 128, 8192, 16, 128, 25, 1024, "bf16", outliers=2)),
+    ("d128_g8_lhp_only", Workload("g8l", 182, 1, 16, 2, 128, 8192, 16, 128, 100, 700, "fp32", outliers=2)),
+    # More than 16384 pages per sequence (page size 4 at 80K): the general page select, split key select.
+    ("p4_80k_20000_pages", Workload("p4l", 183, 1, 8, 2, 128, 80000, 4, 128, 5, 2048, "bf16", outliers=2)),
+    # More than 8192 kept pages: the page list stays in the workspace, one key-select block per head.
+    # Sequence 0 keeps 7500 pages (its list fits in LDS), sequence 1 all 9216 (it does not).
+    ("keep_9216_pages", Workload("k9k", 184, 2, 8, 2, 64, 36864, 4, 64, 100, 3000, "bf16")),
+]
+PATH_LENGTHS = {"keep_9216_pages": [30000, 36864]}
+
+
+@pytest.mark.parametrize("name,wl", PATH_SHAPES, ids=[s[0] for s in PATH_SHAPES])
+def test_decode_parity_paths(dev, name, wl):
+    import hash_sparse_attention_amd as hsa
+    from gpu_common import gpu_dims
+    lay = hsa.workspace_layout(gpu_dims(wl), wl.max_keep, wl.top_k)
+    banner(f"decode parity {name}: max_keep {wl.max_keep}, {lay.total} workspace bytes")
+    d = make_layer(wl, lengths=PATH_LENGTHS.get(name))
     g = run_gpu(wl, d, dev)
     o = run_oracle(wl, d)
     compare(wl, d["seq_len"], g, o, label=name)
