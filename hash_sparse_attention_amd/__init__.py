@@ -55,6 +55,13 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with hash_sparse_attention_amd.build.build()")
+        # torch first: it ships a HIP runtime with the same soname as ROCm's, and whichever loads first is
+        # the one the process uses.  libhhr then runs on torch's runtime, the one that owns the tensors and
+        # streams it is given (loaded the other way round, its launches found no device).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         p, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
         D = ctypes.POINTER(Dims)
@@ -67,6 +74,9 @@ def lib():
             "hhr_decode_step": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, i32, f32, p, p, p, sz, p]),
             "hhr_decode_step_append": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, p, p, i32, i32, f32, p, p,
                                                       p, sz, p]),
+            "hhr_noalloc_scratch_bytes": (sz, []),
+            "hhr_decode_step_append_noalloc": (ctypes.c_int, [D, p, p, p, p, p, p, p, p, p, i32, p, p, i32, i32, f32,
+                                                              p, p, p]),
             "hhr_topk_workspace_layout": (ctypes.c_int, [D, i32, ctypes.POINTER(TopkLayout)]),
             "hhr_topk_workspace_bytes": (sz, [D, i32]),
             "hhr_topk_decode_step": (ctypes.c_int, [D, p, p, p, p, i32, f32, p, p, p, sz, p]),
@@ -88,7 +98,8 @@ def lib():
 
 
 EXPORTED = ("hhr_meta_bytes", "hhr_codes_bytes", "hhr_encode_cache", "hhr_decode_workspace_bytes",
-            "hhr_decode_workspace_layout", "hhr_decode_step", "hhr_decode_step_append", "hhr_topk_workspace_layout",
+            "hhr_decode_workspace_layout", "hhr_decode_step", "hhr_decode_step_append", "hhr_noalloc_scratch_bytes",
+            "hhr_decode_step_append_noalloc", "hhr_topk_workspace_layout",
             "hhr_topk_workspace_bytes", "hhr_topk_decode_step", "hhr_stage_topk_logits", "hhr_stage_qprep",
             "hhr_stage_page_bounds",
             "hhr_stage_select_pages", "hhr_stage_select_keys", "hhr_stage_attend", "hhr_status_str",
@@ -209,6 +220,24 @@ def decode_step_append(dims: Dims, Q, K, V, R, W, meta, codes, append_start, app
                                         _ptr(seq_len), _ptr(keep_pages), int(max_keep), int(top_k), float(scale),
                                         _ptr(out), _ptr(sel_idx), _ptr(workspace), workspace.numel(),
                                         _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the library's static per-GPU scratch (the limit of decode_step_append_noalloc)."""
+    return int(lib().hhr_noalloc_scratch_bytes())
+
+
+def decode_step_append_noalloc(dims: Dims, Q, K, V, R, W, meta, codes, append_start, append_count,
+                               max_append: int, seq_len, keep_pages, max_keep: int, top_k: int, out, sel_idx=None,
+                               scale: float = 0.0, stream=None):
+    """decode_step_append on the library's static per-GPU scratch instead of a caller workspace (nothing is
+    allocated; calls that overlap on one GPU race on that scratch)."""
+    _check_outputs(dims, top_k, out, sel_idx)
+    _check(lib().hhr_decode_step_append_noalloc(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(R), _ptr(W),
+                                                _ptr(meta), _ptr(codes), _ptr(append_start), _ptr(append_count),
+                                                int(max_append), _ptr(seq_len), _ptr(keep_pages), int(max_keep),
+                                                int(top_k), float(scale), _ptr(out), _ptr(sel_idx),
+                                                _stream(stream)))
 
 
 def topk_workspace_layout(dims: Dims, top_k: int) -> TopkLayout:

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "hhr_internal.h"
@@ -222,6 +223,43 @@ void topk_layout(const Shape& s, int top_k, WsLayout& l, TopkLayout& t) {
 
 }  // namespace hhr
 
+// Scratch of hhr_decode_step_append_noalloc: one copy per GPU, alive until the
+// process ends.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is only a stand-in for the symbol); it passes the device
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[HHR_NOALLOC_SCRATCH_BYTES];
+
+namespace hhr {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+hhr_status noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(HHR_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(HHR_E_UNSUPPORTED, "device index %d is beyond the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail(HHR_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        if (!p) return fail(HHR_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return HHR_OK;
+}
+
+}  // namespace
+}  // namespace hhr
+
 using namespace hhr;
 
 extern "C" {
@@ -416,6 +454,29 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
     else
         HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
     return ok();
+}
+
+size_t hhr_noalloc_scratch_bytes(void) { return HHR_NOALLOC_SCRATCH_BYTES; }
+
+hhr_status hhr_decode_step_append_noalloc(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                                          const float* R, const float* W, float* meta, uint64_t* codes,
+                                          const int32_t* append_start, const int32_t* append_count,
+                                          int32_t max_append, const int32_t* seq_len, const int32_t* keep_pages,
+                                          int32_t max_keep_pages, int32_t top_k, float softmax_scale, float* out,
+                                          int32_t* sel_idx, void* stream) {
+    Shape d;
+    HHR_TRY(make_shape(dims, d));
+    const Shape s = selection_shape(d);
+    HHR_TRY(check_sel(s, max_keep_pages, top_k));
+    const size_t need = ws_layout(s, max_keep_pages, top_k).total;
+    if (need > (size_t)HHR_NOALLOC_SCRATCH_BYTES)
+        return fail(HHR_E_WORKSPACE, "these arguments need %zu bytes of scratch; the static scratch holds %zu",
+                    need, (size_t)HHR_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    HHR_TRY(noalloc_scratch(&ws));
+    return hhr_decode_step_append(dims, Q, K, V, R, W, meta, codes, append_start, append_count, max_append, seq_len,
+                                  keep_pages, max_keep_pages, top_k, softmax_scale, out, sel_idx, ws,
+                                  (size_t)HHR_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 hhr_status hhr_stage_qprep(const hhr_dims* dims, const void* Q, const float* R, const float* W,

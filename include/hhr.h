@@ -261,6 +261,34 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * hhr_decode_step_append_noalloc -- hhr_decode_step_append without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It calls no hipMalloc, hipFree or other allocating routine:
+ * its scratch is a static device array of HHR_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * runs on the current device (the one `stream` belongs to); the first call
+ * on a device looks up that device's array once.
+ *   - Arguments, results and errors are those of hhr_decode_step_append;
+ *     out and sel_idx (or NULL) are the caller's.
+ *   - Arguments whose hhr_decode_workspace_bytes exceeds the scratch size
+ *     return HHR_E_WORKSPACE before anything is enqueued.
+ *   - Every call on a GPU shares that GPU's array and leaves its intermediate
+ *     results there (in the hhr_decode_workspace_layout of its arguments)
+ *     until the next call.  Calls that overlap on one GPU (other streams,
+ *     other threads) race on it: serialise them.  Everything a step needs
+ *     cleared is cleared by the step's own kernels.
+ */
+#define HHR_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t hhr_noalloc_scratch_bytes(void);
+hhr_status hhr_decode_step_append_noalloc(const hhr_dims* dims, const void* Q, const void* K, const void* V,
+                                          const float* R, const float* W, float* meta, uint64_t* codes,
+                                          const int32_t* append_start, const int32_t* append_count,
+                                          int32_t max_append, const int32_t* seq_len, const int32_t* keep_pages,
+                                          int32_t max_keep_pages, int32_t top_k, float softmax_scale, float* out,
+                                          int32_t* sel_idx, void* stream);
+
+/*
  * hhr_topk_decode_step -- the TopK (Oracle) comparison step: keys chosen by
  * their exact attention logit, with no page bounds and no codes (the
  * "TopK (Oracle)" rows of Table 1 and Table 2 and "TopK-1.5%" in Appendix

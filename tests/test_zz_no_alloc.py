@@ -1,0 +1,82 @@
+"""The allocation-free entry point, hhr_decode_step_append_noalloc, against
+hhr_decode_step_append on a caller workspace: same selections bit for bit and
+attention within the parity bar (2e-3), on two calls in a row whose second
+input is smaller (the static scratch keeps the first call's contents).
+The oversize check runs on the host and needs no GPU."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from gpu_common import ATOL, banner, gpu_dims, to_dev
+from synth import WORKLOADS, Workload, make_layer
+
+
+def test_noalloc_rejects_oversize_arguments():
+    import hash_sparse_attention_amd as hsa
+    L = hsa.lib()
+    cap = hsa.noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    d = hsa.make_dims(32, 28, 4, 128, 16, 128, 131072, True, per_head=True)
+    need = L.hhr_decode_workspace_bytes(ctypes.byref(d), 820, 4096)
+    assert need > cap
+    fake = ctypes.c_void_p(0x10000)
+    st = L.hhr_decode_step_append_noalloc(ctypes.byref(d), *([fake] * 9), 1, fake, fake, 820, 4096, 0.0, fake, None,
+                                          None)
+    assert st == 5  # HHR_E_WORKSPACE, before any device call
+    assert b"static scratch" in L.hhr_last_error()
+
+
+def _run_pair(wl, d, dev):
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    dims = gpu_dims(wl)
+    t = {k: to_dev(d[k], dev) for k in ("Q", "K", "V", "R", "W")}
+    seq, keep = to_dev(d["seq_len"], dev), to_dev(d["keep"], dev)
+    app_start = to_dev(np.maximum(np.asarray(d["seq_len"], np.int32) - 1, 0), dev)
+    app_count = to_dev(np.minimum(np.asarray(d["seq_len"], np.int32), 1), dev)
+    meta, codes = hsa.alloc_cache(dims, dev)
+    zero = torch.zeros(wl.batch, dtype=torch.int32, device=dev)
+    pre = (seq - app_count).contiguous()
+    hsa.encode_cache(dims, t["K"], t["R"], t["W"], zero, pre, wl.ctx, meta, codes)
+    meta2, codes2 = meta.clone(), codes.clone()
+    cap = hsa.sel_cap(dims, wl.top_k)
+    units = hsa.sel_units(dims)
+    outs, sels = [], []
+    for noalloc, (m, c) in ((False, (meta, codes)), (True, (meta2, codes2))):
+        out = torch.full((wl.batch, wl.n_q_heads, wl.head_dim), float("nan"), dtype=torch.float32, device=dev)
+        sel = torch.full((wl.batch, units, cap), -7, dtype=torch.int32, device=dev)
+        if noalloc:
+            hsa.decode_step_append_noalloc(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], m, c, app_start, app_count,
+                                           1, seq, keep, wl.max_keep, wl.top_k, out, sel_idx=sel)
+        else:
+            ws = hsa.alloc_workspace(dims, wl.max_keep, wl.top_k, dev)
+            ws.fill_(0xA5)
+            hsa.decode_step_append(dims, t["Q"], t["K"], t["V"], t["R"], t["W"], m, c, app_start, app_count, 1, seq,
+                                   keep, wl.max_keep, wl.top_k, out, ws, sel_idx=sel)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        sels.append(sel.cpu().numpy())
+    assert torch.equal(meta, meta2) and torch.equal(codes, codes2), "appended cache differs"
+    assert np.array_equal(sels[0], sels[1]), "selected keys differ"
+    err = float(np.abs(outs[0].astype(np.float64) - outs[1]).max())
+    assert np.isfinite(outs[1]).all() and err <= ATOL, f"attention max |diff| {err}"
+    return err
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_workspace_entry_point_twice():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import hash_sparse_attention_amd as hsa
+    hsa.lib()
+    dev = torch.device("cuda:0")
+    big = WORKLOADS["llama8b_32k"]
+    small = Workload("noalloc_small", 121, 3, 8, 2, 64, 3000, 16, 64, 20, 150, "bf16", ragged=(1, 3000))
+    for wl in (big, small):  # the second call's input is smaller than the first's
+        lay = hsa.workspace_layout(gpu_dims(wl), wl.max_keep, wl.top_k)
+        banner(f"noalloc {wl.name}: {lay.total} scratch bytes")
+        err = _run_pair(wl, make_layer(wl), dev)
+        banner(f"noalloc {wl.name}: equal selections, attention max |diff| {err:.2e}")
