@@ -139,6 +139,14 @@ hhr_status prepare(const hhr_dims* dims, int max_keep, int top_k, void* workspac
 
 float resolve_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / std::sqrt((float)D); }
 
+// Selections and attention of the decode step, after the page bounds.
+hhr_status launch_tail(const DecodeArgs& a, hipStream_t st) {
+    HHR_TRY(hip_check(launch_select(a, st), "select launch"));
+    if (a.lay.sel_splits > 1)
+        return hip_check(launch_compact_attend(a, st), "compaction and attention launch");
+    return hip_check(launch_attend(a, false, st), "attention launch");
+}
+
 }  // namespace
 
 WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
@@ -374,11 +382,7 @@ hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, c
     const hipStream_t st = static_cast<hipStream_t>(stream);
     HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
     HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
-    HHR_TRY(hip_check(launch_select(a, st), "select launch"));
-    if (a.lay.sel_splits > 1)
-        HHR_TRY(hip_check(launch_compact_attend(a, st), "compaction and attention launch"));
-    else
-        HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
+    HHR_TRY(launch_tail(a, st));
     return ok();
 }
 
@@ -448,11 +452,7 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
     }
     HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
-    HHR_TRY(hip_check(launch_select(a, st), "select launch"));
-    if (a.lay.sel_splits > 1)
-        HHR_TRY(hip_check(launch_compact_attend(a, st), "compaction and attention launch"));
-    else
-        HHR_TRY(hip_check(launch_attend(a, false, st), "attention launch"));
+    HHR_TRY(launch_tail(a, st));
     return ok();
 }
 

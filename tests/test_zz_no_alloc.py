@@ -58,7 +58,9 @@ def _run_pair(wl, d, dev):
         torch.cuda.synchronize()
         outs.append(out.cpu().numpy())
         sels.append(sel.cpu().numpy())
-    assert torch.equal(meta, meta2) and torch.equal(codes, codes2), "appended cache differs"
+    # Bit patterns: the unwritten tail of meta may hold NaN left by earlier allocations (identical in the clone).
+    assert torch.equal(meta.view(torch.int32), meta2.view(torch.int32)) and torch.equal(codes, codes2), \
+        "appended cache differs"
     assert np.array_equal(sels[0], sels[1]), "selected keys differ"
     err = float(np.abs(outs[0].astype(np.float64) - outs[1]).max())
     assert np.isfinite(outs[1]).all() and err <= ATOL, f"attention max |diff| {err}"
