@@ -48,7 +48,7 @@ def algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total):
         NP = -(-L // P)
         cand = int(keep[b]) * P  # every kept page is full at these lengths
         units = Hq if wl.per_head else Hkv  # selections: each reads its head's metadata and candidates' codes
-        tot += units * (NP * 2 * D * mb + cand * nb // 8)
+        tot += units * (NP * meta_sides(wl) * D * mb + cand * nb // 8)
     tot += k_eff_total * (2 * D * e + 4)                       # gathered K and V rows + indices
     tot += Hkv * (D * D + nb * D) * 4                          # R_h, W_h
     tot += B * Hq * D * (e + 4)                                # q in, out
@@ -56,11 +56,19 @@ def algorithmic_bytes_per_layer(wl, seq, keep, k_eff_total):
     return tot
 
 
+def meta_sides(wl):
+    """Stored page statistics a selection reads per dimension: both (max, min), or one with sign-split metadata
+    and one query head per selection (the side the query's sign picks)."""
+    g1 = wl.per_head or wl.n_q_heads == wl.n_kv_heads
+    return 1 if (wl.meta_split and g1) else 2
+
+
 def page_bound_bytes_per_launch(wl, seq):
-    """Per page: 2*D stored (max, min) read (fp32, or bf16 metadata) + one fp64 score written."""
+    """Per page: the stored statistics read (2*D, or D with the sign-split one-side read; fp32 or bf16) + one
+    fp64 score written."""
     units = wl.n_q_heads if wl.per_head else wl.n_kv_heads  # selections, each streaming its head's metadata
     pages = sum(-(-int(L) // wl.page_size) for L in seq) * units
-    return pages * (2 * wl.head_dim * (2 if wl.meta_bf16 else 4) + 8), pages
+    return pages * (meta_sides(wl) * wl.head_dim * (2 if wl.meta_bf16 else 4) + 8), pages
 
 
 def source_digest(path=BOUND_SRC):
@@ -418,6 +426,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     ap.add_argument("--meta", choices=("fp32", "bf16"), default="fp32",
                     help="page metadata: fp32 (the workload as specified) or outward-rounded bf16")
+    ap.add_argument("--meta-layout", choices=("interleaved", "split"), default="interleaved",
+                    help="page metadata storage: interleaved (default) or sign-split, where a selection of one "
+                         "query head reads only the side its query's sign picks")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bound-launches", type=int, default=96, help="page-bound launches timed for the roofline")
@@ -461,7 +472,8 @@ def main():
     if args.layers:
         wl = wl.with_(layers=args.layers)
     wl = wl.with_(meta_bf16=args.meta == "bf16", sink_tokens=args.sinks, local_window=args.window,
-                  page_group=args.page_group, hamming_group=args.hamming_group, per_head=args.per_head)
+                  page_group=args.page_group, hamming_group=args.hamming_group, per_head=args.per_head,
+                  meta_split=args.meta_layout == "split")
     if args.keep_percent:
         wl = wl.with_(keep_percent=args.keep_percent)
     if args.top_k:
@@ -473,7 +485,7 @@ def main():
     dims = hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                          wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
                          local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group,
-                         per_head=wl.per_head)
+                         per_head=wl.per_head, meta_split=wl.meta_split)
     layers = []
     t0 = time.perf_counter()
     for l in range(wl.layers):
@@ -604,6 +616,7 @@ def main():
                          ("page score = min over the group; " if wl.page_group else "") +
                          ("Hamming to the group's mean-query code; " if wl.hamming_group else "") +
                          ("one selection per query head; " if wl.per_head else "") +
+                         ("sign-split page metadata; " if wl.meta_split else "") +
                          "one step = per layer a 1-token append + decode"),
             "global_batch": wl.batch, "seq_len": wl.ctx, "layers": wl.layers, "graph": graph is not None,
         },

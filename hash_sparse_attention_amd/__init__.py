@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhhr.so")
 
 HHR_F32, HHR_BF16 = 0, 1
+HHR_META_INTERLEAVED, HHR_META_SIGN_SPLIT = 0, 1
 STATUS = {0: "HHR_OK", 1: "HHR_E_NULL", 2: "HHR_E_SHAPE", 3: "HHR_E_DTYPE", 4: "HHR_E_ALIGN",
           5: "HHR_E_WORKSPACE", 6: "HHR_E_RANGE", 7: "HHR_E_UNSUPPORTED", 8: "HHR_E_HIP"}
 
@@ -30,7 +31,7 @@ class HHRError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_q_heads", "n_kv_heads", "head_dim", "page_size", "hash_bits", "max_ctx", "kv_dtype",
-        "meta_dtype", "sink_tokens", "local_window", "page_group", "hamming_group", "per_head")]
+        "meta_dtype", "sink_tokens", "local_window", "page_group", "hamming_group", "per_head", "meta_layout")]
 
     def __repr__(self):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -135,16 +136,19 @@ def _stream(stream):
 
 def make_dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx, bf16: bool,
               meta_bf16: bool = False, sink_tokens: int = 0, local_window: int = 0, page_group: int = 0,
-              hamming_group: int = 0, per_head: bool = False) -> Dims:
+              hamming_group: int = 0, per_head: bool = False, meta_split: bool = False) -> Dims:
     """meta_bf16: store page metadata as outward-rounded bf16 (half the bytes of the page-bound stream).
     sink_tokens, local_window: keys always attended by the decode step (the first and the last ones); its
     selection rows then hold top_k + sink_tokens + local_window entries (`sel_cap`).
     page_group = 1 scores a page by the min over the GQA group (default 0: max); hamming_group = 1 ranks keys
     by the distance to the code of the group's mean query (default 0: summed over the group's codes).
-    per_head: one selection per query head instead of one per KV head (per-(b, h) rows become per query head)."""
+    per_head: one selection per query head instead of one per KV head (per-(b, h) rows become per query head).
+    meta_split: store page metadata dimension-major with the max and min sides apart, so a selection of one
+    query head reads only the side its query's sign picks (half the bytes of the page-bound stream)."""
     return Dims(batch, n_q_heads, n_kv_heads, head_dim, page_size, hash_bits, max_ctx,
                 HHR_BF16 if bf16 else HHR_F32, HHR_BF16 if meta_bf16 else HHR_F32, int(sink_tokens),
-                int(local_window), int(page_group), int(hamming_group), int(bool(per_head)))
+                int(local_window), int(page_group), int(hamming_group), int(bool(per_head)),
+                HHR_META_SIGN_SPLIT if meta_split else HHR_META_INTERLEAVED)
 
 
 def sel_units(dims: Dims) -> int:
@@ -354,13 +358,17 @@ def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> Workspac
 
 
 def meta_to_pages(meta_flat, dims: Dims):
-    """Reshape the page-block-interleaved meta buffer to [B][Hkv][NPmax][D][2] (max, min) fp32 (bf16 metadata
-    widened exactly); a host-side view helper."""
+    """Reshape the meta buffer (page-block interleaved, or sign-split) to [B][Hkv][NPmax][D][2] (max, min) fp32
+    (bf16 metadata widened exactly); a host-side view helper."""
     import torch
     B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
     NP = -(-dims.max_ctx // dims.page_size)
     NPB = -(-NP // 64)
-    if dims.meta_dtype == HHR_BF16:
+    if dims.meta_layout == HHR_META_SIGN_SPLIT:
+        m = meta_flat.view(torch.bfloat16) if dims.meta_dtype == HHR_BF16 else meta_flat
+        m = m.reshape(B, Hkv, NPB, D, 2, 64)  # [..][blk][dim][max/min][lane]
+        m = m.permute(0, 1, 2, 5, 3, 4).reshape(B, Hkv, NPB * 64, D, 2).float()
+    elif dims.meta_dtype == HHR_BF16:
         m = meta_flat.view(torch.bfloat16).reshape(B, Hkv, NPB, D // 4, 64, 4, 2)  # [..][blk][quad][lane][dim][max/min]
         m = m.permute(0, 1, 2, 4, 3, 5, 6).reshape(B, Hkv, NPB * 64, D, 2).float()
     else:

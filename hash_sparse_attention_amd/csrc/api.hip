@@ -57,6 +57,9 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
         return fail(HHR_E_DTYPE, "kv_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->kv_dtype);
     if (d->meta_dtype != HHR_F32 && d->meta_dtype != HHR_BF16)
         return fail(HHR_E_DTYPE, "meta_dtype must be HHR_F32 or HHR_BF16 (got %d)", d->meta_dtype);
+    if (d->meta_layout != HHR_META_INTERLEAVED && d->meta_layout != HHR_META_SIGN_SPLIT)
+        return fail(HHR_E_RANGE, "meta_layout must be HHR_META_INTERLEAVED or HHR_META_SIGN_SPLIT (got %d)",
+                    d->meta_layout);
     if (d->per_head != 0 && d->per_head != 1)
         return fail(HHR_E_RANGE, "per_head must be 0 or 1 (got %d)", d->per_head);
     if ((d->page_group != 0 && d->page_group != 1) || (d->hamming_group != 0 && d->hamming_group != 1))
@@ -78,6 +81,7 @@ hhr_status make_shape(const hhr_dims* d, Shape& s) {
     s.NPB = (s.NPmax + 63) / 64;
     s.bf16 = d->kv_dtype == HHR_BF16;
     s.meta16 = d->meta_dtype == HHR_BF16;
+    s.msplit = d->meta_layout == HHR_META_SIGN_SPLIT;
     s.nsink = d->sink_tokens;
     s.window = d->local_window;
     s.pg_min = d->page_group == 1;

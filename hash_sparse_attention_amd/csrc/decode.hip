@@ -133,6 +133,108 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     score[bh * NPmax + p] = S;
 }
 
+// Sign-split metadata (dimension-major per 64-page block: the 64 pages' max
+// values of a dimension, then their min values; fp32 or bf16).  With one
+// query head per selection (G = 1) only the side the sign of the rotated
+// query coordinate picks is read: kmax where q >= 0 (q_split's min term is
+// zero), kmin where q < 0.  The side not read would add an exact zero, so the
+// fp64 sum, dimensions ascending, is the interleaved kernel's bit for bit
+// (the sign of a zero score aside, which is normalised).  The side of each
+// dimension is a bit of a wave-uniform mask built by ballots, so every load
+// address is uniform plus the lane: one contiguous 256-byte (fp32) or
+// 128-byte (bf16) run per wave and dimension.  With G > 1 both sides are read.
+template <int D, int G, int U, bool M16, bool PGMIN>
+__global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __restrict__ meta,
+                                                               const double* __restrict__ q_split,
+                                                               const int32_t* __restrict__ seq_len,
+                                                               double* __restrict__ score, int Hkv, int T, int P,
+                                                               int64_t NPB, int64_t NPmax, int share) {
+    using E = typename std::conditional<M16, uint16_t, float>::type;
+    constexpr int NS = G == 1 ? 1 : 2;  // sides read per dimension
+    constexpr int NBT = D / U;          // batches of U dimensions
+    static_assert(D % U == 0 && NBT % 2 == 0, "batches");
+    __shared__ double2 qs[D * G];  // (max(q,0), min(q,0)) per dimension and query head
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int L = clamp_len(seq_len[b], T);
+    const int64_t NP = n_pages_of(L, P);
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if ((int64_t)blockIdx.x * 256 >= NP) return;  // block-uniform
+
+    const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
+    for (int x = threadIdx.x; x < D * G; x += 256) qs[x] = qg[x];
+    __syncthreads();
+    // G = 1: bit d set when q_d < 0 (the min side is read).  Built while every
+    // lane of the wave is active: a ballot leaves out lanes that have exited.
+    const int lane = threadIdx.x & 63;
+    uint64_t neg[D / 64];
+#pragma unroll
+    for (int w = 0; w < D / 64; ++w) neg[w] = G == 1 ? __ballot(qs[w * 64 + lane].y != 0.0) : 0ull;
+    if (p >= NP) return;
+
+    const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
+    const E* mp = reinterpret_cast<const E*>(meta) + ((bhd * NPB + p / 64) * D) * 128 + (p & 63);
+    auto side = [&](int d) { return (int)((neg[d >> 6] >> (d & 63)) & 1u); };
+    auto widen = [](E v) -> double {
+        if constexpr (M16) return (double)__uint_as_float((uint32_t)v << 16);
+        else return (double)v;
+    };
+    double acc[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) acc[i] = 0.0;
+    E A[U][NS], B[U][NS];
+    auto load = [&](E (&v)[U][NS], int k) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int d = k * U + u;
+            if constexpr (G == 1) {
+                v[u][0] = __builtin_nontemporal_load(mp + d * 128 + side(d) * 64);
+            } else {
+                v[u][0] = __builtin_nontemporal_load(mp + d * 128);
+                v[u][1] = __builtin_nontemporal_load(mp + d * 128 + 64);
+            }
+        }
+    };
+    auto sum = [&](const E (&v)[U][NS], int k) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int d = k * U + u;
+            if constexpr (G == 1) {
+                const double2 q = qs[d];
+                acc[0] = __builtin_fma(side(d) ? q.y : q.x, widen(v[u][0]), acc[0]);
+            } else {
+                const double a = widen(v[u][0]), c = widen(v[u][1]);
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const double2 q = qs[d * G + i];
+                    acc[i] = __builtin_fma(q.x, a, acc[i]);
+                    acc[i] = __builtin_fma(q.y, c, acc[i]);
+                }
+            }
+        }
+    };
+    // Double buffering, fully unrolled; the empty asm statements keep the
+    // loads where they are written.
+    load(A, 0);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < NBT; k += 2) {
+        load(B, k + 1);
+        asm volatile("" ::: "memory");
+        sum(A, k);
+        asm volatile("" ::: "memory");
+        if (k + 2 < NBT) load(A, k + 2);
+        asm volatile("" ::: "memory");
+        sum(B, k + 1);
+        asm volatile("" ::: "memory");
+    }
+    double S = acc[0];  // the group's max, or its min (a variant)
+#pragma unroll
+    for (int i = 1; i < G; ++i) S = PGMIN ? (acc[i] < S ? acc[i] : S) : (acc[i] > S ? acc[i] : S);
+    if (S == 0.0) S = 0.0;
+    score[bh * NPmax + p] = S;
+}
+
 // ------------------------------------------------------------------ dispatch helpers
 template <int D, int G>
 hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
@@ -141,6 +243,13 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     // Loads per lane per batch (two batches in flight), measured best per metadata type.
     auto kern = s.meta16 ? (s.pg_min ? page_bound_kernel<D, G, 8, true, true> : page_bound_kernel<D, G, 8, true, false>)
                          : (s.pg_min ? page_bound_kernel<D, G, 4, false, true> : page_bound_kernel<D, G, 4, false, false>);
+    if (s.msplit) {  // dimensions per batch: 16 single-side loads for G = 1, else 8 dimensions of two loads
+        constexpr int US = G == 1 ? 16 : 8;
+        kern = s.meta16 ? (s.pg_min ? page_bound_split_kernel<D, G, US, true, true>
+                                    : page_bound_split_kernel<D, G, US, true, false>)
+                        : (s.pg_min ? page_bound_split_kernel<D, G, US, false, true>
+                                    : page_bound_split_kernel<D, G, US, false, false>);
+    }
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
                        reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax,

@@ -36,7 +36,7 @@ __device__ __forceinline__ EncRange enc_range(const int32_t* start, const int32_
 }
 
 // ------------------------------------------------------------------ bulk
-template <int D, int NB, bool BF16, bool M16>
+template <int D, int NB, bool BF16, bool M16, bool MS>
 __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict__ K, const float* __restrict__ R,
                                                           const float* __restrict__ W,
                                                           const int32_t* __restrict__ start,
@@ -143,7 +143,21 @@ __global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict
         if (leader) {
             // The outputs are read by later steps, not by this launch or the
             // next: stored with the nontemporal hint (measured 2-3% faster).
-            if (M16) {
+            if (MS) {  // sign-split layout: dimension d's max run, then its min run, 64 pages each
+                const int64_t e0 = ((bh * NPB + p / 64) * D + r) * 128 + (p & 63);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (M16) {
+                        uint16_t* m = reinterpret_cast<uint16_t*>(meta) + e0 + q * 128;
+                        __builtin_nontemporal_store((uint16_t)bf16_up(mx[q]), m);
+                        __builtin_nontemporal_store((uint16_t)bf16_down(mn[q]), m + 64);
+                    } else {
+                        float* m = meta + e0 + q * 128;
+                        __builtin_nontemporal_store(mx[q], m);
+                        __builtin_nontemporal_store(mn[q], m + 64);
+                    }
+                }
+            } else if (M16) {
                 typedef uint32_t u2v __attribute__((ext_vector_type(2)));
                 const u2v m2 = {bf16_pair_out(mx[0], mn[0]), bf16_pair_out(mx[1], mn[1])};
                 __builtin_nontemporal_store(m2, reinterpret_cast<u2v*>(mrow16 + (r / 4) * 64 * 2 + (r % 4) / 2));
@@ -176,8 +190,9 @@ template <int D, int NB, bool BF16, bool M16>
 hipError_t launch_dnb(const Shape& s, const void* K, const float* R, const float* W, const int32_t* start,
                       const int32_t* count, int max_count, float* meta, uint64_t* codes, hipStream_t st) {
     const int tiles = (max_count + s.P - 1 + 255) / 256;  // keys [floor(s/P)P, e) in 256-key tiles
-    hipLaunchKernelGGL((encode_bulk_kernel<D, NB, BF16, M16>), dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W,
-                       start, count, max_count, meta, codes, s.Hkv, s.T, s.P, s.NPB);
+    auto kern = s.msplit ? encode_bulk_kernel<D, NB, BF16, M16, true> : encode_bulk_kernel<D, NB, BF16, M16, false>;
+    hipLaunchKernelGGL(kern, dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W, start, count, max_count, meta, codes,
+                       s.Hkv, s.T, s.P, s.NPB);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct Shape {
     int64_t NPB;    // 64-page blocks of meta per (b, h)
     bool bf16;      // Q, K, V are bf16
     bool meta16;    // page metadata is bf16 (outward-rounded)
+    bool msplit;    // page metadata is dimension-major with max and min sides apart (sign-split)
     int nsink, window;  // keys always attended: the first nsink and the last window
     bool pg_min;        // page score = min over the group (else max)
     bool ham_mean;      // Hamming against the group's mean-query code (else summed over the group)

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
     int max_count, int key_blocks, float* __restrict__ meta, uint64_t* __restrict__ codes,
     float* __restrict__ q_rot, uint64_t* __restrict__ code_q, uint64_t* __restrict__ code_qm,
     double* __restrict__ q_split, uint32_t* __restrict__ counters, int n_counters, int Hq, int Hkv, int G, int T,
-    int P, int64_t NPB, bool meta16, bool qmean, bool qs_unit) {
+    int P, int64_t NPB, bool meta16, bool msplit, bool qmean, bool qs_unit) {
     constexpr int RG = (D + NB) / 64;  // row groups of [R_h; W_h]
     constexpr int NW = NB / 64;
     constexpr int LDM = D + 4;         // padded row stride of the tile (floats)
@@ -190,7 +190,17 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
                 mx = fmaxf(mx, red[g][lane][0]);
                 mn = fminf(mn, red[g][lane][1]);
             }
-            if (meta16) {  // bf16 slot (dimension quad row / 4, page p), word row % 4
+            if (msplit) {  // sign-split: (dimension row, max side) run, then its min side, 64 pages each
+                const int64_t e0 = ((bh * NPB + p / 64) * D + row) * 128 + (p & 63);
+                if (meta16) {
+                    uint16_t* mp = reinterpret_cast<uint16_t*>(meta) + e0;
+                    mp[0] = (uint16_t)bf16_up(mx);
+                    mp[64] = (uint16_t)bf16_down(mn);
+                } else {
+                    meta[e0] = mx;
+                    meta[e0 + 64] = mn;
+                }
+            } else if (meta16) {  // bf16 slot (dimension quad row / 4, page p), word row % 4
                 uint32_t* mp = reinterpret_cast<uint32_t*>(meta) +
                                (((bh * NPB + p / 64) * (D / 4) + row / 4) * 64 + (p & 63)) * 4 + (row & 3);
                 *mp = bf16_pair_out(mx, mn);
@@ -210,7 +220,7 @@ hipError_t project_t(const Shape& s, const ProjectArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((project_kernel<D, NB, BF16, KEYS, QUERIES>), dim3(s.Hkv, s.B, blocks),
                        dim3(kProjWaves * 64), 0, st, a.Q, a.K, a.R, a.W, a.start, a.count, a.max_count, key_blocks,
                        a.meta, a.codes, a.q_rot, a.code_q, a.code_qm, a.q_split, a.counters, a.n_counters, s.Hq,
-                       s.Hkv, s.G, s.T, s.P, s.NPB, s.meta16, a.queries && a.qmean, a.qs_unit);
+                       s.Hkv, s.G, s.T, s.P, s.NPB, s.meta16, s.msplit, a.queries && a.qmean, a.qs_unit);
     return hipGetLastError();
 }
 

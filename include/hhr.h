@@ -64,6 +64,15 @@
  *         bf16 (outward), so the page bound below, computed from them, still
  *         bounds every key of the page.  The pointer type stays float* in
  *         the calls; the buffer holds hhr_meta_bytes(dims) bytes either way.
+ *         meta_layout HHR_META_SIGN_SPLIT (either dtype): [B][Hkv][NPB][D][2][64],
+ *         dimension-major: for page block blk, dimension d and side s (0 =
+ *         max, 1 = min) the 64 pages' values are one contiguous run (256 B
+ *         fp32, 128 B bf16).  A selection of one query head (G = 1, or
+ *         per_head = 1) then reads, per dimension, only the side the sign of
+ *         its rotated query coordinate picks -- half the metadata bytes --
+ *         with the same bound bit for bit (the side not read contributes an
+ *         exact zero).  Grouped selections read both sides.  Same byte count
+ *         as the interleaved layout.
  *   out   [B][Hq][D] fp32
  *   sel_idx [B][U][top_k + sink_tokens + local_window] int32, U = Hkv (or Hq
  *         with per_head = 1): the selected key positions, ascending, padded
@@ -98,7 +107,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 6
+#define HHR_ABI_VERSION 7
 
 typedef enum {
     HHR_OK = 0,
@@ -113,6 +122,9 @@ typedef enum {
 } hhr_status;
 
 typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
+
+/* Storage order of the page metadata (see "meta" under Layouts). */
+typedef enum { HHR_META_INTERLEAVED = 0, HHR_META_SIGN_SPLIT = 1 } hhr_meta_layout;
 
 typedef struct {
     int32_t batch;      /* B                                              */
@@ -141,6 +153,10 @@ typedef struct {
                               workspace row and sel_idx row is then per
                               query head ([B][Hq]...), as if each KV head
                               were repeated for its G query heads          */
+    int32_t meta_layout;   /* hhr_meta_layout of the page metadata: HHR_META_INTERLEAVED
+                              (0, the default) or HHR_META_SIGN_SPLIT (1):
+                              selections of one query head read half the
+                              metadata bytes; encode and decode must agree */
 } hhr_dims;
 
 /* Bytes of the meta and codes buffers for these dims (0 if the dims are invalid). */

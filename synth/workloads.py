@@ -49,6 +49,7 @@ class Workload:
     page_group: int = 0          # decode variant: page score over the group, 0 = max, 1 = min
     hamming_group: int = 0       # decode variant: 0 = H summed over the group, 1 = H to the mean query's code
     per_head: bool = False       # decode variant: one selection per query head
+    meta_split: bool = False     # page metadata stored sign-split (dimension-major, max and min sides apart)
 
     @property
     def group(self) -> int:
@@ -75,6 +76,9 @@ WORKLOADS = {
                              outliers=2, ragged=(32768, 65536)),
     "qwen7b_b16": Workload("qwen7b_b16", 4, 16, 28, 4, 128, 131072, 16, 128, 10, 4096, "bf16",
                            outliers=2, append_tokens=4096),
+    # One query head per KV head (G = 1) at the Llama-3.1-8B KV-head shapes: the selection shape of the
+    # sign-split metadata read.
+    "mha_128k": Workload("mha_128k", 5, 1, 8, 8, 128, 131072, 16, 128, 10, 4096, "bf16", layers=32, outliers=2),
 }
 
 

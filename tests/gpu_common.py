@@ -28,7 +28,7 @@ def gpu_dims(wl: Workload):
     return hsa.make_dims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.page_size, wl.hash_bits, wl.ctx,
                          wl.dtype == "bf16", meta_bf16=wl.meta_bf16, sink_tokens=wl.sink_tokens,
                          local_window=wl.local_window, page_group=wl.page_group, hamming_group=wl.hamming_group,
-                         per_head=wl.per_head)
+                         per_head=wl.per_head, meta_split=wl.meta_split)
 
 
 def oracle_dims(wl: Workload):

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(hsa):
 
 def test_version_and_status_strings(hsa):
     L = hsa.lib()
-    assert L.hhr_abi_version() == 6
+    assert L.hhr_abi_version() == 7
     for code, name in hsa.STATUS.items():
         assert L.hhr_status_str(code).decode() == name
 
@@ -89,6 +89,19 @@ def test_bad_meta_dtype_and_meta_bytes(hsa):
     # fp32 meta: B * Hkv * NPB * 64 pages * D * (max, min) * 4 bytes; bf16 meta is half of it
     assert L.hhr_meta_bytes(ctypes.byref(f32)) == 1 * 8 * 128 * 64 * 128 * 2 * 4
     assert L.hhr_meta_bytes(ctypes.byref(b16)) * 2 == L.hhr_meta_bytes(ctypes.byref(f32))
+
+
+def test_meta_layout_checked_and_sized_like_interleaved(hsa):
+    L = hsa.lib()
+    d = dims()
+    d.meta_layout = 2
+    assert call_decode(hsa, d, ws_bytes=1 << 30) == 6  # HHR_E_RANGE
+    assert "meta_layout" in L.hhr_last_error().decode()
+    assert L.hhr_meta_bytes(ctypes.byref(d)) == 0
+    for bf in (False, True):
+        a, b = dims(meta_bf16=bf), dims(meta_bf16=bf, meta_split=True)
+        assert b.meta_layout == hsa.HHR_META_SIGN_SPLIT
+        assert L.hhr_meta_bytes(ctypes.byref(a)) == L.hhr_meta_bytes(ctypes.byref(b)) > 0
 
 
 def test_null_and_alignment(hsa):

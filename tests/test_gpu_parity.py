@@ -245,8 +245,11 @@ def test_qwen7b_b16_append_4096_sampled(dev):
 
 @pytest.mark.parametrize("meta_bf16,variant", [(False, {}), (True, {}),
                                                (False, dict(sink_tokens=3, local_window=40, hamming_group=1)),
-                                               (True, dict(page_group=1)), (False, dict(per_head=True))],
-                         ids=["fp32_meta", "bf16_meta", "sinks_window_mean_code", "bf16_meta_min_page", "per_head"])
+                                               (True, dict(page_group=1)), (False, dict(per_head=True)),
+                                               (False, dict(per_head=True, meta_split=True)),
+                                               (True, dict(meta_split=True))],
+                         ids=["fp32_meta", "bf16_meta", "sinks_window_mean_code", "bf16_meta_min_page", "per_head",
+                              "per_head_sign_split", "bf16_meta_sign_split"])
 def test_decode_step_append_matches_oracle(dev, meta_bf16, variant):
     """hhr_decode_step_append (fused append + query projection) equals the oracle's single-shot encode +
     decode, for a 1-token append, a ragged multi-token append, and an append larger than the fused limit."""
@@ -586,3 +589,49 @@ def test_decode_parity_paths(dev, name, wl):
     g = run_gpu(wl, d, dev)
     o = run_oracle(wl, d)
     compare(wl, d["seq_len"], g, o, label=name)
+
+
+# Sign-split page metadata: encode and append write it, the bound kernel reads one side per dimension for
+# selections of one query head (G = 1, or per-query-head selection) and both sides for grouped selections.
+SPLIT_SHAPES = [
+    ("mha_g1_bf16", Workload("ms1", 190, 2, 4, 4, 128, 3000, 16, 128, 10, 200, "bf16", outliers=2,
+                             ragged=(1000, 3000), meta_split=True)),
+    ("mha_g1_d64_bf16meta_fp32", Workload("ms2", 191, 1, 2, 2, 64, 5000, 8, 64, 15, 300, "fp32", meta_split=True,
+                                          meta_bf16=True)),
+    ("per_head_g4", Workload("ms3", 192, 1, 16, 4, 128, 4096, 16, 128, 10, 256, "bf16", outliers=2, per_head=True,
+                             meta_split=True)),
+    ("shared_g4_both_sides", Workload("ms4", 193, 1, 8, 2, 128, 4096, 16, 128, 25, 512, "bf16", outliers=2,
+                                      meta_split=True)),
+    ("shared_g7_bf16meta_min_page", Workload("ms5", 194, 1, 14, 2, 128, 2000, 16, 128, 10, 150, "bf16",
+                                             meta_split=True, meta_bf16=True, page_group=1)),
+    ("mha_g1_p1_sinks", Workload("ms6", 195, 2, 3, 3, 64, 700, 1, 64, 20, 50, "bf16", ragged=(1, 700),
+                                 meta_split=True, sink_tokens=2, local_window=9)),
+]
+
+
+@pytest.mark.parametrize("name,wl", SPLIT_SHAPES, ids=[s[0] for s in SPLIT_SHAPES])
+def test_sign_split_metadata_parity(dev, name, wl):
+    banner(f"sign-split metadata {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
+
+
+def test_sign_split_encode_in_chunks(dev):
+    """Bulk encode, 1-token appends and a mid-page chunk into the sign-split layout: bit-identical to the oracle's
+    single-shot encode, and the decode on it equal to the oracle's."""
+    wl = Workload("ms_chunks", 196, 2, 8, 8, 128, 1200, 16, 128, 20, 64, "bf16", outliers=2, meta_split=True)
+    banner("sign-split encode in chunks")
+    d = make_layer(wl, lengths=[1100, 1037])
+    chunks = [(np.zeros(2, np.int32), np.array([900, 837], np.int32), 900)]
+    pos = np.array([900, 837], np.int32)
+    for _ in range(3):
+        chunks.append((pos.copy(), np.ones(2, np.int32), 1))
+        pos += 1
+    chunks.append((pos.copy(), np.array([197, 197], np.int32), 197))
+    pos += 197
+    assert list(pos) == [1100, 1037]
+    g = run_gpu(wl, d, dev, chunks=chunks)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label="sign-split chunks")
