@@ -107,3 +107,38 @@ def test_encode_model_counts_partial_pages_once():
     m = bench.encode_model(wl, [5, 7], [40, 7])
     assert m["keys"] == 35 * 2
     assert m["pages"] == 3 * 2  # pages 0, 1, 2 of the first sequence
+
+
+def test_sign_split_halves_the_bound_bytes_of_one_query_head_selections():
+    """With sign-split metadata a selection of one query head reads one stored side per dimension."""
+    seq = [131072]
+    mha = WORKLOADS["mha_128k"]
+    full, pages = bench.page_bound_bytes_per_launch(mha, seq)
+    half, pages2 = bench.page_bound_bytes_per_launch(mha.with_(meta_split=True), seq)
+    assert pages == pages2 == 8 * 8192
+    assert full == pages * (2 * 128 * 4 + 8) and half == pages * (128 * 4 + 8)
+    # Grouped selections read both sides whatever the layout; per-query-head ones read one.
+    llama = WORKLOADS["llama8b_128k"]
+    assert bench.meta_sides(llama.with_(meta_split=True)) == 2
+    assert bench.meta_sides(llama.with_(meta_split=True, per_head=True)) == 1
+    assert bench.meta_sides(llama.with_(per_head=True)) == 2
+
+
+def test_step_spread_and_description():
+    med, p10, p90 = bench.spread([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert med == 3.0 and abs(p10 - 1.4) < 1e-12 and abs(p90 - 4.6) < 1e-12
+    d = bench.describe(WORKLOADS["qwen7b_b16"].with_(meta_split=True))
+    assert d.startswith("qwen7b_b16: Qwen2.5-7B-shaped") and "sign-split" in d
+
+
+def test_counter_traffic_only_for_the_profiled_workload():
+    """The committed bound-kernel counters describe llama8b_128k with fp32 interleaved metadata and shared
+    selections, measured on the current decode.hip; any other workload reports no traffic."""
+    wl = WORKLOADS["llama8b_128k"]
+    rec = json.load(open(bench.PMC_FILE))
+    assert rec["source_sha256_16"] == bench.source_digest(), "page-bound counters predate the current decode.hip"
+    assert bench.traffic_from_profile(wl) == rec["bytes_per_launch"]
+    assert 1.0 <= rec["bytes_per_launch"] / rec["algorithmic_bytes_per_launch"] < 1.05
+    for other in (wl.with_(meta_bf16=True), wl.with_(meta_split=True), wl.with_(per_head=True),
+                  WORKLOADS["qwen7b_b16"]):
+        assert bench.traffic_from_profile(other) is None
