@@ -98,7 +98,7 @@ __device__ __forceinline__ float4 ld_agent4(const float* p) {
 constexpr int kMergeRound = 32;  // split partials merged per round by the last block
 
 template <int D, int G, int NR = 16>
-struct AttnShared {
+struct alignas(16) AttnShared {
     float wo[NR][G][D];     // row partials (o), reused by the final reduction
     float wml[NR][G][2];    // row partials (m, l)
     float cml[G][kMergeRound][2];
@@ -107,6 +107,42 @@ struct AttnShared {
     float bml[G][2];        // block (M, L) per query head
     int last_flag;
 };
+
+// A row's partial o of query head i into sh.wo[rw][i]: lane `sub` owns the
+// DPL = D / 16 dimensions [sub * DPL, sub * DPL + DPL).  With DPL = 8 a lane's
+// 32 bytes go out as two 16-byte stores; written in the same order by every
+// lane, lanes 4 (and 8) apart -- and the rows of a wave, 2 KB apart at G = 4 --
+// would hit the same LDS banks in each store.  Lanes whose bit 2 of `sub`
+// differs from bit 3 store their upper half first, so within every 8 and every
+// 16 consecutive lanes a store's addresses cover distinct banks.  The stored
+// layout is unchanged; only which store carries which half differs.
+template <int D, int G, int NR, int DPL>
+__device__ __forceinline__ void store_row_o(AttnShared<D, G, NR>& sh, int rw, int sub, const float (&o)[G][DPL]) {
+    if constexpr (DPL == 8) {
+        const bool hi_first = ((sub >> 2) ^ (sub >> 3)) & 1;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            float a[4], c[4];  // the first and the second store's values, selected per component
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                a[d] = hi_first ? o[i][4 + d] : o[i][d];
+                c[d] = hi_first ? o[i][d] : o[i][4 + d];
+            }
+            float* base = &sh.wo[rw][i][sub * DPL];
+            *reinterpret_cast<float4*>(base + (hi_first ? 4 : 0)) = make_float4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<float4*>(base + (hi_first ? 0 : 4)) = make_float4(c[0], c[1], c[2], c[3]);
+        }
+    } else if constexpr (DPL == 4) {  // 16 bytes a lane: consecutive lanes, consecutive 16-byte slots
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            *reinterpret_cast<float4*>(&sh.wo[rw][i][sub * DPL]) = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) sh.wo[rw][i][sub * DPL + d] = o[i][d];
+    }
+}
 
 // Log-sum-exp weights of the block's NR row partials: per query head i,
 // M_i = max_r m_r, f_r = exp(m_r - M_i) (0 for a row without keys) and
@@ -462,11 +498,10 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
         m_i[i] = mx;
         l_i[i] = l;
     }
+    store_row_o(sh, rw, sub, o);
+    if (sub == 0) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) sh.wo[rw][i][sub * DPL + d] = o[i][d];
-        if (sub == 0) {
+        for (int i = 0; i < G; ++i) {
             sh.wml[rw][i][0] = m_i[i];
             sh.wml[rw][i][1] = l_i[i];
         }
@@ -506,8 +541,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     constexpr int NWD = BF16 ? DPL / 2 : DPL;
     constexpr uint16_t kNoKey = 0xFFFF;
     __shared__ AttnShared<D, G, NR> sh;
-    __shared__ uint16_t hs[kCompactSlots];
-    __shared__ int ts[kCompactSlots];
+    __shared__ alignas(16) uint16_t hs[kCompactSlots];
+    __shared__ alignas(16) int ts[kCompactSlots];
     __shared__ int list[kCompactSlots];
     __shared__ int scan[16];
     __shared__ int thr[2];
@@ -619,17 +654,32 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     int incl = need - E;
     incl = incl < 0 ? 0 : (incl > own_eq ? own_eq : incl);
 
-    // Ordered compaction of this block's slots (thread tid: slots [tid*SPT, tid*SPT + SPT)).
+    // Ordered compaction of this block's slots (thread tid: slots [tid*SPT, tid*SPT + SPT)),
+    // read as one 8-byte and one 16-byte LDS load per thread (consecutive threads, consecutive
+    // addresses: no bank conflicts, where per-slot loads would be 8 and 16 bytes apart).
+    static_assert(SPT == 4, "slot reads sized for 4 slots per thread");
     uint16_t hv[SPT];
     int tv[SPT];
     int n_lt = 0, n_eq = 0;
+    {
+        const uint2 hw = *reinterpret_cast<const uint2*>(&hs[tid * SPT]);
+        const int4 tw = *reinterpret_cast<const int4*>(&ts[tid * SPT]);
+        hv[0] = (uint16_t)hw.x;
+        hv[1] = (uint16_t)(hw.x >> 16);
+        hv[2] = (uint16_t)hw.y;
+        hv[3] = (uint16_t)(hw.y >> 16);
+        tv[0] = tw.x;
+        tv[1] = tw.y;
+        tv[2] = tw.z;
+        tv[3] = tw.w;
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        const int i = tid * SPT + k;
-        hv[k] = i < nmine ? hs[i] : kNoKey;
-        tv[k] = i < nmine ? ts[i] : 0;
-        n_lt += hv[k] < hstar;
-        n_eq += hv[k] == hstar;
+        for (int k = 0; k < SPT; ++k) {
+            const bool mine = tid * SPT + k < nmine;
+            hv[k] = mine ? hv[k] : kNoKey;
+            tv[k] = mine ? tv[k] : 0;
+            n_lt += hv[k] < hstar;
+            n_eq += hv[k] == hstar;
+        }
     }
     int tot;
     const int packed = block_excl_scan<NT>((n_lt << 16) | n_eq, scan, tot);
@@ -729,11 +779,10 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             l_i[i] = l;
         }
     }
+    store_row_o(sh, rw, sub, o);
+    if (sub == 0) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) sh.wo[rw][i][sub * DPL + d] = o[i][d];
-        if (sub == 0) {
+        for (int i = 0; i < G; ++i) {
             sh.wml[rw][i][0] = m_i[i];
             sh.wml[rw][i][1] = l_i[i];
         }
