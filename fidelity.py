@@ -31,10 +31,11 @@ correlation between -H and z and the share of the exact top 1% keys that
 the Hamming order also puts in its top 1%.
 
 The exact references are plain fp64 numpy on the host: this is a
-measurement tool, not a path of the library.  `python -m
-hash_sparse_attention_amd.fidelity --workload llama8b_32k` runs a sweep of
-keep percentages and code lengths on the GPU and prints one table;
-`--scatter` prints the Hamming-versus-logit table instead.
+measurement tool beside the bench, not a path of the library, which is why
+it sits outside the binding package.  `python fidelity.py --workload
+llama8b_32k` runs a sweep of keep percentages and code lengths on the GPU
+and prints one table; `--scatter` prints the Hamming-versus-logit table
+instead.
 """
 from __future__ import annotations
 

@@ -450,7 +450,7 @@ def test_page_select_stage_on_tied_scores(dev, npages, seq, keep, max_keep):
 def test_fidelity_harness_matches_oracle_selection(dev):
     """The retrieval-fidelity harness, run through the library, reports the same key recall, page coverage,
     attention mass and planted recall as on the oracle's selections (the selections are equal)."""
-    from hash_sparse_attention_amd.fidelity import metrics, run_library
+    from fidelity import metrics, run_library
     wl = WORKLOADS["tiny"].with_(batch=2, ragged=(2000, 4096))
     banner("fidelity harness")
     d = make_layer(wl)
@@ -466,7 +466,7 @@ def test_fidelity_harness_matches_oracle_selection(dev):
 def test_hamming_logit_table_matches_oracle_codes(dev):
     """The Hamming-versus-logit table from the library's key and query codes equals the one from the
     oracle's codes (the codes are bit-exact), with W_h = R_h as in the pages' random-orthogonal setup."""
-    from hash_sparse_attention_amd.fidelity import hamming_logit, run_library
+    from fidelity import hamming_logit, run_library
     wl = WORKLOADS["tiny"].with_(hash_bits=64)
     banner("hamming vs logit table")
     d = make_layer(wl)
