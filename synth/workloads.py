@@ -7,9 +7,9 @@ context of 131072; Mistral-7B-Instruct has 32 layers) and the 128-bit codes of
 Appendix Table 4.  Values imitate the outlier-channel key geometry the GKR
 rotation is meant to spread (Figure 3 caption): per-channel lognormal scales,
 a few 20x outlier key channels, and queries correlated with 8 planted keys
-along the query direction whose logits sit 5 standard deviations above the
-random keys' (close to the top of 128K random logits, so attention stays a
-mixture of planted and random keys).
+along the query direction whose logits sit 8 standard deviations above the
+random keys' mean (the largest of 128K random logits is about 4.5 of them
+above it, so the planted keys lead every exact ranking).
 
 Random numbers:
   numpy path: Generator(PCG64(SeedSequence([seed, workload_id, layer]))) with
@@ -129,10 +129,10 @@ def _lengths(wl: Workload, rng) -> np.ndarray:
 
 
 def _plant(u: np.ndarray, sK_h: np.ndarray) -> np.ndarray:
-    """Key along u with u.k = 5 * std(u.k over the head's random keys)."""
+    """Key along u with u.k = 8 * std(u.k over the head's random keys)."""
     u = u.astype(np.float64)
     sigma = np.sqrt(np.sum(u ** 2 * sK_h ** 2))
-    return (5.0 * sigma / np.sum(u ** 2)) * u
+    return (8.0 * sigma / np.sum(u ** 2)) * u
 
 
 def make_layer(wl: Workload, layer: int = 0, seed: int = 0, lengths=None) -> dict:

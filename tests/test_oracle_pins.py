@@ -566,10 +566,23 @@ def test_rows_past_length_are_ignored(oracle_mod):
         assert np.array_equal(r0[k], r1[k]), k
 
 
+def _planted_hits(wl, d, r):
+    """(planted keys, planted keys whose page was kept, planted keys selected) over all (sequence, KV head)."""
+    tot = kept_n = sel_n = 0
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            kept, sel = set(r["pages"][b, h].tolist()), set(r["sel"][b, h].tolist())
+            for t in d["planted"][b, h]:
+                if t >= 0:
+                    tot += 1
+                    kept_n += int(t // wl.page_size in kept)
+                    sel_n += int(t in sel)
+    return tot, kept_n, sel_n
+
+
 def test_planted_keys_in_kept_pages_are_selected(oracle_mod):
-    """Sanity (not parity): on the tiny workload every planted key whose page survives the coarse stage is
-    kept by the Hamming stage.  (With a random rather than learned R_h the page bound is loose, so the
-    coarse stage itself need not keep every planted page.)"""
+    """End-to-end expectation 1 (sanity, not parity): on the tiny workload every planted key whose page survives
+    the coarse stage is kept by the Hamming stage."""
     wl = WORKLOADS["tiny"]
     d = make_layer(wl)
     dims, meta, codes, r = run(oracle_mod, wl, d)
@@ -582,13 +595,41 @@ def test_planted_keys_in_kept_pages_are_selected(oracle_mod):
     assert hits > 0
 
 
+@pytest.mark.parametrize("name", ["tiny", "llama8b_32k"])
+def test_hamming_stage_selects_every_planted_key(oracle_mod, name):
+    """End-to-end expectation 2: with every page kept, the Hamming stage alone selects all 8 planted keys of
+    every KV head (each sits about 27 degrees from its queries, so its code differs from theirs in far fewer
+    bits than a random key's)."""
+    wl = WORKLOADS[name]
+    d = make_layer(wl)
+    NPg = wl.max_pages
+    _, _, _, r = run(oracle_mod, wl, d, keep=np.full(wl.batch, NPg, np.int32), max_keep=NPg)
+    tot, kept_n, sel_n = _planted_hits(wl, d, r)
+    assert tot == 8 * wl.batch * wl.n_kv_heads and kept_n == tot and sel_n == tot
+
+
+def test_page_stage_keeps_planted_pages_above_chance(oracle_mod):
+    """End-to-end expectation 3: at 32K with 10% of pages kept, the coarse stage keeps planted pages at well
+    over the keep fraction (at least twice it), and each planted key whose page is kept is selected.  With a
+    random rotation the box bound of a random 16-key page sits far above any one key's logit, so a planted
+    page is not kept every time (the seeded layer keeps 19 of 64); all 8 planted keys per head reach the
+    selection only when the page stage passes them."""
+    wl = WORKLOADS["llama8b_32k"]
+    d = make_layer(wl)
+    _, _, _, r = run(oracle_mod, wl, d)
+    tot, kept_n, sel_n = _planted_hits(wl, d, r)
+    frac = float(d["keep"][0]) / wl.max_pages
+    assert tot == 64 and kept_n / tot >= 2.0 * frac
+    assert sel_n == kept_n
+
+
 # ----------------------------------------------------------------------------- fidelity harness metrics
 
 def test_fidelity_metrics_on_oracle_selections(oracle_mod):
     """The harness's metrics on known selections: selecting every key of every page (keep all, top_k >= L)
     gives recall, coverage, mass and planted recall 1 and full attention's output; the oracle's sparse
     selection gives values in [0, 1] and selects the planted keys of kept pages."""
-    from hash_sparse_attention_amd.fidelity import metrics
+    from fidelity import metrics
     wl = WORKLOADS["tiny"]
     d = make_layer(wl)
     NPg = wl.max_pages
@@ -606,7 +647,7 @@ def test_fidelity_metrics_on_oracle_selections(oracle_mod):
 def test_fidelity_recall_counts_the_exact_top_k(oracle_mod):
     """Hand-built selections: the exact top-k itself has recall 1; its first half padded with keys outside
     it has recall 1/2 (recall is measured at the selection's own size)."""
-    from hash_sparse_attention_amd.fidelity import metrics
+    from fidelity import metrics
     wl = WORKLOADS["tiny"]
     d = make_layer(wl)
     dims, meta, codes, r = run(oracle_mod, wl, d)
@@ -731,7 +772,7 @@ def test_hamming_logit_table_on_known_codes():
     """Four keys whose Hamming distances to the query are 0, 10, 20, 64 and whose logits fall 3, 2, 1, 0:
     each lands in its distance bin, the rank correlation of -H with the logit is 1 (and -1 reversed), and
     the exact top key is the Hamming top key."""
-    from hash_sparse_attention_amd.fidelity import hamming_logit, popcount64
+    from fidelity import hamming_logit, popcount64
     wl = Workload("ham_pin", 97, 1, 1, 1, 2, 4, 1, 64, 100, 4, "fp32")
     K = np.zeros((1, 1, 4, 2), np.float32)
     K[0, 0, :, 0] = [3, 2, 1, 0]
