@@ -25,8 +25,17 @@ namespace {
 // (Measured on gfx950: spreading a page over 2, 4 or 8 waves, each summing
 // part of the dimensions, streams no faster than one lane per page, and
 // issuing the first batches before the query terms are staged gains nothing.)  The
-// loads carry the nontemporal hint: every metadata line is read once.  The
-// query terms are staged once per block in LDS and read as broadcasts.
+// loads carry the nontemporal hint: every metadata line is read once.
+//
+// The query terms are block-uniform (a block covers pages of one head).  For
+// G <= 4 they reach the FMAs as scalar loads, an SGPR operand each, so the
+// stream issues no LDS reads at all; a 16-byte LDS broadcast still returns
+// 16 bytes per lane, and at G = 4 a page block needs 512 of them.  The block
+// first pulls its terms into the XCD's L2 with one coalesced round trip: the
+// projection launch has just written them, and scalar misses issued a slot
+// or two ahead would otherwise serialise.  Larger groups need more SGPRs per
+// slot than the scalar file holds without spilling, so they stage the terms
+// once per block in LDS and read them as broadcasts.
 template <int G, int U>
 __device__ __forceinline__ void bound_batch(const float4 (&v)[U], const double2* __restrict__ qs, int j0,
                                             double (&acc)[G]) {
@@ -67,6 +76,22 @@ __device__ __forceinline__ void bound_batch16(const uint4 (&v)[U], const double2
     }
 }
 
+// Every lane of the block loads its share of the head's D * G query terms
+// (all loads issued, then waited for), so the lines sit in this XCD's L2
+// before the waves read them as scalar loads.
+template <int D, int G>
+__device__ __forceinline__ void warm_query_terms(const double2* __restrict__ qg) {
+    constexpr int NQ = (D * G + 255) / 256;
+    double2 t[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const int x = threadIdx.x + r * 256;
+        t[r] = qg[x < D * G ? x : 0];
+    }
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) asm volatile("" ::"v"(t[r].x), "v"(t[r].y));  // wait for every load
+}
+
 template <int D, int G, int U, bool M16, bool PGMIN>
 __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
@@ -75,8 +100,9 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
                                                          int64_t NPB, int64_t NPmax, int share) {
     constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
+    constexpr bool SQ = G <= 4;               // query terms as scalar loads (else LDS broadcasts)
     using V4 = typename std::conditional<M16, uint4, float4>::type;
-    __shared__ double2 qs[D * G];  // (max(q,0), min(q,0)) per dimension and query head
+    __shared__ double2 qs_lds[SQ ? 1 : D * G];  // (max(q,0), min(q,0)) per dimension and query head
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
@@ -85,9 +111,14 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     if ((int64_t)blockIdx.x * 256 >= NP) return;  // block-uniform
 
     const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
-    for (int x = threadIdx.x; x < D * G; x += 256) qs[x] = qg[x];
+    if constexpr (SQ) {
+        warm_query_terms<D, G>(qg);
+    } else {
+        for (int x = threadIdx.x; x < D * G; x += 256) qs_lds[x] = qg[x];
+    }
     __syncthreads();
     if (p >= NP) return;
+    const double2* qs = SQ ? qg : qs_lds;
 
     const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     const V4* mp = reinterpret_cast<const V4*>(meta) + (bhd * NPB + p / 64) * NJ * 64 + (p & 63);
@@ -143,6 +174,9 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
 // dimension is a bit of a wave-uniform mask built by ballots, so every load
 // address is uniform plus the lane: one contiguous 256-byte (fp32) or
 // 128-byte (bf16) run per wave and dimension.  With G > 1 both sides are read.
+// For G = 1 every wave loads the D query terms itself (coalesced, two per
+// lane at D = 128) for the ballots, which also brings them into the XCD's L2,
+// and the sums read them as scalar loads: no LDS and no block barrier.
 template <int D, int G, int U, bool M16, bool PGMIN>
 __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __restrict__ meta,
                                                                const double* __restrict__ q_split,
@@ -153,7 +187,7 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
     constexpr int NS = G == 1 ? 1 : 2;  // sides read per dimension
     constexpr int NBT = D / U;          // batches of U dimensions
     static_assert(D % U == 0 && NBT % 2 == 0, "batches");
-    __shared__ double2 qs[D * G];  // (max(q,0), min(q,0)) per dimension and query head
+    __shared__ double2 qs_lds[G == 1 ? 1 : D * G];  // (max(q,0), min(q,0)) per dimension and query head
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
@@ -162,15 +196,24 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
     if ((int64_t)blockIdx.x * 256 >= NP) return;  // block-uniform
 
     const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
-    for (int x = threadIdx.x; x < D * G; x += 256) qs[x] = qg[x];
-    __syncthreads();
     // G = 1: bit d set when q_d < 0 (the min side is read).  Built while every
     // lane of the wave is active: a ballot leaves out lanes that have exited.
     const int lane = threadIdx.x & 63;
     uint64_t neg[D / 64];
+    if constexpr (G == 1) {
+        double qn[D / 64];
 #pragma unroll
-    for (int w = 0; w < D / 64; ++w) neg[w] = G == 1 ? __ballot(qs[w * 64 + lane].y != 0.0) : 0ull;
+        for (int w = 0; w < D / 64; ++w) qn[w] = qg[w * 64 + lane].y;
+#pragma unroll
+        for (int w = 0; w < D / 64; ++w) neg[w] = __ballot(qn[w] != 0.0);
+    } else {
+        for (int x = threadIdx.x; x < D * G; x += 256) qs_lds[x] = qg[x];
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < D / 64; ++w) neg[w] = 0ull;
+    }
     if (p >= NP) return;
+    const double2* qs = G == 1 ? qg : qs_lds;
 
     const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     const E* mp = reinterpret_cast<const E*>(meta) + ((bhd * NPB + p / 64) * D) * 128 + (p & 63);
@@ -199,9 +242,9 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int d = k * U + u;
-            if constexpr (G == 1) {
-                const double2 q = qs[d];
-                acc[0] = __builtin_fma(side(d) ? q.y : q.x, widen(v[u][0]), acc[0]);
+            if constexpr (G == 1) {  // the sign-selected term only: one scalar load of 8 bytes
+                const double q = reinterpret_cast<const double*>(qs)[2 * d + side(d)];
+                acc[0] = __builtin_fma(q, widen(v[u][0]), acc[0]);
             } else {
                 const double a = widen(v[u][0]), c = widen(v[u][1]);
 #pragma unroll
