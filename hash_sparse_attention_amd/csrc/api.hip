@@ -193,6 +193,11 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
         if (want >= 2 && (slots + want - 1) / want <= room) S = (int)want;
     }
     l.sel_splits = S;
+    // Each of a head's S split blocks repeats the head's page select.  Once
+    // the split blocks of all heads need more than about one and a half
+    // rounds of the GPU's 256 CUs, the repeats cost more than a launch gap:
+    // the page select then runs once per head, and the split blocks only scan.
+    l.sel_pages_apart = S > 1 && BH * (size_t)S > 384;
     l.nbins = s.Gh * s.NB + 1;
     l.part_splits = l.n_splits > S ? l.n_splits : S;
     l.partial = take(BQ * (size_t)l.part_splits * (s.D + 2) * sizeof(float));

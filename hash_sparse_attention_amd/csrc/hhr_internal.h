@@ -65,6 +65,7 @@ struct WsLayout {
     size_t q_rot, code_q, q_split, score, pages, n_pages, ham, sel, k_eff, partial, counters, kcum, total;
     size_t code_qm;  // the group's mean-query code [B][Hkv][NW] (ham_mean)
     int n_splits, sel_splits, part_splits, nbins;
+    bool sel_pages_apart;  // split select: the page select runs once per head in a launch of its own
     size_t ghist_off;  // u32 entries from counters to the head histograms
     int n_clear;       // u32 entries the query prep clears from counters
 };

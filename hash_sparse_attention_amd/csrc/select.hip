@@ -1224,8 +1224,14 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
-    return a.s.NW == 1 ? select_pages_nw<1, true>(a, a.lay.sel_splits, st)
-                       : select_pages_nw<2, true>(a, a.lay.sel_splits, st);
+    const int S = a.lay.sel_splits;
+    if (a.lay.sel_pages_apart) {  // the page list once per head, then S key-scan blocks per head read it
+        const hipError_t e = select_pages_nw<1, false>(a, 1, st);
+        if (e != hipSuccess) return e;
+        return a.s.NW == 1 ? select_launch(select_kernel<1, false, true>, a, S, st)
+                           : select_launch(select_kernel<2, false, true>, a, S, st);
+    }
+    return a.s.NW == 1 ? select_pages_nw<1, true>(a, S, st) : select_pages_nw<2, true>(a, S, st);
 }
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t st) {
     return select_pages_nw<1, false>(a, 1, st);  // the page half does not depend on the code width

@@ -575,6 +575,11 @@ PATH_SHAPES = [
     # More than 8192 kept pages: the page list stays in the workspace, one key-select block per head.
     # Sequence 0 keeps 7500 pages (its list fits in LDS), sequence 1 all 9216 (it does not).
     ("keep_9216_pages", Workload("k9k", 184, 2, 8, 2, 64, 36864, 4, 64, 100, 3000, "bf16")),
+    # Many heads with split key selects: 16 x 8 heads keep up to 512 pages (8192 slots), so each head needs 4
+    # compaction blocks and the 512 split blocks exceed one and a half rounds of the CUs: the page select runs
+    # once per head in its own launch and the split blocks read its list.
+    ("many_heads_pages_apart", Workload("mhp", 185, 16, 32, 8, 64, 16384, 16, 64, 50, 1024, "bf16", outliers=2,
+                                        ragged=(12000, 16384))),
 ]
 PATH_LENGTHS = {"keep_9216_pages": [30000, 36864]}
 
