@@ -33,9 +33,12 @@ namespace {
 // 16 bytes per lane, and at G = 4 a page block needs 512 of them.  The block
 // first pulls its terms into the XCD's L2 with one coalesced round trip: the
 // projection launch has just written them, and scalar misses issued a slot
-// or two ahead would otherwise serialise.  Larger groups need more SGPRs per
-// slot than the scalar file holds without spilling, so they stage the terms
-// once per block in LDS and read them as broadcasts.
+// or two ahead would otherwise serialise.  Larger groups, and bf16 metadata
+// (a 16-byte slot then holds 4 dimensions: 64 SGPRs of terms per slot at
+// G = 4), need more SGPRs per slot than the scalar file holds without
+// stalling or spilling, so they stage the terms once per block in LDS and read
+// them as broadcasts (measured: bf16 metadata at G = 4 ran 17.6 us per launch
+// on scalar terms against 11.6 us on LDS).
 template <int G, int U>
 __device__ __forceinline__ void bound_batch(const float4 (&v)[U], const double2* __restrict__ qs, int j0,
                                             double (&acc)[G]) {
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
                                                          int64_t NPB, int64_t NPmax, int share) {
     constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
-    constexpr bool SQ = G <= 4;               // query terms as scalar loads (else LDS broadcasts)
+    constexpr bool SQ = G <= 4 && !M16;       // query terms as scalar loads (else LDS broadcasts)
     using V4 = typename std::conditional<M16, uint4, float4>::type;
     __shared__ double2 qs_lds[SQ ? 1 : D * G];  // (max(q,0), min(q,0)) per dimension and query head
     const int h = blockIdx.y, b = blockIdx.z;
