@@ -44,6 +44,8 @@ MUTANTS = {
     "forced_keys_compete": ("if (t >= L || t < s_end || t >= w_start) continue;", "if (t >= L) continue;"),
     "window_one_short": ("for (int64_t t = w_start; t < L; ++t) sel[", "for (int64_t t = w_start + 1; t < L; ++t) sel["),
     "value_from_key_rows": ("o[d] += wgt * (double)elem(V, row + d, bf);", "o[d] += wgt * (double)elem(K, row + d, bf);"),
+    "mean_query_first_head_only": ("for (int i = 0; i < G; ++i) acc += q[i * D + d];",
+                                   "for (int i = 0; i < 1; ++i) acc += q[i * D + d];"),
 }
 
 

@@ -896,6 +896,43 @@ def test_hamming_group_mean_uses_the_mean_query_code(oracle_mod, name):
                     assert r["ham"][b, h, j * P + q] == want
 
 
+def test_hamming_group_mean_code_on_exact_means(oracle_mod):
+    """Independent of the oracle's mean and projection: with W_h = I (code bit d = [x_d > 0]) and group
+    queries q_i = m + delta_i whose deltas sum to zero in small dyadic values, the fp32 sum and the division
+    by G = 4 are exact, so the mean is m by construction.  Every kept candidate's distance must then be
+    popcount([m > 0] XOR [k_t > 0]) over the 64 dimensions; the shared (sum over heads) distances must
+    differ somewhere, so the check is not vacuous."""
+    wl = WORKLOADS["tiny"].with_(batch=2, keep_percent=100)
+    d = make_layer(wl)
+    G, D, P = wl.group, wl.head_dim, wl.page_size
+    rng = np.random.default_rng(7)
+    Q = np.zeros((wl.batch, wl.n_q_heads, D), np.float32)
+    means = np.zeros((wl.batch, wl.n_kv_heads, D), np.float32)
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            m = rng.choice([-1, 1], D) * rng.integers(2, 9, D) * 0.5   # +-1 .. +-4 in halves, never 0
+            delta = rng.integers(-12, 13, (G - 1, D)) * 0.25            # up to +-3 in quarters
+            delta = np.vstack([delta, -delta.sum(axis=0)])              # columns sum to exactly 0
+            Q[b, h * G:(h + 1) * G] = (m[None, :] + delta).astype(np.float32)
+            means[b, h] = m
+    d["Q"] = Q
+    d["W"] = np.ascontiguousarray(np.broadcast_to(np.eye(D, dtype=np.float32), (wl.n_kv_heads, D, D)))
+    keep = np.full(wl.batch, wl.max_pages, np.int32)
+    _, _, _, rm = run(oracle_mod, wl.with_(hamming_group=1), d, keep=keep, max_keep=wl.max_pages)
+    _, _, _, rs = run(oracle_mod, wl, d, keep=keep, max_keep=wl.max_pages)
+    K = f32(d["K"], wl)
+    differs = False
+    for b in range(wl.batch):
+        L = int(d["seq_len"][b])
+        for h in range(wl.n_kv_heads):
+            want = ((K[b, h, :L] > 0) != (means[b, h] > 0)[None, :]).sum(axis=1)
+            got = rm["ham"][b, h, :L]  # every page kept: slot j * P + r is key j * P + r
+            assert (rm["pages"][b, h, :-(-L // P)] == np.arange(-(-L // P))).all()
+            assert np.array_equal(got.astype(np.int64), want)
+            differs |= bool((rs["ham"][b, h, :L] != got).any())
+    assert differs
+
+
 def test_hamming_group_mean_with_one_head_is_the_plain_step(oracle_mod):
     """With G = 1 the mean query is the query: both aggregations give the same distances and keys."""
     wl = WORKLOADS["tiny"].with_(n_q_heads=2)
