@@ -483,8 +483,8 @@ def main_encode(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
                     help="workload name (default: llama8b_128k; qwen7b_b16 for --mode encode)")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
@@ -647,10 +647,10 @@ def main_hhr(args):
     flush = args.flush if args.flush is not None else wl.layers == 1
     fbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
 
-    def timed(fn, n):
+    def timed(fn, n, cold=True):
         evs = []
         for i in range(n):
-            if fbuf is not None:
+            if fbuf is not None and cold:
                 fbuf.fill_(i & 0xff)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -672,8 +672,12 @@ def main_hhr(args):
         f"(events); {t_wall / args.steps * 1e3:.3f} ms/step wall" + (" incl. cache flushes" if flush else ""))
     eager = None
     if graph is not None:
-        eager = spread(timed(step, min(args.steps, 10)))
+        eager = spread(timed(step, min(args.steps, 20)))
         log(f"eager (no graph) step: median {eager[0]:.3f} ms")
+    warm = None
+    if flush:  # the same steps back to back, caches left as the previous step leaves them
+        warm = spread(timed(run, min(args.steps, 20), cold=False))
+        log(f"warm (no flush) step: median {warm[0]:.3f} ms")
 
     seq = layers[0]["seq_len_host"]
     keep = layers[0]["keep_host"]
@@ -745,6 +749,7 @@ def main_hhr(args):
         "step_ms_median": med, "step_ms_p10": p10, "step_ms_p90": p90,
         "eager_step_ms_median": eager[0] if eager else None,
         "eager_us_per_layer_median": eager[0] * 1e3 / wl.layers if eager else None,
+        "warm_us_per_layer_median": warm[0] * 1e3 / wl.layers if warm else None,
         "context_keys_per_s": keys_step / (ms_per_step * 1e-3),
         "hamming_candidates_per_s": cand_step / (ms_per_step * 1e-3),
         "hbm_algorithmic_bytes_per_layer": bytes_layer,
