@@ -183,12 +183,12 @@ def cpu_baseline(wl, dims, layers, gpu_sel, gpu_out):
         sample = (f"sequences {bs} of {wl.batch} ({keys} context keys over {wl.n_kv_heads} KV heads): oracle encode "
                   f"+ decode, decode median of 3 ({t:.3f} s each)")
         value, us_layer, units = keys / t, t * 1e6, len(bs) * wl.n_kv_heads
-    out = dict(value=value, unit="keys/s", cores=host_cores(), threads=min(oracle.max_threads(), units),
+    out = dict(value=value, unit="keys/s", cores=min(oracle.max_threads(), units), host_cores=host_cores(),
                kind="oracle", us_per_layer=us_layer, sample=sample, cpu=_cpu_model(),
                encode_keys_per_s=enc_keys / enc_t if enc_t > 0 else None,
                parity={"selected_keys_equal": sel_ok, "attention_max_abs_diff": err,
                        "encode_codes_and_page_bounds_equal": enc_ok})
-    log(f"cpu baseline {value:.3g} keys/s ({out['threads']} threads on {out['cores']} cores); "
+    log(f"cpu baseline {value:.3g} keys/s ({out['cores']} threads of {out['host_cores']} host cores); "
         f"selections equal {sel_ok}, attention max |diff| {err:.2e}, encode equal {enc_ok}")
     return out
 
@@ -344,7 +344,7 @@ def main_topk(args):
         err = float(np.abs(ref_out[0].cpu().numpy().astype(np.float64) - r["out"]).max())
         sel_ok = bool(np.array_equal(ref_sel[0].cpu().numpy(), r["sel"]))
         line["cpu_baseline"] = dict(
-            value=keys / t, unit="keys/s", cores=host_cores(), threads=min(oracle.max_threads(), wl.batch * wl.n_kv_heads),
+            value=keys / t, unit="keys/s", cores=min(oracle.max_threads(), wl.batch * wl.n_kv_heads), host_cores=host_cores(),
             kind="oracle",
             us_per_layer=t * 1e6, cpu=_cpu_model(),
             sample=(f"layer 0 of {wl.layers}: oracle TopK step (all {wl.n_kv_heads} KV heads, {int(seq[0])} keys), "
@@ -446,8 +446,8 @@ def main_encode(args):
             ok &= bool(np.array_equal(gc[i, :, s0:s1], oc[i, :, s0:s1]))
             ok &= bool(np.array_equal(gm[i, :, s0 // P:-(-s1 // P)], om[i, :, s0 // P:-(-s1 // P)]))
         sample_keys = int(new[sample].sum()) * wl.n_kv_heads
-        cpu = dict(value=sample_keys / t, unit="keys/s", cores=host_cores(),
-                   threads=min(oracle.max_threads(), len(sample) * wl.n_kv_heads), kind="oracle",
+        cpu = dict(value=sample_keys / t, unit="keys/s", cores=min(oracle.max_threads(), len(sample) * wl.n_kv_heads),
+                   host_cores=host_cores(), kind="oracle",
                    sample=(f"sequences {sample} of {wl.batch} ({sample_keys} new keys over {wl.n_kv_heads} KV heads): "
                            f"oracle encode of the same chunk, median of 3 ({t:.3f} s each)"),
                    cpu=_cpu_model(), parity={"codes_and_page_bounds_equal": ok})
