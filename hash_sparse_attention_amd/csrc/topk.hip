@@ -49,15 +49,20 @@ constexpr int kLogitResident = 4 * 256;  // blocks the GPU holds at once (LDS: 4
 
 
 // The 8 16-byte pieces this lane loads of one 64-row tile chunk: rows
-// t0 + 8j + lrow, bytes [c*128 + lslot*16, +16) of each row.
+// t0 + 8j + lrow, bytes [c*128 + lslot*16, +16) of each row.  `filler`: the
+// loop's last refill, whose data is never used; it keeps the load count fixed
+// (so the waits stay exact) but every lane reads the same 16 bytes, one cache
+// line per instruction instead of a whole chunk (at 128K a wave has only 8
+// chunks, so re-reading one was 12% of the stream's bytes).
 template <int RB>
 __device__ __forceinline__ void tile_load(u32x4 (&v)[8], const char* __restrict__ kbase, int t0, int T, int c,
-                                          int lrow, int lslot) {
+                                          int lrow, int lslot, bool filler = false) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        int t = t0 + 8 * j + lrow;
+        int t = filler ? t0 : t0 + 8 * j + lrow;
         t = t < T ? t : T - 1;  // rows past the capacity are never used
-        v[j] = load_stream16(kbase + (int64_t)t * RB + c * 128 + lslot * 16);  // K is read once
+        const int off = filler ? 0 : c * 128 + lslot * 16;
+        v[j] = load_stream16(kbase + (int64_t)t * RB + off);  // K is read once
     }
 }
 
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(256) void topk_logit_kernel(const void* __restrict_
         const int na = step + 2 < NS ? step + 2 : step;
         tile_load<D * ES>(B, kbase, t_of(step + 1), T, cb, lrow, lslot);
         stage_chunk(A, st, lrow, lslot);
-        tile_load<D * ES>(A, kbase, t_of(na), T, na % NC, lrow, lslot);
+        tile_load<D * ES>(A, kbase, t_of(na), T, na % NC, lrow, lslot, na == step);
         logit_chunk<D, BF16, G>(st, lane, qh + ca * CD * G, ca == 0, acc);
         if constexpr (NC == 1) logit_finish<G>(acc, t_of(step) + lane, L, T, sc, lh);
         else if constexpr (NC > 2) {
