@@ -351,6 +351,7 @@ def main_topk(args):
                     f"median of 3 ({t:.3f} s each)"),
             layer0_parity={"selected_keys_equal": sel_ok, "attention_max_abs_diff": err})
         log(f"cpu baseline {keys / t:.3g} keys/s; layer-0 parity sel={sel_ok} err={err:.2e}")
+    check_line(line)
     print(json.dumps(line), flush=True)
 
 
@@ -477,6 +478,7 @@ def main_encode(args):
         },
         "cpu_baseline": cpu,
     }
+    check_line(line)
     print(json.dumps(line), flush=True)
 
 
@@ -562,6 +564,37 @@ def spread(ms):
     import numpy as np
     a = np.asarray(ms, dtype=np.float64)
     return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+LINE_KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+             "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline")
+ROOFLINE_KEYS = ("bound", "achieved", "peak", "unit", "frac", "traffic")
+CPU_KEYS = ("value", "unit", "cores", "kind", "sample")
+
+
+def check_line(line):
+    """The result line's contract: every field present, the roofline and CPU-baseline objects complete, the
+    numbers finite.  Raises ValueError naming what is wrong (the line is then not printed)."""
+    import math
+    missing = [k for k in LINE_KEYS if k not in line]
+    if missing:
+        raise ValueError(f"result line lacks {missing}")
+    if not isinstance(line["config"], dict) or "workload" not in line["config"]:
+        raise ValueError("config must name the workload")
+    r = line["roofline"]
+    if not isinstance(r, dict) or [k for k in ROOFLINE_KEYS if k not in r]:
+        raise ValueError(f"roofline lacks {[k for k in ROOFLINE_KEYS if k not in (r or {})]}")
+    if r["bound"] not in ("hbm", "mfma", "alu"):
+        raise ValueError(f"roofline bound {r['bound']!r}")
+    c = line["cpu_baseline"]
+    if c is not None and [k for k in CPU_KEYS if k not in c]:
+        raise ValueError(f"cpu_baseline lacks {[k for k in CPU_KEYS if k not in c]}")
+    for k, v in (("value", line["value"]), ("ms_per_step", line["ms_per_step"]), ("roofline.achieved", r["achieved"]),
+                 ("roofline.frac", r["frac"])):
+        if not isinstance(v, (int, float)) or not math.isfinite(v) or v <= 0:
+            raise ValueError(f"{k} = {v!r}")
+    if abs(r["frac"] - r["achieved"] / r["peak"]) > 1e-9 * max(1.0, r["frac"]):
+        raise ValueError("roofline.frac is not achieved / peak")
 
 
 def host_cores():
@@ -771,6 +804,7 @@ def main_hhr(args):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, dims, layers, ref_sel, ref_out)
+    check_line(line)
     print(json.dumps(line), flush=True)
 
 

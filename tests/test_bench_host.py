@@ -142,3 +142,30 @@ def test_counter_traffic_only_for_the_profiled_workload():
     for other in (wl.with_(meta_bf16=True), wl.with_(meta_split=True), wl.with_(per_head=True),
                   WORKLOADS["qwen7b_b16"]):
         assert bench.traffic_from_profile(other) is None
+
+
+def _line():
+    return {"metric": "m", "value": 2.0e10, "unit": "keys/s", "n_gpus": 1, "steps": 100, "warmup": 10,
+            "ms_per_step": 1.6, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", "config": {"workload": "w"},
+            "roofline": {"bound": "hbm", "achieved": 5000.0, "peak": 8000.0, "unit": "GB/s", "frac": 0.625,
+                         "traffic": None},
+            "cpu_baseline": {"value": 1.4e8, "unit": "keys/s", "cores": 8, "kind": "oracle", "sample": "s"}}
+
+
+def test_result_line_contract_is_checked():
+    """Every mode checks its line before printing: a complete line passes; a missing field, an incomplete
+    roofline or CPU baseline, a non-finite value or an inconsistent fraction is refused."""
+    bench.check_line(_line())
+    bench.check_line(dict(_line(), cpu_baseline=None))
+    for bad in (
+        {k: v for k, v in _line().items() if k != "roofline"},
+        dict(_line(), config={"model": "x"}),
+        dict(_line(), roofline={k: v for k, v in _line()["roofline"].items() if k != "traffic"}),
+        dict(_line(), roofline=dict(_line()["roofline"], bound="dram")),
+        dict(_line(), roofline=dict(_line()["roofline"], frac=0.5)),
+        dict(_line(), cpu_baseline={"value": 1.0, "unit": "keys/s"}),
+        dict(_line(), value=float("nan")),
+    ):
+        with pytest.raises(ValueError):
+            bench.check_line(bad)
