@@ -35,6 +35,15 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Max over the 16 lanes of a DPP row, returned to every lane of the row.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, __int_as_float(dpp_i<kRowRor8, 0xf>(0, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowRor4, 0xf>(0, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowRor2, 0xf>(0, __float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_i<kRowRor1, 0xf>(0, __float_as_int(x))));
+    return x;
+}
+
 // Load this lane's D/16 elements of a K/V/Q row as raw 32-bit words.
 template <int D, bool BF16>
 __device__ __forceinline__ void load_slice(const void* base, int64_t row, int sub, uint32_t (&w)[BF16 ? D / 32 : D / 16]) {
@@ -53,6 +62,8 @@ __device__ __forceinline__ void load_slice(const void* base, int64_t row, int su
 }
 
 typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2;
+typedef __bf16 __attribute__((ext_vector_type(8))) bf16x8;
+typedef float __attribute__((ext_vector_type(4))) f32x4;
 
 // Dot product of this lane's slices of a query and a key: bf16 pairs through
 // the packed bf16 dot instruction with fp32 accumulation, fp32 by FMAs.
@@ -520,8 +531,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
 //    first `need` in slot order win ties) from their cumulative histograms;
 //  - compacts its own selected keys, in slot order (ascending key index),
 //    into sel at its offset and into an LDS list;
-//  - runs gather attention over that list (16-lane rows, online softmax over
-//    batches of 16 * NI keys) and merges with the other blocks as above.
+//  - runs gather attention over that list and merges with the other blocks
+//    as above.  bf16 K/V: the scores come from the matrix cores, 16 keys per
+//    wave per instruction group, and the weights reach 16-lane rows through
+//    LDS for the fp32 weight x V sums; fp32 K/V: 16-lane rows with online
+//    softmax over batches of 16 * NI keys.
 constexpr int kCompactThreads = 512;
 
 template <int D, bool BF16, int G>
@@ -718,11 +732,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     }
     __syncthreads();
 
-    // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
     const int64_t kvb = data_head(b, h, Hkv, share) * T;  // rows of the unit's data head
-    uint32_t qw[G][NWD];  // this lane's slice of each query, raw
-#pragma unroll
-    for (int i = 0; i < G; ++i) load_slice<D, BF16>(Q, q0 + i, sub, qw[i]);
     float m_i[G], l_i[G], o[G][DPL];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -731,6 +741,150 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
 #pragma unroll
         for (int d = 0; d < DPL; ++d) o[i][d] = 0.f;
     }
+    if constexpr (BF16) {
+        // Scores on the matrix cores.  Each wave takes groups of 16 consecutive entries; one
+        // v_mfma_f32_16x16x32_bf16 per 32 dimensions multiplies the queries (A: row i = head i, zero rows
+        // past G) by the gathered keys (B: column j = key j) into S[head 4 (l / 16) + r][key l % 16], held
+        // in component r of lane l.  Lane l supplies dimensions 32 s + 8 (l / 16) + [0, 8) of slice s, so
+        // the four lanes of a key read 64 contiguous bytes per slice; the queries use the same permutation
+        // of the dimensions, which leaves every dot product unchanged.  bf16 products are exact and the
+        // sums fp32, as in the dot-product path.  The online softmax runs in that layout (row maxima and
+        // sums over the 16 keys by DPP); the weights go through a per-wave LDS tile [key][head] -- the
+        // slot staging array, free after the compaction -- to the 16-lane rows, which add weight x V in
+        // fp32 for their own keys (row r of a wave: keys r, r + 4, r + 8, r + 12 of each group).
+        constexpr int KS = D / 32;
+        constexpr int NGRP = 2;                      // groups per wave per batch
+        constexpr int STEP = (NT / 64) * 16 * NGRP;  // entries per block per batch
+        static_assert(D % 32 == 0 && G <= 8, "score tiles hold 8 heads");
+        static_assert(sizeof(ts) >= (NT / 64) * NGRP * 16 * 8 * sizeof(float), "weight tiles fit the staging array");
+        const int wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
+        float* pt = reinterpret_cast<float*>(ts) + wv * (NGRP * 16 * 8);  // [group][key][8 heads]
+        bf16x8 qa[KS];
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (ln < G)
+                w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Q) + (q0 + ln) * D + sl * 32 + 8 * gq);
+            qa[sl] = __builtin_bit_cast(bf16x8, w);
+        }
+        float mr[4], lr[4];  // running max and (per-lane part of the) weight sum of heads 4 gq + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            mr[r] = -__builtin_inff();
+            lr[r] = 0.f;
+        }
+        for (int e0 = 0; e0 < cnt; e0 += STEP) {
+            int tk[NGRP], tv[NGRP][4];
+            bool okk[NGRP];
+#pragma unroll
+            for (int g = 0; g < NGRP; ++g) {
+                const int eb = e0 + (g * (NT / 64) + wv) * 16;
+                okk[g] = eb + ln < cnt;
+                const int t = list[okk[g] ? eb + ln : 0];
+                tk[g] = (t < 0 || t >= L) ? 0 : t;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ev = eb + gq + 4 * q;
+                    const int u = list[ev < cnt ? ev : 0];
+                    tv[g][q] = (u < 0 || u >= L) ? 0 : u;
+                }
+            }
+            u32x4 kb[NGRP][KS];
+            uint32_t vw[NGRP][4][NWD];
+#pragma unroll
+            for (int g = 0; g < NGRP; ++g)
+#pragma unroll
+                for (int sl = 0; sl < KS; ++sl)
+                    kb[g][sl] = load_stream16(static_cast<const uint16_t*>(K) + (kvb + tk[g]) * D + sl * 32 + 8 * gq);
+#pragma unroll
+            for (int g = 0; g < NGRP; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) load_slice<D, BF16>(V, kvb + tv[g][q], sub, vw[g][q]);
+            f32x4 c[NGRP];
+#pragma unroll
+            for (int g = 0; g < NGRP; ++g) {
+                c[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < KS; ++sl)
+                    c[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[sl], __builtin_bit_cast(bf16x8, kb[g][sl]), c[g],
+                                                                  0, 0, 0);
+            }
+            float fr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float sv[NGRP];
+                float bm = -__builtin_inff();
+#pragma unroll
+                for (int g = 0; g < NGRP; ++g) {
+                    sv[g] = okk[g] ? c[g][r] * scale : -__builtin_inff();
+                    bm = fmaxf(bm, sv[g]);
+                }
+                const float mn = fmaxf(mr[r], row_max16(bm));
+                fr[r] = mr[r] == -__builtin_inff() ? 0.f : __expf(mr[r] - mn);
+                float ls = lr[r] * fr[r];
+#pragma unroll
+                for (int g = 0; g < NGRP; ++g) {
+                    sv[g] = sv[g] == -__builtin_inff() ? 0.f : __expf(sv[g] - mn);
+                    ls += sv[g];
+                    c[g][r] = sv[g];  // the weight replaces the score
+                }
+                lr[r] = ls;
+                mr[r] = mn;
+            }
+            if (4 * gq < G) {
+#pragma unroll
+                for (int g = 0; g < NGRP; ++g)
+                    *reinterpret_cast<float4*>(pt + (g * 16 + ln) * 8 + 4 * gq) = make_float4(c[g][0], c[g][1], c[g][2], c[g][3]);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // Rescale the row's accumulators (head i's factor is in lane 16 (i / 4), component i % 4), then
+            // add the row's keys' weight x V.
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fr[i % 4]), 16 * (i / 4)));
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) o[i][d] *= f;
+            }
+#pragma unroll
+            for (int g = 0; g < NGRP; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float* wq = pt + (g * 16 + gq + 4 * q) * 8;
+                    float wgt[8];
+#pragma unroll
+                    for (int i4 = 0; i4 < (G + 3) / 4; ++i4) {
+                        const float4 w4 = *reinterpret_cast<const float4*>(wq + 4 * i4);
+                        wgt[4 * i4] = w4.x;
+                        wgt[4 * i4 + 1] = w4.y;
+                        wgt[4 * i4 + 2] = w4.z;
+                        wgt[4 * i4 + 3] = w4.w;
+                    }
+#pragma unroll
+                    for (int i = 0; i < G; ++i)
+#pragma unroll
+                        for (int d = 0; d < DPL; ++d)
+                            o[i][d] = __builtin_fmaf(wgt[i], slice_elem<D, BF16>(vw[g][q], d), o[i][d]);
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        // The wave's (max, weight sum) per head: its four rows share the max and each reports a quarter of
+        // the sum, so the block merge weighs their partial outputs alike.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lr[r] = row_sum16(lr[r]);
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            m_i[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr[i % 4]), 16 * (i / 4)));
+            l_i[i] = 0.25f * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr[i % 4]), 16 * (i / 4)));
+        }
+    } else {
+    // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
+    uint32_t qw[G][NWD];  // this lane's slice of each query, raw
+#pragma unroll
+    for (int i = 0; i < G; ++i) load_slice<D, BF16>(Q, q0 + i, sub, qw[i]);
     for (int e0 = 0; e0 < cnt; e0 += NR * NI) {
         int t[NI];
         bool ok[NI];
@@ -778,6 +932,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             m_i[i] = mb;
             l_i[i] = l;
         }
+    }
     }
     store_row_o(sh, rw, sub, o);
     if (sub == 0) {
