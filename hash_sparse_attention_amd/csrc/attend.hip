@@ -108,12 +108,15 @@ __device__ __forceinline__ float4 ld_agent4(const float* p) {
 
 constexpr int kMergeRound = 32;  // split partials merged per round by the last block
 
-template <int D, int G, int NR = 16>
+// NR partials (16-lane rows, or waves) of a block of NT threads.
+template <int D, int G, int NR = 16, int NT = NR * 16>
 struct alignas(16) AttnShared {
-    float wo[NR][G][D];     // row partials (o), reused by the final reduction
-    float wml[NR][G][2];    // row partials (m, l)
+    static constexpr int kWo = NR * G * D > 4 * NT ? NR * G * D : 4 * NT;
+    float wo_[kWo];         // partials (o) [NR][G][D], reused by the final reduction (NT float4)
+    float wml[NR][G][2];    // partials (m, l)
     float cml[G][kMergeRound][2];
-    float lred[NR * 16];
+    float lred[NT];
+    __device__ __forceinline__ float* wo(int r, int i) { return wo_ + (r * G + i) * D; }
     float fr[NR][G];        // row weights exp(m_r - M) of the block combine
     float bml[G][2];        // block (M, L) per query head
     int last_flag;
@@ -127,8 +130,8 @@ struct alignas(16) AttnShared {
 // differs from bit 3 store their upper half first, so within every 8 and every
 // 16 consecutive lanes a store's addresses cover distinct banks.  The stored
 // layout is unchanged; only which store carries which half differs.
-template <int D, int G, int NR, int DPL>
-__device__ __forceinline__ void store_row_o(AttnShared<D, G, NR>& sh, int rw, int sub, const float (&o)[G][DPL]) {
+template <int D, int G, int NR, int NT, int DPL>
+__device__ __forceinline__ void store_row_o(AttnShared<D, G, NR, NT>& sh, int rw, int sub, const float (&o)[G][DPL]) {
     if constexpr (DPL == 8) {
         const bool hi_first = ((sub >> 2) ^ (sub >> 3)) & 1;
 #pragma unroll
@@ -139,19 +142,19 @@ __device__ __forceinline__ void store_row_o(AttnShared<D, G, NR>& sh, int rw, in
                 a[d] = hi_first ? o[i][4 + d] : o[i][d];
                 c[d] = hi_first ? o[i][d] : o[i][4 + d];
             }
-            float* base = &sh.wo[rw][i][sub * DPL];
+            float* base = sh.wo(rw, i) + sub * DPL;
             *reinterpret_cast<float4*>(base + (hi_first ? 4 : 0)) = make_float4(a[0], a[1], a[2], a[3]);
             *reinterpret_cast<float4*>(base + (hi_first ? 0 : 4)) = make_float4(c[0], c[1], c[2], c[3]);
         }
     } else if constexpr (DPL == 4) {  // 16 bytes a lane: consecutive lanes, consecutive 16-byte slots
 #pragma unroll
         for (int i = 0; i < G; ++i)
-            *reinterpret_cast<float4*>(&sh.wo[rw][i][sub * DPL]) = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+            *reinterpret_cast<float4*>(sh.wo(rw, i) + sub * DPL) = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
     } else {
 #pragma unroll
         for (int i = 0; i < G; ++i)
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) sh.wo[rw][i][sub * DPL + d] = o[i][d];
+            for (int d = 0; d < DPL; ++d) sh.wo(rw, i)[sub * DPL + d] = o[i][d];
     }
 }
 
@@ -160,8 +163,8 @@ __device__ __forceinline__ void store_row_o(AttnShared<D, G, NR>& sh, int rw, in
 // L_i = sum_r f_r l_r, one thread per (i, r) with butterflies over the rows
 // (NR is a power of two, so a row group never straddles a wave).  Every
 // thread of the block calls it, after a barrier that follows the row writes.
-template <int D, int G, int NR>
-__device__ __forceinline__ void row_weights(AttnShared<D, G, NR>& sh) {
+template <int D, int G, int NR, int NT>
+__device__ __forceinline__ void row_weights(AttnShared<D, G, NR, NT>& sh) {
     static_assert((NR & (NR - 1)) == 0 && NR <= 64, "row groups within a wave");
     const int tid = threadIdx.x;
     if (tid < G * NR) {
@@ -196,13 +199,13 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
                                              float* __restrict__ out) {
     constexpr int NP = NT / 16;
     const int tid = threadIdx.x;
-    row_weights<D, G, NP>(sh);
+    row_weights(sh);
     if (has_keys) {
         for (int x = tid; x < G * D; x += NT) {
             const int i = x / D, d = x % D;
             float acc = 0.f;
 #pragma unroll
-            for (int r = 0; r < NP; ++r) acc = __builtin_fmaf(sh.wo[r][i][d], sh.fr[r][i], acc);
+            for (int r = 0; r < NP; ++r) acc = __builtin_fmaf(sh.wo(r, i)[d], sh.fr[r][i], acc);
             st_agent(part_o + ((q0 + i) * stride + split) * D + d, acc);
             if (d == 0) {
                 st_agent(part_ml + ((q0 + i) * stride + split) * 2, sh.bml[i][0]);
@@ -286,7 +289,7 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
         __syncthreads();
     }
     // Sum the groups and normalise.
-    float4* red = reinterpret_cast<float4*>(&sh.wo[0][0][0]);  // NGR * NC <= NP * G * D / 4 float4
+    float4* red = reinterpret_cast<float4*>(sh.wo_);  // NGR * NC <= NT float4
     if (act) {
         red[g * NC + c] = acc;
         sh.lred[g * NC + c] = Lacc;
@@ -316,18 +319,17 @@ __device__ __forceinline__ void merge_splits(AttnShared<D, G, NT / 16>& sh, bool
 // kMaxPolls rounds the head's outputs are set to NaN rather than hang.
 constexpr int kMaxPolls = 1 << 20;
 
-template <int D, int G, int NT>
-__device__ __forceinline__ void merge_polled(AttnShared<D, G, NT / 16>& sh, int split, int stride, int S,
+template <int D, int G, int NT, int NP>
+__device__ __forceinline__ void merge_polled(AttnShared<D, G, NP, NT>& sh, int split, int stride, int S,
                                              int64_t q0, float* __restrict__ part_o, float* __restrict__ part_ml,
                                              float* __restrict__ out) {
-    constexpr int NP = NT / 16;
     const int tid = threadIdx.x;
-    row_weights<D, G, NP>(sh);
+    row_weights(sh);
     for (int x = tid; x < G * D; x += NT) {
         const int i = x / D, d = x % D;
         float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < NP; ++r) acc = __builtin_fmaf(sh.wo[r][i][d], sh.fr[r][i], acc);
+        for (int r = 0; r < NP; ++r) acc = __builtin_fmaf(sh.wo(r, i)[d], sh.fr[r][i], acc);
         st_agent(part_o + ((q0 + i) * stride + split) * D + d, acc);
         if (d == 0) {
             st_agent(part_ml + ((q0 + i) * stride + split) * 2, sh.bml[i][0]);
@@ -337,17 +339,20 @@ __device__ __forceinline__ void merge_polled(AttnShared<D, G, NT / 16>& sh, int 
     if (!sh.last_flag) return;
 
     // Columns of 4 output floats; NGR groups of threads split the splits, NB
-    // loads each per round, so one batch covers a round of kMergeRound.
-    constexpr int NC = G * D / 4, NGR = NT / NC, NB = 16;
-    static_assert(NGR >= 1 && NB * NGR >= kMergeRound, "one batch per merge round");
-    constexpr int NML = (G * kMergeRound + NT - 1) / NT;
+    // loads each per round, so one batch covers a round of RND splits.  At
+    // most 8 loads a thread keep the polling loop's addresses in registers.
+    constexpr int NC = G * D / 4, NGR = NT / NC;
+    constexpr int NB = (kMergeRound + NGR - 1) / NGR < 8 ? (kMergeRound + NGR - 1) / NGR : 8;
+    constexpr int RND = NB * NGR < kMergeRound ? NB * NGR : kMergeRound;
+    static_assert(NGR >= 1 && NB * NGR >= RND, "one batch per merge round");
+    constexpr int NML = (G * RND + NT - 1) / NT;
     const int c = tid % NC, g = tid / NC, qi = c / (D / 4);
     const bool act = g < NGR;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float Lacc = 0.f, Mrun = -__builtin_inff();
     bool failed = false;
-    for (int s0 = 0; s0 < S && !failed; s0 += kMergeRound) {
-        const int ns = S - s0 < kMergeRound ? S - s0 : kMergeRound;
+    for (int s0 = 0; s0 < S && !failed; s0 += RND) {
+        const int ns = S - s0 < RND ? S - s0 : RND;
         const float* po = part_o + ((q0 + qi) * stride + s0) * D + (c % (D / 4)) * 4;
         float2 ml[NML];
         float4 v[NB];
@@ -411,7 +416,7 @@ __device__ __forceinline__ void merge_polled(AttnShared<D, G, NT / 16>& sh, int 
         __syncthreads();
     }
     // Sum the groups and normalise.
-    float4* red = reinterpret_cast<float4*>(&sh.wo[0][0][0]);  // NGR * NC <= NP * G * D / 4 float4
+    float4* red = reinterpret_cast<float4*>(sh.wo_);  // NGR * NC <= NT float4
     if (act) {
         red[g * NC + c] = acc;
         sh.lred[g * NC + c] = Lacc;
@@ -533,13 +538,14 @@ __global__ __launch_bounds__(256) void attend_kernel(const void* __restrict__ Q,
 //    into sel at its offset and into an LDS list;
 //  - runs gather attention over that list and merges with the other blocks
 //    as above.  bf16 K/V: the scores come from the matrix cores, 16 keys per
-//    wave per instruction group, and the weights reach 16-lane rows through
-//    LDS for the fp32 weight x V sums; fp32 K/V: 16-lane rows with online
-//    softmax over batches of 16 * NI keys.
+//    wave per instruction group, the weights reach half-wave rows through
+//    LDS for the fp32 weight x V sums, and each wave leaves one partial;
+//    fp32 K/V: 16-lane rows with online softmax over batches of 16 * NI
+//    keys, one partial per row.
 constexpr int kCompactThreads = 512;
 
 template <int D, bool BF16, int G>
-__global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
+__global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 2))) void compact_attend_kernel(
     const void* __restrict__ Q, const void* __restrict__ K, const void* __restrict__ V,
     const int32_t* __restrict__ pages, const int32_t* __restrict__ n_pages, const uint16_t* __restrict__ ham,
     const uint32_t* __restrict__ cum, const uint32_t* __restrict__ ghist, const int32_t* __restrict__ seq_len,
@@ -554,7 +560,8 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
     constexpr int DPL = D / 16;
     constexpr int NWD = BF16 ? DPL / 2 : DPL;
     constexpr uint16_t kNoKey = 0xFFFF;
-    __shared__ AttnShared<D, G, NR> sh;
+    // Partials per wave with bf16 K/V (the rows of a wave share its running max), else per 16-lane row.
+    __shared__ AttnShared<D, G, (BF16 ? NT / 64 : NR), NT> sh;
     __shared__ alignas(16) uint16_t hs[kCompactSlots];
     __shared__ alignas(16) int ts[kCompactSlots];
     __shared__ int list[kCompactSlots];
@@ -749,15 +756,19 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
         // the four lanes of a key read 64 contiguous bytes per slice; the queries use the same permutation
         // of the dimensions, which leaves every dot product unchanged.  bf16 products are exact and the
         // sums fp32, as in the dot-product path.  The online softmax runs in that layout (row maxima and
-        // sums over the 16 keys by DPP); the weights go through a per-wave LDS tile [key][head] -- the
-        // slot staging array, free after the compaction -- to the 16-lane rows, which add weight x V in
-        // fp32 for their own keys (row r of a wave: keys r, r + 4, r + 8, r + 12 of each group).
+        // sums over the 16 keys by DPP).  The weights go through a per-wave LDS tile [key][head] -- the
+        // slot staging array, free after the compaction -- to the weight x V sums, where each half-wave
+        // covers a V row (D / 32 dimensions a lane) and takes 8 of the group's keys: half h takes keys
+        // h, h + 2, ..., h + 14.  A lane thus holds G x D / 32 accumulators, which leaves room for two
+        // blocks per compute unit.
         constexpr int KS = D / 32;
-        constexpr int NGRP = 2;                      // groups per wave per batch
+        constexpr int DPW = D / 32;                  // dimensions per lane in the weight x V sums
+        constexpr int NGRP = 1;                      // groups per wave per batch
         constexpr int STEP = (NT / 64) * 16 * NGRP;  // entries per block per batch
         static_assert(D % 32 == 0 && G <= 8, "score tiles hold 8 heads");
         static_assert(sizeof(ts) >= (NT / 64) * NGRP * 16 * 8 * sizeof(float), "weight tiles fit the staging array");
-        const int wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const int wv = tid >> 6, gq = lane >> 4, ln = lane & 15, hw = lane >> 5, hl = lane & 31;
         float* pt = reinterpret_cast<float*>(ts) + wv * (NGRP * 16 * 8);  // [group][key][8 heads]
         bf16x8 qa[KS];
 #pragma unroll
@@ -773,8 +784,13 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             mr[r] = -__builtin_inff();
             lr[r] = 0.f;
         }
+        float ow[G][DPW];  // this lane's dimensions [hl * DPW, hl * DPW + DPW) of the half-wave's outputs
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int d = 0; d < DPW; ++d) ow[i][d] = 0.f;
         for (int e0 = 0; e0 < cnt; e0 += STEP) {
-            int tk[NGRP], tv[NGRP][4];
+            int tk[NGRP], tv[NGRP][8];
             bool okk[NGRP];
 #pragma unroll
             for (int g = 0; g < NGRP; ++g) {
@@ -783,14 +799,14 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
                 const int t = list[okk[g] ? eb + ln : 0];
                 tk[g] = (t < 0 || t >= L) ? 0 : t;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int ev = eb + gq + 4 * q;
+                for (int q = 0; q < 8; ++q) {
+                    const int ev = eb + hw + 2 * q;
                     const int u = list[ev < cnt ? ev : 0];
                     tv[g][q] = (u < 0 || u >= L) ? 0 : u;
                 }
             }
             u32x4 kb[NGRP][KS];
-            uint32_t vw[NGRP][4][NWD];
+            uint32_t vw[NGRP][8][DPW / 2];
 #pragma unroll
             for (int g = 0; g < NGRP; ++g)
 #pragma unroll
@@ -799,7 +815,16 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
 #pragma unroll
             for (int g = 0; g < NGRP; ++g)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) load_slice<D, BF16>(V, kvb + tv[g][q], sub, vw[g][q]);
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t* vp = static_cast<const uint32_t*>(V) + (kvb + tv[g][q]) * (D / 2) + hl * (DPW / 2);
+                    if constexpr (DPW == 4) {
+                        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp));
+                        vw[g][q][0] = v.x;
+                        vw[g][q][1] = v.y;
+                    } else {
+                        vw[g][q][0] = __builtin_nontemporal_load(vp);
+                    }
+                }
             f32x4 c[NGRP];
 #pragma unroll
             for (int g = 0; g < NGRP; ++g) {
@@ -839,19 +864,19 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // Rescale the row's accumulators (head i's factor is in lane 16 (i / 4), component i % 4), then
-            // add the row's keys' weight x V.
+            // Rescale the accumulators (head i's factor is in lane 16 (i / 4), component i % 4), then add the
+            // half-wave's keys' weight x V.
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fr[i % 4]), 16 * (i / 4)));
 #pragma unroll
-                for (int d = 0; d < DPL; ++d) o[i][d] *= f;
+                for (int d = 0; d < DPW; ++d) ow[i][d] *= f;
             }
 #pragma unroll
             for (int g = 0; g < NGRP; ++g)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float* wq = pt + (g * 16 + gq + 4 * q) * 8;
+                for (int q = 0; q < 8; ++q) {
+                    const float* wq = pt + (g * 16 + hw + 2 * q) * 8;
                     float wgt[8];
 #pragma unroll
                     for (int i4 = 0; i4 < (G + 3) / 4; ++i4) {
@@ -864,21 +889,42 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
 #pragma unroll
                     for (int i = 0; i < G; ++i)
 #pragma unroll
-                        for (int d = 0; d < DPL; ++d)
-                            o[i][d] = __builtin_fmaf(wgt[i], slice_elem<D, BF16>(vw[g][q], d), o[i][d]);
+                        for (int d = 0; d < DPW; ++d)
+                            ow[i][d] = __builtin_fmaf(wgt[i], slice_elem<D, BF16>(vw[g][q], d), ow[i][d]);
                 }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        // The wave's (max, weight sum) per head: its four rows share the max and each reports a quarter of
-        // the sum, so the block merge weighs their partial outputs alike.
+        // The wave's partial: its (max, weight sum) per head, and the sum of its two halves' outputs, which
+        // the first half stores.
 #pragma unroll
         for (int r = 0; r < 4; ++r) lr[r] = row_sum16(lr[r]);
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             m_i[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr[i % 4]), 16 * (i / 4)));
-            l_i[i] = 0.25f * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr[i % 4]), 16 * (i / 4)));
+            l_i[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lr[i % 4]), 16 * (i / 4)));
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int d = 0; d < DPW; ++d) ow[i][d] += __shfl_xor(ow[i][d], 32);
+        if (hw == 0) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                float* dst = sh.wo(wv, i) + hl * DPW;
+                if constexpr (DPW == 4)
+                    *reinterpret_cast<float4*>(dst) = make_float4(ow[i][0], ow[i][1], ow[i][2], ow[i][3]);
+                else
+                    *reinterpret_cast<float2*>(dst) = make_float2(ow[i][0], ow[i][1]);
+            }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                sh.wml[wv][i][0] = m_i[i];
+                sh.wml[wv][i][1] = l_i[i];
+            }
         }
     } else {
     // Attention over list[0, cnt): row rw takes entries e0 + rw + NR j.
@@ -933,7 +979,6 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             l_i[i] = l;
         }
     }
-    }
     store_row_o(sh, rw, sub, o);
     if (sub == 0) {
 #pragma unroll
@@ -941,6 +986,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_attend_kernel(
             sh.wml[rw][i][0] = m_i[i];
             sh.wml[rw][i][1] = l_i[i];
         }
+    }
     }
     if (tid == NT - 64) sh.last_flag = ticket == (uint32_t)(S - 1);
     __syncthreads();
