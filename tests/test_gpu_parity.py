@@ -583,6 +583,33 @@ PATH_SHAPES = [
 ]
 PATH_LENGTHS = {"keep_9216_pages": [30000, 36864]}
 
+# bf16 K/V on the split path scores on the matrix cores: the query rows of the score tile are the group's
+# heads, so the group sizes the shapes above leave out are covered here (one head per selection with Hq = Hkv;
+# a second row of four heads that is partly empty at G = 5, 6, 7), with ragged lengths, and with sink tokens
+# and a local window listed after the ranked keys of the first split.
+MFMA_SHAPES = [
+    ("bf16_split_d128_g1_mha", Workload("mf1", 200, 1, 4, 4, 128, 8192, 16, 128, 25, 512, "bf16", outliers=2)),
+    ("bf16_split_d128_g2_ragged", Workload("mf2", 201, 2, 4, 2, 128, 6000, 16, 128, 20, 400, "bf16",
+                                          ragged=(3000, 6000))),
+    ("bf16_split_d64_g3", Workload("mf3", 202, 1, 6, 2, 64, 8192, 16, 64, 25, 600, "bf16")),
+    ("bf16_split_d128_g5", Workload("mf5", 203, 1, 10, 2, 128, 8192, 16, 128, 25, 700, "bf16", outliers=2)),
+    ("bf16_split_d64_g6_ragged", Workload("mf6", 204, 2, 12, 2, 64, 4096, 8, 64, 30, 300, "bf16",
+                                         ragged=(1000, 4096))),
+    ("bf16_split_d128_g6", Workload("mf7", 205, 1, 12, 2, 128, 8192, 16, 128, 25, 512, "bf16")),
+    ("bf16_split_d64_g7", Workload("mf8", 206, 1, 14, 2, 64, 8192, 32, 64, 25, 800, "bf16", outliers=2)),
+    ("bf16_split_d128_g2_sinks_window", Workload("mf9", 207, 2, 4, 2, 128, 8192, 16, 128, 25, 500, "bf16",
+                                                ragged=(5000, 8192), sink_tokens=4, local_window=64)),
+]
+
+
+@pytest.mark.parametrize("name,wl", MFMA_SHAPES, ids=[s[0] for s in MFMA_SHAPES])
+def test_bf16_split_group_sizes(dev, name, wl):
+    banner(f"decode parity {name}: G {wl.n_q_heads // wl.n_kv_heads}, max_keep {wl.max_keep}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
+
 
 @pytest.mark.parametrize("name,wl", PATH_SHAPES, ids=[s[0] for s in PATH_SHAPES])
 def test_decode_parity_paths(dev, name, wl):
