@@ -175,16 +175,23 @@ WsLayout ws_layout(const Shape& s, int max_keep, int top_k) {
     l.ham = take(BH * (size_t)max_keep * s.P * sizeof(uint16_t));
     l.sel = take(BH * (size_t)sel_cap * sizeof(int32_t));
     l.k_eff = take(BH * sizeof(int32_t));
-    // Split key select: about 512 candidate slots per block, and no more
-    // blocks than the GPU holds at once (each one repeats the page select),
-    // unless more are needed for the compaction's kCompactSlots per block;
-    // at most 64 blocks per head (then they run in rounds: the merge never
-    // waits for a block that has not started).
+    // Split key select.  A split block's latency grows with its share of the
+    // candidate slots (the Hamming scan, the compaction and the gathers),
+    // the head's merge with the number of splits.  Measured with 8 KV heads,
+    // the layer is fastest near S = sqrt(slots / 32): 10 splits at 32K
+    // context (3,280 slots) and 20 at 128K (13,120), against the 7 and 26 of
+    // 512 slots per block, 2.3 and 0.9 us faster.  Below 2,048 slots the
+    // blocks' fixed costs dominate and 512 slots per block stays faster.  No
+    // more blocks than the GPU holds at once (each one repeats the page
+    // select), unless more are needed for the compaction's kCompactSlots per
+    // block; at most 64 blocks per head (then they run in rounds: the merge
+    // never waits for a block that has not started).
     const size_t slots = (size_t)max_keep * s.P;
     const size_t BHs = BH > 0 ? BH : 1;
     int S = 1;
     if (max_keep <= kSelListLds && forced < (size_t)kCompactSlots) {
-        size_t want = (slots + 511) / 512, cap = 256 / BHs;
+        size_t want = slots >= 2048 ? (size_t)std::lround(std::sqrt((double)slots / 32.0)) : (slots + 511) / 512;
+        const size_t cap = 256 / BHs;
         want = want < cap ? want : cap;
         const size_t room = kCompactSlots - forced;  // candidate slots a block can take
         const size_t need = (slots + room - 1) / room;
