@@ -496,6 +496,67 @@ __device__ __forceinline__ void load_code(const uint64_t* __restrict__ ck, int t
     }
 }
 
+// One split block's share of a head's key scan: the Hamming distances of
+// slots [split * per, split * per + per) of the kept pages (page list in
+// LDS), written to hm and counted in the LDS histogram `hist` (zeroed by the
+// caller, before a barrier); then the block's inclusive cumulative histogram
+// goes to cum and its counts into the head's (ghist).  The split count keeps
+// per <= kCompactSlots, so a thread has at most kSplitRun slots.
+constexpr int kSplitRun = kCompactSlots / kSelThreads;
+static_assert(kSplitRun * kSelThreads == kCompactSlots, "a split's slots fit the run");
+template <int NW>
+__device__ __forceinline__ void split_scan(const uint64_t* __restrict__ ck, const uint64_t (&cq)[kMaxGroup * NW], int G,
+                                           const int* plist, int nslots, int P, int s_end, int w_start, int max_keep,
+                                           uint16_t* __restrict__ hm, int* hist, int* scan, int split, int S,
+                                           uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist) {
+    const int NBINS = G * NW * 64 + 1;
+    const int tid = threadIdx.x;
+    const int lp = 31 - __clz(P);  // P is a power of two
+    const int per = (nslots + S - 1) / S;
+    const int lo = split * per < nslots ? split * per : nslots, hi = lo + per < nslots ? lo + per : nslots;
+    int tk[kSplitRun];
+    uint64_t kc[kSplitRun][NW];
+#pragma unroll
+    for (int k = 0; k < kSplitRun; ++k) {  // lookups, then every code load, before any use
+        const int s = lo + k * kSelThreads + tid;
+        const int ss = s < hi ? s : 0;
+        const int t = plist[ss >> lp] * P + (ss & (P - 1));
+        tk[k] = (s < hi && t >= s_end && t < w_start) ? t : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kSplitRun; ++k) load_code<NW>(ck, tk[k] >= 0 ? tk[k] : 0, kc[k]);
+#pragma unroll
+    for (int k = 0; k < kSplitRun; ++k) {
+        const int s = lo + k * kSelThreads + tid;
+        int hsum = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxGroup; ++i) {
+            if (i >= G) break;  // uniform
+#pragma unroll
+            for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
+        }
+        if (tk[k] >= 0) atomicAdd(&hist[hsum], 1);
+        if (s < hi) hm[s] = tk[k] < 0 ? kNoKey : (uint16_t)hsum;
+    }
+    if (split == 0)
+        for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
+    __syncthreads();
+    // Thread i owns bins 2i and 2i+1: inclusive cumulative counts, and the
+    // head's histogram (device atomics on the bins this block hit).
+    const int b0 = 2 * tid;
+    const int c0 = b0 < NBINS ? hist[b0] : 0, c1 = b0 + 1 < NBINS ? hist[b0 + 1] : 0;
+    int tot;
+    const int before = block_excl_scan<kSelThreads>(c0 + c1, scan, tot);
+    if (b0 < NBINS) {
+        cum[split * NBINS + b0] = (uint32_t)(before + c0);
+        if (c0) atomicAdd(&ghist[b0], (uint32_t)c0);
+    }
+    if (b0 + 1 < NBINS) {
+        cum[split * NBINS + b0 + 1] = (uint32_t)(before + c0 + c1);
+        if (c1) atomicAdd(&ghist[b0 + 1], (uint32_t)c1);
+    }
+}
+
 // LDSLIST: the kept-page list is read from LDS (else from the workspace); a
 // compile-time choice, so every read is a plain LDS or global load rather
 // than a generic one that waits on both queues.
@@ -570,54 +631,8 @@ __device__ __forceinline__ void select_keys_block(const uint64_t* __restrict__ c
     __syncthreads();
 
     if (LDSLIST && S > 1) {
-        const int per = (nslots + S - 1) / S;
-        const int lo = split * per, hi = lo + per < nslots ? lo + per : nslots;
-        const int kr = hi > lo ? (hi - lo + kSelThreads - 1) / kSelThreads : 0;
-        uint64_t kc[kRun][NW];
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) {  // lookups, then every code load, before any use
-            Hreg[k] = -1;
-            if (k < kr) {
-                const int s = lo + k * kSelThreads + tid;
-                const int ss = s < hi ? s : 0;
-                const int t = sh.plist[ss >> lp] * P + (ss & (P - 1));
-                Hreg[k] = (s < hi && t >= s_end && t < w_start) ? t : -1;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kRun; ++k)
-            if (k < kr) load_code<NW>(ck, Hreg[k] >= 0 ? Hreg[k] : 0, kc[k]);
-#pragma unroll
-        for (int k = 0; k < kRun; ++k) {
-            const int s = lo + k * kSelThreads + tid;
-            if (k >= kr) continue;
-            int hsum = 0;
-#pragma unroll
-            for (int i = 0; i < kMaxGroup; ++i) {
-                if (i >= G) break;  // uniform
-#pragma unroll
-                for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[k][w]);
-            }
-            if (Hreg[k] >= 0) atomicAdd(&sh.hist[hsum], 1);
-            if (s < hi) hm[s] = Hreg[k] < 0 ? kNoKey : (uint16_t)hsum;
-        }
-        if (split == 0)
-            for (int s = nslots + tid; s < max_keep * P; s += kSelThreads) hm[s] = kNoKey;
-        __syncthreads();
-        // Thread i owns bins 2i and 2i+1: inclusive cumulative counts, and the
-        // head's histogram (device atomics on the bins this block hit).
-        const int b0 = 2 * tid;
-        const int c0 = b0 < NBINS ? sh.hist[b0] : 0, c1 = b0 + 1 < NBINS ? sh.hist[b0 + 1] : 0;
-        int tot;
-        const int before = block_excl_scan<kSelThreads>(c0 + c1, sh.scan, tot);
-        if (b0 < NBINS) {
-            cum[split * NBINS + b0] = (uint32_t)(before + c0);
-            if (c0) atomicAdd(&ghist[b0], (uint32_t)c0);
-        }
-        if (b0 + 1 < NBINS) {
-            cum[split * NBINS + b0 + 1] = (uint32_t)(before + c0 + c1);
-            if (c1) atomicAdd(&ghist[b0 + 1], (uint32_t)c1);
-        }
+        split_scan<NW>(ck, cq, G, sh.plist, nslots, P, s_end, w_start, max_keep, hm, sh.hist, sh.scan, split, S, cum,
+                       ghist);
         return;
     } else {
         for (int c = 0; c < nchunks; ++c) {
@@ -793,6 +808,47 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     keys_half<NW, KEYS>(sh, codes, code_q, pl, np, list_in_lds, ham, sel, k_eff_out, cum, ghist, split, S, b, h, bh,
                         bhd, Gh, T, P, L, max_keep, top_k, nsink, window);
     if (KEYS && S > 1) mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
+}
+
+// Split key scan after a separate page-select launch (S > 1, kept-page list
+// within kListLds): only the split block's share of the scan, so the kernel
+// holds few registers and two 1024-thread blocks share a compute unit.
+struct SplitShared {
+    int hist[kMaxGroup * 128 + 1];
+    int scan[32];
+    int plist[kListLds];
+};
+
+template <int NW>
+__global__ __launch_bounds__(kSelThreads) void select_split_kernel(
+    const double* __restrict__ score, const int32_t* __restrict__ keep_pages, const uint64_t* __restrict__ codes,
+    const uint64_t* __restrict__ code_q, const int32_t* __restrict__ seq_len, int32_t* __restrict__ pages,
+    int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham, int32_t* __restrict__ sel,
+    int32_t* __restrict__ k_eff_out, uint32_t* __restrict__ cum, uint32_t* __restrict__ ghist, float* __restrict__ part_o,
+    float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
+    int max_keep, int top_k, int nsink, int window, int share) {
+    __shared__ SplitShared sh;
+    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
+    const int NBINS = Gh * NW * 64 + 1;
+    uint64_t cq[kMaxGroup * NW];
+#pragma unroll
+    for (int i = 0; i < kMaxGroup * NW; ++i) cq[i] = code_q[bh * Gh * NW + (i < Gh * NW ? i : 0)];
+    const int L = clamp_len(seq_len[b], T);
+    int np = n_pages[bh];
+    np = np < 0 ? 0 : (np > max_keep ? max_keep : np);  // memory safety for a hand-filled workspace
+    np = np > kListLds ? kListLds : np;                  // the launch guarantees max_keep <= kListLds
+    const int32_t* pl = pages + bh * max_keep;
+    for (int i = tid; i < np; i += kSelThreads) sh.plist[i] = pl[i];
+    for (int i = tid; i < NBINS; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    const int s_end = nsink < L ? nsink : L;
+    const int w_start = L - window > s_end ? L - window : s_end;
+    split_scan<NW>(codes + bhd * (int64_t)T * NW, cq, Gh, sh.plist, np * P, P, s_end, w_start, max_keep,
+                   ham + bh * (int64_t)max_keep * P, sh.hist, sh.scan, split, S, cum + bh * (int64_t)S * NBINS,
+                   ghist + bh * (int64_t)NBINS);
+    mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
 }
 
 // Fast select kernel: at most RUN * 1024 pages (one chunk, RUN items per
@@ -1228,8 +1284,9 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
     if (a.lay.sel_pages_apart) {  // the page list once per head, then S key-scan blocks per head read it
         const hipError_t e = select_pages_nw<1, false>(a, 1, st);
         if (e != hipSuccess) return e;
-        return a.s.NW == 1 ? select_launch(select_kernel<1, false, true>, a, S, st)
-                           : select_launch(select_kernel<2, false, true>, a, S, st);
+        if (a.max_keep > kListLds) return hipErrorInvalidValue;  // the split count is chosen so
+        return a.s.NW == 1 ? select_launch(select_split_kernel<1>, a, S, st)
+                           : select_launch(select_split_kernel<2>, a, S, st);
     }
     return a.s.NW == 1 ? select_pages_nw<1, true>(a, S, st) : select_pages_nw<2, true>(a, S, st);
 }
