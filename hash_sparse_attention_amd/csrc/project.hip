@@ -215,7 +215,11 @@ __global__ __launch_bounds__(kProjWaves * 64) void project_kernel(
 template <int D, int NB, bool BF16, bool KEYS, bool QUERIES>
 hipError_t project_t(const Shape& s, const ProjectArgs& a, hipStream_t st) {
     constexpr int RG = (D + NB) / 64;
-    const int key_blocks = KEYS ? (a.max_count - 1) / s.P + 2 : 0;
+    // Pages that max_count consecutive tokens can touch: floor((c + 2P - 2) / P)
+    // (one for a single token, where (c - 1) / P + 2 launched an idle second
+    // page's blocks).
+    const int key_pages = (a.max_count + 2 * s.P - 2) / s.P;
+    const int key_blocks = KEYS ? (key_pages > 1 ? key_pages : 1) : 0;
     const int blocks = (key_blocks + (QUERIES ? 1 : 0)) * RG;
     hipLaunchKernelGGL((project_kernel<D, NB, BF16, KEYS, QUERIES>), dim3(s.Hkv, s.B, blocks),
                        dim3(kProjWaves * 64), 0, st, a.Q, a.K, a.R, a.W, a.start, a.count, a.max_count, key_blocks,
