@@ -85,6 +85,7 @@ def lib():
             "hhr_stage_qprep": (ctypes.c_int, [D, p, p, p, i32, i32, p, sz, p]),
             "hhr_stage_page_bounds": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
             "hhr_stage_select_pages": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
+            "hhr_stage_hamming": (ctypes.c_int, [D, p, p, i32, i32, p, sz, p]),
             "hhr_stage_select_keys": (ctypes.c_int, [D, p, p, i32, i32, p, p, sz, p]),
             "hhr_stage_attend": (ctypes.c_int, [D, p, p, p, p, i32, i32, f32, p, p, p, sz, p]),
             "hhr_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -103,7 +104,8 @@ EXPORTED = ("hhr_meta_bytes", "hhr_codes_bytes", "hhr_encode_cache", "hhr_decode
             "hhr_decode_step_append_noalloc", "hhr_topk_workspace_layout",
             "hhr_topk_workspace_bytes", "hhr_topk_decode_step", "hhr_stage_topk_logits", "hhr_stage_qprep",
             "hhr_stage_page_bounds",
-            "hhr_stage_select_pages", "hhr_stage_select_keys", "hhr_stage_attend", "hhr_status_str",
+            "hhr_stage_select_pages", "hhr_stage_hamming", "hhr_stage_select_keys", "hhr_stage_attend",
+            "hhr_status_str",
             "hhr_last_error", "hhr_abi_version")
 
 
@@ -300,6 +302,11 @@ def stage_page_bounds(dims, meta, seq_len, max_keep, top_k, workspace, stream=No
 def stage_select_pages(dims, seq_len, keep_pages, max_keep, top_k, workspace, stream=None):
     _check(lib().hhr_stage_select_pages(ctypes.byref(dims), _ptr(seq_len), _ptr(keep_pages), int(max_keep),
                                         int(top_k), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def stage_hamming(dims, codes, seq_len, max_keep, top_k, workspace, stream=None):
+    _check(lib().hhr_stage_hamming(ctypes.byref(dims), _ptr(codes), _ptr(seq_len), int(max_keep), int(top_k),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def stage_select_keys(dims, codes, seq_len, max_keep, top_k, workspace, sel_idx=None, stream=None):

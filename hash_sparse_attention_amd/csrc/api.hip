@@ -536,6 +536,19 @@ hhr_status hhr_stage_select_pages(const hhr_dims* dims, const int32_t* seq_len, 
     return ok();
 }
 
+hhr_status hhr_stage_hamming(const hhr_dims* dims, const uint64_t* codes, const int32_t* seq_len,
+                             int32_t max_keep_pages, int32_t top_k, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    DecodeArgs a;
+    HHR_TRY(prepare(dims, max_keep_pages, top_k, workspace, workspace_bytes, a));
+    HHR_TRY(check_ptr(codes, "codes"));
+    HHR_TRY(check_ptr(seq_len, "seq_len", 4));
+    a.codes = codes;
+    a.seq_len = seq_len;
+    HHR_TRY(hip_check(launch_hamming(a, static_cast<hipStream_t>(stream)), "Hamming launch"));
+    return ok();
+}
+
 hhr_status hhr_stage_select_keys(const hhr_dims* dims, const uint64_t* codes, const int32_t* seq_len,
                                  int32_t max_keep_pages, int32_t top_k, int32_t* sel_idx, void* workspace,
                                  size_t workspace_bytes, void* stream) {

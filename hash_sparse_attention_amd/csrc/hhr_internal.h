@@ -135,6 +135,7 @@ hipError_t launch_qprep(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_page_bounds(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_select(const DecodeArgs& a, hipStream_t stream);  // pages, then keys, one launch
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_hamming(const DecodeArgs& a, hipStream_t stream);  // ham only
 hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_attend(const DecodeArgs& a, bool zero_counters, hipStream_t stream);
 // Threshold, ordered compaction and attention of the split key select (the decode step when sel_splits > 1).

@@ -851,6 +851,48 @@ __global__ __launch_bounds__(kSelThreads) void select_split_kernel(
     mark_partials(part_o, part_ml, (int64_t)b * Hq + (int64_t)h * G, G, D, split, pstride);
 }
 
+// Hamming stage alone: the distance of every candidate slot of the kept
+// pages (pages, n_pages and the query codes from the workspace) to the
+// group's query codes, summed over the Gh codes, or 0xFFFF for a slot past
+// the kept pages, past the sequence, or on a sink or window key -- the
+// values the key select writes to ham.  One thread per slot.
+template <int NW>
+__global__ __launch_bounds__(256) void hamming_kernel(const uint64_t* __restrict__ codes,
+                                                      const uint64_t* __restrict__ code_q,
+                                                      const int32_t* __restrict__ seq_len,
+                                                      const int32_t* __restrict__ pages,
+                                                      const int32_t* __restrict__ n_pages, uint16_t* __restrict__ ham,
+                                                      int Gh, int Hkv, int T, int P, int max_keep, int nsink,
+                                                      int window, int share) {
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nslot = (int64_t)max_keep * P;
+    if (s >= nslot) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int L = clamp_len(seq_len[b], T);
+    int np = n_pages[bh];
+    np = np < 0 ? 0 : (np > max_keep ? max_keep : np);
+    const int s_end = nsink < L ? nsink : L;
+    const int w_start = L - window > s_end ? L - window : s_end;  // ranked keys: [s_end, w_start)
+    const int lp = 31 - __clz(P);
+    uint16_t out = kNoKey;
+    if (s < (int64_t)np * P) {
+        const int64_t t = (int64_t)pages[bh * max_keep + (s >> lp)] * P + (s & (P - 1));
+        if (t >= s_end && t < w_start) {
+            const uint64_t* ck = codes + data_head(b, h, Hkv, share) * (int64_t)T * NW;
+            uint64_t kc[NW];
+            load_code<NW>(ck, (int)t, kc);
+            const uint64_t* cq = code_q + bh * Gh * NW;
+            int hsum = 0;
+            for (int i = 0; i < Gh; ++i)
+#pragma unroll
+                for (int w = 0; w < NW; ++w) hsum += __popcll(cq[i * NW + w] ^ kc[w]);
+            out = (uint16_t)hsum;
+        }
+    }
+    ham[bh * nslot + s] = out;
+}
+
 // Fast select kernel: at most RUN * 1024 pages (one chunk, RUN items per
 // thread known at compile time) and at most kListLds kept pages; scores are
 // loaded before the length is known.
@@ -1292,6 +1334,23 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
 }
 hipError_t launch_select_pages(const DecodeArgs& a, hipStream_t st) {
     return select_pages_nw<1, false>(a, 1, st);  // the page half does not depend on the code width
+}
+hipError_t launch_hamming(const DecodeArgs& a, hipStream_t st) {
+    const Shape& s = a.s;
+    const int64_t nslot = (int64_t)a.max_keep * s.P;
+    if (nslot <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((nslot + 255) / 256), s.Hkv, s.B);
+    const uint64_t* cq = reinterpret_cast<const uint64_t*>(a.ws + (s.ham_mean ? a.lay.code_qm : a.lay.code_q));
+    const int32_t* pg = reinterpret_cast<const int32_t*>(a.ws + a.lay.pages);
+    const int32_t* npg = reinterpret_cast<const int32_t*>(a.ws + a.lay.n_pages);
+    uint16_t* hm = reinterpret_cast<uint16_t*>(a.ws + a.lay.ham);
+    if (s.NW == 1)
+        hipLaunchKernelGGL(hamming_kernel<1>, grid, dim3(256), 0, st, a.codes, cq, a.seq_len, pg, npg, hm, s.Gh, s.Hkv,
+                           s.T, s.P, a.max_keep, s.nsink, s.window, s.share);
+    else
+        hipLaunchKernelGGL(hamming_kernel<2>, grid, dim3(256), 0, st, a.codes, cq, a.seq_len, pg, npg, hm, s.Gh, s.Hkv,
+                           s.T, s.P, a.max_keep, s.nsink, s.window, s.share);
+    return hipGetLastError();
 }
 hipError_t launch_select_keys(const DecodeArgs& a, hipStream_t st) {
     return a.s.NW == 1 ? select_launch(select_kernel<1, false, true>, a, 1, st)

@@ -107,7 +107,7 @@
 extern "C" {
 #endif
 
-#define HHR_ABI_VERSION 7
+#define HHR_ABI_VERSION 8
 
 typedef enum {
     HHR_OK = 0,
@@ -361,6 +361,7 @@ hhr_status hhr_stage_topk_logits(const hhr_dims* dims, const void* K, const int3
  *   qprep         Q, R, W              -> q_rot, code_q, q_split
  *   page_bounds   meta, seq_len        -> score            (reads q_split)
  *   select_pages  seq_len, keep_pages  -> pages, n_pages   (reads score)
+ *   hamming       codes, seq_len       -> ham              (reads pages, n_pages, code_q)
  *   select_keys   codes, seq_len       -> ham, sel/sel_idx, k_eff (reads pages, n_pages, code_q)
  *   attend        Q, K, V, seq_len     -> out              (reads sel/sel_idx, k_eff)
  */
@@ -373,6 +374,18 @@ hhr_status hhr_stage_page_bounds(const hhr_dims* dims, const float* meta, const 
 hhr_status hhr_stage_select_pages(const hhr_dims* dims, const int32_t* seq_len, const int32_t* keep_pages,
                                   int32_t max_keep_pages, int32_t top_k, void* workspace,
                                   size_t workspace_bytes, void* stream);
+/* Hamming stage alone (LHP; rit.work HHR blog post, section "Почему
+ * расстояние Хэмминга пропускает важные ключи"): for every candidate slot of
+ * the kept pages, the Hamming distance between the slot key's code and the
+ * group's query codes (summed over the group's Gh codes, or to the mean
+ * query's code with hamming_group = 1), as uint16 in the workspace's ham
+ * region, [B][units][max_keep_pages * page_size]; 0xFFFF for a slot past the
+ * kept pages or the sequence, or on a sink or window key.  These are the
+ * values hhr_stage_select_keys also writes there.  Same argument checks and
+ * error codes as the other stage entry points. */
+hhr_status hhr_stage_hamming(const hhr_dims* dims, const uint64_t* codes, const int32_t* seq_len,
+                             int32_t max_keep_pages, int32_t top_k, void* workspace,
+                             size_t workspace_bytes, void* stream);
 hhr_status hhr_stage_select_keys(const hhr_dims* dims, const uint64_t* codes, const int32_t* seq_len,
                                  int32_t max_keep_pages, int32_t top_k, int32_t* sel_idx,
                                  void* workspace, size_t workspace_bytes, void* stream);

@@ -399,6 +399,11 @@ def test_stages_from_oracle_intermediates(dev):
     v.pages.copy_(torch.from_numpy(o["pages"]).to(dev))
     v.n_pages.copy_(torch.from_numpy(o["n_pages"]).to(dev))
     v.code_q.copy_(torch.from_numpy(o["code_q"].view(np.int64)).to(dev))
+    v.ham.fill_(0x1234)
+    hsa.stage_hamming(dims, codes_gpu, seq, mk, tk, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(v.ham.cpu().numpy().view(np.uint16), o["ham"])
+    v.ham.fill_(0x1234)
     sel = torch.empty((2, wl.n_kv_heads, tk), dtype=torch.int32, device=dev)
     hsa.stage_select_keys(dims, codes_gpu, seq, mk, tk, ws, sel_idx=sel)
     torch.cuda.synchronize()
@@ -411,6 +416,35 @@ def test_stages_from_oracle_intermediates(dev):
     hsa.stage_attend(dims, t["Q"], t["K"], t["V"], seq, mk, tk, out, ws, sel_idx=osel)
     torch.cuda.synchronize()
     assert np.abs(out.cpu().numpy().astype(np.float64) - o["out"]).max() <= 2e-3
+
+
+# The Hamming stage alone, after a full step on the same workspace: the distances of every candidate slot
+# equal the oracle's, forced (sink and window) slots and slots past the kept pages or the sequence included.
+HAM_SHAPES = [
+    ("tiny_ragged", WORKLOADS["tiny"].with_(batch=2, ragged=(1000, 4096))),
+    ("sinks_window_b64", Workload("hs1", 210, 2, 8, 2, 128, 3000, 16, 64, 20, 200, "bf16", ragged=(100, 3000),
+                                  sink_tokens=4, local_window=40)),
+    ("mean_code_g7", Workload("hs2", 211, 1, 14, 2, 128, 2000, 16, 128, 10, 150, "bf16", hamming_group=1)),
+    ("p32_b64_fp32", Workload("hs3", 212, 2, 8, 2, 64, 4096, 32, 64, 15, 256, "fp32", ragged=(2000, 4096))),
+]
+
+
+@pytest.mark.parametrize("name,wl", HAM_SHAPES, ids=[s[0] for s in HAM_SHAPES])
+def test_hamming_stage_alone(dev, name, wl):
+    import torch
+
+    import hash_sparse_attention_amd as hsa
+    banner(f"Hamming stage {name}")
+    d = make_layer(wl)
+    g = run_gpu(wl, d, dev)
+    o = run_oracle(wl, d)
+    x = g["_dev"]
+    v = hsa.workspace_view(x["dims"], x["max_keep"], x["top_k"], x["ws"])
+    assert np.array_equal(g["ham"], o["ham"])
+    v.ham.fill_(0x1234)
+    hsa.stage_hamming(x["dims"], x["codes"], x["seq"], x["max_keep"], x["top_k"], x["ws"])
+    torch.cuda.synchronize()
+    assert np.array_equal(v.ham.cpu().numpy().view(np.uint16), o["ham"])
 
 
 @pytest.mark.parametrize("npages,seq,keep,max_keep", [
