@@ -33,11 +33,12 @@ _LIB_OVERRIDE = os.environ.get("HHR_ORACLE_LIB")
 _lib = None
 
 
-def compile_source(src: str, out: str) -> str:
-    """gcc build of an oracle source file (IEEE fp32/fp64, no contraction, no fast-math)."""
+def compile_source(src: str, out: str, extra=()) -> str:
+    """gcc build of an oracle source file (IEEE fp32/fp64, no contraction, no fast-math); `extra` adds
+    flags (the sanitizer test builds with -fsanitize=address,undefined)."""
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-mfma",
-           "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter", "-o", tmp, src, "-lm"]
+           "-std=c11", "-Wall", "-Wextra", "-Wno-unused-parameter", *extra, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
