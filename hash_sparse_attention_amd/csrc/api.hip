@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -117,6 +118,48 @@ hhr_status hip_check(hipError_t e, const char* what) {
     return HHR_OK;
 }
 
+// Test and debug switches, read once per process from the environment.
+//  HHR_TEST_FAIL=<text>: every launch whose name contains <text> ("*" for
+//    all) fails with HHR_E_HIP before anything is enqueued, so callers' error
+//    paths can be tested without a GPU.
+//  HHR_DEBUG_SYNC=1: after every launch, synchronize the stream and check
+//    for errors, so an asynchronous fault is reported by the call that
+//    launched it (not allowed under stream capture).
+const char* test_fail_target() {
+    static const char* v = [] {
+        const char* e = std::getenv("HHR_TEST_FAIL");
+        return (e && *e) ? e : nullptr;
+    }();
+    return v;
+}
+bool debug_sync() {
+    static const bool on = [] {
+        const char* e = std::getenv("HHR_DEBUG_SYNC");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+hhr_status before_launch(const char* what) {
+    const char* t = test_fail_target();
+    if (t && (std::strcmp(t, "*") == 0 || std::strstr(what, t)))
+        return fail(HHR_E_HIP, "%s: failed on purpose (HHR_TEST_FAIL=%s)", what, t);
+    return HHR_OK;
+}
+hhr_status after_launch(hipStream_t st, const char* what) {
+    if (!debug_sync()) return HHR_OK;
+    const hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(HHR_E_HIP, "%s (HHR_DEBUG_SYNC): %s", what, hipGetErrorString(e));
+    return hip_check(hipGetLastError(), what);
+}
+
+// Every kernel launch of the library: the test switch, the launch, then the debug check.
+#define HHR_LAUNCH(expr, what, stream)               \
+    do {                                              \
+        HHR_TRY(before_launch(what));                 \
+        HHR_TRY(hip_check((expr), what));             \
+        HHR_TRY(after_launch((stream), what));        \
+    } while (0)
+
 // Common front half of the decode step and its stages.
 hhr_status prepare(const hhr_dims* dims, int max_keep, int top_k, void* workspace, size_t ws_bytes,
                    DecodeArgs& a) {
@@ -145,10 +188,12 @@ float resolve_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / st
 
 // Selections and attention of the decode step, after the page bounds.
 hhr_status launch_tail(const DecodeArgs& a, hipStream_t st) {
-    HHR_TRY(hip_check(launch_select(a, st), "select launch"));
+    HHR_LAUNCH(launch_select(a, st), "select launch", st);
     if (a.lay.sel_splits > 1)
-        return hip_check(launch_compact_attend(a, st), "compaction and attention launch");
-    return hip_check(launch_attend(a, false, st), "attention launch");
+        HHR_LAUNCH(launch_compact_attend(a, st), "compaction and attention launch", st);
+    else
+        HHR_LAUNCH(launch_attend(a, false, st), "attention launch", st);
+    return HHR_OK;
 }
 
 }  // namespace
@@ -327,9 +372,9 @@ hhr_status hhr_encode_cache(const hhr_dims* dims, const void* K, const float* R,
         p.max_count = max_count;
         p.meta = meta;
         p.codes = codes;
-        HHR_TRY(hip_check(launch_project(s, p, st), "append launch"));
+        HHR_LAUNCH(launch_project(s, p, st), "append launch", st);
     } else {
-        HHR_TRY(hip_check(launch_encode(s, K, R, W, start, count, max_count, meta, codes, st), "encode launch"));
+        HHR_LAUNCH(launch_encode(s, K, R, W, start, count, max_count, meta, codes, st), "encode launch", st);
     }
     return ok();
 }
@@ -396,8 +441,8 @@ hhr_status hhr_decode_step(const hhr_dims* dims, const void* Q, const void* K, c
     a.scale = resolve_scale(softmax_scale, a.s.D);
     if (sel_idx) a.sel = sel_idx;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
-    HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
+    HHR_LAUNCH(launch_qprep(a, st), "qprep launch", st);
+    HHR_LAUNCH(launch_page_bounds(a, st), "page-bound launch", st);
     HHR_TRY(launch_tail(a, st));
     return ok();
 }
@@ -460,14 +505,14 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         p.n_counters = a.lay.n_clear;
         p.qmean = a.s.ham_mean;
         p.qs_unit = a.s.share > 1;
-        HHR_TRY(hip_check(launch_project(a.sd, p, st), "append + qprep launch"));
+        HHR_LAUNCH(launch_project(a.sd, p, st), "append + qprep launch", st);
     } else {
         if (max_append > 0)
-            HHR_TRY(hip_check(launch_encode(a.sd, K, R, W, append_start, append_count, max_append, meta, codes, st),
-                              "encode launch"));
-        HHR_TRY(hip_check(launch_qprep(a, st), "qprep launch"));
+            HHR_LAUNCH(launch_encode(a.sd, K, R, W, append_start, append_count, max_append, meta, codes, st),
+                       "encode launch", st);
+        HHR_LAUNCH(launch_qprep(a, st), "qprep launch", st);
     }
-    HHR_TRY(hip_check(launch_page_bounds(a, st), "page-bound launch"));
+    HHR_LAUNCH(launch_page_bounds(a, st), "page-bound launch", st);
     HHR_TRY(launch_tail(a, st));
     return ok();
 }
@@ -506,7 +551,8 @@ hhr_status hhr_stage_qprep(const hhr_dims* dims, const void* Q, const float* R, 
     a.Q = Q;
     a.R = R;
     a.W = W;
-    HHR_TRY(hip_check(launch_qprep(a, static_cast<hipStream_t>(stream)), "qprep launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_qprep(a, st), "qprep launch", st);
     return ok();
 }
 
@@ -519,7 +565,8 @@ hhr_status hhr_stage_page_bounds(const hhr_dims* dims, const float* meta, const 
     HHR_TRY(check_ptr(seq_len, "seq_len", 4));
     a.meta = meta;
     a.seq_len = seq_len;
-    HHR_TRY(hip_check(launch_page_bounds(a, static_cast<hipStream_t>(stream)), "page-bound launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_page_bounds(a, st), "page-bound launch", st);
     return ok();
 }
 
@@ -532,7 +579,8 @@ hhr_status hhr_stage_select_pages(const hhr_dims* dims, const int32_t* seq_len, 
     HHR_TRY(check_ptr(keep_pages, "keep_pages", 4));
     a.seq_len = seq_len;
     a.keep_pages = keep_pages;
-    HHR_TRY(hip_check(launch_select_pages(a, static_cast<hipStream_t>(stream)), "page-select launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_select_pages(a, st), "page-select launch", st);
     return ok();
 }
 
@@ -545,7 +593,8 @@ hhr_status hhr_stage_hamming(const hhr_dims* dims, const uint64_t* codes, const 
     HHR_TRY(check_ptr(seq_len, "seq_len", 4));
     a.codes = codes;
     a.seq_len = seq_len;
-    HHR_TRY(hip_check(launch_hamming(a, static_cast<hipStream_t>(stream)), "Hamming launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_hamming(a, st), "Hamming launch", st);
     return ok();
 }
 
@@ -560,7 +609,8 @@ hhr_status hhr_stage_select_keys(const hhr_dims* dims, const uint64_t* codes, co
     a.codes = codes;
     a.seq_len = seq_len;
     if (sel_idx) a.sel = sel_idx;
-    HHR_TRY(hip_check(launch_select_keys(a, static_cast<hipStream_t>(stream)), "key-select launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_select_keys(a, st), "key-select launch", st);
     return ok();
 }
 
@@ -583,7 +633,8 @@ hhr_status hhr_stage_attend(const hhr_dims* dims, const void* Q, const void* K, 
     a.out = out;
     a.scale = resolve_scale(softmax_scale, a.s.D);
     if (sel_idx) a.sel = const_cast<int32_t*>(sel_idx);
-    HHR_TRY(hip_check(launch_attend(a, true, static_cast<hipStream_t>(stream)), "attention launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_attend(a, true, st), "attention launch", st);
     return ok();
 }
 
@@ -636,7 +687,8 @@ hhr_status hhr_stage_topk_logits(const hhr_dims* dims, const void* K, const int3
     HHR_TRY(check_ptr(seq_len, "seq_len", 4));
     a.d.K = K;
     a.d.seq_len = seq_len;
-    HHR_TRY(hip_check(launch_topk_logits(a, static_cast<hipStream_t>(stream)), "logit launch"));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    HHR_LAUNCH(launch_topk_logits(a, st), "logit launch", st);
     return ok();
 }
 
@@ -659,10 +711,10 @@ hhr_status hhr_topk_decode_step(const hhr_dims* dims, const void* Q, const void*
     a.d.scale = resolve_scale(softmax_scale, a.d.s.D);
     if (sel_idx) a.d.sel = sel_idx;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    HHR_TRY(hip_check(launch_topk_prep(a, st), "top-k prep launch"));
-    HHR_TRY(hip_check(launch_topk_logits(a, st), "logit launch"));
-    HHR_TRY(hip_check(launch_topk_select(a, st), "top-k select launch"));
-    HHR_TRY(hip_check(launch_attend(a.d, false, st), "attention launch"));
+    HHR_LAUNCH(launch_topk_prep(a, st), "top-k prep launch", st);
+    HHR_LAUNCH(launch_topk_logits(a, st), "logit launch", st);
+    HHR_LAUNCH(launch_topk_select(a, st), "top-k select launch", st);
+    HHR_LAUNCH(launch_attend(a.d, false, st), "attention launch", st);
     return ok();
 }
 

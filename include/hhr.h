@@ -29,6 +29,13 @@
  *    failure nothing is enqueued, nothing is written, a nonzero hhr_status is
  *    returned and hhr_last_error() describes it.  A failed launch returns
  *    HHR_E_HIP with the HIP error text.
+ *  - Two environment switches, read once per process: HHR_TEST_FAIL=<text>
+ *    makes every launch whose name contains <text> ("*": every launch) fail
+ *    with HHR_E_HIP before anything is enqueued, for testing callers' error
+ *    paths without a GPU; HHR_DEBUG_SYNC=1 synchronizes the stream and checks
+ *    for errors after every launch, so an asynchronous fault is reported by
+ *    the call that launched it (the one case where the library synchronizes;
+ *    not for use under stream capture).
  *  - Per-sequence values held in device arrays (start, count, seq_len,
  *    keep_pages) are clamped inside the kernels so that no access leaves its
  *    buffer: seq_len to [0, max_ctx]; start to [0, max_ctx]; count to
