@@ -569,7 +569,9 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
     __shared__ int thr[2];
     __shared__ int offs[3];
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Same grid order as the select kernels, (Hkv, B, S): a block lands on the XCD whose L2 holds the
+    // slots and histograms the select block of the same (head, split) wrote.
+    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 15, rw = tid >> 4;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t q0 = (int64_t)b * Hq + (int64_t)h * G;
@@ -1033,7 +1035,7 @@ hipError_t compact_g(const DecodeArgs& a, hipStream_t st) {
     float* po = reinterpret_cast<float*>(a.ws + a.lay.partial);
     float* pml = po + (size_t)s.B * s.Hq * a.lay.part_splits * s.D;
     uint32_t* counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
-    hipLaunchKernelGGL((compact_attend_kernel<D, BF16, G>), dim3(S, s.Hkv, s.B), dim3(kCompactThreads), 0, st, a.Q,
+    hipLaunchKernelGGL((compact_attend_kernel<D, BF16, G>), dim3(s.Hkv, s.B, S), dim3(kCompactThreads), 0, st, a.Q,
                        a.K, a.V,
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.pages),
                        reinterpret_cast<const int32_t*>(a.ws + a.lay.n_pages),
