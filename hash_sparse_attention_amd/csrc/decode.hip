@@ -100,18 +100,23 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
-                                                         int64_t NPB, int64_t NPmax, int share) {
+                                                         int64_t NPB, int64_t NPmax, int share, int nbatch) {
     constexpr int NJ = M16 ? D / 4 : D / 2;  // 16-byte slots per page
     static_assert(NJ % U == 0, "batches");
     constexpr bool SQ = G <= 4 && !M16;       // query terms as scalar loads (else LDS broadcasts)
     using V4 = typename std::conditional<M16, uint4, float4>::type;
     __shared__ double2 qs_lds[SQ ? 1 : D * G];  // (max(q,0), min(q,0)) per dimension and query head
-    const int h = blockIdx.y, b = blockIdx.z;
+    // One-dimensional grid in (head, sequence, page block) order, head fastest: the workgroups of a
+    // (sequence, head) share an XCD with the projection blocks that wrote its query terms and the select
+    // blocks that read its scores (workgroups go to the XCDs in turn by linear index).
+    const int h = (int)(blockIdx.x % (unsigned)Hkv);
+    const int b = (int)((blockIdx.x / (unsigned)Hkv) % (unsigned)nbatch);
+    const int64_t pb = blockIdx.x / ((unsigned)Hkv * (unsigned)nbatch);
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
     const int64_t NP = n_pages_of(L, P);
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if ((int64_t)blockIdx.x * 256 >= NP) return;  // block-uniform
+    const int64_t p = pb * 256 + threadIdx.x;
+    if (pb * 256 >= NP) return;  // block-uniform
 
     const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
     if constexpr (SQ) {
@@ -185,18 +190,23 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
                                                                const double* __restrict__ q_split,
                                                                const int32_t* __restrict__ seq_len,
                                                                double* __restrict__ score, int Hkv, int T, int P,
-                                                               int64_t NPB, int64_t NPmax, int share) {
+                                                               int64_t NPB, int64_t NPmax, int share, int nbatch) {
     using E = typename std::conditional<M16, uint16_t, float>::type;
     constexpr int NS = G == 1 ? 1 : 2;  // sides read per dimension
     constexpr int NBT = D / U;          // batches of U dimensions
     static_assert(D % U == 0 && NBT % 2 == 0, "batches");
     __shared__ double2 qs_lds[G == 1 ? 1 : D * G];  // (max(q,0), min(q,0)) per dimension and query head
-    const int h = blockIdx.y, b = blockIdx.z;
+    // One-dimensional grid in (head, sequence, page block) order, head fastest: the workgroups of a
+    // (sequence, head) share an XCD with the projection blocks that wrote its query terms and the select
+    // blocks that read its scores (workgroups go to the XCDs in turn by linear index).
+    const int h = (int)(blockIdx.x % (unsigned)Hkv);
+    const int b = (int)((blockIdx.x / (unsigned)Hkv) % (unsigned)nbatch);
+    const int64_t pb = blockIdx.x / ((unsigned)Hkv * (unsigned)nbatch);
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
     const int64_t NP = n_pages_of(L, P);
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if ((int64_t)blockIdx.x * 256 >= NP) return;  // block-uniform
+    const int64_t p = pb * 256 + threadIdx.x;
+    if (pb * 256 >= NP) return;  // block-uniform
 
     const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
     // G = 1: bit d set when q_d < 0 (the min side is read).  Built while every
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
 template <int D, int G>
 hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
-    const dim3 grid((unsigned)((s.NPmax + 255) / 256), s.Hkv, s.B);
+    const dim3 grid((unsigned)(((s.NPmax + 255) / 256) * s.Hkv * s.B));
     // Loads per lane per batch (two batches in flight), measured best per metadata type.
     auto kern = s.meta16 ? (s.pg_min ? page_bound_kernel<D, G, 8, true, true> : page_bound_kernel<D, G, 8, true, false>)
                          : (s.pg_min ? page_bound_kernel<D, G, 4, false, true> : page_bound_kernel<D, G, 4, false, false>);
@@ -299,7 +309,7 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
                        reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax,
-                       s.share);
+                       s.share, s.B);
     return hipGetLastError();
 }
 
