@@ -471,7 +471,7 @@ def main_encode(args):
         "hbm_algorithmic_bytes_per_launch": hbm,
         "hbm_GBps": hbm / (us * 1e-6) / 1e9,
         "roofline": {
-            "kernel": "encode_bulk_kernel", "bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
+            "kernel": "encode_tile_kernel", "bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": tflops / FP32_PEAK_TFLOPS, "traffic": None,
             "peak_without_packed_fp32": FP32_PEAK_UNPACKED_TFLOPS, "flops_per_launch": flops,
             "keys_per_launch": keys, "us_per_launch": us,

@@ -8,13 +8,10 @@
 // c ascending from acc = +0, so any IEEE implementation of it -- on either
 // mapping below -- produces the same bits.
 //
-// This file holds the bulk mapping on gfx950 (wave64), used for many keys:
-// one lane per key.  The key row sits in VGPRs as fp32; the rows of
-// [R_h; W_h] are wave-uniform, so they come in through scalar loads, one
-// chunk ahead, and feed v_fma as SGPR operands.  A page is P adjacent lanes: its max/min is a
-// butterfly over P lanes.  Each lane packs its own code words and stores
-// them contiguously.  Appends of a few keys (the token just generated) use
-// the row-per-lane projection kernel instead.
+// This file holds the bulk mapping on gfx950 (wave64), used for many keys: a
+// register-tiled product of [R_h; W_h] with a 64-key tile, both operands
+// staged in LDS (below).  Appends of a few keys (the token just generated)
+// use the row-per-lane projection kernel instead.
 #include "hhr_internal.h"
 
 namespace hhr {
@@ -36,162 +33,213 @@ __device__ __forceinline__ EncRange enc_range(const int32_t* start, const int32_
 }
 
 // ------------------------------------------------------------------ bulk
+// A block owns a tile of 64 consecutive keys (a page boundary first, so every
+// page of the tile is whole: P divides 64) and all D + NB rows of [R_h; W_h],
+// one wave per 64 rows.  Columns arrive in chunks of 32: the keys (widened
+// to fp32) and the rows are staged in LDS with coalesced 16-byte loads, then
+// each thread runs an 8 x 8 register tile -- keys kg + 8j, rows rg + 8i of its
+// wave's 64, lane = kg + 8 rg -- reading 4 columns of a key or row per
+// 16-byte LDS read, so 16 reads feed 256 FMAs.  Every accumulator is one
+// canonical chain (columns ascending from +0).  Padding rows of the two LDS
+// tiles to 36 floats puts the 8 keys (or rows) a read touches in 8 distinct
+// 4-bank groups.
+//
+// Epilogue: a rotation wave reduces each dimension's values over a page --
+// within the thread over the keys of its register tile, then across the kg
+// lanes -- pairs dimensions r, r + 1 (lanes 8 apart) and stores the page's
+// metadata; a hash wave sets bit rg + 8i of its code word per key and ORs the
+// word over the 8 rg lanes, and lane (kg, rg) stores key kg + 8 rg's word.
+constexpr int kEncKeys = 64;            // keys per tile
+constexpr int kEncCols = 32;            // columns per staged chunk
+constexpr int kEncStride = kEncCols + 4;  // LDS row stride in floats (16-byte aligned, conflict-free reads)
+
 template <int D, int NB, bool BF16, bool M16, bool MS>
-__global__ __launch_bounds__(256) void encode_bulk_kernel(const void* __restrict__ K, const float* __restrict__ R,
-                                                          const float* __restrict__ W,
-                                                          const int32_t* __restrict__ start,
-                                                          const int32_t* __restrict__ count, int max_count,
-                                                          float* __restrict__ meta, uint64_t* __restrict__ codes,
-                                                          int Hkv, int T, int P, int64_t NPB) {
-    constexpr int NW = NB / 64;
+__global__ __launch_bounds__(D + NB) __attribute__((amdgpu_waves_per_eu(3))) void encode_tile_kernel(
+    const void* __restrict__ K, const float* __restrict__ R, const float* __restrict__ W,
+    const int32_t* __restrict__ start, const int32_t* __restrict__ count, int max_count, float* __restrict__ meta,
+    uint64_t* __restrict__ codes, int Hkv, int T, int P, int64_t NPB) {
+    constexpr int MR = D + NB, NT = MR, NCH = D / kEncCols;
+    static_assert(MR % 64 == 0 && D % kEncCols == 0, "tile shape");
+    __shared__ float ks[kEncKeys * kEncStride];  // [key][column] of the chunk
+    __shared__ float ms[MR * kEncStride];        // [row][column] of the chunk
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * Hkv + h;
-    const EncRange rg = enc_range(start, count, b, max_count, T);
-    if (rg.e <= rg.s) return;
-    const int base = (rg.s / P) * P + blockIdx.x * 256;  // a page boundary
-    if (base + (int)(threadIdx.x & ~63) >= rg.e) return;  // whole wave past the range (no barriers below)
-    const int t = base + threadIdx.x;
-    const bool valid = t < rg.e;
-
-    float k[D];
-    if (valid) {
-        if (BF16) {
-            const uint4* kr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(K) + (bh * T + t) * D);
-#pragma unroll
-            for (int i = 0; i < D / 8; ++i) {
-                const uint4 u = kr[i];
-                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    k[8 * i + 2 * q] = __uint_as_float(w4[q] << 16);
-                    k[8 * i + 2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
-                }
-            }
-        } else {
-            const float4* kr = reinterpret_cast<const float4*>(static_cast<const float*>(K) + (bh * T + t) * D);
-#pragma unroll
-            for (int i = 0; i < D / 4; ++i) {
-                const float4 f = kr[i];
-                k[4 * i] = f.x; k[4 * i + 1] = f.y; k[4 * i + 2] = f.z; k[4 * i + 3] = f.w;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < D; ++i) k[i] = 0.f;
-    }
-
-    // Rows of [R_h; W_h] stream in as wave-uniform chunks of CH columns:
-    // scalar loads into SGPRs, which feed v_fma as operands.  Scalar loads
-    // can return out of order, so a wait can only be for all of them; one
-    // chunk is kept in flight: wait for the current chunk, issue the next
-    // one, then run the CH FMAs of the current one, which cover its latency
-    // (across row boundaries too).  Each chain is the canonical one: acc = +0,
-    // c ascending.
-    constexpr int CH = 32;       // columns per chunk
-    constexpr int NCH = D / CH;  // chunks per row: even, so buffer A holds a row's first chunk on entry
-    static_assert(NCH % 2 == 0, "chunks per row");
+    const EncRange rng = enc_range(start, count, b, max_count, T);
+    if (rng.e <= rng.s) return;
+    const int tb = (rng.s / P) * P + blockIdx.x * kEncKeys;  // a page boundary
+    if (tb >= rng.e) return;                                  // block-uniform
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kg = lane & 7, rg = lane >> 3;
     const float* Rh = R + (int64_t)h * D * D;
     const float* Wh = W + (int64_t)h * NB * D;
-    float A[CH], Bc[CH];
-    auto load = [&](float (&c)[CH], const float* p) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) c[i] = p[i];
-    };
-    // The chain of the row at p_row; leaves the first chunk of the row at p_next in A.
-    auto row_chain = [&](const float* p_row, const float* p_next) {
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            float(&cur)[CH] = (q & 1) ? Bc : A;
-            float(&nxt)[CH] = (q & 1) ? A : Bc;
-            // Wait for chunk q (then the only scalar load in flight), then issue
-            // chunk q + 1, so the wait never covers the chunk just issued.
-            // 0xc07f: lgkmcnt(0), vmcnt and expcnt left at their maximum.
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_sched_barrier(0);
-            load(nxt, q + 1 < NCH ? p_row + (q + 1) * CH : p_next);
-            __builtin_amdgcn_sched_barrier(0);  // the loads (and their address math) stay ahead of the FMAs
-#pragma unroll
-            for (int i = 0; i < CH; ++i) acc = __builtin_fmaf(cur[i], k[q * CH + i], acc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        return acc;
-    };
-    load(A, Rh);
 
-    // Rotation rows, two at a time so a page leader stores one float4 per pair.
-    const int p = t / P;
-    const bool leader = (t - base) % P == 0 && valid;
-    float4* mrow = reinterpret_cast<float4*>(meta) + (bh * NPB + p / 64) * (D / 2) * 64 + (p & 63);
-    // bf16 meta: dimension quad r/4 of page p is one 16-byte slot; a pair is its (r % 4) / 2 half.
-    uint2* mrow16 = reinterpret_cast<uint2*>(meta) + ((bh * NPB + p / 64) * (D / 4) * 64 + (p & 63)) * 2;
-#pragma unroll 1
-    for (int r = 0; r < D; r += 2) {
-        float mx[2], mn[2];
+    float acc[8][8];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const float* row = Rh + (int64_t)(r + q) * D;
-            const float acc = row_chain(row, r + q + 1 < D ? row + D : Wh);  // then hash row 0
-            const float v = acc == 0.f ? 0.f : acc;
-            mx[q] = valid ? v : -__builtin_inff();
-            mn[q] = valid ? v : __builtin_inff();
-            for (int o = 1; o < P; o <<= 1) {
-                mx[q] = fmaxf(mx[q], __shfl_xor(mx[q], o, 64));
-                mn[q] = fminf(mn[q], __shfl_xor(mn[q], o, 64));
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+
+    for (int c = 0; c < NCH; ++c) {
+        if (c) __syncthreads();  // the previous chunk has been read
+        // Keys: 64 x 32 columns, 16-byte pieces; keys past the range are zero.
+        if constexpr (BF16) {
+            for (int x = tid; x < kEncKeys * 4; x += NT) {
+                const int kk = x >> 2, q = x & 3, t = tb + kk;
+                u32x4 u = {0u, 0u, 0u, 0u};
+                if (t < rng.e)
+                    u = load_stream16(static_cast<const uint16_t*>(K) + (bh * T + t) * D + c * kEncCols + q * 8);
+                float* dst = ks + kk * kEncStride + q * 8;
+                *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                                              __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
+                                                                  __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u));
+            }
+        } else {
+            for (int x = tid; x < kEncKeys * 8; x += NT) {
+                const int kk = x >> 3, q = x & 7, t = tb + kk;
+                u32x4 u = {0u, 0u, 0u, 0u};
+                if (t < rng.e) u = load_stream16(static_cast<const float*>(K) + (bh * T + t) * D + c * kEncCols + q * 4);
+                *reinterpret_cast<float4*>(ks + kk * kEncStride + q * 4) =
+                    make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
             }
         }
-        if (leader) {
-            // The outputs are read by later steps, not by this launch or the
-            // next: stored with the nontemporal hint (measured 2-3% faster).
-            if (MS) {  // sign-split layout: dimension d's max run, then its min run, 64 pages each
-                const int64_t e0 = ((bh * NPB + p / 64) * D + r) * 128 + (p & 63);
+        // Rows: MR x 32 columns, 8 pieces a row, 8 a thread.
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    if (M16) {
-                        uint16_t* m = reinterpret_cast<uint16_t*>(meta) + e0 + q * 128;
-                        __builtin_nontemporal_store((uint16_t)bf16_up(mx[q]), m);
-                        __builtin_nontemporal_store((uint16_t)bf16_down(mn[q]), m + 64);
-                    } else {
-                        float* m = meta + e0 + q * 128;
-                        __builtin_nontemporal_store(mx[q], m);
-                        __builtin_nontemporal_store(mn[q], m + 64);
+        for (int u = 0; u < 8; ++u) {
+            const int x = tid + u * NT, r = x >> 3, q = x & 7;
+            const float* src = (r < D ? Rh + (int64_t)r * D : Wh + (int64_t)(r - D) * D) + c * kEncCols + q * 4;
+            *reinterpret_cast<float4*>(ms + r * kEncStride + q * 4) = *reinterpret_cast<const float4*>(src);
+        }
+        __syncthreads();
+        const float* kp = ks + kg * kEncStride;
+        const float* rp = ms + (wave * 64 + rg) * kEncStride;
+#pragma unroll
+        for (int c4 = 0; c4 < kEncCols; c4 += 4) {
+            float4 kv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kv[j] = *reinterpret_cast<const float4*>(kp + 8 * j * kEncStride + c4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 rv = *reinterpret_cast<const float4*>(rp + 8 * i * kEncStride + c4);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    acc[i][j] = __builtin_fmaf(rv.x, kv[j].x, acc[i][j]);
+                    acc[i][j] = __builtin_fmaf(rv.y, kv[j].y, acc[i][j]);
+                    acc[i][j] = __builtin_fmaf(rv.z, kv[j].z, acc[i][j]);
+                    acc[i][j] = __builtin_fmaf(rv.w, kv[j].w, acc[i][j]);
+                }
+            }
+        }
+    }
+
+    if (wave * 64 < D) {  // rotation rows: page max / min (wave-uniform branch)
+        // With P >= 8 the 64 / P pages of the tile start at keys 8j, j a
+        // multiple of P / 8, and lane kg = page stores; with P < 8 a page is
+        // P adjacent kg lanes of one j, and its first lane stores.
+        bool ok[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ok[j] = tb + kg + 8 * j < rng.e;
+        const int pj = P >= 8 ? P / 8 : 1;  // register-tile keys per page
+        const int pl = P >= 8 ? 8 : P;      // lanes per page
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = wave * 64 + rg + 8 * i;  // dimension
+            float mx[8], mn[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = acc[i][j] == 0.f ? 0.f : acc[i][j];
+                mx[j] = ok[j] ? v : -__builtin_inff();
+                mn[j] = ok[j] ? v : __builtin_inff();
+            }
+#pragma unroll
+            for (int sj = 1; sj < 8; sj <<= 1) {
+                if (sj < pj) {  // uniform
+#pragma unroll
+                    for (int j = 0; j < 8; j += 2 * sj) {
+                        mx[j] = fmaxf(mx[j], mx[j + sj]);
+                        mn[j] = fminf(mn[j], mn[j + sj]);
                     }
                 }
-            } else if (M16) {
-                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
-                const u2v m2 = {bf16_pair_out(mx[0], mn[0]), bf16_pair_out(mx[1], mn[1])};
-                __builtin_nontemporal_store(m2, reinterpret_cast<u2v*>(mrow16 + (r / 4) * 64 * 2 + (r % 4) / 2));
-            } else {
-                typedef float f4v __attribute__((ext_vector_type(4)));
-                const f4v m4 = {mx[0], mn[0], mx[1], mn[1]};
-                __builtin_nontemporal_store(m4, reinterpret_cast<f4v*>(mrow + (r / 2) * 64));
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j % pj) continue;  // uniform
+                for (int o = 1; o < pl; o <<= 1) {
+                    mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], o, 64));
+                    mn[j] = fminf(mn[j], __shfl_xor(mn[j], o, 64));
+                }
+                // Dimension r + 1 sits 8 lanes up (rg + 1).
+                const float mx1 = __shfl_xor(mx[j], 8, 64), mn1 = __shfl_xor(mn[j], 8, 64);
+                const int kk0 = P >= 8 ? 8 * j : ((kg + 8 * j) & ~(P - 1));  // the page's first key in the tile
+                const bool store = (rg & 1) == 0 && (P >= 8 ? kg == j / pj : (kg & (P - 1)) == 0) && tb + kk0 < rng.e;
+                if (!store) continue;
+                const int64_t p = (tb + kk0) / P;
+                // The outputs are read by later steps, not by this launch or the
+                // next: stored with the nontemporal hint.
+                if (MS) {  // sign-split layout: dimension d's max run, then its min run, 64 pages each
+                    const int64_t e0 = ((bh * NPB + p / 64) * D + r) * 128 + (p & 63);
+                    if (M16) {
+                        uint16_t* m = reinterpret_cast<uint16_t*>(meta) + e0;
+                        __builtin_nontemporal_store((uint16_t)bf16_up(mx[j]), m);
+                        __builtin_nontemporal_store((uint16_t)bf16_down(mn[j]), m + 64);
+                        __builtin_nontemporal_store((uint16_t)bf16_up(mx1), m + 128);
+                        __builtin_nontemporal_store((uint16_t)bf16_down(mn1), m + 192);
+                    } else {
+                        float* m = meta + e0;
+                        __builtin_nontemporal_store(mx[j], m);
+                        __builtin_nontemporal_store(mn[j], m + 64);
+                        __builtin_nontemporal_store(mx1, m + 128);
+                        __builtin_nontemporal_store(mn1, m + 192);
+                    }
+                } else if (M16) {  // dimension quad r / 4 is one 16-byte slot; the pair is its (r % 4) / 2 half
+                    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                    const u2v m2 = {bf16_pair_out(mx[j], mn[j]), bf16_pair_out(mx1, mn1)};
+                    uint2* m = reinterpret_cast<uint2*>(meta) + ((bh * NPB + p / 64) * (D / 4) * 64 + (p & 63)) * 2 +
+                               (r / 4) * 64 * 2 + (r % 4) / 2;
+                    __builtin_nontemporal_store(m2, reinterpret_cast<u2v*>(m));
+                } else {  // dimension pair r / 2 is one 16-byte slot
+                    typedef float f4v __attribute__((ext_vector_type(4)));
+                    const f4v m4 = {mx[j], mn[j], mx1, mn1};
+                    float4* m = reinterpret_cast<float4*>(meta) + (bh * NPB + p / 64) * (D / 2) * 64 + (r / 2) * 64 + (p & 63);
+                    __builtin_nontemporal_store(m4, reinterpret_cast<f4v*>(m));
+                }
             }
         }
-    }
-
-    // Hash rows: this lane's own code words.
-    uint64_t code[NW];
+    } else {  // hash rows: code word wave - D / 64, bit rg + 8i
+        uint32_t lo[8], hi[8];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) code[w] = 0;
-#pragma unroll 1
-    for (int j = 0; j < NB; ++j) {
-        const float* row = Wh + (int64_t)j * D;
-        const float acc = row_chain(row, j + 1 < NB ? row + D : row);  // the last row reloads itself (in bounds)
-        if (acc > 0.f) code[j >> 6] |= 1ull << (j & 63);
-    }
-    if (valid && t >= rg.s) {
-        uint64_t* cp = codes + (bh * T + t) * NW;
+        for (int j = 0; j < 8; ++j) {
+            lo[j] = 0u;
+            hi[j] = 0u;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) __builtin_nontemporal_store(code[w], cp + w);
+            for (int i = 0; i < 4; ++i) {
+                lo[j] |= (acc[i][j] > 0.f ? 1u : 0u) << (rg + 8 * i);
+                hi[j] |= (acc[i + 4][j] > 0.f ? 1u : 0u) << (rg + 8 * i);
+            }
+#pragma unroll
+            for (int o = 8; o < 64; o <<= 1) {
+                lo[j] |= __shfl_xor(lo[j], o, 64);
+                hi[j] |= __shfl_xor(hi[j], o, 64);
+            }
+        }
+        uint32_t wl = lo[0], wh = hi[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+            wl = rg == j ? lo[j] : wl;
+            wh = rg == j ? hi[j] : wh;
+        }
+        const int t = tb + kg + 8 * rg;
+        if (t >= rng.s && t < rng.e)
+            __builtin_nontemporal_store(((uint64_t)wh << 32) | wl, codes + (bh * T + t) * (NB / 64) + (wave - D / 64));
     }
 }
 
 template <int D, int NB, bool BF16, bool M16>
 hipError_t launch_dnb(const Shape& s, const void* K, const float* R, const float* W, const int32_t* start,
                       const int32_t* count, int max_count, float* meta, uint64_t* codes, hipStream_t st) {
-    const int tiles = (max_count + s.P - 1 + 255) / 256;  // keys [floor(s/P)P, e) in 256-key tiles
-    auto kern = s.msplit ? encode_bulk_kernel<D, NB, BF16, M16, true> : encode_bulk_kernel<D, NB, BF16, M16, false>;
-    hipLaunchKernelGGL(kern, dim3(tiles, s.Hkv, s.B), dim3(256), 0, st, K, R, W, start, count, max_count, meta, codes,
+    const int tiles = (max_count + s.P - 1 + kEncKeys - 1) / kEncKeys;  // keys [floor(s/P)P, e) in 64-key tiles
+    auto kern = s.msplit ? encode_tile_kernel<D, NB, BF16, M16, true> : encode_tile_kernel<D, NB, BF16, M16, false>;
+    hipLaunchKernelGGL(kern, dim3(tiles, s.Hkv, s.B), dim3(D + NB), 0, st, K, R, W, start, count, max_count, meta, codes,
                        s.Hkv, s.T, s.P, s.NPB);
     return hipGetLastError();
 }
