@@ -35,7 +35,7 @@ __device__ __forceinline__ EncRange enc_range(const int32_t* start, const int32_
 // ------------------------------------------------------------------ bulk
 // A block owns a tile of 64 consecutive keys (a page boundary first, so every
 // page of the tile is whole: P divides 64) and all D + NB rows of [R_h; W_h],
-// one wave per 64 rows.  Columns arrive in chunks of 32: the keys (widened
+// one wave per 64 rows.  Columns arrive in chunks of kEncCols: the keys (widened
 // to fp32) and the rows are staged in LDS with coalesced 16-byte loads, then
 // each thread runs an 8 x 8 register tile -- keys kg + 8j, rows rg + 8i of its
 // wave's 64, lane = kg + 8 rg -- reading 4 columns of a key or row per
@@ -50,7 +50,7 @@ __device__ __forceinline__ EncRange enc_range(const int32_t* start, const int32_
 // metadata; a hash wave sets bit rg + 8i of its code word per key and ORs the
 // word over the 8 rg lanes, and lane (kg, rg) stores key kg + 8 rg's word.
 constexpr int kEncKeys = 64;            // keys per tile
-constexpr int kEncCols = 32;            // columns per staged chunk
+constexpr int kEncCols = 16;            // columns per staged chunk
 constexpr int kEncStride = kEncCols + 4;  // LDS row stride in floats (16-byte aligned, conflict-free reads)
 
 template <int D, int NB, bool BF16, bool M16, bool MS>
@@ -59,7 +59,8 @@ __global__ __launch_bounds__(D + NB) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int32_t* __restrict__ start, const int32_t* __restrict__ count, int max_count, float* __restrict__ meta,
     uint64_t* __restrict__ codes, int Hkv, int T, int P, int64_t NPB) {
     constexpr int MR = D + NB, NT = MR, NCH = D / kEncCols;
-    static_assert(MR % 64 == 0 && D % kEncCols == 0, "tile shape");
+    static_assert(MR % 64 == 0 && D % kEncCols == 0 && kEncCols % 8 == 0, "tile shape");
+    static_assert(kEncStride % 4 == 0 && kEncStride >= kEncCols, "16-byte aligned LDS rows");
     __shared__ float ks[kEncKeys * kEncStride];  // [key][column] of the chunk
     __shared__ float ms[MR * kEncStride];        // [row][column] of the chunk
     const int h = blockIdx.y, b = blockIdx.z;
@@ -81,10 +82,11 @@ __global__ __launch_bounds__(D + NB) __attribute__((amdgpu_waves_per_eu(3))) voi
 
     for (int c = 0; c < NCH; ++c) {
         if (c) __syncthreads();  // the previous chunk has been read
-        // Keys: 64 x 32 columns, 16-byte pieces; keys past the range are zero.
+        // Keys: 64 x kEncCols columns in 16-byte pieces; keys past the range are zero.
         if constexpr (BF16) {
-            for (int x = tid; x < kEncKeys * 4; x += NT) {
-                const int kk = x >> 2, q = x & 3, t = tb + kk;
+            constexpr int PK = kEncCols / 8;  // pieces per key
+            for (int x = tid; x < kEncKeys * PK; x += NT) {
+                const int kk = x / PK, q = x % PK, t = tb + kk;
                 u32x4 u = {0u, 0u, 0u, 0u};
                 if (t < rng.e)
                     u = load_stream16(static_cast<const uint16_t*>(K) + (bh * T + t) * D + c * kEncCols + q * 8);
@@ -95,18 +97,20 @@ __global__ __launch_bounds__(D + NB) __attribute__((amdgpu_waves_per_eu(3))) voi
                                                                   __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u));
             }
         } else {
-            for (int x = tid; x < kEncKeys * 8; x += NT) {
-                const int kk = x >> 3, q = x & 7, t = tb + kk;
+            constexpr int PK = kEncCols / 4;
+            for (int x = tid; x < kEncKeys * PK; x += NT) {
+                const int kk = x / PK, q = x % PK, t = tb + kk;
                 u32x4 u = {0u, 0u, 0u, 0u};
                 if (t < rng.e) u = load_stream16(static_cast<const float*>(K) + (bh * T + t) * D + c * kEncCols + q * 4);
                 *reinterpret_cast<float4*>(ks + kk * kEncStride + q * 4) =
                     make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
             }
         }
-        // Rows: MR x 32 columns, 8 pieces a row, 8 a thread.
+        // Rows: MR x kEncCols columns, PR pieces of 4 a row, PR a thread.
+        constexpr int PR = kEncCols / 4;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int x = tid + u * NT, r = x >> 3, q = x & 7;
+        for (int u = 0; u < PR; ++u) {
+            const int x = tid + u * NT, r = x / PR, q = x % PR;
             const float* src = (r < D ? Rh + (int64_t)r * D : Wh + (int64_t)(r - D) * D) + c * kEncCols + q * 4;
             *reinterpret_cast<float4*>(ms + r * kEncStride + q * 4) = *reinterpret_cast<const float4*>(src);
         }
