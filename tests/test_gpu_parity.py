@@ -701,3 +701,32 @@ def test_sign_split_encode_in_chunks(dev):
     g = run_gpu(wl, d, dev, chunks=chunks)
     o = run_oracle(wl, d)
     compare(wl, d["seq_len"], g, o, label="sign-split chunks")
+
+
+BULK_CHUNK_SHAPES = [
+    # name, workload (B=2, G=2); every page-size branch of the tiled encode's page reduction
+    ("p1_d64_b128_bf16", Workload("bc1", 201, 2, 4, 2, 64, 1000, 1, 128, 20, 64, "bf16")),
+    ("p2_d128_b64_fp32_m16", Workload("bc2", 202, 2, 4, 2, 128, 1000, 2, 64, 20, 64, "fp32", meta_bf16=True)),
+    ("p4_d128_b128_fp32_split", Workload("bc4", 203, 2, 4, 2, 128, 1000, 4, 128, 20, 64, "fp32", meta_split=True)),
+    ("p8_d64_b64_bf16", Workload("bc8", 204, 2, 4, 2, 64, 1000, 8, 64, 20, 64, "bf16", outliers=2)),
+    ("p32_d128_b64_bf16_m16_split", Workload("bc32", 205, 2, 4, 2, 128, 1000, 32, 64, 20, 64, "bf16",
+                                             meta_bf16=True, meta_split=True)),
+    ("p64_d64_b128_fp32", Workload("bc64", 206, 2, 4, 2, 64, 1000, 64, 128, 30, 64, "fp32")),
+]
+
+
+@pytest.mark.parametrize("name,wl", BULK_CHUNK_SHAPES, ids=[s[0] for s in BULK_CHUNK_SHAPES])
+def test_bulk_encode_mid_page_chunks(dev, name, wl):
+    """Bulk encodes (more than 64 keys, the tiled kernel) that start mid-page and mid-tile, with ragged and zero
+    counts and max_count above every count: codes and page bounds bit-identical to the oracle's single-shot encode,
+    and the decode on them equal to the oracle's."""
+    banner(f"bulk encode mid-page chunks {name}")
+    d = make_layer(wl, lengths=[977, 941])
+    chunks = [(np.zeros(2, np.int32), np.array([301, 299], np.int32), 301),      # ends mid-page, mid-tile
+              (np.array([301, 299], np.int32), np.array([130, 0], np.int32), 200),  # sequence 1 appends nothing
+              (np.array([431, 299], np.int32), np.array([67, 197], np.int32), 250),
+              (np.array([498, 496], np.int32), np.array([479, 445], np.int32), 479)]
+    assert [int(s + c) for s, c in zip(chunks[-1][0], chunks[-1][1])] == [977, 941]
+    g = run_gpu(wl, d, dev, chunks=chunks)
+    o = run_oracle(wl, d)
+    compare(wl, d["seq_len"], g, o, label=name)
