@@ -30,12 +30,10 @@ namespace {
 // The query terms are block-uniform (a block covers pages of one head).  For
 // G <= 4 they reach the FMAs as scalar loads, an SGPR operand each, so the
 // stream issues no LDS reads at all; a 16-byte LDS broadcast still returns
-// 16 bytes per lane, and at G = 4 a page block needs 512 of them.  The
-// projection blocks that wrote a head's terms ran on the XCD this head's
-// blocks run on (both grids put the head fastest, and workgroups go to the
-// XCDs in turn), so the scalar loads find them in that L2 and the stream
-// starts at once (measured: a coalesced warm-up pass of the terms before the
-// stream cost 0.2 us per layer at 128K).  Larger groups, and bf16 metadata
+// 16 bytes per lane, and at G = 4 a page block needs 512 of them.  The block
+// first pulls its terms into the XCD's L2 with one coalesced round trip: the
+// projection launch has just written them, and scalar misses issued a slot
+// or two ahead would otherwise serialise.  Larger groups, and bf16 metadata
 // (a 16-byte slot then holds 4 dimensions: 64 SGPRs of terms per slot at
 // G = 4), need more SGPRs per slot than the scalar file holds without
 // stalling or spilling, so they stage the terms once per block in LDS and read
@@ -81,6 +79,22 @@ __device__ __forceinline__ void bound_batch16(const uint4 (&v)[U], const double2
     }
 }
 
+// Every lane of the block loads its share of the head's D * G query terms
+// (all loads issued, then waited for), so the lines sit in this XCD's L2
+// before the waves read them as scalar loads.
+template <int D, int G>
+__device__ __forceinline__ void warm_query_terms(const double2* __restrict__ qg) {
+    constexpr int NQ = (D * G + 255) / 256;
+    double2 t[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        const int x = threadIdx.x + r * 256;
+        t[r] = qg[x < D * G ? x : 0];
+    }
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) asm volatile("" ::"v"(t[r].x), "v"(t[r].y));  // wait for every load
+}
+
 template <int D, int G, int U, bool M16, bool PGMIN>
 __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
@@ -105,10 +119,12 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     if (pb * 256 >= NP) return;  // block-uniform
 
     const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
-    if constexpr (!SQ) {
+    if constexpr (SQ) {
+        warm_query_terms<D, G>(qg);
+    } else {
         for (int x = threadIdx.x; x < D * G; x += 256) qs_lds[x] = qg[x];
-        __syncthreads();
     }
+    __syncthreads();
     if (p >= NP) return;
     const double2* qs = SQ ? qg : qs_lds;
 
