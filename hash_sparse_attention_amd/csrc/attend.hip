@@ -622,7 +622,7 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
     for (int r = 0; r < BPT; ++r)
         if (tid * BPT + r < nbins) sum += (int)gh[r];
     int nvalid;
-    int run = block_excl_scan<NT>(sum, scan, nvalid);
+    int run = block_excl_scan<NT, false>(sum, scan, nvalid);
     const int keff = nvalid < top_k ? nvalid : top_k;
 #pragma unroll
     for (int r = 0; r < BPT; ++r) {
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
         }
     }
     int tot;
-    const int packed = block_excl_scan<NT>((n_lt << 16) | n_eq, scan, tot);
+    const int packed = block_excl_scan<NT, false>((n_lt << 16) | n_eq, scan, tot);
     int eq_rank = packed & 0xffff;
     int pos = (packed >> 16) + (eq_rank < incl ? eq_rank : incl);
     // Forced keys (sink tokens, local window): [0, s_end) and [w_start, L),

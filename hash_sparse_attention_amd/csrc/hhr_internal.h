@@ -277,7 +277,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // most 1024; a constant, since blockDim.x is a load from the dispatch packet).
 // `scratch` holds >= 16 ints of LDS.  Returns the prefix and the block total;
 // every thread of the block must call it.
-template <int NT>
+template <int NT, bool TAIL = true>
 __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
     static_assert(NT % 64 == 0 && NT <= 1024, "block size");
     constexpr int nw = NT / 64;
@@ -293,7 +293,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) 
         tot += t;
     }
     total = tot;
-    __syncthreads();
+    if (TAIL) __syncthreads();  // scratch may be rewritten next (TAIL = false: the caller passes a barrier first)
     return base + x - v;
 }
 

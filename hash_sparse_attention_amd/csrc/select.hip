@@ -382,7 +382,7 @@ __device__ __forceinline__ int select_pages_fast(const double* __restrict__ sc, 
             sum += cnt[j];
         }
         int tot;
-        int above = block_excl_scan<kSelThreads>(sum, sh.scan, tot);
+        int above = block_excl_scan<kSelThreads, false>(sum, sh.scan, tot);
 #pragma unroll
         for (int j = 0; j < DPT; ++j) {
             if (above < need && above + cnt[j] >= need) {
@@ -546,7 +546,7 @@ __device__ __forceinline__ void split_scan(const uint64_t* __restrict__ ck, cons
     const int b0 = 2 * tid;
     const int c0 = b0 < NBINS ? hist[b0] : 0, c1 = b0 + 1 < NBINS ? hist[b0 + 1] : 0;
     int tot;
-    const int before = block_excl_scan<kSelThreads>(c0 + c1, scan, tot);
+    const int before = block_excl_scan<kSelThreads, false>(c0 + c1, scan, tot);
     if (b0 < NBINS) {
         cum[split * NBINS + b0] = (uint32_t)(before + c0);
         if (c0) atomicAdd(&ghist[b0], (uint32_t)c0);
