@@ -82,21 +82,29 @@ __device__ __forceinline__ void bound_batch16(const uint4 (&v)[U], const double2
 // Every lane of the block loads its share of the head's D * G query terms
 // (all loads issued, then waited for), so the lines sit in this XCD's L2
 // before the waves read them as scalar loads.
-template <int D, int G>
+template <int D, int G, int NT>
 __device__ __forceinline__ void warm_query_terms(const double2* __restrict__ qg) {
-    constexpr int NQ = (D * G + 255) / 256;
+    constexpr int NQ = (D * G + NT - 1) / NT;
     double2 t[NQ];
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
-        const int x = threadIdx.x + r * 256;
+        const int x = threadIdx.x + r * NT;
         t[r] = qg[x < D * G ? x : 0];
     }
 #pragma unroll
     for (int r = 0; r < NQ; ++r) asm volatile("" ::"v"(t[r].x), "v"(t[r].y));  // wait for every load
 }
 
-template <int D, int G, int U, bool M16, bool PGMIN>
-__global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict__ meta,
+// Pages (lanes) per block: 128 when the query terms are scalar loads -- at
+// batch 8 and 32K the finer blocks spread the stream more evenly over the
+// compute units (measured: the launch 7-8% shorter, the same at 128K) --
+// and 256 when each block stages the terms in LDS first (G > 4 or bf16
+// metadata), where halving the blocks would double the staging.
+template <int D, int G, bool M16>
+constexpr int bound_block_pages() { return (G <= 4 && !M16) ? 128 : 256; }
+
+template <int D, int G, int U, bool M16, bool PGMIN, int BP = bound_block_pages<D, G, M16>()>
+__global__ __launch_bounds__(BP) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
                                                          double* __restrict__ score, int Hkv, int T, int P,
@@ -115,14 +123,14 @@ __global__ __launch_bounds__(256) void page_bound_kernel(const float* __restrict
     const int64_t bh = (int64_t)b * Hkv + h;
     const int L = clamp_len(seq_len[b], T);
     const int64_t NP = n_pages_of(L, P);
-    const int64_t p = pb * 256 + threadIdx.x;
-    if (pb * 256 >= NP) return;  // block-uniform
+    const int64_t p = pb * BP + threadIdx.x;
+    if (pb * BP >= NP) return;  // block-uniform
 
     const double2* qg = reinterpret_cast<const double2*>(q_split) + bh * D * G;
     if constexpr (SQ) {
-        warm_query_terms<D, G>(qg);
+        warm_query_terms<D, G, BP>(qg);
     } else {
-        for (int x = threadIdx.x; x < D * G; x += 256) qs_lds[x] = qg[x];
+        for (int x = threadIdx.x; x < D * G; x += BP) qs_lds[x] = qg[x];
     }
     __syncthreads();
     if (p >= NP) return;
@@ -295,7 +303,9 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
 template <int D, int G>
 hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
-    const dim3 grid((unsigned)(((s.NPmax + 255) / 256) * s.Hkv * s.B));
+    // Pages per block: the interleaved kernel's choice, or 256 for the sign-split kernel.
+    const int bp = s.msplit ? 256 : (s.meta16 ? bound_block_pages<D, G, true>() : bound_block_pages<D, G, false>());
+    const dim3 grid((unsigned)(((s.NPmax + bp - 1) / bp) * s.Hkv * s.B));
     // Loads per lane per batch (two batches in flight), measured best per metadata type.
     auto kern = s.meta16 ? (s.pg_min ? page_bound_kernel<D, G, 8, true, true> : page_bound_kernel<D, G, 8, true, false>)
                          : (s.pg_min ? page_bound_kernel<D, G, 4, false, true> : page_bound_kernel<D, G, 4, false, false>);
@@ -306,7 +316,7 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
                         : (s.pg_min ? page_bound_split_kernel<D, G, US, false, true>
                                     : page_bound_split_kernel<D, G, US, false, false>);
     }
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a.meta,
+    hipLaunchKernelGGL(kern, grid, dim3(bp), 0, st, a.meta,
                        reinterpret_cast<const double*>(a.ws + a.lay.q_split), a.seq_len,
                        reinterpret_cast<double*>(a.ws + a.lay.score), s.Hkv, s.T, s.P, s.NPB, s.NPmax,
                        s.share, s.B);
