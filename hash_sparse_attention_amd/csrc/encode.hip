@@ -5,8 +5,9 @@
 // stored page bounds).
 //
 // Every projection is the canonical fp32 chain acc = fma(M[r][c], k[c], acc),
-// c ascending from acc = +0, so any IEEE implementation of it -- on either
-// mapping below -- produces the same bits.
+// c ascending from acc = +0, so any IEEE implementation of it -- the tiled
+// mapping below or the row-per-lane projection kernel -- produces the same
+// bits.
 //
 // This file holds the bulk mapping on gfx950 (wave64), used for many keys: a
 // register-tiled product of [R_h; W_h] with a 64-key tile, both operands
@@ -40,9 +41,9 @@ __device__ __forceinline__ EncRange enc_range(const int32_t* start, const int32_
 // each thread runs an 8 x 8 register tile -- keys kg + 8j, rows rg + 8i of its
 // wave's 64, lane = kg + 8 rg -- reading 4 columns of a key or row per
 // 16-byte LDS read, so 16 reads feed 256 FMAs.  Every accumulator is one
-// canonical chain (columns ascending from +0).  Padding rows of the two LDS
-// tiles to 36 floats puts the 8 keys (or rows) a read touches in 8 distinct
-// 4-bank groups.
+// canonical chain (columns ascending from +0).  Padding each LDS row by 4
+// floats (a stride of kEncStride = 20) puts the 8 keys (or rows) a read
+// touches in 8 distinct 4-bank groups.
 //
 // Epilogue: a rotation wave reduces each dimension's values over a page --
 // within the thread over the keys of its register tile, then across the kg
