@@ -343,6 +343,11 @@ def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> Workspac
     Hkv = sel_units(dims)  # per-(b, h) rows: query heads with per-query-head selection
     G, NW = Hq // Hkv, dims.hash_bits // 64
     NP = -(-dims.max_ctx // P)
+    # The bound terms keep the per-KV-head layout unless per-query-head selection reads sign-split metadata
+    # (one pass over a KV head's interleaved metadata serves all its query heads).
+    Hd = dims.n_kv_heads
+    split_units = Hkv != Hd and dims.meta_layout == HHR_META_SIGN_SPLIT
+    qs_shape = (B, Hkv, D, G, 2) if (Hkv == Hd or split_units) else (B, Hd, D, Hq // Hd, 2)
 
     def region(off, dtype, shape):
         n = 1
@@ -354,7 +359,7 @@ def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> Workspac
     return WorkspaceView(
         q_rot=region(lay.q_rot, torch.float32, (B, Hq, D)),
         code_q=region(lay.code_q, torch.int64, (B, Hq, NW)),
-        q_split=region(lay.q_split, torch.float64, (B, Hkv, D, G, 2)),
+        q_split=region(lay.q_split, torch.float64, qs_shape),
         score=region(lay.score, torch.float64, (B, Hkv, NP)),
         pages=region(lay.pages, torch.int32, (B, Hkv, max_keep)),
         n_pages=region(lay.n_pages, torch.int32, (B, Hkv)),

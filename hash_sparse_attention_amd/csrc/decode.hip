@@ -103,7 +103,11 @@ __device__ __forceinline__ void warm_query_terms(const double2* __restrict__ qg)
 template <int D, int G, bool M16>
 constexpr int bound_block_pages() { return (G <= 4 && !M16) ? 128 : 256; }
 
-template <int D, int G, int U, bool M16, bool PGMIN, int BP = bound_block_pages<D, G, M16>()>
+// PU (per-query-head selection with interleaved metadata): the launch runs
+// over data heads, and each of the group's G sums is written as its own
+// unit's score (unit = data head * G + i) instead of their max, so a KV
+// head's metadata is streamed once for its G selection units.
+template <int D, int G, int U, bool M16, bool PGMIN, int BP = bound_block_pages<D, G, M16>(), bool PU = false>
 __global__ __launch_bounds__(BP) void page_bound_kernel(const float* __restrict__ meta,
                                                          const double* __restrict__ q_split,
                                                          const int32_t* __restrict__ seq_len,
@@ -179,6 +183,11 @@ __global__ __launch_bounds__(BP) void page_bound_kernel(const float* __restrict_
             if (k + 1 < NBT) bound_batch<G, U>(B, qs, (k + 1) * U, acc);
         }
         asm volatile("" ::: "memory");
+    }
+    if constexpr (PU) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) score[(bh * G + i) * NPmax + p] = acc[i] == 0.0 ? 0.0 : acc[i];
+        return;
     }
     double S = acc[0];  // the group's max, or its min (a variant)
 #pragma unroll
@@ -337,8 +346,36 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Per-query-head selection on interleaved metadata: one pass per data head
+// (G = the units per data head), each unit's score written separately.
+template <int D, int G>
+hipError_t bounds_units(const DecodeArgs& a, hipStream_t st) {
+    const Shape& s = a.s;
+    const int Hd = s.Hkv / G;  // data heads (s.Hkv counts the units)
+    constexpr int BP16 = bound_block_pages<D, G, true>(), BP32 = bound_block_pages<D, G, false>();
+    const int bp = s.meta16 ? BP16 : BP32;
+    const dim3 grid((unsigned)(((s.NPmax + bp - 1) / bp) * Hd * s.B));
+    auto kern = s.meta16 ? page_bound_kernel<D, G, 8, true, false, BP16, true>
+                         : page_bound_kernel<D, G, 4, false, false, BP32, true>;
+    hipLaunchKernelGGL(kern, grid, dim3(bp), 0, st, a.meta, reinterpret_cast<const double*>(a.ws + a.lay.q_split),
+                       a.seq_len, reinterpret_cast<double*>(a.ws + a.lay.score), Hd, s.T, s.P, s.NPB, s.NPmax, 1,
+                       s.B);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t bounds_d(const DecodeArgs& a, hipStream_t st) {
+    if (a.s.share > 1 && !a.s.msplit) {
+        switch (a.s.share) {
+            case 2: return bounds_units<D, 2>(a, st);
+            case 3: return bounds_units<D, 3>(a, st);
+            case 4: return bounds_units<D, 4>(a, st);
+            case 5: return bounds_units<D, 5>(a, st);
+            case 6: return bounds_units<D, 6>(a, st);
+            case 7: return bounds_units<D, 7>(a, st);
+            default: return bounds_units<D, 8>(a, st);
+        }
+    }
     switch (a.s.G) {
         case 1: return bounds_g<D, 1>(a, st);
         case 2: return bounds_g<D, 2>(a, st);
@@ -366,7 +403,7 @@ hipError_t launch_qprep(const DecodeArgs& a, hipStream_t st) {
     p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
     p.n_counters = a.lay.n_clear;
     p.qmean = a.s.ham_mean;
-    p.qs_unit = a.s.share > 1;
+    p.qs_unit = a.s.share > 1 && a.s.msplit;  // per-unit terms only for the sign-split G = 1 kernel
     return launch_project(a.sd, p, st);  // per KV head of the cache
 }
 

@@ -159,7 +159,8 @@ typedef struct {
                               selection per query head: every per-(b, h)
                               workspace row and sel_idx row is then per
                               query head ([B][Hq]...), as if each KV head
-                              were repeated for its G query heads          */
+                              were repeated for its G query heads (q_split
+                              aside: see the workspace layout)             */
     int32_t meta_layout;   /* hhr_meta_layout of the page metadata: HHR_META_INTERLEAVED
                               (0, the default) or HHR_META_SIGN_SPLIT (1):
                               selections of one query head read half the
@@ -203,7 +204,10 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, 
  * every stage of the last step:
  *   q_rot   fp32   [B][Hq][D]      R_h q_i (canonical chain)
  *   code_q  uint64 [B][Hq][NW]     LHP code of q_i
- *   q_split fp64   [B][Hkv][D][G][2]  (max(q,0), min(q,0)) of q_rot, per dim and head
+ *   q_split fp64   [B][Hkv][D][G][2]  (max(q,0), min(q,0)) of q_rot, per dim and head;
+ *                  with per_head = 1 this region keeps the KV-head layout for
+ *                  interleaved metadata (one pass over a KV head's metadata
+ *                  serves its G selections) and is [B][Hq][D][2] for sign-split
  *   score   fp64   [B][Hkv][NPmax] page score S(p); entries p >= NP(L) unspecified
  *   pages   int32  [B][Hkv][max_keep]  kept pages ascending, -1 padded
  *   n_pages int32  [B][Hkv]
