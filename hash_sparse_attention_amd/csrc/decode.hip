@@ -121,14 +121,8 @@ __global__ __launch_bounds__(BP) void page_bound_kernel(const float* __restrict_
     // One-dimensional grid in (head, sequence, page block) order, head fastest: the workgroups of a
     // (sequence, head) share an XCD with the projection blocks that wrote its query terms and the select
     // blocks that read its scores (workgroups go to the XCDs in turn by linear index).
-    // With per-query-head selection the units of one data head come next in
-    // that order (unit = data head * share + replica), so they run on that
-    // data head's XCD and read its metadata through one L2.
-    int h = (int)(blockIdx.x % (unsigned)Hkv);
-    if (share > 1) {  // block-uniform; the shared-selection prologue keeps its two divisions
-        const unsigned Hd = (unsigned)(Hkv / share);
-        h = (int)((blockIdx.x % Hd) * (unsigned)share + (blockIdx.x / Hd) % (unsigned)share);
-    }
+    // (Per-query-head selection runs this kernel over KV heads with PU set.)
+    const int h = (int)(blockIdx.x % (unsigned)Hkv);
     const int b = (int)((blockIdx.x / (unsigned)Hkv) % (unsigned)nbatch);
     const int64_t pb = blockIdx.x / ((unsigned)Hkv * (unsigned)nbatch);
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -223,9 +217,9 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
     // One-dimensional grid in (head, sequence, page block) order, head fastest: the workgroups of a
     // (sequence, head) share an XCD with the projection blocks that wrote its query terms and the select
     // blocks that read its scores (workgroups go to the XCDs in turn by linear index).
-    // With per-query-head selection the units of one data head come next in
-    // that order (unit = data head * share + replica), so they run on that
-    // data head's XCD and read its metadata through one L2.
+    // With per-query-head selection (each unit reads its own sides) the units
+    // of one data head come next in that order (unit = data head * share +
+    // replica), so they run on that data head's XCD and share its L2.
     int h = (int)(blockIdx.x % (unsigned)Hkv);
     if (share > 1) {  // block-uniform; the shared-selection prologue keeps its two divisions
         const unsigned Hd = (unsigned)(Hkv / share);
