@@ -343,11 +343,10 @@ def workspace_view(dims: Dims, max_keep: int, top_k: int, workspace) -> Workspac
     Hkv = sel_units(dims)  # per-(b, h) rows: query heads with per-query-head selection
     G, NW = Hq // Hkv, dims.hash_bits // 64
     NP = -(-dims.max_ctx // P)
-    # The bound terms keep the per-KV-head layout unless per-query-head selection reads sign-split metadata
-    # (one pass over a KV head's interleaved metadata serves all its query heads).
+    # The bound terms keep the per-KV-head layout, per-query-head selection included (one pass over a KV
+    # head's metadata serves all its query heads).
     Hd = dims.n_kv_heads
-    split_units = Hkv != Hd and dims.meta_layout == HHR_META_SIGN_SPLIT
-    qs_shape = (B, Hkv, D, G, 2) if (Hkv == Hd or split_units) else (B, Hd, D, Hq // Hd, 2)
+    qs_shape = (B, Hd, D, Hq // Hd, 2)
 
     def region(off, dtype, shape):
         n = 1

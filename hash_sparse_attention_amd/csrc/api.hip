@@ -504,7 +504,6 @@ hhr_status hhr_decode_step_append(const hhr_dims* dims, const void* Q, const voi
         p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
         p.n_counters = a.lay.n_clear;
         p.qmean = a.s.ham_mean;
-        p.qs_unit = a.s.share > 1 && a.s.msplit;  // per-unit terms only for the sign-split G = 1 kernel
         HHR_LAUNCH(launch_project(a.sd, p, st), "append + qprep launch", st);
     } else {
         if (max_append > 0)

@@ -203,7 +203,11 @@ __global__ __launch_bounds__(BP) void page_bound_kernel(const float* __restrict_
 // For G = 1 every wave loads the D query terms itself (coalesced, two per
 // lane at D = 128) for the ballots, which also brings them into the XCD's L2,
 // and the sums read them as scalar loads: no LDS and no block barrier.
-template <int D, int G, int U, bool M16, bool PGMIN>
+// PU: as in page_bound_kernel, one pass per data head writes each of the G
+// sums as its own unit's score (per-query-head selection).  Each sum adds
+// both sides of every dimension; the side a head's sign does not pick adds
+// an exact zero, so the bits are those of that head's one-side sum.
+template <int D, int G, int U, bool M16, bool PGMIN, bool PU = false>
 __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __restrict__ meta,
                                                                const double* __restrict__ q_split,
                                                                const int32_t* __restrict__ seq_len,
@@ -217,14 +221,8 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
     // One-dimensional grid in (head, sequence, page block) order, head fastest: the workgroups of a
     // (sequence, head) share an XCD with the projection blocks that wrote its query terms and the select
     // blocks that read its scores (workgroups go to the XCDs in turn by linear index).
-    // With per-query-head selection (each unit reads its own sides) the units
-    // of one data head come next in that order (unit = data head * share +
-    // replica), so they run on that data head's XCD and share its L2.
-    int h = (int)(blockIdx.x % (unsigned)Hkv);
-    if (share > 1) {  // block-uniform; the shared-selection prologue keeps its two divisions
-        const unsigned Hd = (unsigned)(Hkv / share);
-        h = (int)((blockIdx.x % Hd) * (unsigned)share + (blockIdx.x / Hd) % (unsigned)share);
-    }
+    // (Per-query-head selection runs this kernel over KV heads with PU set.)
+    const int h = (int)(blockIdx.x % (unsigned)Hkv);
     const int b = (int)((blockIdx.x / (unsigned)Hkv) % (unsigned)nbatch);
     const int64_t pb = blockIdx.x / ((unsigned)Hkv * (unsigned)nbatch);
     const int64_t bh = (int64_t)b * Hkv + h;
@@ -309,6 +307,11 @@ __global__ __launch_bounds__(256) void page_bound_split_kernel(const float* __re
         sum(B, k + 1);
         asm volatile("" ::: "memory");
     }
+    if constexpr (PU) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) score[(bh * G + i) * NPmax + p] = acc[i] == 0.0 ? 0.0 : acc[i];
+        return;
+    }
     double S = acc[0];  // the group's max, or its min (a variant)
 #pragma unroll
     for (int i = 1; i < G; ++i) S = PGMIN ? (acc[i] < S ? acc[i] : S) : (acc[i] > S ? acc[i] : S);
@@ -340,17 +343,20 @@ hipError_t bounds_g(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Per-query-head selection on interleaved metadata: one pass per data head
-// (G = the units per data head), each unit's score written separately.
+// Per-query-head selection: one pass per data head (G = the units per data
+// head), each unit's score written separately.
 template <int D, int G>
 hipError_t bounds_units(const DecodeArgs& a, hipStream_t st) {
     const Shape& s = a.s;
     const int Hd = s.Hkv / G;  // data heads (s.Hkv counts the units)
     constexpr int BP16 = bound_block_pages<D, G, true>(), BP32 = bound_block_pages<D, G, false>();
-    const int bp = s.meta16 ? BP16 : BP32;
+    const int bp = s.msplit ? 256 : (s.meta16 ? BP16 : BP32);
     const dim3 grid((unsigned)(((s.NPmax + bp - 1) / bp) * Hd * s.B));
     auto kern = s.meta16 ? page_bound_kernel<D, G, 8, true, false, BP16, true>
                          : page_bound_kernel<D, G, 4, false, false, BP32, true>;
+    if (s.msplit)  // both sides of 8 dimensions a batch, as for a shared selection
+        kern = s.meta16 ? page_bound_split_kernel<D, G, 8, true, false, true>
+                        : page_bound_split_kernel<D, G, 8, false, false, true>;
     hipLaunchKernelGGL(kern, grid, dim3(bp), 0, st, a.meta, reinterpret_cast<const double*>(a.ws + a.lay.q_split),
                        a.seq_len, reinterpret_cast<double*>(a.ws + a.lay.score), Hd, s.T, s.P, s.NPB, s.NPmax, 1,
                        s.B);
@@ -359,7 +365,7 @@ hipError_t bounds_units(const DecodeArgs& a, hipStream_t st) {
 
 template <int D>
 hipError_t bounds_d(const DecodeArgs& a, hipStream_t st) {
-    if (a.s.share > 1 && !a.s.msplit) {
+    if (a.s.share > 1) {
         switch (a.s.share) {
             case 2: return bounds_units<D, 2>(a, st);
             case 3: return bounds_units<D, 3>(a, st);
@@ -397,7 +403,6 @@ hipError_t launch_qprep(const DecodeArgs& a, hipStream_t st) {
     p.counters = reinterpret_cast<uint32_t*>(a.ws + a.lay.counters);
     p.n_counters = a.lay.n_clear;
     p.qmean = a.s.ham_mean;
-    p.qs_unit = a.s.share > 1 && a.s.msplit;  // per-unit terms only for the sign-split G = 1 kernel
     return launch_project(a.sd, p, st);  // per KV head of the cache
 }
 

@@ -125,7 +125,6 @@ struct ProjectArgs {
     uint32_t* counters;
     int n_counters;
     bool qmean;    // also code the group's mean query into code_qm (queries only)
-    bool qs_unit;  // q_split per query head [B][Hq][D][1][2] (per-query-head selection)
 };
 // Appends of at most this many keys per sequence go through the projection kernel.
 constexpr int kAppendMax = 64;

@@ -74,12 +74,13 @@
  *         meta_layout HHR_META_SIGN_SPLIT (either dtype): [B][Hkv][NPB][D][2][64],
  *         dimension-major: for page block blk, dimension d and side s (0 =
  *         max, 1 = min) the 64 pages' values are one contiguous run (256 B
- *         fp32, 128 B bf16).  A selection of one query head (G = 1, or
- *         per_head = 1) then reads, per dimension, only the side the sign of
- *         its rotated query coordinate picks -- half the metadata bytes --
- *         with the same bound bit for bit (the side not read contributes an
- *         exact zero).  Grouped selections read both sides.  Same byte count
- *         as the interleaved layout.
+ *         fp32, 128 B bf16).  With one query head per KV head (G = 1)
+ *         the bound pass then reads, per dimension, only the side the sign
+ *         of the rotated query coordinate picks -- half the metadata bytes
+ *         -- with the same bound bit for bit (the side not read contributes
+ *         an exact zero).  Grouped heads, per_head = 1 included (one pass
+ *         per KV head serves its G query heads), read both sides.  Same
+ *         byte count as the interleaved layout.
  *   out   [B][Hq][D] fp32
  *   sel_idx [B][U][top_k + sink_tokens + local_window] int32, U = Hkv (or Hq
  *         with per_head = 1): the selected key positions, ascending, padded
@@ -163,7 +164,7 @@ typedef struct {
                               aside: see the workspace layout)             */
     int32_t meta_layout;   /* hhr_meta_layout of the page metadata: HHR_META_INTERLEAVED
                               (0, the default) or HHR_META_SIGN_SPLIT (1):
-                              selections of one query head read half the
+                              with G = 1 the bound pass reads half the
                               metadata bytes; encode and decode must agree */
 } hhr_dims;
 
@@ -205,9 +206,8 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, int32_t max_keep_pages, 
  *   q_rot   fp32   [B][Hq][D]      R_h q_i (canonical chain)
  *   code_q  uint64 [B][Hq][NW]     LHP code of q_i
  *   q_split fp64   [B][Hkv][D][G][2]  (max(q,0), min(q,0)) of q_rot, per dim and head;
- *                  with per_head = 1 this region keeps the KV-head layout for
- *                  interleaved metadata (one pass over a KV head's metadata
- *                  serves its G selections) and is [B][Hq][D][2] for sign-split
+ *                  with per_head = 1 this region keeps the KV-head layout
+ *                  (one pass over a KV head's metadata serves its G selections)
  *   score   fp64   [B][Hkv][NPmax] page score S(p); entries p >= NP(L) unspecified
  *   pages   int32  [B][Hkv][max_keep]  kept pages ascending, -1 padded
  *   n_pages int32  [B][Hkv]
