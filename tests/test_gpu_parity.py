@@ -586,6 +586,10 @@ PER_HEAD = [
     ("g4_per_head_mean_min_fp32", Workload("ph3", 182, 2, 8, 2, 64, 1500, 8, 128, 15, 90, "fp32",
                                            ragged=(700, 1500), per_head=True, page_group=1, hamming_group=1)),
     ("llama8b_32k_per_head", WORKLOADS["llama8b_32k"].with_(per_head=True)),
+    # one bound pass per KV head writes its query heads' bounds: more group sizes of that pass
+    ("g2_per_head_p4_ragged", Workload("ph4", 183, 2, 4, 2, 128, 1200, 4, 128, 20, 80, "bf16", ragged=(600, 1200),
+                                       per_head=True)),
+    ("g3_per_head_d64_fp32", Workload("ph5", 184, 1, 6, 2, 64, 2000, 16, 64, 10, 100, "fp32", per_head=True)),
 ]
 
 
@@ -657,8 +661,9 @@ def test_decode_parity_paths(dev, name, wl):
     compare(wl, d["seq_len"], g, o, label=name)
 
 
-# Sign-split page metadata: encode and append write it, the bound kernel reads one side per dimension for
-# selections of one query head (G = 1, or per-query-head selection) and both sides for grouped selections.
+# Sign-split page metadata: encode and append write it, the bound kernel reads one side per dimension when a
+# KV head has one query head (G = 1), and both sides for grouped heads, per-query-head selection included
+# (one pass per KV head).
 SPLIT_SHAPES = [
     ("mha_g1_bf16", Workload("ms1", 190, 2, 4, 4, 128, 3000, 16, 128, 10, 200, "bf16", outliers=2,
                              ragged=(1000, 3000), meta_split=True)),
@@ -672,6 +677,10 @@ SPLIT_SHAPES = [
                                              meta_split=True, meta_bf16=True, page_group=1)),
     ("mha_g1_p1_sinks", Workload("ms6", 195, 2, 3, 3, 64, 700, 1, 64, 20, 50, "bf16", ragged=(1, 700),
                                  meta_split=True, sink_tokens=2, local_window=9)),
+    ("per_head_g8_d64_bf16meta", Workload("ms7", 197, 2, 16, 2, 64, 2500, 32, 64, 20, 120, "fp32",
+                                          ragged=(900, 2500), per_head=True, meta_split=True, meta_bf16=True)),
+    ("per_head_g2_ragged", Workload("ms8", 198, 3, 4, 2, 128, 1800, 8, 128, 15, 100, "bf16", ragged=(1, 1800),
+                                    per_head=True, meta_split=True)),
 ]
 
 
