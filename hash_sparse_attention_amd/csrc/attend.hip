@@ -571,7 +571,15 @@ __global__ __launch_bounds__(kCompactThreads) __attribute__((amdgpu_waves_per_eu
 
     // Same grid order as the select kernels, (Hkv, B, S): a block lands on the XCD whose L2 holds the
     // slots and histograms the select block of the same (head, split) wrote.
-    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+    const int b = blockIdx.y, split = blockIdx.z;
+    // Per-query-head selection: the units of one data head take the grid
+    // slots of that head's XCD (workgroups go to the XCDs in turn), where its
+    // page-bound pass left their scores.
+    int h = blockIdx.x;
+    if (share > 1) {  // block-uniform
+        const unsigned Hd = (unsigned)(Hkv / share);
+        h = (int)((blockIdx.x % Hd) * (unsigned)share + blockIdx.x / Hd);
+    }
     const int tid = threadIdx.x, lane = tid & 63, sub = lane & 15, rw = tid >> 4;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t q0 = (int64_t)b * Hq + (int64_t)h * G;

@@ -905,7 +905,15 @@ __global__ __launch_bounds__(kSelThreads) void select_fast_kernel(
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
     int max_keep, int top_k, int nsink, int window, int share) {
     __shared__ SelShared sh;
-    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+    const int b = blockIdx.y, split = blockIdx.z;
+    // Per-query-head selection: the units of one data head take the grid
+    // slots of that head's XCD (workgroups go to the XCDs in turn), where its
+    // page-bound pass left their scores.
+    int h = blockIdx.x;
+    if (share > 1) {  // block-uniform
+        const unsigned Hd = (unsigned)(Hkv / share);
+        h = (int)((blockIdx.x % Hd) * (unsigned)share + blockIdx.x / Hd);
+    }
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     const double* scp = score + bh * NPmax;
