@@ -778,7 +778,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
     int max_keep, int top_k, int nsink, int window, int share) {
     __shared__ SelShared sh;
-    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+    const int b = blockIdx.y, split = blockIdx.z;
+    // Per-query-head selection: a KV head's units on its XCD (as the select kernels).
+    int h = blockIdx.x;
+    if (share > 1) {  // block-uniform
+        const unsigned Hd = (unsigned)(Hkv / share);
+        h = (int)((blockIdx.x % Hd) * (unsigned)share + blockIdx.x / Hd);
+    }
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     uint64_t pre[kRun];  // unused here: the general page select loads its chunks itself
@@ -828,7 +834,13 @@ __global__ __launch_bounds__(kSelThreads) void select_split_kernel(
     float* __restrict__ part_ml, int pstride, int D, int S, int G, int Gh, int Hq, int Hkv, int T, int P, int64_t NPmax,
     int max_keep, int top_k, int nsink, int window, int share) {
     __shared__ SplitShared sh;
-    const int h = blockIdx.x, b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
+    const int b = blockIdx.y, split = blockIdx.z, tid = threadIdx.x;
+    // Per-query-head selection: a KV head's units on its XCD (as the select kernels).
+    int h = blockIdx.x;
+    if (share > 1) {  // block-uniform
+        const unsigned Hd = (unsigned)(Hkv / share);
+        h = (int)((blockIdx.x % Hd) * (unsigned)share + blockIdx.x / Hd);
+    }
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t bhd = data_head(b, h, Hkv, share);  // the unit's data head
     const int NBINS = Gh * NW * 64 + 1;
